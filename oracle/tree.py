@@ -1,0 +1,126 @@
+"""Tree metadata, written out plainly (test infrastructure only).
+
+What it follows:
+
+* Decoding-extensions glossary ("Beam Search、约束解码与 Tree/Self
+  Speculation"), section "Packed tree attention": unique nodes are packed in
+  topological order; each node has a token, a parent, a depth and a position
+  id; a node sees the whole committed prefix and its own ancestor chain (self
+  included), never siblings or cousins; siblings share a position, and the
+  packed index is never used as the position.
+* Same page, packed-vs-branch experiment: depth by walking the parent chain,
+  ancestor path by walking it and reversing.  The page counts depth from 1 and
+  uses position = prefix + depth - 1; here depth counts from 0 (a node hanging
+  off the committed prefix has depth 0) and position = context + depth, which
+  is the same position.
+* "02 · Token Tree 与 Tree Attention", section 3: positions are context length
+  plus tree depth (depths [0,1,1,2] with a 7-token prompt give [7,8,8,9]); the
+  mask is kept QLEN-only / bit-packed; retrieve_index, retrieve_next_token and
+  retrieve_next_sibling are the indices used to walk the tree after verify.
+
+Readings where the pages leave the step open:
+
+* next_token[i] is i's first child (smallest index j with parent[j] == i),
+  next_sibling[i] the next child of i's parent after i; -1 when none.
+* retrieve_index[i] is the global logits row of node i: request b's rows start
+  at node_offsets[b] + b, row 0 of a request is the last committed token and
+  row 1 + i belongs to node i.
+* Mask rows are uint32 words, bit j % 32 of word j // 32 (LSB first), row
+  stride ``mask_words``, unused bits zero.  Context columns are always visible
+  and are not stored.
+* Error bits per request: 1 = a parent outside [-1, i-1]; 2 = more nodes than
+  ``n_max``.  A flagged request's outputs are left as zeros here and are not
+  compared.
+"""
+
+from typing import Dict, List
+
+import numpy as np
+
+ERR_BAD_PARENT = 1
+ERR_TOO_MANY_NODES = 2
+
+
+def parents_valid(parents) -> bool:
+    """Topological packing: every parent is -1 or an earlier node."""
+    return all(-1 <= int(p) < i for i, p in enumerate(parents))
+
+
+def depth_of(node: int, parents) -> int:
+    """Number of ancestors of ``node`` (0 for a node hanging off the context)."""
+    d, cur = 0, int(parents[node])
+    while cur != -1:
+        d += 1
+        cur = int(parents[cur])
+    return d
+
+
+def ancestor_path(node: int, parents) -> List[int]:
+    """Nodes from the top of the tree down to ``node`` (inclusive)."""
+    path = []
+    cur = int(node)
+    while cur != -1:
+        path.append(cur)
+        cur = int(parents[cur])
+    return path[::-1]
+
+
+def build_request(parents, ctx_len: int) -> Dict[str, object]:
+    """Metadata of one request's tree (local node indices)."""
+    parents = [int(p) for p in parents]
+    n = len(parents)
+    depth = [depth_of(i, parents) for i in range(n)]
+    positions = [int(ctx_len) + d for d in depth]
+    visible = [ancestor_path(i, parents) for i in range(n)]
+    next_token, next_sibling = [], []
+    for i in range(n):
+        kids = [j for j in range(n) if parents[j] == i]
+        next_token.append(kids[0] if kids else -1)
+        later = [j for j in range(i + 1, n) if parents[j] == parents[i]]
+        next_sibling.append(later[0] if later else -1)
+    return dict(depth=depth, positions=positions, visible=visible,
+                next_token=next_token, next_sibling=next_sibling)
+
+
+def build(parents_all, node_offsets, ctx_lens, n_max: int, mask_words: int) -> Dict[str, np.ndarray]:
+    """Batched metadata in the layout the C ABI returns.
+
+    Returns int32 arrays ``depth``, ``positions``, ``retrieve_index``,
+    ``retrieve_next_token``, ``retrieve_next_sibling`` of length T, uint32
+    ``mask`` [T, mask_words] and int32 ``err`` [B].
+    """
+    node_offsets = np.asarray(node_offsets)
+    B = len(node_offsets) - 1
+    T = int(node_offsets[-1])
+    out = {k: np.zeros(T, dtype=np.int32) for k in
+           ("depth", "positions", "retrieve_index", "retrieve_next_token", "retrieve_next_sibling")}
+    out["mask"] = np.zeros((T, mask_words), dtype=np.uint32)
+    out["err"] = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        s, e = int(node_offsets[b]), int(node_offsets[b + 1])
+        par = [int(p) for p in parents_all[s:e]]
+        if e - s > n_max:
+            out["err"][b] |= ERR_TOO_MANY_NODES
+        if not parents_valid(par):
+            out["err"][b] |= ERR_BAD_PARENT
+        if out["err"][b]:
+            continue
+        md = build_request(par, int(ctx_lens[b]))
+        for i in range(e - s):
+            out["depth"][s + i] = md["depth"][i]
+            out["positions"][s + i] = md["positions"][i]
+            out["retrieve_index"][s + i] = s + b + 1 + i
+            out["retrieve_next_token"][s + i] = md["next_token"][i]
+            out["retrieve_next_sibling"][s + i] = md["next_sibling"][i]
+            for j in md["visible"][i]:
+                out["mask"][s + i, j // 32] |= np.uint32(1 << (j % 32))
+    return out
+
+
+def mask_bool(mask_rows: np.ndarray, n: int) -> np.ndarray:
+    """Unpack n bit-packed mask rows into a dense [n, n] bool matrix."""
+    dense = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        for j in range(n):
+            dense[i, j] = bool((int(mask_rows[i, j // 32]) >> (j % 32)) & 1)
+    return dense

@@ -1,0 +1,134 @@
+"""Pins of the tree-metadata oracle against the pages and brute force."""
+
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import tree as T
+from conftest import golden
+
+
+def test_packed_table_pin():
+    g = golden("packed_table.json")
+    md = T.build_request(g["parents"], g["prefix_length"])
+    assert [d + 1 for d in md["depth"]] == g["depth_one_based"]
+    assert md["positions"] == g["positions"]
+    assert md["visible"] == g["visible_candidate_ancestors"]
+    assert [len(v) + g["prefix_length"] for v in md["visible"]] == g["tree_mask_visible_counts_with_prefix"]
+    # Bit-packed rows carry the same sets.
+    out = T.build(np.array(g["parents"]), np.array([0, 8]), np.array([g["prefix_length"]]), 8, 1)
+    dense = T.mask_bool(out["mask"], 8)
+    for i, vis in enumerate(g["visible_candidate_ancestors"]):
+        assert sorted(np.nonzero(dense[i])[0].tolist()) == vis
+    assert (dense.sum(1) + g["prefix_length"]).tolist() == g["tree_mask_visible_counts_with_prefix"]
+
+
+def test_branch_dedup_counts():
+    g = golden("packed_table.json")
+    prefixes = {tuple(br[:d]) for br in g["branches"] for d in range(1, len(br) + 1)}
+    assert sum(len(br) for br in g["branches"]) == g["branch_expanded_nodes"]
+    assert len(prefixes) == g["unique_tree_nodes"] == len(g["parents"])
+    # Each unique prefix is exactly one packed node: token path from the root.
+    toks, par = g["tokens"], g["parents"]
+    paths = {tuple(toks[j] for j in T.ancestor_path(i, par)) for i in range(len(par))}
+    assert paths == prefixes
+
+
+def test_positions_pin():
+    g = golden("positions_example.json")
+    md = T.build_request([-1, 0, 0, 1], g["prompt_length"])
+    assert md["depth"] == g["depths"]
+    assert md["positions"] == g["positions"]
+
+
+def test_medusa_counts_pin():
+    import synth
+    g = golden("medusa_counts.json")
+    for case in g["cases"]:
+        par = synth.medusa_tree(case["tops"])
+        md = T.build_request(par, 0)
+        assert len(par) == case["nodes"]
+        leaves = sum(1 for x in md["next_token"] if x == -1)
+        assert leaves == case["paths"]
+        # Closed form of the page: sum_k prod_{i<=k} s_i nodes, prod s_i paths.
+        assert case["nodes"] == sum(int(np.prod(case["tops"][:k + 1])) for k in range(len(case["tops"])))
+        assert case["paths"] == int(np.prod(case["tops"]))
+
+
+def _closure(parents):
+    """Reflexive-transitive closure of the child->parent relation by boolean matrix powers."""
+    n = len(parents)
+    A = np.zeros((n, n), dtype=np.int64)
+    for i, p in enumerate(parents):
+        if p >= 0:
+            A[i, p] = 1
+    R = np.eye(n, dtype=np.int64)
+    P = np.eye(n, dtype=np.int64)
+    for _ in range(n):
+        P = (P @ A > 0).astype(np.int64)
+        R = R | P
+    return R.astype(bool)
+
+
+def _all_parent_lists(n):
+    return itertools.product(*[range(-1, i) for i in range(n)])
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7])
+def test_bruteforce_all_trees(n):
+    for parents in _all_parent_lists(n):
+        parents = list(parents)
+        ctx = 5
+        out = T.build(np.array(parents), np.array([0, n]), np.array([ctx]), n, 1)
+        assert out["err"][0] == 0
+        dense = T.mask_bool(out["mask"], n)
+        R = _closure(parents)
+        assert np.array_equal(dense, R)
+        # Depth is the number of strict ancestors; positions follow it.
+        assert out["depth"].tolist() == (R.sum(1) - 1).tolist()
+        assert out["positions"].tolist() == (ctx + R.sum(1) - 1).tolist()
+        # First child / next sibling from a sort of (parent, index) pairs.
+        order = sorted(range(n), key=lambda j: (parents[j], j))
+        first_child = [-1] * n
+        next_sib = [-1] * n
+        for a, b in zip(order, order[1:]):
+            if parents[a] == parents[b]:
+                next_sib[a] = b
+        for j in reversed(order):
+            if parents[j] >= 0:
+                first_child[parents[j]] = j
+        assert out["retrieve_next_token"].tolist() == first_child
+        assert out["retrieve_next_sibling"].tolist() == next_sib
+        # Rows of the logits: request 0 starts at row 0, node i at row 1 + i.
+        assert out["retrieve_index"].tolist() == [1 + i for i in range(n)]
+
+
+def test_unused_mask_bits_zero_and_stride():
+    par = list(range(-1, 39))  # a 40-node chain
+    out = T.build(np.array(par), np.array([0, 40]), np.array([3]), 64, 3)
+    assert out["mask"].shape == (40, 3)
+    assert (out["mask"][:, 2] == 0).all()
+    dense = T.mask_bool(out["mask"], 40)
+    assert np.array_equal(dense, np.tril(np.ones((40, 40), dtype=bool)))
+
+
+def test_error_bits():
+    # bad parent (>= i) in request 0, too many nodes in request 1, request 2 fine
+    parents = [-1, 1, -1, 0, 1, -1, 0]
+    offs = [0, 2, 5, 7]
+    out = T.build(np.array(parents), np.array(offs), np.array([1, 1, 1]), 2, 1)
+    assert out["err"][0] & T.ERR_BAD_PARENT
+    assert out["err"][1] & T.ERR_TOO_MANY_NODES
+    assert out["err"][2] == 0
+    out2 = T.build(np.array([-2]), np.array([0, 1]), np.array([0]), 4, 1)
+    assert out2["err"][0] & T.ERR_BAD_PARENT
+
+
+def test_empty_request_and_retrieve_rows():
+    parents = [-1, 0, -1, -1, 1]
+    offs = [0, 2, 2, 5]      # request 1 is empty
+    out = T.build(np.array(parents), np.array(offs), np.array([4, 9, 0]), 3, 1)
+    assert out["err"].tolist() == [0, 0, 0]
+    assert out["retrieve_index"].tolist() == [1, 2, 5, 6, 7]
+    assert out["positions"].tolist() == [4, 5, 0, 0, 1]
