@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of one token-tree verification round on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+tree_build -> tree_attention_verify (one layer) -> tree_greedy_accept ->
+tree_kv_commit (plus, for paged caches, restoring the block table that the
+previous round's commit released, i.e. re-mapping the tentative blocks).
+
+Default workload: an EAGLE-style 64-node tree (depth 6, top-4 expansion,
+reranked), batch 1, committed context 4096, 32 query / 8 KV heads, head_dim
+128, bf16 K/V/Q, vocab 128256 bf16 logits, contiguous cache.  ``--workload``
+selects the other shapes (tiny_medusa, batched, ddtree, medusa_long,
+ddtree_deep).
+
+Inputs are uploaded before timing and rotated over enough copies (> 512 MB)
+that each step reads cold HBM rather than the 256 MB Infinity Cache.  W
+warm-up steps, then K timed steps between two synchronisations; the
+attention call is additionally bracketed by HIP events on its stream.
+
+Prints ONE JSON line: throughput in verified tree tokens/s (tree nodes per
+second), ms and us per step, the attention roofline (algorithmic bytes per
+call / measured call time, against 8 TB/s HBM), and the CPU oracle's rate on
+a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified tree tokens/sec + µs/verify step at 1 GPU; % of HBM roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+WORKLOADS = {
+    "tiny_medusa": 0, "eagle": 1, "batched": 2, "ddtree": 3, "medusa_long": 4, "ddtree_deep": 5,
+}
+
+
+def describe(wl):
+    import numpy as np
+    n = np.diff(wl.node_offsets)
+    return {
+        "workload": wl.name,
+        "batch": int(wl.batch),
+        "tree_nodes_total": int(wl.total_nodes),
+        "tree_nodes_per_request": [int(n.min()), int(n.max())],
+        "ctx_tokens": [int(wl.ctx_lens.min()), int(wl.ctx_lens.max())],
+        "heads_q_kv_dim": [wl.n_heads, wl.n_kv_heads, wl.head_dim],
+        "vocab": wl.vocab,
+        "logits_dtype": wl.logits_dtype,
+        "kv_layout": wl.layout,
+        "rope_base": wl.rope_base,
+    }
+
+
+def algorithmic(wl):
+    """Algorithmic bytes and flops of one attention call and one accept call."""
+    import numpy as np
+    D, Hq, Hkv = wl.head_dim, wl.n_heads, wl.n_kv_heads
+    W = max(1, (wl.n_max + 31) // 32)
+    attn_bytes = 0
+    flops = 0
+    for b in range(wl.batch):
+        s, e = int(wl.node_offsets[b]), int(wl.node_offsets[b + 1])
+        n, ctx = e - s, int(wl.ctx_lens[b])
+        attn_bytes += ctx * Hkv * D * 4          # context K + V (bf16)
+        attn_bytes += n * Hq * D * 4             # Q in + O out
+        attn_bytes += n * Hkv * D * 8            # k/v_new in + tentative K/V out
+        attn_bytes += n * W * 4 + n * 4          # mask rows + positions
+        par = wl.parents[s:e]
+        depth = np.zeros(n, np.int64)
+        for i in range(n):
+            depth[i] = 0 if par[i] < 0 else depth[par[i]] + 1
+        flops += int(4 * D * Hq * np.sum(ctx + depth + 1))
+    esz = 4 if wl.logits_dtype == "fp32" else 2
+    accept_bytes = (wl.total_nodes + wl.batch) * wl.vocab * esz
+    return attn_bytes, flops, accept_bytes
+
+
+def cpu_baseline(wl, budget_s):
+    """Time the oracle on a bounded sample: whole requests' verify rounds."""
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle import accept as O_acc
+    from oracle import attention as O_att
+    from oracle import bf16 as O_bf16
+    from oracle import tree as O_tree
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    cores = min(len(os.sched_getaffinity(0)), max(1, blas_threads))
+    t0 = time.perf_counter()
+    nodes_done = 0
+    reqs_done = 0
+    for b in range(wl.batch):
+        s, e = int(wl.node_offsets[b]), int(wl.node_offsets[b + 1])
+        n, ctx = e - s, int(wl.ctx_lens[b])
+        sl = slice(s, e)
+        O_tree.build(wl.parents[sl], np.array([0, n]), np.array([ctx]), max(1, n), max(1, (n + 31) // 32))
+        kc, vc = O_att.context_of(wl.k_cache, wl.v_cache, b, ctx, wl.layout, wl.block_table)
+        # attention for as many nodes as the time budget allows (at least one)
+        done_nodes = 0
+        for i in range(n):
+            O_att.attention_request(wl.q[sl], wl.k_new[sl], wl.v_new[sl], kc, vc, wl.parents[sl], ctx,
+                                    nodes=[i])
+            done_nodes += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        rows = wl.logits[s + b: e + b + 1]
+        rows = O_bf16.to_f64(rows) if wl.logits_dtype == "bf16" else rows.astype(np.float64)
+        choice = O_acc.row_argmax(rows)
+        O_acc.greedy_walk(choice, wl.tokens[sl], wl.parents[sl], 64)
+        nodes_done += done_nodes
+        reqs_done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": nodes_done / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nodes_done} tree nodes of {reqs_done} request(s): float64 oracle build, "
+                      f"per-node path attention, argmax+walk of those requests ({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="eagle", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--rotate-mb", type=float, default=600.0,
+                    help="rotate input copies until this many MB are in play (defeats the MALL)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the verification path "
+              f"has no multi-GPU mode in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import token_tree_attention_amd as tta
+    from synth.device import to_device
+    from token_tree_attention_amd.step import VerifyStep
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    tta.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = WORKLOADS[args.workload]
+    wl = synth.make_workload(cfg, args.seed)
+    base = to_device(wl, dev)
+    per_set = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
+    n_sets = int(max(1, min(64, np.ceil(args.rotate_mb * 1e6 / per_set))))
+    free = torch.cuda.mem_get_info()[0]
+    n_sets = int(max(1, min(n_sets, (free * 0.6) // max(1, per_set))))
+    sets = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()} for _ in range(n_sets - 1)]
+    steps = []
+    pristine_tables = []
+    for d in sets:
+        bt = tta.Batch(d["node_offsets"], d["ctx_lens"], wl.n_max, total_nodes=wl.total_nodes)
+        cache = tta.KVCache(d["k_cache"], d["v_cache"], d["block_table"])
+        steps.append((d, VerifyStep(bt, cache, wl.n_heads, wl.vocab, max_accept=64)))
+        pristine_tables.append(None if d["block_table"] is None else d["block_table"].clone())
+    stream = torch.cuda.current_stream()
+
+    def run(i, ev=None):
+        d, st = steps[i % n_sets]
+        if pristine_tables[i % n_sets] is not None:
+            d["block_table"].copy_(pristine_tables[i % n_sets], non_blocking=True)
+        st.build(d["parents"])
+        if ev is not None:
+            ev[0].record(stream)
+        st.attention(d["q"], d["k_new"], d["v_new"])
+        if ev is not None:
+            ev[1].record(stream)
+        st.accept(d["logits"], d["tokens"])
+        st.commit()
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    errs = steps[0][1].meta["err"].cpu().numpy()
+    if (errs != 0).any():
+        print(f"device error bits after warm-up: {errs.tolist()}", file=sys.stderr)
+        sys.exit(1)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        run(args.warmup + k, evs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    attn_bytes, flops, accept_bytes = algorithmic(wl)
+    acc_len = steps[0][1].acc["accept_len"].cpu().numpy()
+    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": wl.total_nodes / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "us_per_step": ms_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": describe(wl),
+        "roofline": {
+            "kernel": "tree_attention_verify (prep + main + combine launches, HIP events on its stream)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "algorithmic_bytes": attn_bytes,
+            "attention_us": attn_ms * 1e3,
+            "attention_tflops": flops / (attn_ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (attn_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        },
+        "accept_len_hist": np.bincount(acc_len).tolist(),
+        "input_sets_rotated": n_sets,
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,258 @@
+/*
+ * treeverify.h -- C ABI of the MI355X (gfx950) token-tree verification path.
+ *
+ * One verification round of tree speculative decoding, as four calls:
+ *
+ *   tree_build             parent list -> ancestor mask, depths, positions,
+ *                          retrieve / next-token / next-sibling indices
+ *   tree_attention_verify  one attention layer over committed KV + ancestors
+ *   tree_greedy_accept     vocab argmax per node + greedy walk from the root
+ *   tree_kv_commit         move accepted K/V into place, release the rest
+ *
+ * Pages that define the operations (cited by title and section):
+ *   [GLOSSARY] "Beam Search、约束解码与 Tree/Self Speculation"
+ *              (llm-glossary.tokens-kit.com, decoding extensions): sections
+ *              "Tree/Self Speculation", "Packed tree attention", the
+ *              packed-vs-branch experiment and the verify_tree experiment.
+ *   [ESSAY]    "投机解码的树状注意力验证" (wiblog.cn): custom attention mask;
+ *              KV cache and batching constraints.
+ *   [ATLAS]    "02 · Token Tree 与 Tree Attention" (llm-infra-atlas): §2 token
+ *              tree, §3 mask rules and build_tree_kernel_efficient I/O, §4
+ *              verify flow and KV release.
+ *   [DDTREE]   "Accelerating Speculative Decoding with Block Diffusion Draft
+ *              Trees" notes: §6 worked example, §7 tree attention and walk.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer inside a call is a DEVICE pointer unless stated otherwise;
+ *   the ttv_batch / ttv_kv_cache structs themselves live in host memory and
+ *   are read during the call only.
+ * - Requests: B requests; request b owns nodes node_offsets[b] ..
+ *   node_offsets[b+1]-1 of every per-node array (T = node_offsets[B] nodes in
+ *   all).  Node indices inside a request are local (0 .. N_b-1).
+ * - Trees are packed in topological order: parent[i] is -1 (the node hangs off
+ *   the committed context) or a local index < i ([GLOSSARY] "Packed tree
+ *   attention"; [ESSAY] mask section: level order or depth-first order).
+ * - Logits rows: request b owns rows node_offsets[b] + b ... (N_b + 1 rows);
+ *   its row 0 is the target's prediction at the last committed token (the
+ *   walk's root) and row 1 + i the prediction after node i.
+ * - bf16 is the upper half of an IEEE float32 (uint16 storage).
+ * - Ownership: the caller allocates every buffer, including workspaces.  The
+ *   library allocates nothing, frees nothing, keeps no state between calls
+ *   and keeps no pointer once the call returns.  Calls are asynchronous on
+ *   the given stream, reentrant and thread-safe.
+ * - Host-level errors: the return value is TTV_OK, or TTV_EINVAL (a null
+ *   pointer, a size out of range, an unsupported head_dim / head ratio /
+ *   dtype / layout; nothing is launched), TTV_ENOSPC (workspace too small;
+ *   nothing launched) or TTV_EHIP (a launch failed).
+ * - Device-level errors: err[B] (int32, device).  tree_build WRITES err[b];
+ *   the later calls OR bits into it.  A flagged request's outputs are
+ *   undefined; the other requests are unaffected.  The caller reads err
+ *   after its single synchronisation.
+ */
+#ifndef TREEVERIFY_H
+#define TREEVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TTV_API __attribute__((visibility("default")))
+
+/* Host return codes. */
+#define TTV_OK      0
+#define TTV_EINVAL -1
+#define TTV_EHIP   -2
+#define TTV_ENOSPC -3
+
+/* Device error bits in err[b]. */
+#define TTV_ERR_BAD_PARENT      1   /* a parent outside [-1, i-1] */
+#define TTV_ERR_TOO_MANY_NODES  2   /* N_b > n_max, or node_offsets not non-decreasing */
+#define TTV_ERR_CAPACITY        4   /* ctx_b + N_b beyond the cache (capacity / mapped blocks) */
+#define TTV_ERR_BLOCK_TABLE     8   /* a needed block-table entry is -1 or >= num_blocks */
+#define TTV_ERR_ACCEPT          16  /* the walk would exceed max_accept, or commit got a bad path */
+#define TTV_ERR_BAD_LENGTH      32  /* ctx_lens[b] < 0 */
+
+/* Limits. */
+#define TTV_MAX_TREE_NODES 1024     /* N_b <= 1024, so mask rows need <= 32 words */
+#define TTV_BLOCK_SIZE     16       /* paged cache block size (tokens) */
+
+/* Logits dtypes. */
+#define TTV_DTYPE_FP32 0
+#define TTV_DTYPE_BF16 1
+
+/* KV cache layouts. */
+#define TTV_KV_CONTIGUOUS 0         /* k, v: bf16 [B, n_kv_heads, capacity, head_dim] */
+#define TTV_KV_PAGED      1         /* k, v: bf16 [num_blocks, n_kv_heads, block_size, head_dim] */
+
+typedef struct ttv_batch {
+    int32_t batch;                  /* B >= 0 */
+    int32_t n_max;                  /* host bound on N_b, 0 .. TTV_MAX_TREE_NODES */
+    int64_t total_nodes;            /* T = node_offsets[B] (host copy) */
+    const int32_t* node_offsets;    /* device int32 [B+1], node_offsets[0] = 0, non-decreasing */
+    const int32_t* ctx_lens;        /* device int32 [B], committed tokens per request */
+} ttv_batch;
+
+typedef struct ttv_kv_cache {
+    void* k;                        /* device bf16, layout below */
+    void* v;                        /* device bf16, same layout as k */
+    int32_t layout;                 /* TTV_KV_CONTIGUOUS or TTV_KV_PAGED */
+    int32_t n_kv_heads;             /* Hkv >= 1 */
+    int32_t head_dim;               /* D: 64 or 128 */
+    int32_t capacity;               /* contiguous: slots per request (>= max ctx_b + N_b) */
+    int32_t* block_table;           /* paged: device int32 [B, max_blocks]; logical block j of
+                                       request b is physical block block_table[b*max_blocks + j];
+                                       -1 = unmapped.  tree_kv_commit writes -1 into released
+                                       entries. */
+    int32_t max_blocks;             /* paged: columns of block_table */
+    int32_t block_size;             /* paged: must be TTV_BLOCK_SIZE */
+    int32_t num_blocks;             /* paged: physical blocks in the pool */
+} ttv_kv_cache;
+
+/* Library version (major*10000 + minor*100 + patch). */
+TTV_API int32_t ttv_version(void);
+
+/* Short description of a TTV_* return code (static string). */
+TTV_API const char* ttv_status_string(int32_t status);
+
+/*
+ * tree_build -- flatten each request's draft tree ([GLOSSARY] "Packed tree
+ * attention" node table; [ATLAS] §3 build_tree_kernel_efficient outputs).
+ *
+ * in : parents      int32 [T]   local parent of every node (-1 = off the context)
+ * out: mask         uint32 [T, mask_words]; bit (j % 32) of word (j / 32) of
+ *                   node i's row is set iff local node j is i or an ancestor
+ *                   of i (ancestor-only visibility, self included).  The
+ *                   committed context is always visible and not stored
+ *                   (QLEN-only form).  Unused bits are 0.
+ *                   mask_words >= ceil(n_max / 32).
+ *      depth        int32 [T]   0 for a node hanging off the context
+ *      positions    int32 [T]   ctx_b + depth: siblings share a position, the
+ *                               packed index is never the position
+ *                               ([ATLAS] §3: depths [0,1,1,2], prompt 7 ->
+ *                               [7,8,8,9])
+ *      retrieve_index        int32 [T]  global logits row of node i:
+ *                                       node_offsets[b] + b + 1 + i
+ *      retrieve_next_token   int32 [T]  first child of node i (smallest local j
+ *                                       with parent j == i), else -1
+ *      retrieve_next_sibling int32 [T]  next child of i's parent after i, else -1
+ *      err          int32 [B]   written: TTV_ERR_BAD_PARENT, _TOO_MANY_NODES,
+ *                               _BAD_LENGTH
+ */
+TTV_API int tree_build(const ttv_batch* bt, const int32_t* parents,
+                       uint32_t* mask, int32_t mask_words,
+                       int32_t* depth, int32_t* positions, int32_t* retrieve_index,
+                       int32_t* retrieve_next_token, int32_t* retrieve_next_sibling,
+                       int32_t* err, hipStream_t stream);
+
+/*
+ * Workspace bytes tree_attention_verify needs for this batch and cache (host
+ * call, no device access).  Depends only on the host fields of bt and cache
+ * and on n_heads.  Returns 0 for invalid arguments.
+ */
+TTV_API size_t tree_attention_workspace_bytes(const ttv_batch* bt, const ttv_kv_cache* cache,
+                                              int32_t n_heads);
+
+/*
+ * tree_attention_verify -- one attention layer of the target's verify pass
+ * ([GLOSSARY] "Packed tree attention" and the packed-vs-branch experiment;
+ * [ATLAS] §3; [DDTREE] §7.1).
+ *
+ * For request b, node i, query head h (KV head h / (n_heads / n_kv_heads)):
+ *   q' = RoPE(q[i,h], positions[i]), k'_j = RoPE(k_new[j], positions[j]),
+ *   interleaved pairs (x_2m, x_2m+1), inv_freq_m = rope_base^(-2m/D),
+ *   (x0 cos - x1 sin, x1 cos + x0 sin);
+ *   keys = committed K[0 .. ctx_b-1] (already rotated in the cache) followed
+ *   by k'_j for every j with mask bit j of row i set; values likewise (V is
+ *   not rotated);  out[i,h] = softmax(q'.keys * scale) . values, with the
+ *   softmax max and sum in fp32.
+ * Side effect: k'_j (bf16) and v_new[j] are written into slots ctx_b + j of
+ * the cache (the tentative region, [ESSAY] KV cache section).
+ *
+ * in : q       bf16 [T, n_heads, D];  k_new, v_new  bf16 [T, n_kv_heads, D]
+ *      mask, mask_words, positions  as produced by tree_build
+ *      cache   ctx_b + N_b <= capacity (contiguous) or every logical block
+ *              < ceil((ctx_b + N_b) / 16) mapped (paged); else err bit 4 / 8
+ *      rope_base > 0; softmax_scale 0 means 1/sqrt(D)
+ * out: out     bf16 [T, n_heads, D]
+ *      workspace  device, >= tree_attention_workspace_bytes(), 256-byte aligned
+ *      err     OR-ed: TTV_ERR_CAPACITY, TTV_ERR_BLOCK_TABLE, _TOO_MANY_NODES
+ * Supported: D in {64, 128}; n_heads % n_kv_heads == 0; n_max <= 1024.
+ */
+TTV_API int tree_attention_verify(const ttv_batch* bt, const void* q, const void* k_new,
+                                  const void* v_new, const uint32_t* mask, int32_t mask_words,
+                                  const int32_t* positions, const ttv_kv_cache* cache,
+                                  int32_t n_heads, float rope_base, float softmax_scale,
+                                  void* out, void* workspace, size_t workspace_bytes,
+                                  int32_t* err, hipStream_t stream);
+
+/* Workspace bytes tree_greedy_accept needs (host call).  0 for invalid arguments. */
+TTV_API size_t tree_greedy_accept_workspace_bytes(const ttv_batch* bt, int64_t vocab);
+
+/*
+ * tree_greedy_accept -- greedy verification walk ([GLOSSARY] verify_tree
+ * experiment; [ATLAS] §4; [DDTREE] §7.2).
+ *
+ * For each request: choice[r] = argmax_v logits[row r, v] (ties to the lowest
+ * v; -0.0 equals +0.0; inputs must be finite), for its N_b + 1 rows.  Then,
+ * from the root (row 0), take the lowest-index child whose token equals the
+ * current choice (children of the root are the nodes with parent -1, reached
+ * from node 0 through retrieve_next_sibling; children of node j from
+ * retrieve_next_token[j]); repeat with that child's row; stop when no child
+ * matches.  The last choice is the bonus / correction token.
+ *
+ * in : logits   fp32 or bf16 [T + B, vocab] (row-major, row stride = vocab)
+ *      tokens   int32 [T];  retrieve_next_token, retrieve_next_sibling from tree_build
+ *      max_accept >= 1: capacity of accepted_nodes rows
+ * out: accept_len     int32 [B]                  a_b accepted nodes
+ *      accepted_nodes int32 [B, max_accept]      local node ids at depths 0..a_b-1
+ *                                                (entries >= a_b set to -1)
+ *      out_tokens     int32 [B, max_accept + 1]  accepted tokens then the bonus
+ *                                                (entries > a_b set to -1)
+ *      row_argmax     int32 [T + B] or NULL      choice of every logits row
+ *      workspace      device, >= tree_greedy_accept_workspace_bytes()
+ *      err            OR-ed: TTV_ERR_ACCEPT if a further match exists at max_accept
+ */
+TTV_API int tree_greedy_accept(const ttv_batch* bt, const void* logits, int32_t logits_dtype,
+                               int64_t vocab, const int32_t* tokens,
+                               const int32_t* retrieve_next_token,
+                               const int32_t* retrieve_next_sibling, int32_t max_accept,
+                               int32_t* accept_len, int32_t* accepted_nodes, int32_t* out_tokens,
+                               int32_t* row_argmax, void* workspace, size_t workspace_bytes,
+                               int32_t* err, hipStream_t stream);
+
+/*
+ * tree_kv_commit -- commit the accepted path and roll back the rest
+ * ([GLOSSARY] "Tree/Self Speculation": cache [10,11] + accepted [4,7] ->
+ * [10,11,4,7]; [ESSAY] KV cache section; [ATLAS] §4 after acceptance).
+ *
+ * For each request: the accepted node at depth d (local id i_d) moves from
+ * slot ctx_b + i_d to slot ctx_b + d, K and V, every KV head, bit-exact,
+ * reading the values the slots held before the call (in-place safe).  The
+ * bonus token has no KV yet and is not committed.  new_lens[b] = ctx_b + a_b.
+ * Contiguous: slots >= new_len become free (contents undefined).
+ * Paged: logical blocks j in [ceil(new_len/16), ceil((ctx_b + N_b)/16)) are
+ * released: their physical ids go to released_blocks[b*max_blocks + k] in
+ * logical order, num_released[b] is set, and block_table entries become -1.
+ *
+ * in : accept_len [B], accepted_nodes [B, max_accept] from tree_greedy_accept
+ * out: new_lens int32 [B]; released_blocks int32 [B, max_blocks] and
+ *      num_released int32 [B] (paged only; may be NULL for contiguous)
+ *      err  OR-ed: TTV_ERR_ACCEPT (accept_len or a node id out of range, or
+ *           the ids not a root-down path by increasing index), _CAPACITY,
+ *           _BLOCK_TABLE.  A flagged request is left untouched.
+ */
+TTV_API int tree_kv_commit(const ttv_batch* bt, const ttv_kv_cache* cache,
+                           const int32_t* accept_len, const int32_t* accepted_nodes,
+                           int32_t max_accept, int32_t* new_lens, int32_t* released_blocks,
+                           int32_t* num_released, int32_t* err, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREEVERIFY_H */

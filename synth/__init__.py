@@ -40,7 +40,7 @@ import numpy as np
 
 __all__ = [
     "CONFIGS", "Workload", "make_workload", "bf16_bits_from_f32", "f32_from_bf16_bits",
-    "medusa_tree", "eagle_tree", "random_tree", "ddtree_tree", "BLOCK_SIZE",
+    "medusa_tree", "eagle_tree", "random_tree", "ddtree_tree", "BLOCK_SIZE", "make_trees", "TreeBatch",
 ]
 
 BLOCK_SIZE = 16
@@ -334,22 +334,45 @@ def _tree_for(cfg: dict, rng_tree, rng_tok, vocab, draft_vocab, ddtree_budget):
     raise ValueError(kind)
 
 
-def make_workload(cfg_id: int, seed: int = 0, **over) -> Workload:
-    """Build one seeded workload.
+@dataclasses.dataclass
+class TreeBatch:
+    """Trees, tokens and context lengths of one batch (no activations)."""
+    parents: np.ndarray
+    tokens: np.ndarray
+    node_offsets: np.ndarray
+    ctx_lens: np.ndarray
+    accept_p: np.ndarray
+    per_request_parents: list
+    per_request_tokens: list
 
-    ``over`` may replace any CONFIGS field (``batch``, ``ctx``, ``tree``,
-    ``heads``, ``vocab``, ``logits``, ``p``, ``layout``) to draw a scaled-down
-    case of the same structure, plus ``ddtree_budget`` and ``spare_slots``.
-    """
+    @property
+    def batch(self) -> int:
+        return len(self.ctx_lens)
+
+    @property
+    def total_nodes(self) -> int:
+        return int(self.node_offsets[-1])
+
+    @property
+    def n_max(self) -> int:
+        return int(np.diff(self.node_offsets).max(initial=0))
+
+    def request_nodes(self, b: int) -> slice:
+        return slice(int(self.node_offsets[b]), int(self.node_offsets[b + 1]))
+
+
+def _config(cfg_id: int, over: dict) -> dict:
     cfg = dict(CONFIGS[cfg_id])
-    ddtree_budget = int(over.pop("ddtree_budget", 1024))
-    spare = int(over.pop("spare_slots", 0))
     cfg.update(over)
+    return cfg
+
+
+def make_trees(cfg_id: int, seed: int = 0, ddtree_budget: int = 1024, **over) -> TreeBatch:
+    """The tree / token / context-length part of ``make_workload``."""
+    cfg = _config(cfg_id, over)
     B = int(cfg["batch"])
-    hq, hkv, D = cfg["heads"]
     V = int(cfg["vocab"])
     r_tree, r_tok, r_len = _rng(seed, cfg_id, _S_TREE), _rng(seed, cfg_id, _S_TOKENS), _rng(seed, cfg_id, _S_LENS)
-
     parents, tokens, sizes = [], [], []
     for _b in range(B):
         p, t = _tree_for(cfg, r_tree, r_tok, V, V, ddtree_budget)
@@ -365,6 +388,26 @@ def make_workload(cfg_id: int, seed: int = 0, **over) -> Workload:
     T = int(node_offsets[-1])
     parents_all = np.concatenate(parents).astype(np.int32) if T else np.zeros(0, np.int32)
     tokens_all = np.concatenate(tokens).astype(np.int32) if T else np.zeros(0, np.int32)
+    return TreeBatch(parents_all, tokens_all, node_offsets, ctx, accept_p, parents, tokens)
+
+
+def make_workload(cfg_id: int, seed: int = 0, **over) -> Workload:
+    """Build one seeded workload.
+
+    ``over`` may replace any CONFIGS field (``batch``, ``ctx``, ``tree``,
+    ``heads``, ``vocab``, ``logits``, ``p``, ``layout``) to draw a scaled-down
+    case of the same structure, plus ``ddtree_budget`` and ``spare_slots``.
+    """
+    ddtree_budget = int(over.pop("ddtree_budget", 1024))
+    spare = int(over.pop("spare_slots", 0))
+    cfg = _config(cfg_id, over)
+    tb = make_trees(cfg_id, seed, ddtree_budget=ddtree_budget, **over)
+    B = tb.batch
+    hq, hkv, D = cfg["heads"]
+    V = int(cfg["vocab"])
+    T = tb.total_nodes
+    sizes = np.diff(tb.node_offsets)
+    ctx = tb.ctx_lens
 
     r_qkv = _rng(seed, cfg_id, _S_QKV)
     q = _normal_bf16(r_qkv, (T, hq, D))
@@ -372,7 +415,7 @@ def make_workload(cfg_id: int, seed: int = 0, **over) -> Workload:
     v_new = _normal_bf16(r_qkv, (T, hkv, D))
 
     r_cache = _rng(seed, cfg_id, _S_CACHE)
-    need = ctx + np.asarray(sizes, dtype=np.int32)
+    need = ctx + sizes.astype(np.int32)
     if cfg["layout"] == "contiguous":
         cap = int(-(-(int(need.max(initial=1)) + spare) // BLOCK_SIZE) * BLOCK_SIZE)
         k_cache = _normal_bf16(r_cache, (B, hkv, cap, D))
@@ -393,10 +436,11 @@ def make_workload(cfg_id: int, seed: int = 0, **over) -> Workload:
         cap = 0
 
     logits, planted = _planted_logits(_rng(seed, cfg_id, _S_LOGITS), _rng(seed, cfg_id, _S_PLANT),
-                                      parents, tokens, accept_p, V, cfg["logits"])
+                                      tb.per_request_parents, tb.per_request_tokens, tb.accept_p, V,
+                                      cfg["logits"])
     return Workload(name=cfg["name"], seed=seed, n_heads=hq, n_kv_heads=hkv, head_dim=D, vocab=V,
-                    logits_dtype=cfg["logits"], layout=cfg["layout"], parents=parents_all,
-                    tokens=tokens_all, node_offsets=node_offsets, ctx_lens=ctx, accept_p=accept_p,
+                    logits_dtype=cfg["logits"], layout=cfg["layout"], parents=tb.parents,
+                    tokens=tb.tokens, node_offsets=tb.node_offsets, ctx_lens=ctx, accept_p=tb.accept_p,
                     q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, capacity=cap,
                     block_table=block_table, logits=logits, planted=planted)
 

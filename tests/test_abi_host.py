@@ -1,0 +1,130 @@
+"""The C ABI library on the host (no GPU needed): it loads, exports every
+function the headers declare, and rejects bad arguments before launching."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import token_tree_attention_amd as tta
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        names += re.findall(r"TTV_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tta.library_path()):
+        pytest.skip("library not built (run python -m token_tree_attention_amd.build)")
+    return tta.load_library()
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("tree_build", "tree_attention_verify", "tree_greedy_accept", "tree_kv_commit",
+              "tree_attention_workspace_bytes", "tree_greedy_accept_workspace_bytes"):
+        assert n in names
+    assert sorted(tta.EXPORTED_SYMBOLS) == names
+
+
+def test_every_declared_symbol_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status(lib):
+    assert tta.ttv_version() >= 100
+    assert "invalid" in tta.ttv_status_string(tta.TTV_EINVAL)
+    assert "workspace" in tta.ttv_status_string(tta.TTV_ENOSPC)
+
+
+def _batch(B=2, n_max=8, T=10, offs=0x1000, ctx=0x2000):
+    return tta._CBatch(B, n_max, T, offs, ctx)
+
+
+def _cache(layout=0, hkv=2, D=128, cap=64, table=None, max_blocks=0, bs=0, nb=0):
+    return tta._CCache(0x10000, 0x20000, layout, hkv, D, cap, table, max_blocks, bs, nb)
+
+
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def test_tree_build_rejects(lib):
+    b = _batch()
+    args = [FAKE] * 6
+    assert lib.tree_build(None, FAKE, FAKE, 1, *args[:5], FAKE, None) == tta.TTV_EINVAL
+    bad = _batch(n_max=2000)
+    assert lib.tree_build(ctypes.byref(bad), FAKE, FAKE, 63, *args[:5], FAKE, None) == tta.TTV_EINVAL
+    assert lib.tree_build(ctypes.byref(b), FAKE, FAKE, 0, *args[:5], FAKE, None) == tta.TTV_EINVAL  # mask_words
+    assert lib.tree_build(ctypes.byref(b), None, FAKE, 1, *args[:5], FAKE, None) == tta.TTV_EINVAL
+    over = _batch(B=1, n_max=4, T=5)
+    assert lib.tree_build(ctypes.byref(over), FAKE, FAKE, 1, *args[:5], FAKE, None) == tta.TTV_EINVAL
+    empty = _batch(B=0, T=0)
+    assert lib.tree_build(ctypes.byref(empty), None, None, 1, None, None, None, None, None, None, None) == tta.TTV_OK
+
+
+def test_attention_rejects_and_sizes(lib):
+    b = _batch()
+    ok = _cache()
+    ws = lib.tree_attention_workspace_bytes(ctypes.byref(b), ctypes.byref(ok), 8)
+    assert ws > 0 and ws % 256 == 0
+    assert lib.tree_attention_workspace_bytes(ctypes.byref(b), ctypes.byref(_cache(D=96)), 8) == 0
+    assert lib.tree_attention_workspace_bytes(ctypes.byref(b), ctypes.byref(ok), 7) == 0  # 7 % 2
+    paged_bad = _cache(layout=1, bs=32, max_blocks=4, nb=10, table=FAKE)
+    assert lib.tree_attention_workspace_bytes(ctypes.byref(b), ctypes.byref(paged_bad), 8) == 0
+
+    def call(bt=b, cache=ok, heads=8, base=10000.0, scale=0.0, ws_ptr=FAKE * 16, ws_bytes=ws, words=1,
+             q=FAKE):
+        return lib.tree_attention_verify(ctypes.byref(bt), q, FAKE, FAKE, FAKE, words, FAKE,
+                                         ctypes.byref(cache), heads, base, scale, FAKE, ws_ptr, ws_bytes,
+                                         FAKE, None)
+
+    assert call(heads=3) == tta.TTV_EINVAL
+    assert call(base=0.0) == tta.TTV_EINVAL
+    assert call(scale=-1.0) == tta.TTV_EINVAL
+    assert call(words=0) == tta.TTV_EINVAL
+    assert call(q=None) == tta.TTV_EINVAL
+    assert call(ws_ptr=FAKE * 16 + 8) == tta.TTV_EINVAL          # workspace not 256-aligned
+    assert call(ws_bytes=ws - 1) == tta.TTV_ENOSPC
+    assert call(cache=_cache(D=64 + 32)) == tta.TTV_EINVAL
+    assert call(bt=_batch(B=5000, T=10)) == tta.TTV_EINVAL
+
+
+def test_accept_rejects_and_sizes(lib):
+    b = _batch()
+    need = lib.tree_greedy_accept_workspace_bytes(ctypes.byref(b), 128256)
+    assert need >= 8 * (10 + 2)
+    assert lib.tree_greedy_accept_workspace_bytes(ctypes.byref(b), 0) == 0
+
+    def call(dtype=1, vocab=128256, max_accept=16, ws_bytes=need, logits=FAKE):
+        return lib.tree_greedy_accept(ctypes.byref(b), logits, dtype, vocab, FAKE, FAKE, FAKE, max_accept,
+                                      FAKE, FAKE, FAKE, None, FAKE, ws_bytes, FAKE, None)
+
+    assert call(dtype=7) == tta.TTV_EINVAL
+    assert call(vocab=0) == tta.TTV_EINVAL
+    assert call(max_accept=0) == tta.TTV_EINVAL
+    assert call(logits=None) == tta.TTV_EINVAL
+    assert call(ws_bytes=need - 1) == tta.TTV_ENOSPC
+
+
+def test_commit_rejects(lib):
+    b = _batch()
+
+    def call(cache, max_accept=16, rel=FAKE, nrel=FAKE):
+        return lib.tree_kv_commit(ctypes.byref(b), ctypes.byref(cache), FAKE, FAKE, max_accept, FAKE, rel,
+                                  nrel, FAKE, None)
+
+    assert call(_cache(D=80)) == tta.TTV_EINVAL
+    assert call(_cache(), max_accept=0) == tta.TTV_EINVAL
+    assert call(_cache(layout=1, bs=16, max_blocks=4, nb=10, table=None)) == tta.TTV_EINVAL
+    assert call(_cache(layout=1, bs=16, max_blocks=4, nb=10, table=FAKE), rel=None) == tta.TTV_EINVAL
+    assert call(_cache(layout=5)) == tta.TTV_EINVAL

@@ -1,0 +1,89 @@
+"""tree_greedy_accept on the GPU against the oracle: bit-exact."""
+
+import numpy as np
+import pytest
+
+import synth
+import token_tree_attention_amd as tta
+from gpu_helpers import host, require_gpu, say
+from parity import check_accept
+
+
+pytestmark = pytest.mark.gpu
+
+
+def run_accept(wl, max_accept=16, logits_override=None):
+    import torch
+    from synth.device import to_device
+    d = to_device(wl)
+    if logits_override is not None:
+        d["logits"] = logits_override
+    bt = tta.Batch(d["node_offsets"], d["ctx_lens"], max(1, wl.n_max), total_nodes=wl.total_nodes)
+    meta = tta.tree_build(bt, d["parents"])
+    acc = tta.tree_greedy_accept(bt, d["logits"], d["tokens"], meta["retrieve_next_token"],
+                                 meta["retrieve_next_sibling"], max_accept, meta["err"])
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in acc.items()}, host(meta["err"])
+
+
+SMALL = {
+    0: dict(),
+    1: dict(vocab=5000, ctx=(4, 4)),
+    2: dict(vocab=3001, ctx=(4, 9), batch=12),
+    3: dict(vocab=4096, ctx=(4, 4), ddtree_budget=200),
+    4: dict(vocab=2000, ctx=(4, 9), batch=6),
+    5: dict(vocab=4096, ctx=(4, 4), ddtree_budget=300),
+}
+
+
+@pytest.mark.parametrize("cfg", sorted(SMALL))
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_accept_scaled(cfg, seed):
+    require_gpu()
+    wl = synth.make_workload(cfg, seed, **SMALL[cfg])
+    say(f"tree_greedy_accept cfg={cfg} seed={seed} T={wl.total_nodes} V={wl.vocab} {wl.logits_dtype}")
+    acc, err = run_accept(wl)
+    assert (err == 0).all()
+    check_accept(wl, acc, 16)
+
+
+def test_accept_ties_signed_zero_and_unaligned_vocab():
+    require_gpu()
+    import torch
+    for dtype, V in (("bf16", 1001), ("fp32", 999), ("bf16", 8192 * 3 + 5)):
+        wl = synth.make_workload(2, 3, vocab=V, ctx=(4, 9), batch=5, logits=dtype)
+        rows = wl.logits.copy()
+        # plant exact ties at two or three indices and a -0/+0 row
+        rng = np.random.default_rng(V)
+        for r in range(rows.shape[0]):
+            a, b, c = sorted(rng.choice(V, 3, replace=False))
+            if dtype == "bf16":
+                top = rows[r].view(np.uint16)
+                val = synth.f32_from_bf16_bits(top).max()
+                hi = synth.bf16_bits_from_f32(np.array([val + 2.0], np.float32))[0]
+                top[[b, c]] = hi
+                if r % 3 == 0:
+                    top[:] = 0x8000
+                    top[a] = 0
+            else:
+                val = rows[r].max()
+                rows[r, [b, c]] = val + 2.0
+                if r % 3 == 0:
+                    rows[r, :] = -0.0
+                    rows[r, a] = 0.0
+        wl.logits = rows
+        say(f"tree_greedy_accept ties dtype={dtype} V={V}")
+        acc, _ = run_accept(wl)
+        check_accept(wl, acc, 16)
+
+
+def test_accept_overflow_flag():
+    require_gpu()
+    wl = synth.make_workload(2, 4, vocab=64, ctx=(4, 9), batch=3, p=(1.0, 1.0),
+                             tree=("parents", list(range(-1, 11))))
+    say("tree_greedy_accept max_accept overflow")
+    acc, err = run_accept(wl, max_accept=3)
+    assert (acc["accept_len"] <= 3).all()
+    for b in range(wl.batch):
+        if acc["accept_len"][b] == 3:
+            assert err[b] & tta.ERR_ACCEPT

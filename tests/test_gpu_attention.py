@@ -1,0 +1,97 @@
+"""tree_attention_verify on the GPU against the float64 oracle.
+
+Scaled cases span several 32-slot tiles, several 256-row tiles, split and
+unsplit contexts and ragged tails; outputs must be within 1e-2 + 1e-2|ref|,
+the tentative K within one bf16 ulp of the rounded rotation, V exact.
+"""
+
+import numpy as np
+import pytest
+
+import synth
+import token_tree_attention_amd as tta
+from gpu_helpers import bits, region_bits, require_gpu, say
+from parity import check_attention_request, check_tentative
+
+pytestmark = pytest.mark.gpu
+
+
+def run_attention(wl, rope_base=10000.0):
+    import torch
+    from synth.device import to_device
+    d = to_device(wl)
+    bt = tta.Batch(d["node_offsets"], d["ctx_lens"], max(1, wl.n_max), total_nodes=wl.total_nodes)
+    cache = tta.KVCache(d["k_cache"], d["v_cache"], d["block_table"])
+    meta = tta.tree_build(bt, d["parents"])
+    out = tta.tree_attention_verify(bt, d["q"], d["k_new"], d["v_new"], meta["mask"], meta["positions"],
+                                    cache, meta["err"], rope_base=rope_base)
+    torch.cuda.synchronize()
+    return d, bits(out), meta["err"].cpu().numpy()
+
+
+SCALED = [
+    # (cfg, overrides): several tiles of rows and keys, ragged tails
+    (0, dict()),
+    (0, dict(ctx=(300, 300))),
+    (1, dict(ctx=(700, 700), vocab=64)),
+    (1, dict(ctx=(33, 33), vocab=64)),
+    (2, dict(batch=5, ctx=(100, 1300), vocab=64)),
+    (3, dict(ctx=(513, 513), vocab=64, ddtree_budget=100, batch=2)),
+    (4, dict(batch=3, ctx=(40, 900), vocab=64)),
+    (5, dict(ctx=(257, 257), vocab=64, ddtree_budget=130, batch=2)),
+    (2, dict(batch=3, ctx=(0, 0), vocab=64)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SCALED)))
+@pytest.mark.parametrize("seed", [0, 1])
+def test_attention_scaled(case, seed):
+    require_gpu()
+    cfg, over = SCALED[case]
+    wl = synth.make_workload(cfg, seed, **over)
+    say(f"tree_attention_verify cfg={cfg} seed={seed} {over} T={wl.total_nodes} "
+        f"heads={wl.n_heads}/{wl.n_kv_heads}/{wl.head_dim} layout={wl.layout}")
+    d, out, err = run_attention(wl)
+    assert (err == 0).all(), err
+    for b in range(wl.batch):
+        sl = wl.request_nodes(b)
+        check_attention_request(wl, b, out[sl])
+        n = sl.stop - sl.start
+        kb = region_bits(d, wl, b, int(wl.ctx_lens[b]), n, "k")
+        vb = region_bits(d, wl, b, int(wl.ctx_lens[b]), n, "v")
+        check_tentative(wl, b, kb, vb)
+
+
+def test_attention_rope_base_and_capacity_flag():
+    require_gpu()
+    wl = synth.make_workload(1, 3, ctx=(90, 90), vocab=64)
+    say("tree_attention_verify rope_base=500000")
+    d, out, err = run_attention(wl, rope_base=500000.0)
+    check_attention_request(wl, 0, out, rope_base=500000.0)
+    # A contiguous cache too small for ctx + N flags the request and writes nothing outside.
+    import torch
+    small = wl.ctx_lens[0] + wl.total_nodes - 1
+    k = d["k_cache"][:, :, :small].contiguous()
+    v = d["v_cache"][:, :, :small].contiguous()
+    bt = tta.Batch(d["node_offsets"], d["ctx_lens"], wl.n_max, total_nodes=wl.total_nodes)
+    meta = tta.tree_build(bt, d["parents"])
+    tta.tree_attention_verify(bt, d["q"], d["k_new"], d["v_new"], meta["mask"], meta["positions"],
+                              tta.KVCache(k, v), meta["err"])
+    torch.cuda.synchronize()
+    assert meta["err"].cpu().numpy()[0] & tta.ERR_CAPACITY
+
+
+def test_attention_softmax_scale_argument():
+    require_gpu()
+    import torch
+    wl = synth.make_workload(0, 5)
+    d = __import__("synth.device", fromlist=["to_device"]).to_device(wl)
+    bt = tta.Batch(d["node_offsets"], d["ctx_lens"], wl.n_max, total_nodes=wl.total_nodes)
+    meta = tta.tree_build(bt, d["parents"])
+    cache = tta.KVCache(d["k_cache"], d["v_cache"])
+    o0 = tta.tree_attention_verify(bt, d["q"], d["k_new"], d["v_new"], meta["mask"], meta["positions"],
+                                   cache, meta["err"], softmax_scale=0.0).clone()
+    o1 = tta.tree_attention_verify(bt, d["q"], d["k_new"], d["v_new"], meta["mask"], meta["positions"],
+                                   cache, meta["err"], softmax_scale=1.0 / 8.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1)  # 1/sqrt(64) explicitly == default

@@ -1,0 +1,318 @@
+"""token_tree_attention_amd -- MI355X (gfx950) token-tree verification.
+
+A thin ctypes binding of ``libtreeverify.so`` (declared in
+``include/treeverify.h``).  Functions carry the C names and only marshal
+arguments: torch tensors go in as raw device pointers on the caller's current
+stream; every step of the path runs in the library's HIP kernels.  Importing
+works without a GPU; calling a compute function needs the built library and
+a ROCm device, and raises if either is missing (there is no CPU fallback).
+
+Typical round (all tensors on one ``cuda`` device)::
+
+    bt = Batch(node_offsets, ctx_lens, n_max)
+    meta = tree_build(bt, parents)
+    out = tree_attention_verify(bt, q, k_new, v_new, meta["mask"], meta["positions"], cache)
+    acc = tree_greedy_accept(bt, logits, tokens, meta["retrieve_next_token"],
+                             meta["retrieve_next_sibling"], max_accept=16, err=meta["err"])
+    com = tree_kv_commit(bt, cache, acc["accept_len"], acc["accepted_nodes"], err=meta["err"])
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+__all__ = [
+    "Batch", "KVCache", "library_path", "load_library", "ttv_version", "ttv_status_string",
+    "tree_build", "tree_attention_workspace_bytes", "tree_attention_verify",
+    "tree_greedy_accept_workspace_bytes", "tree_greedy_accept", "tree_kv_commit",
+    "TTV_OK", "TTV_EINVAL", "TTV_EHIP", "TTV_ENOSPC", "ERR_BAD_PARENT", "ERR_TOO_MANY_NODES",
+    "ERR_CAPACITY", "ERR_BLOCK_TABLE", "ERR_ACCEPT", "ERR_BAD_LENGTH", "MAX_TREE_NODES",
+    "BLOCK_SIZE", "EXPORTED_SYMBOLS",
+]
+
+TTV_OK, TTV_EINVAL, TTV_EHIP, TTV_ENOSPC = 0, -1, -2, -3
+ERR_BAD_PARENT, ERR_TOO_MANY_NODES, ERR_CAPACITY = 1, 2, 4
+ERR_BLOCK_TABLE, ERR_ACCEPT, ERR_BAD_LENGTH = 8, 16, 32
+MAX_TREE_NODES = 1024
+BLOCK_SIZE = 16
+DTYPE_FP32, DTYPE_BF16 = 0, 1
+KV_CONTIGUOUS, KV_PAGED = 0, 1
+
+EXPORTED_SYMBOLS = (
+    "ttv_version", "ttv_status_string", "tree_build", "tree_attention_workspace_bytes",
+    "tree_attention_verify", "tree_greedy_accept_workspace_bytes", "tree_greedy_accept",
+    "tree_kv_commit",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libtreeverify.so")
+
+
+class _CBatch(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_max", ctypes.c_int32),
+                ("total_nodes", ctypes.c_int64), ("node_offsets", ctypes.c_void_p),
+                ("ctx_lens", ctypes.c_void_p)]
+
+
+class _CCache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("layout", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("block_table", ctypes.c_void_p),
+                ("max_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32)]
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libtreeverify.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with python -m token_tree_attention_amd.build")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    BP, CP = ctypes.POINTER(_CBatch), ctypes.POINTER(_CCache)
+    lib.ttv_version.restype = I32
+    lib.ttv_version.argtypes = []
+    lib.ttv_status_string.restype = ctypes.c_char_p
+    lib.ttv_status_string.argtypes = [I32]
+    lib.tree_build.restype = ctypes.c_int
+    lib.tree_build.argtypes = [BP, P, P, I32, P, P, P, P, P, P, P]
+    lib.tree_attention_workspace_bytes.restype = SZ
+    lib.tree_attention_workspace_bytes.argtypes = [BP, CP, I32]
+    lib.tree_attention_verify.restype = ctypes.c_int
+    lib.tree_attention_verify.argtypes = [BP, P, P, P, P, I32, P, CP, I32, F32, F32, P, P, SZ, P, P]
+    lib.tree_greedy_accept_workspace_bytes.restype = SZ
+    lib.tree_greedy_accept_workspace_bytes.argtypes = [BP, I64]
+    lib.tree_greedy_accept.restype = ctypes.c_int
+    lib.tree_greedy_accept.argtypes = [BP, P, I32, I64, P, P, P, I32, P, P, P, P, P, SZ, P, P]
+    lib.tree_kv_commit.restype = ctypes.c_int
+    lib.tree_kv_commit.argtypes = [BP, CP, P, P, I32, P, P, P, P, P]
+    _LIB = lib
+    return lib
+
+
+def ttv_version() -> int:
+    return int(load_library().ttv_version())
+
+
+def ttv_status_string(status: int) -> str:
+    return load_library().ttv_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != TTV_OK:
+        raise RuntimeError(f"{what}: {ttv_status_string(status)} (status {status})")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _dev(t, dtype, name, numel=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm device, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    return t
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+class Batch:
+    """Requests of one verify round: node_offsets [B+1] and ctx_lens [B] (int32, device)."""
+
+    def __init__(self, node_offsets, ctx_lens, n_max: int, total_nodes: Optional[int] = None):
+        torch = _torch()
+        self.node_offsets = _dev(node_offsets, torch.int32, "node_offsets")
+        self.ctx_lens = _dev(ctx_lens, torch.int32, "ctx_lens")
+        self.batch = int(ctx_lens.numel())
+        if node_offsets.numel() != self.batch + 1:
+            raise ValueError("node_offsets must have batch + 1 entries")
+        self.n_max = int(n_max)
+        self.total_nodes = int(total_nodes) if total_nodes is not None else int(node_offsets[-1].item())
+        self._c = _CBatch(self.batch, self.n_max, self.total_nodes,
+                          _ptr(self.node_offsets), _ptr(self.ctx_lens))
+
+    @property
+    def mask_words(self) -> int:
+        return max(1, (self.n_max + 31) // 32)
+
+
+class KVCache:
+    """bf16 K/V cache: contiguous [B, Hkv, capacity, D] or paged [num_blocks, Hkv, 16, D]."""
+
+    def __init__(self, k, v, block_table=None):
+        torch = _torch()
+        self.k = _dev(k, torch.bfloat16, "k")
+        self.v = _dev(v, torch.bfloat16, "v")
+        if k.shape != v.shape or k.dim() != 4:
+            raise ValueError("k and v must have the same 4-d shape")
+        self.block_table = block_table
+        if block_table is None:
+            self.layout = KV_CONTIGUOUS
+            _, hkv, cap, d = k.shape
+            self._c = _CCache(_ptr(k), _ptr(v), KV_CONTIGUOUS, hkv, d, cap, None, 0, 0, 0)
+        else:
+            _dev(block_table, torch.int32, "block_table")
+            if block_table.dim() != 2:
+                raise ValueError("block_table must be [B, max_blocks]")
+            self.layout = KV_PAGED
+            nb, hkv, bs, d = k.shape
+            if bs != BLOCK_SIZE:
+                raise ValueError(f"paged blocks must hold {BLOCK_SIZE} tokens")
+            self._c = _CCache(_ptr(k), _ptr(v), KV_PAGED, hkv, d, 0, _ptr(block_table),
+                              block_table.shape[1], bs, nb)
+        self.n_kv_heads = int(k.shape[1])
+        self.head_dim = int(k.shape[3])
+
+    @property
+    def max_blocks(self) -> int:
+        return 0 if self.block_table is None else int(self.block_table.shape[1])
+
+
+def tree_build(bt: Batch, parents, out: Optional[Dict] = None, stream=None) -> Dict:
+    """Masks, depths, positions and retrieve indices for every request's tree."""
+    torch = _torch()
+    lib = load_library()
+    T = bt.total_nodes
+    _dev(parents, torch.int32, "parents", T)
+    dev = parents.device
+    W = bt.mask_words
+    if out is None:
+        out = {"mask": torch.empty((T, W), dtype=torch.int32, device=dev)}
+        for k in ("depth", "positions", "retrieve_index", "retrieve_next_token", "retrieve_next_sibling"):
+            out[k] = torch.empty(T, dtype=torch.int32, device=dev)
+        out["err"] = torch.empty(bt.batch, dtype=torch.int32, device=dev)
+    st = lib.tree_build(ctypes.byref(bt._c), _ptr(parents), _ptr(out["mask"]), W, _ptr(out["depth"]),
+                        _ptr(out["positions"]), _ptr(out["retrieve_index"]),
+                        _ptr(out["retrieve_next_token"]), _ptr(out["retrieve_next_sibling"]),
+                        _ptr(out["err"]), _stream(stream))
+    _check(st, "tree_build")
+    return out
+
+
+def tree_attention_workspace_bytes(bt: Batch, cache: KVCache, n_heads: int) -> int:
+    return int(load_library().tree_attention_workspace_bytes(ctypes.byref(bt._c), ctypes.byref(cache._c), int(n_heads)))
+
+
+def tree_attention_verify(bt: Batch, q, k_new, v_new, mask, positions, cache: KVCache, err,
+                          rope_base: float = 10000.0, softmax_scale: float = 0.0, out=None,
+                          workspace=None, stream=None):
+    """One layer of tree attention; writes rotated K / V into the tentative slots."""
+    torch = _torch()
+    lib = load_library()
+    T = bt.total_nodes
+    if q.dim() != 3 or q.shape[0] != T:
+        raise ValueError("q must be [T, n_heads, D]")
+    n_heads = int(q.shape[1])
+    _dev(q, torch.bfloat16, "q")
+    _dev(k_new, torch.bfloat16, "k_new", T * cache.n_kv_heads * cache.head_dim)
+    _dev(v_new, torch.bfloat16, "v_new", T * cache.n_kv_heads * cache.head_dim)
+    _dev(mask, torch.int32, "mask")
+    _dev(positions, torch.int32, "positions", T)
+    _dev(err, torch.int32, "err", bt.batch)
+    W = int(mask.shape[1]) if mask.dim() == 2 else bt.mask_words
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.bfloat16, "out", q.numel())
+    need = tree_attention_workspace_bytes(bt, cache, n_heads)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.tree_attention_verify(ctypes.byref(bt._c), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(mask), W,
+                                   _ptr(positions), ctypes.byref(cache._c), n_heads, float(rope_base),
+                                   float(softmax_scale), _ptr(out), _ptr(workspace), workspace.numel(),
+                                   _ptr(err), _stream(stream))
+    _check(st, "tree_attention_verify")
+    return out
+
+
+def tree_greedy_accept_workspace_bytes(bt: Batch, vocab: int) -> int:
+    return int(load_library().tree_greedy_accept_workspace_bytes(ctypes.byref(bt._c), int(vocab)))
+
+
+def tree_greedy_accept(bt: Batch, logits, tokens, retrieve_next_token, retrieve_next_sibling,
+                       max_accept: int, err, out: Optional[Dict] = None, workspace=None,
+                       want_row_argmax: bool = True, stream=None) -> Dict:
+    """Row argmax of every logits row and the greedy walk of every request."""
+    torch = _torch()
+    lib = load_library()
+    T, B = bt.total_nodes, bt.batch
+    if logits.dim() != 2 or logits.shape[0] != T + B:
+        raise ValueError("logits must be [T + B, vocab]")
+    if logits.dtype == torch.float32:
+        dt = DTYPE_FP32
+    elif logits.dtype == torch.bfloat16:
+        dt = DTYPE_BF16
+    else:
+        raise TypeError("logits must be float32 or bfloat16")
+    _dev(logits, logits.dtype, "logits")
+    vocab = int(logits.shape[1])
+    _dev(tokens, torch.int32, "tokens", T)
+    _dev(retrieve_next_token, torch.int32, "retrieve_next_token", T)
+    _dev(retrieve_next_sibling, torch.int32, "retrieve_next_sibling", T)
+    _dev(err, torch.int32, "err", B)
+    dev = logits.device
+    if out is None:
+        out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+               "accepted_nodes": torch.empty((B, max_accept), dtype=torch.int32, device=dev),
+               "out_tokens": torch.empty((B, max_accept + 1), dtype=torch.int32, device=dev)}
+        if want_row_argmax:
+            out["row_argmax"] = torch.empty(T + B, dtype=torch.int32, device=dev)
+    need = tree_greedy_accept_workspace_bytes(bt, vocab)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = lib.tree_greedy_accept(ctypes.byref(bt._c), _ptr(logits), dt, vocab, _ptr(tokens),
+                                _ptr(retrieve_next_token), _ptr(retrieve_next_sibling), int(max_accept),
+                                _ptr(out["accept_len"]), _ptr(out["accepted_nodes"]), _ptr(out["out_tokens"]),
+                                _ptr(out.get("row_argmax")), _ptr(workspace), workspace.numel(), _ptr(err),
+                                _stream(stream))
+    _check(st, "tree_greedy_accept")
+    return out
+
+
+def tree_kv_commit(bt: Batch, cache: KVCache, accept_len, accepted_nodes, err,
+                   out: Optional[Dict] = None, stream=None) -> Dict:
+    """Move the accepted nodes' K/V into place; paged caches also release blocks."""
+    torch = _torch()
+    lib = load_library()
+    B = bt.batch
+    _dev(accept_len, torch.int32, "accept_len", B)
+    _dev(accepted_nodes, torch.int32, "accepted_nodes")
+    max_accept = int(accepted_nodes.shape[1])
+    _dev(err, torch.int32, "err", B)
+    dev = accept_len.device
+    if out is None:
+        out = {"new_lens": torch.empty(B, dtype=torch.int32, device=dev)}
+        if cache.layout == KV_PAGED:
+            out["released_blocks"] = torch.empty((B, cache.max_blocks), dtype=torch.int32, device=dev)
+            out["num_released"] = torch.empty(B, dtype=torch.int32, device=dev)
+    st = lib.tree_kv_commit(ctypes.byref(bt._c), ctypes.byref(cache._c), _ptr(accept_len),
+                            _ptr(accepted_nodes), max_accept, _ptr(out["new_lens"]),
+                            _ptr(out.get("released_blocks")), _ptr(out.get("num_released")),
+                            _ptr(err), _stream(stream))
+    _check(st, "tree_kv_commit")
+    return out

@@ -1,0 +1,240 @@
+// tree_greedy_accept: vocab argmax of every logits row, then the greedy walk.
+//
+// The walk follows the decoding-extensions glossary (verify_tree experiment:
+// keep the candidates that extend the accepted prefix with the target's next
+// token, stop at the first depth without a match), "02 · Token Tree 与 Tree
+// Attention" §4 (from the root, accept the child equal to the target's greedy
+// choice, continue from it; with no matching child the choice is the
+// correction / bonus token) and the DDTree notes §7.2 (all node logits come
+// from the one verify pass, so the walk needs no further target pass).
+//
+// Kernel 1 streams the logits: each workgroup scans one vocab chunk of one
+// row with 16-byte loads, keeps a (value, lowest index) pair per thread, and
+// reduces to one 64-bit key (order-preserving value bits, then the
+// complemented index, so a plain max picks the lowest index on ties).
+// Kernel 2 runs one workgroup per request: it reduces the chunk keys of the
+// request's rows, stages tokens and retrieve links in LDS and walks.
+
+#include "ttv_device.h"
+
+namespace {
+
+constexpr int kArgmaxThreads = 256;
+constexpr int64_t kChunkQuantum = 2048;    // elements; keeps 16-byte alignment for fp32 and bf16
+constexpr int64_t kTargetWorkgroups = 2048;
+constexpr int kWalkThreads = 256;
+
+struct ChunkPlan {
+    int64_t chunk_len;
+    int64_t n_chunks;
+};
+
+ChunkPlan plan_chunks(int64_t rows, int64_t vocab) {
+    ChunkPlan p;
+    int64_t want = rows > 0 ? (kTargetWorkgroups + rows - 1) / rows : 1;
+    if (want < 1) want = 1;
+    int64_t len = (vocab + want - 1) / want;
+    len = ((len + kChunkQuantum - 1) / kChunkQuantum) * kChunkQuantum;
+    if (len < 2 * kChunkQuantum) len = 2 * kChunkQuantum;
+    p.chunk_len = len;
+    p.n_chunks = (vocab + len - 1) / len;
+    return p;
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(kArgmaxThreads) void row_argmax_partial_kernel(
+    const void* __restrict__ logits, int64_t vocab, int64_t chunk_len, int64_t n_chunks,
+    uint64_t* __restrict__ partial) {
+    __shared__ uint64_t s_red[kArgmaxThreads / TTV_WAVE];
+    const int64_t row = blockIdx.x / n_chunks;
+    const int64_t chunk = blockIdx.x % n_chunks;
+    const int64_t e0 = chunk * chunk_len;
+    const int64_t e1 = e0 + chunk_len < vocab ? e0 + chunk_len : vocab;
+    const int tid = threadIdx.x;
+    constexpr int kEpv = kBf16 ? 8 : 4;  // elements per 16-byte vector
+    const size_t esize = kBf16 ? 2 : 4;
+    const char* row_base = (const char*)logits + (size_t)row * (size_t)vocab * esize;
+
+    // Start from the thread's first element so an all -inf range still names
+    // its lowest index; threads with no element report key 0 (below any value).
+    float best = -INFINITY;
+    const bool vec_ok = ((vocab * (int64_t)esize) % 16 == 0) && (((uintptr_t)logits & 15) == 0);
+    uint32_t best_i = 0xFFFFFFFFu;
+    {
+        const int64_t first = e0 + (int64_t)tid * (vec_ok ? kEpv : 1);
+        if (first < e1) best_i = (uint32_t)first;
+    }
+    if (vec_ok) {
+        const ttv_u32x4* vbase = (const ttv_u32x4*)row_base;
+        const int64_t stride = (int64_t)kArgmaxThreads * kEpv;
+        for (int64_t base = e0 + (int64_t)tid * kEpv; base < e1; base += 4 * stride) {
+            ttv_u32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t idx = base + u * stride;
+                if (idx < e1) v[u] = __builtin_nontemporal_load(vbase + idx / kEpv);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t idx = base + u * stride;
+                if (idx < e1) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        if (kBf16) {
+                            const float f0 = ttv_bf16_lo(v[u][w]);
+                            const float f1 = ttv_bf16_hi(v[u][w]);
+                            if (f0 > best) { best = f0; best_i = (uint32_t)(idx + 2 * w); }
+                            if (f1 > best) { best = f1; best_i = (uint32_t)(idx + 2 * w + 1); }
+                        } else {
+                            const float f = __uint_as_float(v[u][w]);
+                            if (f > best) { best = f; best_i = (uint32_t)(idx + w); }
+                        }
+                    }
+                }
+            }
+        }
+    } else {
+        for (int64_t idx = e0 + tid; idx < e1; idx += kArgmaxThreads) {
+            float f;
+            if (kBf16) f = __uint_as_float((uint32_t)((const uint16_t*)row_base)[idx] << 16);
+            else f = ((const float*)row_base)[idx];
+            if (f > best) { best = f; best_i = (uint32_t)idx; }
+        }
+    }
+    uint64_t key = best_i == 0xFFFFFFFFu ? 0ull : ttv_argmax_key(__float_as_uint(best), best_i);
+    key = ttv_wave_max_u64(key);
+    if ((tid & (TTV_WAVE - 1)) == 0) s_red[tid / TTV_WAVE] = key;
+    __syncthreads();
+    if (tid == 0) {
+        uint64_t k = s_red[0];
+#pragma unroll
+        for (int w = 1; w < kArgmaxThreads / TTV_WAVE; ++w) k = s_red[w] > k ? s_red[w] : k;
+        partial[row * n_chunks + chunk] = k;
+    }
+}
+
+__global__ __launch_bounds__(kWalkThreads) void greedy_walk_kernel(
+    const int32_t* __restrict__ node_offsets, int32_t n_max, int64_t total_nodes, const uint64_t* __restrict__ partial,
+    int64_t n_chunks, const int32_t* __restrict__ tokens, const int32_t* __restrict__ next_token,
+    const int32_t* __restrict__ next_sibling, int32_t max_accept, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ accepted_nodes, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ row_argmax, int32_t* __restrict__ err) {
+    __shared__ int32_t s_choice[TTV_MAX_TREE_NODES + 1];
+    __shared__ int32_t s_tok[TTV_MAX_TREE_NODES];
+    __shared__ int32_t s_first[TTV_MAX_TREE_NODES];
+    __shared__ int32_t s_next[TTV_MAX_TREE_NODES];
+    __shared__ int32_t s_path[TTV_MAX_TREE_NODES + 1];
+    __shared__ int32_t s_len;
+    __shared__ int32_t s_bonus;
+
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int s = node_offsets[b];
+    const int n = node_offsets[b + 1] - s;
+    if (s < 0 || n < 0 || n > n_max || (int64_t)s + n > total_nodes) {  // uniform
+        if (tid == 0) {
+            accept_len[b] = 0;
+            atomicOr(err + b, TTV_ERR_TOO_MANY_NODES);
+        }
+        return;
+    }
+    const int64_t row0 = (int64_t)s + b;
+    for (int r = tid; r <= n; r += kWalkThreads) {
+        const uint64_t* pk = partial + (row0 + r) * n_chunks;
+        uint64_t k = pk[0];
+        for (int64_t c = 1; c < n_chunks; ++c) k = pk[c] > k ? pk[c] : k;
+        const int32_t choice = (int32_t)ttv_key_index(k);
+        s_choice[r] = choice;
+        if (row_argmax) row_argmax[row0 + r] = choice;
+    }
+    for (int i = tid; i < n; i += kWalkThreads) {
+        s_tok[i] = tokens[s + i];
+        s_first[i] = next_token[s + i];
+        s_next[i] = next_sibling[s + i];
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int a = 0, flags = 0;
+        int target = s_choice[0];
+        int j = n > 0 ? 0 : -1;  // node 0 is the root's first child (parent[0] == -1)
+        while (j >= 0) {
+            // scan the sibling list starting at j for the target token
+            while (j >= 0 && s_tok[j] != target) {
+                const int nx = s_next[j];
+                j = (nx > j && nx < n) ? nx : -1;
+            }
+            if (j < 0) break;
+            if (a == max_accept) {
+                flags |= TTV_ERR_ACCEPT;
+                break;
+            }
+            s_path[a++] = j;
+            target = s_choice[1 + j];
+            const int fc = s_first[j];
+            j = (fc > j && fc < n) ? fc : -1;
+        }
+        s_len = a;
+        s_bonus = target;
+        accept_len[b] = a;
+        if (flags) atomicOr(err + b, flags);
+    }
+    __syncthreads();
+    const int a = s_len;
+    for (int k = tid; k < max_accept; k += kWalkThreads)
+        accepted_nodes[(int64_t)b * max_accept + k] = k < a ? s_path[k] : -1;
+    for (int k = tid; k <= max_accept; k += kWalkThreads)
+        out_tokens[(int64_t)b * (max_accept + 1) + k] =
+            k < a ? s_tok[s_path[k]] : (k == a ? s_bonus : -1);
+}
+
+}  // namespace
+
+extern "C" TTV_API size_t tree_greedy_accept_workspace_bytes(const ttv_batch* bt, int64_t vocab) {
+    if (!bt || bt->batch < 0 || bt->total_nodes < 0 || vocab <= 0 || vocab >= (1ll << 31))
+        return 0;
+    const int64_t rows = bt->total_nodes + bt->batch;
+    const ChunkPlan p = plan_chunks(rows, vocab);
+    const size_t bytes = (size_t)rows * (size_t)p.n_chunks * sizeof(uint64_t);
+    return bytes > 0 ? bytes : 256;
+}
+
+extern "C" TTV_API int tree_greedy_accept(
+    const ttv_batch* bt, const void* logits, int32_t logits_dtype, int64_t vocab,
+    const int32_t* tokens, const int32_t* retrieve_next_token,
+    const int32_t* retrieve_next_sibling, int32_t max_accept, int32_t* accept_len,
+    int32_t* accepted_nodes, int32_t* out_tokens, int32_t* row_argmax, void* workspace,
+    size_t workspace_bytes, int32_t* err, hipStream_t stream) {
+    if (!bt || bt->batch < 0 || bt->n_max < 0 || bt->n_max > TTV_MAX_TREE_NODES ||
+        bt->total_nodes < 0 || bt->total_nodes > (int64_t)bt->batch * bt->n_max)
+        return TTV_EINVAL;
+    if (logits_dtype != TTV_DTYPE_FP32 && logits_dtype != TTV_DTYPE_BF16) return TTV_EINVAL;
+    if (vocab <= 0 || vocab >= (1ll << 31) || max_accept < 1 || max_accept > TTV_MAX_TREE_NODES)
+        return TTV_EINVAL;
+    if (bt->batch == 0) return TTV_OK;
+    if (!bt->node_offsets || !logits || !accept_len || !accepted_nodes || !out_tokens || !err ||
+        !workspace)
+        return TTV_EINVAL;
+    if (bt->total_nodes > 0 && (!tokens || !retrieve_next_token || !retrieve_next_sibling))
+        return TTV_EINVAL;
+    const size_t need = tree_greedy_accept_workspace_bytes(bt, vocab);
+    if (workspace_bytes < need) return TTV_ENOSPC;
+    const int64_t rows = bt->total_nodes + bt->batch;
+    const ChunkPlan p = plan_chunks(rows, vocab);
+    const int64_t grid = rows * p.n_chunks;
+    if (grid > 0x7FFFFFFF) return TTV_EINVAL;
+    uint64_t* partial = (uint64_t*)workspace;
+    if (logits_dtype == TTV_DTYPE_BF16)
+        hipLaunchKernelGGL(row_argmax_partial_kernel<true>, dim3((unsigned)grid),
+                           dim3(kArgmaxThreads), 0, stream, logits, vocab, p.chunk_len, p.n_chunks,
+                           partial);
+    else
+        hipLaunchKernelGGL(row_argmax_partial_kernel<false>, dim3((unsigned)grid),
+                           dim3(kArgmaxThreads), 0, stream, logits, vocab, p.chunk_len, p.n_chunks,
+                           partial);
+    if (hipGetLastError() != hipSuccess) return TTV_EHIP;
+    hipLaunchKernelGGL(greedy_walk_kernel, dim3(bt->batch), dim3(kWalkThreads), 0, stream,
+                       bt->node_offsets, bt->n_max, bt->total_nodes, partial, p.n_chunks, tokens,
+                       retrieve_next_token, retrieve_next_sibling, max_accept, accept_len,
+                       accepted_nodes, out_tokens, row_argmax, err);
+    return hipGetLastError() == hipSuccess ? TTV_OK : TTV_EHIP;
+}

@@ -1,0 +1,63 @@
+// Device-side helpers shared by the verification kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "treeverify.h"
+
+#define TTV_WAVE 64
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 ttv_bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float ttv_f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t ttv_u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t ttv_u32x2;
+
+// ---- bf16 <-> fp32 -------------------------------------------------------
+
+__device__ __forceinline__ float ttv_bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float ttv_bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round fp32 to bf16, nearest-even (finite inputs).
+__device__ __forceinline__ uint32_t ttv_f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t ttv_pack_bf16x2(float lo, float hi) {
+    return ttv_f32_to_bf16_bits(lo) | (ttv_f32_to_bf16_bits(hi) << 16);
+}
+
+// ---- ordered keys for argmax ---------------------------------------------
+
+// Map float bits to an unsigned key with the same order; -0.0 maps like +0.0.
+__device__ __forceinline__ uint32_t ttv_order_key(uint32_t fbits) {
+    if (fbits == 0x80000000u) fbits = 0u;
+    return (fbits & 0x80000000u) ? ~fbits : (fbits | 0x80000000u);
+}
+
+// 64-bit argmax key: larger value wins, then smaller index.
+__device__ __forceinline__ uint64_t ttv_argmax_key(uint32_t fbits, uint32_t idx) {
+    return ((uint64_t)ttv_order_key(fbits) << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+}
+
+__device__ __forceinline__ uint32_t ttv_key_index(uint64_t key) {
+    return 0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull);
+}
+
+// ---- wave reductions ------------------------------------------------------
+
+__device__ __forceinline__ uint64_t ttv_wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+        uint32_t olo = __shfl_xor(lo, off, TTV_WAVE);
+        uint32_t ohi = __shfl_xor(hi, off, TTV_WAVE);
+        uint64_t o = ((uint64_t)ohi << 32) | olo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int ttv_div_up(int a, int b) { return (a + b - 1) / b; }
