@@ -14,8 +14,11 @@ ddtree_deep).
 
 Inputs are uploaded before timing and rotated over enough copies (> 512 MB)
 that each step reads cold HBM rather than the 256 MB Infinity Cache.  W
-warm-up steps, then K timed steps between two synchronisations; the
-attention call is additionally bracketed by HIP events on its stream.
+eager warm-up steps; then exactly K steps are captured in one HIP graph (the
+way a serving loop replays a verify step per tree-size bucket) and one replay
+is timed between two synchronisations.  The attention call's duration comes
+from a second graph of K attention calls, timed with HIP events on its
+stream.  The eager (host-launched) time per step is reported too.
 
 Prints ONE JSON line: throughput in verified tree tokens/s (tree nodes per
 second), ms and us per step, the attention roofline (algorithmic bytes per
@@ -176,16 +179,12 @@ def main():
         pristine_tables.append(None if d["block_table"] is None else d["block_table"].clone())
     stream = torch.cuda.current_stream()
 
-    def run(i, ev=None):
+    def run(i):
         d, st = steps[i % n_sets]
         if pristine_tables[i % n_sets] is not None:
             d["block_table"].copy_(pristine_tables[i % n_sets], non_blocking=True)
         st.build(d["parents"])
-        if ev is not None:
-            ev[0].record(stream)
         st.attention(d["q"], d["k_new"], d["v_new"])
-        if ev is not None:
-            ev[1].record(stream)
         st.accept(d["logits"], d["tokens"])
         st.commit()
 
@@ -196,19 +195,59 @@ def main():
     if (errs != 0).any():
         print(f"device error bits after warm-up: {errs.tolist()}", file=sys.stderr)
         sys.exit(1)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    ref_acc = {k: v.clone() for k, v in steps[0][1].acc.items()}
+
+    # Eager timing (host-launched, for reference).
+    t0e = torch.cuda.Event(enable_timing=True)
+    t1e = torch.cuda.Event(enable_timing=True)
+    t0e.record(stream)
+    for k in range(args.steps):
+        run(args.warmup + k)
+    t1e.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = t0e.elapsed_time(t1e) / args.steps
+
+    # The timed region: exactly K steps captured in one HIP graph (rotating
+    # input sets), replayed once after one untimed replay.
+    g_step = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_step):
+        for k in range(args.steps):
+            run(k)
+    g_attn = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_attn):
+        for k in range(args.steps):
+            d, st = steps[k % n_sets]
+            st.attention(d["q"], d["k_new"], d["v_new"])
+    g_step.replay()
+    torch.cuda.synchronize()
+    for key, ref in ref_acc.items():  # graph replay reproduces the eager result
+        if not torch.equal(steps[0][1].acc[key], ref):
+            print(f"graph replay differs from eager in {key}", file=sys.stderr)
+            sys.exit(1)
+    stream = torch.cuda.current_stream()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for k in range(args.steps):
-        run(args.warmup + k, evs[k])
+    g_step.replay()
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    # Attention calls alone: K calls back to back, same stream, HIP events around the replay.
+    g_attn.replay()
+    torch.cuda.synchronize()
+    a0 = torch.cuda.Event(enable_timing=True)
+    a1 = torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    g_attn.replay()
+    a1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = a0.elapsed_time(a1) / args.steps
+    for key, ref in ref_acc.items():
+        if not torch.equal(steps[0][1].acc[key], ref):
+            print(f"graph replay differs from eager in {key}", file=sys.stderr)
+            sys.exit(1)
     attn_bytes, flops, accept_bytes = algorithmic(wl)
     acc_len = steps[0][1].acc["accept_len"].cpu().numpy()
     achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
@@ -221,6 +260,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms_step,
         "us_per_step": ms_step * 1e3,
+        "eager_us_per_step": eager_ms * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -228,7 +268,7 @@ def main():
         "data": "synthetic",
         "config": describe(wl),
         "roofline": {
-            "kernel": "tree_attention_verify (prep + main + combine launches, HIP events on its stream)",
+            "kernel": "tree_attention_verify call (prep + main + combine launches), K calls in one graph replay, HIP events on its stream",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

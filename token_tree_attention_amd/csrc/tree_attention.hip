@@ -33,6 +33,8 @@
 //  3. attn_combine_kernel: log-sum-exp merge of the chunks of row tiles whose
 //     context was split; single-chunk tiles are written directly by step 2.
 
+#include <type_traits>
+
 #include "ttv_device.h"
 
 namespace {
@@ -46,7 +48,7 @@ constexpr int kTargetItems = 1024;      // chunking aims at about this many work
 constexpr int kChunkMin = 256;          // shortest context chunk (slots)
 constexpr int kMaxBatch = 4096;         // plan keeps per-request prefix sums in LDS
 constexpr int kNumXcd = 8;
-constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kPreciseCtx = 256;       // requests with a shorter context run every tile precise
 constexpr float kNegBig = -1.0e30f;
 
 struct PlanHeader {
@@ -69,7 +71,7 @@ struct Combine {
 
 struct Layout {
     int64_t max_groups, max_items, max_partials;
-    size_t off_items, off_combine, off_q, off_po, off_pml, total;
+    size_t off_items, off_combine, off_q, off_qlo, off_po, off_pml, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -86,6 +88,8 @@ Layout make_layout(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D) {
     L.off_combine = off;
     off = align256(off + (size_t)L.max_groups * sizeof(Combine));
     L.off_q = off;
+    off = align256(off + (size_t)T * Hq * D * 2);
+    L.off_qlo = off;
     off = align256(off + (size_t)T * Hq * D * 2);
     L.off_po = off;
     off = align256(off + (size_t)L.max_partials * kTileM * D * 4);
@@ -279,8 +283,9 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
     int n_max, int64_t total_nodes, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ positions, CacheView cache, int Hq, float rope_base,
-    float q_mult, uint16_t* __restrict__ q_rot, PlanHeader* hdr, Item* items, Combine* combine,
-    int64_t max_items, int64_t max_groups, int64_t max_partials, int32_t* __restrict__ err) {
+    double q_mult, uint16_t* __restrict__ q_hi, uint16_t* __restrict__ q_lo, PlanHeader* hdr,
+    Item* items, Combine* combine, int64_t max_items, int64_t max_groups, int64_t max_partials,
+    int32_t* __restrict__ err) {
     const int b = blockIdx.y;
     const int Hkv = cache.hkv;
     const int G = Hq / Hkv;
@@ -299,40 +304,50 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
     if (i >= n) return;
     if (!cache.paged && (int64_t)ctx + n > cache.cap) return;  // flagged by the plan
 
-    __shared__ float s_cos[D / 2], s_sin[D / 2];
+    // Rotation in fp64: with fp32, x0 cos - x1 sin loses absolute accuracy
+    // when the two products nearly cancel, which shows up as several bf16
+    // ulps on small results.  The work is N_b * (Hq + Hkv) * D/2 pairs.
+    __shared__ double s_cos[D / 2], s_sin[D / 2];
     const int tid = threadIdx.x;
     const int node = s + i;
     const int pos = positions[node];
     if (tid < D / 2) {
-        // inv_freq_m = base^(-2m/D); the angle is reduced modulo 2*pi in fp64.
+        // inv_freq_m = base^(-2m/D); the angle is reduced modulo 2*pi first.
         const double inv = exp2(-(2.0 * tid / D) * log2((double)rope_base));
         const double ang = (double)pos * inv;
         const double two_pi = 6.283185307179586476925;
         const double red = ang - two_pi * rint(ang / two_pi);
-        float sn, cs;
-        sincosf((float)red, &sn, &cs);
+        double sn, cs;
+        sincos(red, &sn, &cs);
         s_cos[tid] = cs;
         s_sin[tid] = sn;
     }
     __syncthreads();
-    // Q: Hq * D elements, 8 per thread-step (16 bytes).
     constexpr int kVec = 8;
+    // Q: rotated, scaled by softmax_scale*log2(e), stored as bf16 hi + lo parts.
     const int q_vecs = Hq * D / kVec;
     for (int v = tid; v < q_vecs; v += kThreads) {
         const int64_t e = (int64_t)node * Hq * D + (int64_t)v * kVec;
         const ttv_u32x4 in = *(const ttv_u32x4*)(q + e);
         const int d0 = (v * kVec) % D;
-        ttv_u32x4 o;
+        ttv_u32x4 hi4, lo4;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const float x0 = ttv_bf16_lo(in[w]), x1 = ttv_bf16_hi(in[w]);
+            const double x0 = ttv_bf16_bits_to_f64(in[w] & 0xFFFFu);
+            const double x1 = ttv_bf16_bits_to_f64(in[w] >> 16);
             const int m = (d0 >> 1) + w;
-            const float c = s_cos[m], sn = s_sin[m];
-            o[w] = ttv_pack_bf16x2((x0 * c - x1 * sn) * q_mult, (x1 * c + x0 * sn) * q_mult);
+            const double c = s_cos[m], sn = s_sin[m];
+            const double r0 = (x0 * c - x1 * sn) * q_mult;
+            const double r1 = (x1 * c + x0 * sn) * q_mult;
+            const uint32_t h0 = ttv_f64_to_bf16_bits(r0), h1 = ttv_f64_to_bf16_bits(r1);
+            hi4[w] = h0 | (h1 << 16);
+            lo4[w] = ttv_f64_to_bf16_bits(r0 - ttv_bf16_bits_to_f64(h0)) |
+                     (ttv_f64_to_bf16_bits(r1 - ttv_bf16_bits_to_f64(h1)) << 16);
         }
-        *(ttv_u32x4*)(q_rot + e) = o;
+        *(ttv_u32x4*)(q_hi + e) = hi4;
+        *(ttv_u32x4*)(q_lo + e) = lo4;
     }
-    // K (rotated) and V (copied) into slot ctx + i of every KV head.
+    // K (rotated, rounded once from fp64) and V (copied) into slot ctx + i.
     const int kv_vecs = Hkv * D / kVec;
     for (int v = tid; v < kv_vecs; v += kThreads) {
         const int h = (v * kVec) / D;
@@ -347,10 +362,12 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
         ttv_u32x4 ko;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const float x0 = ttv_bf16_lo(kin[w]), x1 = ttv_bf16_hi(kin[w]);
+            const double x0 = ttv_bf16_bits_to_f64(kin[w] & 0xFFFFu);
+            const double x1 = ttv_bf16_bits_to_f64(kin[w] >> 16);
             const int m = (d0 >> 1) + w;
-            const float c = s_cos[m], sn = s_sin[m];
-            ko[w] = ttv_pack_bf16x2(x0 * c - x1 * sn, x1 * c + x0 * sn);
+            const double c = s_cos[m], sn = s_sin[m];
+            ko[w] = ttv_f64_to_bf16_bits(x0 * c - x1 * sn) |
+                    (ttv_f64_to_bf16_bits(x1 * c + x0 * sn) << 16);
         }
         *(ttv_u32x4*)(cache.k + dst + d0) = ko;
         *(ttv_u32x4*)(cache.v + dst + d0) = *(const ttv_u32x4*)(v_new + e);
@@ -365,8 +382,10 @@ template <int D>
 struct Smem {
     static constexpr int kKStride = D + 8;        // bf16 elements per K row (pad 16 B)
     static constexpr int kVStride = kKT + 4;      // bf16 elements per transposed V row (8-byte aligned rows)
+    static constexpr int kQStride = D + 8;        // bf16 elements per staged Q-lo row
     uint16_t k[2][kKT * kKStride];
     uint16_t vt[2][D * kVStride];
+    uint16_t qlo[kTileM * kQStride];              // low parts of the tile's Q (precise tiles)
 };
 
 template <int D>
@@ -448,9 +467,10 @@ __device__ __forceinline__ void store_tile(Smem<D>& sm, int buf,
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_main_kernel(
     const PlanHeader* __restrict__ hdr, const Item* __restrict__ items,
-    const uint16_t* __restrict__ q_rot, const uint32_t* __restrict__ mask, int mask_words,
-    CacheView cache, int Hq, uint16_t* __restrict__ out, float* __restrict__ part_o,
-    float2* __restrict__ part_ml, int32_t* __restrict__ err) {
+    const uint16_t* __restrict__ q_hi, const uint16_t* __restrict__ q_lo,
+    const uint32_t* __restrict__ mask, int mask_words, CacheView cache, int Hq,
+    uint16_t* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
+    int32_t* __restrict__ err) {
     __shared__ Smem<D> sm;
     constexpr int KC = D / 32;   // 32-wide k chunks of the head dim
     constexpr int DB = D / 16;   // 16-row blocks of the head dim
@@ -471,6 +491,14 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
         const Item it = items[x];
         const int rows = it.n * G;
         const int row_base = it.tile * kTileM + wave * kRowsPerWave;
+        const int n_ctx_tiles = (it.c1 - it.c0 + kKT - 1) / kKT;
+        const int n_tree_tiles = (it.kmax + kKT - 1) / kKT;
+        const int n_tiles = n_ctx_tiles + n_tree_tiles;
+        // Tiles where few keys can dominate a row's softmax get Q and P as
+        // bf16 hi + lo pairs (two MFMAs each): tree tiles, and every tile of a
+        // short-context request.
+        const bool precise_ctx = it.ctx < kPreciseCtx;
+        const bool any_precise = n_tree_tiles > 0 || precise_ctx;
 
         // Q^T operands: qreg[mb][kc] holds Q[row 16mb + l16][32kc + 8g4 .. +7].
         ttv_bf16x8 qreg[4][KC];
@@ -482,12 +510,26 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
             const int node = ok ? r / G : 0;
             const int g = ok ? r % G : 0;
             row_node[mb] = ok ? node : -1;
-            const uint16_t* src = q_rot + ((int64_t)(it.s + node) * Hq + it.kvh * G + g) * D;
+            const uint16_t* src = q_hi + ((int64_t)(it.s + node) * Hq + it.kvh * G + g) * D;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 ttv_u32x4 v = {0u, 0u, 0u, 0u};
                 if (ok) v = *(const ttv_u32x4*)(src + 32 * kc + 8 * g4);
                 qreg[mb][kc] = __builtin_bit_cast(ttv_bf16x8, v);
+            }
+        }
+        if (any_precise) {  // stage the tile's Q low parts in LDS
+            constexpr int kPieces = D / 8;
+            for (int p = tid; p < kTileM * kPieces; p += kThreads) {
+                const int rl = p / kPieces, piece = p % kPieces;
+                const int r = it.tile * kTileM + rl;
+                ttv_u32x4 v = {0u, 0u, 0u, 0u};
+                if (r < rows) {
+                    const int node = r / G, g = r % G;
+                    v = *(const ttv_u32x4*)(q_lo + ((int64_t)(it.s + node) * Hq + it.kvh * G + g) * D +
+                                            piece * 8);
+                }
+                *(ttv_u32x4*)(&sm.qlo[rl * Smem<D>::kQStride + piece * 8]) = v;
             }
         }
 
@@ -503,10 +545,6 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
             l_run[mb] = 0.f;
         }
 
-        const int n_ctx_tiles = (it.c1 - it.c0 + kKT - 1) / kKT;
-        const int n_tree_tiles = (it.kmax + kKT - 1) / kKT;
-        const int n_tiles = n_ctx_tiles + n_tree_tiles;
-
         ttv_u32x4 kreg[TileShape<D>::kKIter], vreg[2 * TileShape<D>::kVIter];
         auto tile_src = [&](int tau, int& slot0, int& valid) {
             if (tau < n_ctx_tiles) {
@@ -518,24 +556,14 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
                 valid = min(kKT, it.kmax - k0);
             }
         };
-        if (n_tiles > 0) {
-            int slot0, valid;
-            tile_src(0, slot0, valid);
-            load_tile<D>(cache, it.b, it.kvh, slot0, valid, kreg, vreg, tid, err);
-            store_tile<D>(sm, 0, kreg, vreg, tid);
-        }
-        __syncthreads();
-        for (int tau = 0; tau < n_tiles; ++tau) {
-            const int buf = tau & 1;
-            if (tau + 1 < n_tiles) {  // next tile in flight while this one is consumed
-                int slot0, valid;
-                tile_src(tau + 1, slot0, valid);
-                load_tile<D>(cache, it.b, it.kvh, slot0, valid, kreg, vreg, tid, err);
-            }
+
+        // One tile: scores, mask, online softmax, P.V.  kPrecise selects the
+        // hi + lo variant.
+        auto consume = [&](auto precise_tag, int tau, int buf) {
+            constexpr bool kPrecise = decltype(precise_tag)::value;
             int slot0, valid;
             tile_src(tau, slot0, valid);
             const bool tree = tau >= n_ctx_tiles;
-
             // S^T[key][row] for keys 16kb + 4g4 + r, rows 16mb + l16.
             ttv_f32x4 sacc[2][4];
 #pragma unroll
@@ -544,14 +572,25 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
                 for (int mb = 0; mb < 4; ++mb) sacc[kb][mb] = ttv_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
+                ttv_bf16x8 qlo[4];
+                if (kPrecise) {
+#pragma unroll
+                    for (int mb = 0; mb < 4; ++mb)
+                        qlo[mb] = *(const ttv_bf16x8*)(&sm.qlo[(wave * kRowsPerWave + 16 * mb + l16) *
+                                                                  Smem<D>::kQStride + 32 * kc + 8 * g4]);
+                }
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     const ttv_bf16x8 a = *(const ttv_bf16x8*)(
                         &sm.k[buf][(16 * kb + l16) * Smem<D>::kKStride + 32 * kc + 8 * g4]);
 #pragma unroll
-                    for (int mb = 0; mb < 4; ++mb)
-                        sacc[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            a, qreg[mb][kc], sacc[kb][mb], 0, 0, 0);
+                    for (int mb = 0; mb < 4; ++mb) {
+                        sacc[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[mb][kc],
+                                                                               sacc[kb][mb], 0, 0, 0);
+                        if (kPrecise)
+                            sacc[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[mb],
+                                                                                   sacc[kb][mb], 0, 0, 0);
+                    }
                 }
             }
             // Mask: keys past the valid count, and (tree tiles) non-ancestors.
@@ -566,7 +605,7 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
                 }
                 vis[mb] = w;
             }
-            ttv_bf16x8 pb[4];
+            ttv_bf16x8 pb[4], pl[4];
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
                 float sv[8];
@@ -586,16 +625,22 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
                 const float alpha = exp2f(m_run[mb] - m_new);
                 m_run[mb] = m_new;
                 float psum = 0.f;
-                uint32_t packed[4];
+                uint32_t packed[4], packed_lo[4];
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
                     const float p0 = exp2f(sv[e] - m_new);
                     const float p1 = exp2f(sv[e + 1] - m_new);
                     psum += p0 + p1;
                     packed[e >> 1] = ttv_pack_bf16x2(p0, p1);
+                    if (kPrecise)
+                        packed_lo[e >> 1] = ttv_pack_bf16x2(p0 - ttv_bf16_lo(packed[e >> 1]),
+                                                            p1 - ttv_bf16_hi(packed[e >> 1]));
                 }
                 l_run[mb] = l_run[mb] * alpha + psum;
                 pb[mb] = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{packed[0], packed[1], packed[2], packed[3]});
+                if (kPrecise)
+                    pl[mb] = __builtin_bit_cast(ttv_bf16x8,
+                                                ttv_u32x4{packed_lo[0], packed_lo[1], packed_lo[2], packed_lo[3]});
 #pragma unroll
                 for (int db = 0; db < DB; ++db) o[db][mb] *= alpha;
             }
@@ -608,10 +653,32 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
                 const ttv_u32x2 hi = *(const ttv_u32x2*)(vrow + 16 + 4 * g4);
                 const ttv_bf16x8 a = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
+                for (int mb = 0; mb < 4; ++mb) {
                     o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[mb], o[db][mb], 0, 0, 0);
+                    if (kPrecise)
+                        o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[mb], o[db][mb], 0, 0, 0);
+                }
             }
-            __syncthreads();  // everyone is done with buffer buf^1's previous contents
+        };
+
+        if (n_tiles > 0) {
+            int slot0, valid;
+            tile_src(0, slot0, valid);
+            load_tile<D>(cache, it.b, it.kvh, slot0, valid, kreg, vreg, tid, err);
+            store_tile<D>(sm, 0, kreg, vreg, tid);
+        }
+        __syncthreads();
+        for (int tau = 0; tau < n_tiles; ++tau) {
+            const int buf = tau & 1;
+            if (tau + 1 < n_tiles) {  // next tile in flight while this one is consumed
+                int slot0, valid;
+                tile_src(tau + 1, slot0, valid);
+                load_tile<D>(cache, it.b, it.kvh, slot0, valid, kreg, vreg, tid, err);
+            }
+            if (precise_ctx || tau >= n_ctx_tiles)
+                consume(std::integral_constant<bool, true>{}, tau, buf);
+            else
+                consume(std::integral_constant<bool, false>{}, tau, buf);
             if (tau + 1 < n_tiles) store_tile<D>(sm, buf ^ 1, kreg, vreg, tid);
             __syncthreads();
         }
@@ -647,6 +714,7 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
                     part_ml[(int64_t)it.pslot * kTileM + r_local] = make_float2(m_run[mb], l_run[mb]);
             }
         }
+        __syncthreads();  // the next item restages Q-lo and tile 0
     }
 }
 
@@ -728,7 +796,7 @@ template <int D>
 int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_new,
                      const uint16_t* v_new, const uint32_t* mask, int32_t mask_words,
                      const int32_t* positions, const ttv_kv_cache* cache, int32_t n_heads,
-                     float rope_base, float scale, uint16_t* out, char* ws, const Layout& L,
+                     float rope_base, double scale, uint16_t* out, char* ws, const Layout& L,
                      int32_t* err, hipStream_t stream) {
     CacheView cv;
     cv.k = (uint16_t*)cache->k;
@@ -742,14 +810,15 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
     PlanHeader* hdr = (PlanHeader*)ws;
     Item* items = (Item*)(ws + L.off_items);
     Combine* comb = (Combine*)(ws + L.off_combine);
-    uint16_t* q_rot = (uint16_t*)(ws + L.off_q);
+    uint16_t* q_hi = (uint16_t*)(ws + L.off_q);
+    uint16_t* q_lo = (uint16_t*)(ws + L.off_qlo);
     float* po = (float*)(ws + L.off_po);
     float2* pml = (float2*)(ws + L.off_pml);
-    const float q_mult = scale * kLog2e;
+    const double q_mult = scale * 1.4426950408889634074;  // scores come out in log2 units
     dim3 prep_grid(bt->n_max > 0 ? bt->n_max : 1, bt->batch + 1);
     hipLaunchKernelGGL(attn_prep_kernel<D>, prep_grid, dim3(kThreads), 0, stream,
                        bt->node_offsets, bt->ctx_lens, bt->batch, bt->n_max, bt->total_nodes, q,
-                       k_new, v_new, positions, cv, n_heads, rope_base, q_mult, q_rot, hdr, items,
+                       k_new, v_new, positions, cv, n_heads, rope_base, q_mult, q_hi, q_lo, hdr, items,
                        comb, L.max_items, L.max_groups, L.max_partials, err);
     if (hipGetLastError() != hipSuccess) return TTV_EHIP;
     const int cus = num_cus();
@@ -757,7 +826,7 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
     if (grid > L.max_items) grid = ((L.max_items + kNumXcd - 1) / kNumXcd) * kNumXcd;
     grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
     hipLaunchKernelGGL(attn_main_kernel<D>, dim3((unsigned)grid), dim3(kThreads), 0, stream, hdr,
-                       items, q_rot, mask, mask_words, cv, n_heads, out, po, pml, err);
+                       items, q_hi, q_lo, mask, mask_words, cv, n_heads, out, po, pml, err);
     if (hipGetLastError() != hipSuccess) return TTV_EHIP;
     hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((unsigned)(2 * cus)), dim3(kThreads), 0,
                        stream, hdr, comb, n_heads, cache->n_kv_heads, po, pml, out);
@@ -797,8 +866,8 @@ extern "C" TTV_API int tree_attention_verify(const ttv_batch* bt, const void* q,
     const Layout L =
         make_layout(bt->batch, bt->total_nodes, n_heads, cache->n_kv_heads, cache->head_dim);
     if (workspace_bytes < L.total) return TTV_ENOSPC;
-    const float scale =
-        softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)cache->head_dim);
+    const double scale =
+        softmax_scale > 0.f ? (double)softmax_scale : 1.0 / sqrt((double)cache->head_dim);
     if (cache->head_dim == 128)
         return launch_attention<128>(bt, (const uint16_t*)q, (const uint16_t*)k_new,
                                      (const uint16_t*)v_new, mask, mask_words, positions, cache,

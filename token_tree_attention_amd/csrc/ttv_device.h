@@ -25,6 +25,19 @@ __device__ __forceinline__ uint32_t ttv_f32_to_bf16_bits(float f) {
     return u >> 16;
 }
 
+// Round fp64 to bf16, nearest-even, without double rounding: truncate to fp32,
+// set the sticky bit when inexact (round to odd), then round fp32 -> bf16.
+__device__ __forceinline__ uint32_t ttv_f64_to_bf16_bits(double d) {
+    const float f = __double2float_rz(d);
+    uint32_t u = __float_as_uint(f);
+    if ((double)f != d) u |= 1u;
+    return ttv_f32_to_bf16_bits(__uint_as_float(u));
+}
+
+__device__ __forceinline__ double ttv_bf16_bits_to_f64(uint32_t h) {
+    return (double)__uint_as_float(h << 16);
+}
+
 __device__ __forceinline__ uint32_t ttv_pack_bf16x2(float lo, float hi) {
     return ttv_f32_to_bf16_bits(lo) | (ttv_f32_to_bf16_bits(hi) << 16);
 }
