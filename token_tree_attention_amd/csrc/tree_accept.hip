@@ -142,6 +142,7 @@ __global__ __launch_bounds__(kWalkThreads) void greedy_walk_kernel(
     for (int r = tid; r <= n; r += kWalkThreads) {
         const uint64_t* pk = partial + (row0 + r) * n_chunks;
         uint64_t k = pk[0];
+#pragma unroll 8
         for (int64_t c = 1; c < n_chunks; ++c) k = pk[c] > k ? pk[c] : k;
         const int32_t choice = (int32_t)ttv_key_index(k);
         s_choice[r] = choice;

@@ -39,8 +39,9 @@
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kRowsPerWave = 64;
+constexpr int kWaves = 8;
+constexpr int kRowsPerWave = 32;        // query rows per wave: kMB blocks of 16
+constexpr int kMB = kRowsPerWave / 16;
 constexpr int kTileM = kWaves * kRowsPerWave;
 constexpr int kThreads = kWaves * TTV_WAVE;
 constexpr int kKT = 32;                 // key slots per LDS tile (= one mask word)
@@ -49,6 +50,7 @@ constexpr int kChunkMin = 256;          // shortest context chunk (slots)
 constexpr int kMaxBatch = 4096;         // plan keeps per-request prefix sums in LDS
 constexpr int kNumXcd = 8;
 constexpr int kPreciseCtx = 256;       // requests with a shorter context run every tile precise
+constexpr float kLazyRescale = 8.0f;    // log2 headroom before the running max is moved
 constexpr float kNegBig = -1.0e30f;
 
 struct PlanHeader {
@@ -376,107 +378,168 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
 
 // ---------------------------------------------------------------------------
 // 2. Main kernel.
+//
+// LDS holds a ring of kStages (K tile, V tile) pairs, the tile's Q low parts
+// (precise tiles) and the tile nodes' mask rows, all filled by direct
+// global->LDS loads (global_load_lds: no registers hold data in flight).  A
+// tile is 32 key slots; wave w < kChunks loads chunk w of K and of V, so each
+// loading wave issues two DMA instructions per tile and waits on its own
+// vmcnt before a barrier publishes the tile.  The DMA is issued through
+// inline asm: the compiler then neither counts it nor guards every later LDS
+// read with a wait for all loads in flight; the explicit vmcnt ladder and the
+// raw barriers order it.
+//
+// K rows are stored with an XOR swizzle of their 16-byte pieces
+// (piece ^ row % P) so the 16 rows an MFMA operand read touches fall in
+// distinct banks.  V rows are stored row-major with piece ^ (2 row % P) and
+// read with ds_read_b64_tr_b16, which hands each lane four keys of one
+// head-dim column: exactly the V^T operand, no transposing store.
 // ---------------------------------------------------------------------------
 
 template <int D>
-struct Smem {
-    static constexpr int kKStride = D + 8;        // bf16 elements per K row (pad 16 B)
-    static constexpr int kVStride = kKT + 4;      // bf16 elements per transposed V row (8-byte aligned rows)
-    static constexpr int kQStride = D + 8;        // bf16 elements per staged Q-lo row
-    uint16_t k[2][kKT * kKStride];
-    uint16_t vt[2][D * kVStride];
-    uint16_t qlo[kTileM * kQStride];              // low parts of the tile's Q (precise tiles)
+struct MainCfg {
+    static constexpr int kPieces = D / 8;                  // 16-byte pieces per row
+    static constexpr int kRowBytes = D * 2;
+    static constexpr int kTileBytes = kKT * kRowBytes;     // one K or V tile
+    static constexpr int kChunkRows = 1024 / kRowBytes;    // rows per DMA instruction (64 x 16 B)
+    static constexpr int kChunks = kKT / kChunkRows;       // DMA instructions per K (or V) tile
+    static_assert(kChunks <= kWaves, "one K chunk and one V chunk per wave at most");
+    static constexpr int kStages = 4;
+    static constexpr int kStageBytes = 2 * kTileBytes;
+    static constexpr int kRingBytes = kStages * kStageBytes;
+    static constexpr int kQloBytes = kTileM * kRowBytes;
+    static constexpr int kQloChunks = kQloBytes / 1024;    // DMA instructions for the Q low parts
 };
 
-template <int D>
-struct TileShape {
-    static constexpr int kPieces = D / 8;                       // 16-byte pieces per row
-    static constexpr int kKIter = kKT * kPieces / kThreads;     // K pieces per thread
-    static constexpr int kVPairs = (kKT / 2) * kPieces;         // (key pair, piece) units
-    static constexpr int kVIter = (kVPairs + kThreads - 1) / kThreads;
-    static_assert(kKT * kPieces % kThreads == 0, "K tile must split evenly");
-};
+__device__ __forceinline__ int swz_k(int row, int piece, int P) { return piece ^ (row & (P - 1)); }
+__device__ __forceinline__ int swz_v(int row, int piece, int P) { return piece ^ ((2 * row) & (P - 1)); }
 
-template <int D>
-__device__ __forceinline__ void load_tile(const CacheView& c, int b, int kvh, int slot0,
-                                          int valid, ttv_u32x4 (&kreg)[TileShape<D>::kKIter],
-                                          ttv_u32x4 (&vreg)[2 * TileShape<D>::kVIter], int tid,
-                                          int32_t* err) {
-    using TS = TileShape<D>;
-#pragma unroll
-    for (int u = 0; u < TS::kKIter; ++u) {
-        const int p = tid + kThreads * u;
-        const int key = p / TS::kPieces, piece = p % TS::kPieces;
-        ttv_u32x4 val = {0u, 0u, 0u, 0u};
-        if (key < valid) {
-            const int64_t r = cache_row(c, b, kvh, slot0 + key, D);
-            if (r >= 0) val = *(const ttv_u32x4*)(c.k + r + piece * 8);
-            else atomicOr(err + b, TTV_ERR_BLOCK_TABLE);
-        }
-        kreg[u] = val;
-    }
-    // V: thread handles keys 2kp and 2kp+1 of one piece, for the transposed store.
-#pragma unroll
-    for (int u = 0; u < TS::kVIter; ++u) {
-        const int p = tid + kThreads * u;
-        const int kp = p / TS::kPieces, piece = p % TS::kPieces;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int key = 2 * kp + h;
-            ttv_u32x4 val = {0u, 0u, 0u, 0u};
-            if (p < TS::kVPairs && key < valid) {
-                const int64_t r = cache_row(c, b, kvh, slot0 + key, D);
-                if (r >= 0) val = *(const ttv_u32x4*)(c.v + r + piece * 8);
-            }
-            vreg[2 * u + h] = val;
-        }
-    }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    // s_waitcnt: vmcnt[3:0] | expcnt(7) << 4 | lgkmcnt(15) << 8 | vmcnt[5:4] << 14
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(Smem<D>& sm, int buf,
-                                           const ttv_u32x4 (&kreg)[TileShape<D>::kKIter],
-                                           const ttv_u32x4 (&vreg)[2 * TileShape<D>::kVIter],
-                                           int tid) {
-    using TS = TileShape<D>;
-#pragma unroll
-    for (int u = 0; u < TS::kKIter; ++u) {
-        const int p = tid + kThreads * u;
-        const int key = p / TS::kPieces, piece = p % TS::kPieces;
-        *(ttv_u32x4*)(&sm.k[buf][key * Smem<D>::kKStride + piece * 8]) = kreg[u];
-    }
-    uint32_t* base = (uint32_t*)&sm.vt[buf][0];
-#pragma unroll
-    for (int u = 0; u < TS::kVIter; ++u) {
-        const int p = tid + kThreads * u;
-        if (p >= TS::kVPairs) continue;
-        const int kp = p / TS::kPieces, piece = p % TS::kPieces;
-        const ttv_u32x4 a = vreg[2 * u], bb = vreg[2 * u + 1];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            // rows d = piece*8 + 2w and d + 1; columns (keys) 2kp, 2kp+1
-            const uint32_t lo = (a[w] & 0xFFFFu) | (bb[w] << 16);
-            const uint32_t hi = (a[w] >> 16) | (bb[w] & 0xFFFF0000u);
-            const int d = piece * 8 + 2 * w;
-            base[(d * Smem<D>::kVStride + 2 * kp) >> 1] = lo;
-            base[((d + 1) * Smem<D>::kVStride + 2 * kp) >> 1] = hi;
-        }
-    }
+// Wait until at most 2*k of this wave's loads are outstanding (k in 0..3).
+__device__ __forceinline__ void wait_vmcnt_pairs(int k) {
+    if (k >= 3) wait_vmcnt<6>();
+    else if (k == 2) wait_vmcnt<4>();
+    else if (k == 1) wait_vmcnt<2>();
+    else wait_vmcnt<0>();
 }
 
-template <int D>
+__device__ __forceinline__ void raw_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+typedef short ttv_i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) ttv_i16x4 lds_i16x4;
+typedef __bf16 ttv_bf16x2v __attribute__((ext_vector_type(2)));
+typedef float ttv_f32x2v __attribute__((ext_vector_type(2)));
+
+// Byte address of an LDS location, as the ds_* instructions take it.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// 16 (or 4) bytes per lane from global memory into LDS at base + lane * 16 (4).
+// lds_base must be wave-uniform.
+__device__ __forceinline__ void dma16(uint32_t lds_base, const void* g) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(g)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t lds_base, const void* g) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(base), "v"(g)
+                 : "memory", "m0");
+}
+
+// Round two floats to a bf16 pair (hardware round-to-nearest-even).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((ttv_f32x2v){a, b}, ttv_bf16x2v));
+}
+
+// max over the four lanes l, l^16, l^32, l^48 (the lane groups sharing a row)
+__device__ __forceinline__ float group_max(float t) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+    t = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float t) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+    t = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <int D, bool kPaged>
+__device__ __forceinline__ const uint16_t* kv_row_ptr(const CacheView& c, const uint16_t* base,
+                                                      int b, int h, int slot, int blk) {
+    if (!kPaged) return base + (((int64_t)b * c.hkv + h) * c.cap + slot) * D;
+    return base + (((int64_t)blk * c.hkv + h) * TTV_BLOCK_SIZE + (slot & 15)) * D;
+}
+
+// Issue the LDS-DMA loads of one tile (slots slot0 .. slot0 + valid - 1; rows
+// past valid repeat the last valid slot, so every LDS byte is defined).
+// Wave w < kChunks loads chunk w (kChunkRows rows) of K and of V.
+template <int D, bool kPaged>
+__device__ __forceinline__ void issue_tile(const CacheView& c, const int32_t* __restrict__ table,
+                                           int b, int kvh, int slot0, int valid, uint32_t stage,
+                                           int wave, int lane, int32_t* err) {
+    using MC = MainCfg<D>;
+    constexpr int P = MC::kPieces;
+    if (wave >= MC::kChunks) return;
+    const int r_first = min(wave * MC::kChunkRows, valid - 1);
+    int blk_first = 0, blk_last = 0;
+    if (kPaged) {
+        // wave-uniform scalar reads of the (at most two) blocks these rows touch
+        const int r_last = min(wave * MC::kChunkRows + MC::kChunkRows - 1, valid - 1);
+        const int lb0 = (slot0 + r_first) >> 4;
+        const int lb1 = (slot0 + r_last) >> 4;
+        blk_first = lb0 < c.max_blocks ? table[(int64_t)b * c.max_blocks + lb0] : -1;
+        blk_last = lb1 < c.max_blocks ? table[(int64_t)b * c.max_blocks + lb1] : -1;
+        if (blk_first < 0 || blk_first >= c.num_blocks || blk_last < 0 || blk_last >= c.num_blocks) {
+            if (lane == 0) atomicOr(err + b, TTV_ERR_BLOCK_TABLE);
+            blk_first = blk_last = 0;  // load a valid block; the request is flagged
+        }
+    }
+    const int row = wave * MC::kChunkRows + lane / P;
+    const int phys = lane % P;
+    const int slot = slot0 + min(row, valid - 1);
+    const int blk = (!kPaged || (slot >> 4) == ((slot0 + r_first) >> 4)) ? blk_first : blk_last;
+    const uint16_t* krow = kv_row_ptr<D, kPaged>(c, c.k, b, kvh, slot, blk);
+    const uint16_t* vrow = kv_row_ptr<D, kPaged>(c, c.v, b, kvh, slot, blk);
+    const uint32_t chunk_off = wave * MC::kChunkRows * MC::kRowBytes;
+    dma16(stage + chunk_off, krow + 8 * swz_k(row, phys, P));
+    dma16(stage + MC::kTileBytes + chunk_off, vrow + 8 * swz_v(row, phys, P));
+}
+
+template <int D, bool kPaged>
 __global__ __launch_bounds__(kThreads) void attn_main_kernel(
     const PlanHeader* __restrict__ hdr, const Item* __restrict__ items,
-    const uint16_t* __restrict__ q_hi, const uint16_t* __restrict__ q_lo,
-    const uint32_t* __restrict__ mask, int mask_words, CacheView cache, int Hq,
-    uint16_t* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    int32_t* __restrict__ err) {
-    __shared__ Smem<D> sm;
+    const uint16_t* q_hi,  // not __restrict__: keeps its loads ahead of the prologue fence
+    const uint16_t* __restrict__ q_lo, const uint32_t* __restrict__ mask, int mask_words,
+    CacheView cache, const int32_t* __restrict__ table, int Hq, uint16_t* __restrict__ out,
+    float* __restrict__ part_o, float2* __restrict__ part_ml, int32_t* __restrict__ err) {
+    using MC = MainCfg<D>;
+    constexpr int P = MC::kPieces;
     constexpr int KC = D / 32;   // 32-wide k chunks of the head dim
     constexpr int DB = D / 16;   // 16-row blocks of the head dim
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const uint32_t ring = lds_offset(smem);
+    const uint32_t qlo_s = ring + MC::kRingBytes;
+    const uint32_t mask_base = qlo_s + MC::kQloBytes;
+    const uint32_t* mask_s = (const uint32_t*)(smem + MC::kRingBytes + MC::kQloBytes);
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave index as a scalar, so branches on it stay uniform (an exec-masked
+    // branch would run both sides' s_waitcnt)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15;
     const int g4 = lane >> 4;
     const int n_items = hdr->n_items;
@@ -486,6 +549,13 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
     // workgroup x on XCD x % 8).
     const int per_xcd = gridDim.x / kNumXcd;
     const int vid = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
+
+    // Per-lane LDS byte offsets inside a stage / the Q-lo block.
+    uint32_t koff[KC];  // K operand: row l16 (+16 kb), piece 4kc + g4
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) koff[kc] = l16 * MC::kRowBytes + 16 * swz_k(l16, 4 * kc + g4, P);
+    const int tr_row = 4 * g4 + (l16 >> 2);     // V^T operand rows (16h + tr_row)
+    const int tr_col = 4 * (l16 & 3);          // head-dim offset inside a 16-block
 
     for (int x = vid; x < n_items; x += gridDim.x) {
         const Item it = items[x];
@@ -499,92 +569,109 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
         // short-context request.
         const bool precise_ctx = it.ctx < kPreciseCtx;
         const bool any_precise = n_tree_tiles > 0 || precise_ctx;
+        const int node0 = (it.tile * kTileM) / G;
+        const int node1 = min(it.n - 1, (it.tile * kTileM + kTileM - 1) / G);
+        const int tree_limit = it.ctx + it.kmax;
+        auto tile_slot0 = [&](int tau) {
+            return tau < n_ctx_tiles ? it.c0 + tau * kKT : it.ctx + (tau - n_ctx_tiles) * kKT;
+        };
+        auto tile_valid = [&](int tau, int slot0) {
+            return min(kKT, (tau < n_ctx_tiles ? it.c1 : tree_limit) - slot0);
+        };
+        auto issue = [&](int tau) {
+            const int slot0 = tile_slot0(tau);
+            issue_tile<D, kPaged>(cache, table, it.b, it.kvh, slot0, tile_valid(tau, slot0),
+                                  ring + (tau % MC::kStages) * MC::kStageBytes, wave, lane, err);
+        };
 
-        // Q^T operands: qreg[mb][kc] holds Q[row 16mb + l16][32kc + 8g4 .. +7].
-        ttv_bf16x8 qreg[4][KC];
-        int row_node[4];
+        // ---- prologue: Q lo, mask rows and the first tiles go to LDS by DMA,
+        // then Q hi into registers with ordinary loads; one wait covers all of
+        // them (they are in flight together), so the tile loop below starts
+        // with nothing but tiles outstanding.
+        if (any_precise) {
+            // Q low parts, swizzled like K; rows past the tile's last row
+            // repeat that row (finite, never written out)
+            for (int j = wave; j < MC::kQloChunks; j += kWaves) {
+                const int rl = j * MC::kChunkRows + lane / P;
+                const int phys = lane % P;
+                const int r = min(it.tile * kTileM + rl, rows - 1);
+                const int node = r / G, g = r % G;
+                dma16(qlo_s + j * 1024,
+                      q_lo + ((int64_t)(it.s + node) * Hq + it.kvh * G + g) * D + 8 * swz_k(rl, phys, P));
+            }
+        }
+        if (n_tree_tiles > 0) {
+            // the tile nodes' mask rows, copied flat (row stride mask_words)
+            const int words = (node1 - node0 + 1) * mask_words;
+            const uint32_t* src = mask + (int64_t)(it.s + node0) * mask_words;
+            for (int j = wave; j * 64 < words; j += kWaves)
+                dma4(mask_base + j * 256, src + min(j * 64 + lane, words - 1));
+        }
+        constexpr int kAhead = MC::kStages - 1;
+        for (int j = 0; j < kAhead && j < n_tiles; ++j) issue(j);
+        ttv_bf16x8 qreg[kMB][KC];
+        int row_node[kMB];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < kMB; ++mb) {
             const int r = row_base + 16 * mb + l16;
             const bool ok = r < rows;
-            const int node = ok ? r / G : 0;
-            const int g = ok ? r % G : 0;
-            row_node[mb] = ok ? node : -1;
+            const int rc = min(r, rows - 1);  // rows past the tile end reuse its last row
+            const int node = rc / G, g = rc % G;
+            row_node[mb] = ok ? node - node0 : -1;
             const uint16_t* src = q_hi + ((int64_t)(it.s + node) * Hq + it.kvh * G + g) * D;
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                ttv_u32x4 v = {0u, 0u, 0u, 0u};
-                if (ok) v = *(const ttv_u32x4*)(src + 32 * kc + 8 * g4);
-                qreg[mb][kc] = __builtin_bit_cast(ttv_bf16x8, v);
-            }
+            for (int kc = 0; kc < KC; ++kc)
+                qreg[mb][kc] = *(const ttv_bf16x8*)(src + 32 * kc + 8 * g4);
         }
-        if (any_precise) {  // stage the tile's Q low parts in LDS
-            constexpr int kPieces = D / 8;
-            for (int p = tid; p < kTileM * kPieces; p += kThreads) {
-                const int rl = p / kPieces, piece = p % kPieces;
-                const int r = it.tile * kTileM + rl;
-                ttv_u32x4 v = {0u, 0u, 0u, 0u};
-                if (r < rows) {
-                    const int node = r / G, g = r % G;
-                    v = *(const ttv_u32x4*)(q_lo + ((int64_t)(it.s + node) * Hq + it.kvh * G + g) * D +
-                                            piece * 8);
-                }
-                *(ttv_u32x4*)(&sm.qlo[rl * Smem<D>::kQStride + piece * 8]) = v;
-            }
-        }
+        // A full wait and a fenced barrier (not the loop's raw one, so the two
+        // cannot be merged): Q lo, mask rows and tiles 0..2 are in LDS and Q
+        // hi in registers before the loop, which then carries no compiler
+        // wait on the tiles in flight.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
 
-        ttv_f32x4 o[DB][4];
+        ttv_f32x4 o[DB][kMB];
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) o[db][mb] = ttv_f32x4{0.f, 0.f, 0.f, 0.f};
-        float m_run[4], l_run[4];
+            for (int mb = 0; mb < kMB; ++mb) o[db][mb] = ttv_f32x4{0.f, 0.f, 0.f, 0.f};
+        float m_run[kMB], l_run[kMB];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < kMB; ++mb) {
             m_run[mb] = kNegBig;
             l_run[mb] = 0.f;
         }
 
-        ttv_u32x4 kreg[TileShape<D>::kKIter], vreg[2 * TileShape<D>::kVIter];
-        auto tile_src = [&](int tau, int& slot0, int& valid) {
-            if (tau < n_ctx_tiles) {
-                slot0 = it.c0 + tau * kKT;
-                valid = min(kKT, it.c1 - slot0);
-            } else {
-                const int k0 = (tau - n_ctx_tiles) * kKT;
-                slot0 = it.ctx + k0;
-                valid = min(kKT, it.kmax - k0);
-            }
-        };
-
-        // One tile: scores, mask, online softmax, P.V.  kPrecise selects the
-        // hi + lo variant.
-        auto consume = [&](auto precise_tag, int tau, int buf) {
+        // One tile: scores, mask, online softmax (lazy rescale), P.V.
+        auto consume = [&](auto precise_tag, int tau) {
             constexpr bool kPrecise = decltype(precise_tag)::value;
-            int slot0, valid;
-            tile_src(tau, slot0, valid);
+            const uint32_t kst = ring + (tau % MC::kStages) * MC::kStageBytes;
+            const uint32_t vst = kst + MC::kTileBytes;
+            const int valid = tile_valid(tau, tile_slot0(tau));
             const bool tree = tau >= n_ctx_tiles;
             // S^T[key][row] for keys 16kb + 4g4 + r, rows 16mb + l16.
-            ttv_f32x4 sacc[2][4];
+            ttv_f32x4 sacc[2][kMB];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) sacc[kb][mb] = ttv_f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int mb = 0; mb < kMB; ++mb) sacc[kb][mb] = ttv_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
-                ttv_bf16x8 qlo[4];
+                ttv_bf16x8 qlo[kMB];
                 if (kPrecise) {
 #pragma unroll
-                    for (int mb = 0; mb < 4; ++mb)
-                        qlo[mb] = *(const ttv_bf16x8*)(&sm.qlo[(wave * kRowsPerWave + 16 * mb + l16) *
-                                                                  Smem<D>::kQStride + 32 * kc + 8 * g4]);
+                    for (int mb = 0; mb < kMB; ++mb) {
+                        const int rl = wave * kRowsPerWave + 16 * mb + l16;
+                        qlo[mb] = *(const ttv_bf16x8*)(smem + (qlo_s - ring) + rl * MC::kRowBytes +
+                                                       16 * swz_k(rl, 4 * kc + g4, P));
+                    }
                 }
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const ttv_bf16x8 a = *(const ttv_bf16x8*)(
-                        &sm.k[buf][(16 * kb + l16) * Smem<D>::kKStride + 32 * kc + 8 * g4]);
+                    const ttv_bf16x8 a = *(const ttv_bf16x8*)(smem + (kst - ring) + koff[kc] +
+                                                              kb * 16 * MC::kRowBytes);
 #pragma unroll
-                    for (int mb = 0; mb < 4; ++mb) {
+                    for (int mb = 0; mb < kMB; ++mb) {
                         sacc[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[mb][kc],
                                                                                sacc[kb][mb], 0, 0, 0);
                         if (kPrecise)
@@ -593,67 +680,82 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
                     }
                 }
             }
-            // Mask: keys past the valid count, and (tree tiles) non-ancestors.
-            uint32_t vis[4];
+            // Mask (in place) on partial and tree tiles only.
+            if (tree || valid < kKT) {
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                uint32_t w = valid >= 32 ? 0xFFFFFFFFu : ((1u << valid) - 1u);
-                if (tree) {
-                    const int k0 = (tau - n_ctx_tiles) * kKT;
-                    const int node = row_node[mb];
-                    w &= node >= 0 ? mask[(int64_t)(it.s + node) * mask_words + (k0 >> 5)] : 0u;
-                }
-                vis[mb] = w;
-            }
-            ttv_bf16x8 pb[4], pl[4];
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                float sv[8];
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int key = 16 * kb + 4 * g4 + r;
-                        sv[4 * kb + r] = ((vis[mb] >> key) & 1u) ? sacc[kb][mb][r] : -INFINITY;
+                for (int mb = 0; mb < kMB; ++mb) {
+                    uint32_t w = valid >= 32 ? 0xFFFFFFFFu : ((1u << valid) - 1u);
+                    if (tree) {
+                        const int nl = row_node[mb];
+                        w &= nl >= 0 ? mask_s[nl * mask_words + (tau - n_ctx_tiles)] : 0u;
                     }
-                float tmax = sv[0];
+                    w >>= 4 * g4;
 #pragma unroll
-                for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, sv[e]);
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 16, TTV_WAVE));
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 32, TTV_WAVE));
-                const float m_new = fmaxf(m_run[mb], tmax);
-                const float alpha = exp2f(m_run[mb] - m_new);
-                m_run[mb] = m_new;
-                float psum = 0.f;
-                uint32_t packed[4], packed_lo[4];
+                    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const float p0 = exp2f(sv[e] - m_new);
-                    const float p1 = exp2f(sv[e + 1] - m_new);
-                    psum += p0 + p1;
-                    packed[e >> 1] = ttv_pack_bf16x2(p0, p1);
-                    if (kPrecise)
-                        packed_lo[e >> 1] = ttv_pack_bf16x2(p0 - ttv_bf16_lo(packed[e >> 1]),
-                                                            p1 - ttv_bf16_hi(packed[e >> 1]));
+                        for (int r = 0; r < 4; ++r)
+                            if (!((w >> (16 * kb + r)) & 1u)) sacc[kb][mb][r] = -INFINITY;
                 }
-                l_run[mb] = l_run[mb] * alpha + psum;
-                pb[mb] = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{packed[0], packed[1], packed[2], packed[3]});
-                if (kPrecise)
-                    pl[mb] = __builtin_bit_cast(ttv_bf16x8,
-                                                ttv_u32x4{packed_lo[0], packed_lo[1], packed_lo[2], packed_lo[3]});
-#pragma unroll
-                for (int db = 0; db < DB; ++db) o[db][mb] *= alpha;
             }
-            // O^T[d][row] += V^T[d][key] P^T[key][row]; MFMA k index 8g4 + j maps to
-            // key 4g4 + j (j < 4) and 16 + 4g4 + j - 4 (j >= 4).
+            float tmax[kMB];
+            bool need = false;
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb) {
+                float t = fmaxf(fmaxf(fmaxf(sacc[0][mb][0], sacc[0][mb][1]), fmaxf(sacc[0][mb][2], sacc[0][mb][3])),
+                                fmaxf(fmaxf(sacc[1][mb][0], sacc[1][mb][1]), fmaxf(sacc[1][mb][2], sacc[1][mb][3])));
+                t = group_max(t);
+                tmax[mb] = t;
+                need |= t > m_run[mb] + kLazyRescale;
+            }
+            // Lazy rescale: keep the running max unless some row's max grew by
+            // more than 2^kLazyRescale (then p <= 2^kLazyRescale meanwhile).
+            if (__ballot(need)) {
+#pragma unroll
+                for (int mb = 0; mb < kMB; ++mb) {
+                    const float m_new = fmaxf(m_run[mb], tmax[mb]);
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[mb] - m_new);
+                    m_run[mb] = m_new;
+                    l_run[mb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) o[db][mb] *= alpha;
+                }
+            }
+            ttv_bf16x8 pb[kMB], pl[kMB];
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb) {
+                float p[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sacc[e >> 2][mb][e & 3] - m_run[mb]);
+                l_run[mb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+                uint32_t packed[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) packed[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
+                pb[mb] = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{packed[0], packed[1], packed[2], packed[3]});
+                if (kPrecise) {
+                    uint32_t lo[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        lo[e] = pack_bf16(p[2 * e] - ttv_bf16_lo(packed[e]), p[2 * e + 1] - ttv_bf16_hi(packed[e]));
+                    pl[mb] = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{lo[0], lo[1], lo[2], lo[3]});
+                }
+            }
+            // O^T[d][row] += V^T[d][key] P^T[key][row].  MFMA k index 8g4 + j
+            // is key 4g4 + j (j < 4) or 16 + 4g4 + j - 4 (j >= 4); each half
+            // comes from one ds_read_b64_tr_b16 over rows 16h + 4g4 .. +3.
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const uint16_t* vrow = &sm.vt[buf][(16 * db + l16) * Smem<D>::kVStride];
-                const ttv_u32x2 lo = *(const ttv_u32x2*)(vrow + 4 * g4);
-                const ttv_u32x2 hi = *(const ttv_u32x2*)(vrow + 16 + 4 * g4);
-                const ttv_bf16x8 a = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{lo[0], lo[1], hi[0], hi[1]});
+                ttv_i16x4 half[2];
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
+                for (int h = 0; h < 2; ++h) {
+                    const int row = 16 * h + tr_row;
+                    const int d = 16 * db + tr_col;
+                    const uint32_t addr = vst + row * MC::kRowBytes + 16 * swz_v(row, d >> 3, P) + 2 * (d & 7);
+                    half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
+                }
+                const ttv_bf16x8 a = __builtin_bit_cast(
+                    ttv_bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                for (int mb = 0; mb < kMB; ++mb) {
                     o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[mb], o[db][mb], 0, 0, 0);
                     if (kPrecise)
                         o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[mb], o[db][mb], 0, 0, 0);
@@ -661,37 +763,27 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
             }
         };
 
-        if (n_tiles > 0) {
-            int slot0, valid;
-            tile_src(0, slot0, valid);
-            load_tile<D>(cache, it.b, it.kvh, slot0, valid, kreg, vreg, tid, err);
-            store_tile<D>(sm, 0, kreg, vreg, tid);
-        }
-        __syncthreads();
-        for (int tau = 0; tau < n_tiles; ++tau) {
-            const int buf = tau & 1;
-            if (tau + 1 < n_tiles) {  // next tile in flight while this one is consumed
-                int slot0, valid;
-                tile_src(tau + 1, slot0, valid);
-                load_tile<D>(cache, it.b, it.kvh, slot0, valid, kreg, vreg, tid, err);
+        auto step = [&](int tau) {
+            if (tau > 0) {
+                // this wave's loads of tile tau have landed; later tiles may
+                // stay in flight
+                if (wave < MC::kChunks) wait_vmcnt_pairs(min(kAhead - 1, n_tiles - 1 - tau));
+                raw_barrier();  // tile tau visible to all waves; stage of tau-1 free
             }
+            if (tau + kAhead < n_tiles) issue(tau + kAhead);
             if (precise_ctx || tau >= n_ctx_tiles)
-                consume(std::integral_constant<bool, true>{}, tau, buf);
+                consume(std::integral_constant<bool, true>{}, tau);
             else
-                consume(std::integral_constant<bool, false>{}, tau, buf);
-            if (tau + 1 < n_tiles) store_tile<D>(sm, buf ^ 1, kreg, vreg, tid);
-            __syncthreads();
-        }
+                consume(std::integral_constant<bool, false>{}, tau);
+        };
+        for (int tau = 0; tau < n_tiles; ++tau) step(tau);
 
         // Row sums across the 4 lane groups holding a row's keys.
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            l_run[mb] += __shfl_xor(l_run[mb], 16, TTV_WAVE);
-            l_run[mb] += __shfl_xor(l_run[mb], 32, TTV_WAVE);
-        }
+        for (int mb = 0; mb < kMB; ++mb) l_run[mb] = group_sum(l_run[mb]);
         // Lane holds O^T[d = 16db + 4g4 + r][row 16mb + l16].
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < kMB; ++mb) {
             const int r_local = wave * kRowsPerWave + 16 * mb + l16;
             const int r = it.tile * kTileM + r_local;
             if (r >= rows) continue;
@@ -702,8 +794,8 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     ttv_u32x2 w;
-                    w[0] = ttv_pack_bf16x2(o[db][mb][0] * inv_l, o[db][mb][1] * inv_l);
-                    w[1] = ttv_pack_bf16x2(o[db][mb][2] * inv_l, o[db][mb][3] * inv_l);
+                    w[0] = pack_bf16(o[db][mb][0] * inv_l, o[db][mb][1] * inv_l);
+                    w[1] = pack_bf16(o[db][mb][2] * inv_l, o[db][mb][3] * inv_l);
                     *(ttv_u32x2*)(dst + 16 * db + 4 * g4) = w;
                 }
             } else {
@@ -714,8 +806,16 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
                     part_ml[(int64_t)it.pslot * kTileM + r_local] = make_float2(m_run[mb], l_run[mb]);
             }
         }
-        __syncthreads();  // the next item restages Q-lo and tile 0
+        __syncthreads();  // LDS (ring, Q-lo, mask) is reused by the next item
     }
+}
+
+template <int D>
+size_t main_lds_bytes(int G, int mask_words) {
+    using MC = MainCfg<D>;
+    const int nodes = kTileM / G + 2;
+    const size_t mask_bytes = (size_t)((nodes * mask_words + 63) / 64) * 256;
+    return (size_t)MC::kRingBytes + MC::kQloBytes + mask_bytes;
 }
 
 // ---------------------------------------------------------------------------
@@ -739,18 +839,21 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(
         const int d = (tid % kLanesPerRow) * 4;
         const int r = cb.tile * kTileM + r_local;
         if (r >= cb.n * G) continue;
-        float mmax = kNegBig;
-        for (int c = 0; c < cb.nc; ++c)
-            mmax = fmaxf(mmax, part_ml[(int64_t)(cb.pslot0 + c * cb.stride) * kTileM + r_local].x);
-        float lsum = 0.f;
+        // One pass with a running max; the chunk loads are independent, so the
+        // unrolled loop keeps several in flight.
+        float mmax = kNegBig, lsum = 0.f;
         ttv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
         for (int c = 0; c < cb.nc; ++c) {
             const int64_t ps = cb.pslot0 + (int64_t)c * cb.stride;
             const float2 ml = part_ml[ps * kTileM + r_local];
-            const float w = exp2f(ml.x - mmax);
-            lsum += w * ml.y;
             const ttv_f32x4 v = *(const ttv_f32x4*)(part_o + (ps * kTileM + r_local) * D + d);
-            acc += w * v;
+            const float m_new = fmaxf(mmax, ml.x);
+            const float a_old = __builtin_amdgcn_exp2f(mmax - m_new);
+            const float a_new = __builtin_amdgcn_exp2f(ml.x - m_new);
+            lsum = lsum * a_old + ml.y * a_new;
+            acc = acc * a_old + v * a_new;
+            mmax = m_new;
         }
         const float inv = 1.0f / lsum;
         const int node = r / G, g = r % G;
@@ -825,8 +928,16 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
     int64_t grid = (int64_t)cus;  // one 256-row workgroup per CU (LDS and registers bound it)
     if (grid > L.max_items) grid = ((L.max_items + kNumXcd - 1) / kNumXcd) * kNumXcd;
     grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
-    hipLaunchKernelGGL(attn_main_kernel<D>, dim3((unsigned)grid), dim3(kThreads), 0, stream, hdr,
-                       items, q_hi, q_lo, mask, mask_words, cv, n_heads, out, po, pml, err);
+    const size_t lds = main_lds_bytes<D>(n_heads / cache->n_kv_heads, mask_words);
+    if (lds > 160 * 1024) return TTV_EINVAL;
+    auto kern = cv.paged ? attn_main_kernel<D, true> : attn_main_kernel<D, false>;
+    static bool attr_set[2] = {false, false};
+    if (!attr_set[cv.paged]) {
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        attr_set[cv.paged] = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, stream, hdr, items, q_hi,
+                       q_lo, mask, mask_words, cv, cache->block_table, n_heads, out, po, pml, err);
     if (hipGetLastError() != hipSuccess) return TTV_EHIP;
     hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((unsigned)(2 * cus)), dim3(kThreads), 0,
                        stream, hdr, comb, n_heads, cache->n_kv_heads, po, pml, out);
