@@ -29,6 +29,7 @@ a bounded sample of the same workload.
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -131,6 +132,45 @@ def cpu_baseline(wl, budget_s):
                       f"per-node path attention, argmax+walk of those requests ({dt:.1f} s)"}
 
 
+def copy_reference(args, dev):
+    """K plain copies of a fixed buffer: the known-size kernel that FETCH_SIZE and
+    WRITE_SIZE are scaled by."""
+    import torch
+    nbytes = int(args.copy_reference * 1e6) // 4096 * 4096
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).random_()
+    dst = torch.empty_like(src)
+    for _ in range(max(1, args.warmup)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"copy_reference_bytes": nbytes, "steps": args.steps,
+                      "us_per_copy": dt * 1e6, "GBps_read_plus_write": 2 * nbytes / dt / 1e9}))
+
+
+def stored_traffic(workload):
+    """HBM bytes per attention call from the committed counter summary, or None
+    when the summary is missing or the attention source changed since."""
+    import hashlib
+    src = os.path.join(ROOT, "token_tree_attention_amd", "csrc", "tree_attention.hip")
+    path = os.path.join(ROOT, "profiles", f"tree_attention_{workload}_hbm_counters.md")
+    try:
+        text = open(path).read()
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = dict(re.findall(r"^- (\w+): (\S+)$", text, re.M))
+    if fields.get("source_sha256") != digest:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,10 +182,15 @@ def main():
                     help="rotate input copies until this many MB are in play (defeats the MALL)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--eager-only", action="store_true",
+                    help="host-launched steps only, no graph capture (for counter collection)")
+    ap.add_argument("--copy-reference", type=float, default=0.0, metavar="MB",
+                    help="instead of the path, run K device-to-device copies of MB megabytes "
+                         "(the reference kernel for scaling the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the verification path "
-              f"has no multi-GPU mode in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU (asked for --gpus {args.gpus}); the verification path "
+              f"runs on a single GPU and has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -159,9 +204,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
-    tta.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_reference > 0:
+        copy_reference(args, dev)
+        return
+    tta.load_library()
     cfg = WORKLOADS[args.workload]
     wl = synth.make_workload(cfg, args.seed)
     base = to_device(wl, dev)
@@ -207,47 +255,52 @@ def main():
     torch.cuda.synchronize()
     eager_ms = t0e.elapsed_time(t1e) / args.steps
 
-    # The timed region: exactly K steps captured in one HIP graph (rotating
-    # input sets), replayed once after one untimed replay.
-    g_step = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_step):
-        for k in range(args.steps):
-            run(k)
-    g_attn = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_attn):
+    def check_replay():
+        for key, ref in ref_acc.items():  # a replay reproduces the eager result
+            if not torch.equal(steps[0][1].acc[key], ref):
+                print(f"graph replay differs from eager in {key}", file=sys.stderr)
+                sys.exit(1)
+
+    def timed(fn):
+        """fn() between two HIP events on the stream the kernels run on (ms)."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    def attention_calls():
         for k in range(args.steps):
             d, st = steps[k % n_sets]
             st.attention(d["q"], d["k_new"], d["v_new"])
-    g_step.replay()
-    torch.cuda.synchronize()
-    for key, ref in ref_acc.items():  # graph replay reproduces the eager result
-        if not torch.equal(steps[0][1].acc[key], ref):
-            print(f"graph replay differs from eager in {key}", file=sys.stderr)
-            sys.exit(1)
-    stream = torch.cuda.current_stream()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    g_step.replay()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
-    # Attention calls alone: K calls back to back, same stream, HIP events around the replay.
-    g_attn.replay()
-    torch.cuda.synchronize()
-    a0 = torch.cuda.Event(enable_timing=True)
-    a1 = torch.cuda.Event(enable_timing=True)
-    a0.record(stream)
-    g_attn.replay()
-    a1.record(stream)
-    torch.cuda.synchronize()
-    attn_ms = a0.elapsed_time(a1) / args.steps
-    for key, ref in ref_acc.items():
-        if not torch.equal(steps[0][1].acc[key], ref):
-            print(f"graph replay differs from eager in {key}", file=sys.stderr)
-            sys.exit(1)
+
+    if args.eager_only:
+        ms_step = eager_ms
+        attention_calls()
+        attn_ms = timed(attention_calls) / args.steps
+        timing = "host-launched steps"
+    else:
+        # The timed region: exactly K steps captured in one HIP graph (rotating
+        # input sets), replayed once after one untimed replay.
+        g_step = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step):
+            for k in range(args.steps):
+                run(k)
+        g_attn = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_attn):
+            attention_calls()
+        g_step.replay()
+        torch.cuda.synchronize()
+        check_replay()
+        ms_step = timed(g_step.replay) / args.steps
+        # Attention calls alone: K calls back to back in one replay.
+        g_attn.replay()
+        attn_ms = timed(g_attn.replay) / args.steps
+        check_replay()
+        timing = "K steps in one HIP graph replay"
     attn_bytes, flops, accept_bytes = algorithmic(wl)
     acc_len = steps[0][1].acc["accept_len"].cpu().numpy()
     achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
@@ -268,13 +321,13 @@ def main():
         "data": "synthetic",
         "config": describe(wl),
         "roofline": {
-            "kernel": "tree_attention_verify call (prep + main + combine launches), K calls in one graph replay, HIP events on its stream",
+            "kernel": "tree_attention_verify call (prep + main + combine launches), K calls back to back, HIP events on their stream",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": stored_traffic(wl.name),
             "algorithmic_bytes": attn_bytes,
             "attention_us": attn_ms * 1e3,
             "attention_tflops": flops / (attn_ms * 1e-3) / 1e12,
@@ -282,6 +335,7 @@ def main():
         },
         "accept_len_hist": np.bincount(acc_len).tolist(),
         "input_sets_rotated": n_sets,
+        "timing": timing,
     }
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)

@@ -52,6 +52,10 @@ constexpr int kNumXcd = 8;
 constexpr int kPreciseCtx = 256;       // requests with a shorter context run every tile precise
 constexpr float kLazyRescale = 8.0f;    // log2 headroom before the running max is moved
 constexpr float kNegBig = -1.0e30f;
+// Tile classes of the attention loop (see attn_main_kernel).
+constexpr int kClassPlain = 0;
+constexpr int kClassMasked = 1;
+constexpr int kClassPrecise = 2;
 
 struct PlanHeader {
     int32_t n_items;
@@ -379,8 +383,9 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
 // ---------------------------------------------------------------------------
 // 2. Main kernel.
 //
-// LDS holds a ring of kStages (K tile, V tile) pairs, the tile's Q low parts
-// (precise tiles) and the tile nodes' mask rows, all filled by direct
+// LDS holds a ring of (K tile, V tile) stages -- 8 for items with a long
+// context, 4 for precise items, whose rows' Q low parts take the space of
+// the other 4 -- and the tile nodes' mask rows, all filled by direct
 // global->LDS loads (global_load_lds: no registers hold data in flight).  A
 // tile is 32 key slots; wave w < kChunks loads chunk w of K and of V, so each
 // loading wave issues two DMA instructions per tile and waits on its own
@@ -404,10 +409,15 @@ struct MainCfg {
     static constexpr int kChunkRows = 1024 / kRowBytes;    // rows per DMA instruction (64 x 16 B)
     static constexpr int kChunks = kKT / kChunkRows;       // DMA instructions per K (or V) tile
     static_assert(kChunks <= kWaves, "one K chunk and one V chunk per wave at most");
-    static constexpr int kStages = 4;
     static constexpr int kStageBytes = 2 * kTileBytes;
-    static constexpr int kRingBytes = kStages * kStageBytes;
+    // LDS: 8 stages; precise items use the first 4 and keep their rows' Q
+    // low parts in the space of the other 4.
+    static constexpr int kStagesShort = 4;
+    static constexpr int kStagesLong = 8;
+    static constexpr int kQloOffset = kStagesShort * kStageBytes;
     static constexpr int kQloBytes = kTileM * kRowBytes;
+    static constexpr int kMainBytes = kStagesLong * kStageBytes;
+    static_assert(kQloOffset + kQloBytes == kMainBytes, "Q lo fills stages 4..7");
     static constexpr int kQloChunks = kQloBytes / 1024;    // DMA instructions for the Q low parts
 };
 
@@ -420,9 +430,11 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Wait until at most 2*k of this wave's loads are outstanding (k in 0..3).
+// Wait until at most 2*k of this wave's loads are outstanding (k in 0..5).
 __device__ __forceinline__ void wait_vmcnt_pairs(int k) {
-    if (k >= 3) wait_vmcnt<6>();
+    if (k >= 5) wait_vmcnt<10>();
+    else if (k == 4) wait_vmcnt<8>();
+    else if (k == 3) wait_vmcnt<6>();
     else if (k == 2) wait_vmcnt<4>();
     else if (k == 1) wait_vmcnt<2>();
     else wait_vmcnt<0>();
@@ -462,6 +474,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((ttv_f32x2v){a, b}, ttv_bf16x2v));
 }
 
+// x *= a, written back into x's own register: the rare rescale branch then
+// leaves the accumulators where the MFMAs keep them (no copies on the path
+// that skips it).
+__device__ __forceinline__ void scale_in_place(ttv_f32x4& v, float a) { v *= a; }
+
 // max over the four lanes l, l^16, l^32, l^48 (the lane groups sharing a row)
 __device__ __forceinline__ float group_max(float t) {
     auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false, false);
@@ -483,34 +500,47 @@ __device__ __forceinline__ const uint16_t* kv_row_ptr(const CacheView& c, const 
     return base + (((int64_t)blk * c.hkv + h) * TTV_BLOCK_SIZE + (slot & 15)) * D;
 }
 
+// Physical blocks holding the rows that wave w loads for a tile (slots slot0
+// .. slot0 + valid - 1): the first and the last of those rows, which span at
+// most two blocks.  Wave-uniform scalar reads of the block table; the tile
+// loop fetches them one tile ahead of the loads that use them.
+struct TileBlocks {
+    int32_t first, last;
+};
+
+template <int D, bool kPaged>
+__device__ __forceinline__ TileBlocks tile_blocks(const CacheView& c, const int32_t* __restrict__ table,
+                                                  int b, int slot0, int valid, int wave) {
+    using MC = MainCfg<D>;
+    TileBlocks tb{0, 0};
+    if (!kPaged || wave >= MC::kChunks) return tb;
+    const int r_first = min(wave * MC::kChunkRows, valid - 1);
+    const int r_last = min(wave * MC::kChunkRows + MC::kChunkRows - 1, valid - 1);
+    const int lb0 = (slot0 + r_first) >> 4;
+    const int lb1 = (slot0 + r_last) >> 4;
+    tb.first = lb0 < c.max_blocks ? table[(int64_t)b * c.max_blocks + lb0] : -1;
+    tb.last = lb1 < c.max_blocks ? table[(int64_t)b * c.max_blocks + lb1] : -1;
+    return tb;
+}
+
 // Issue the LDS-DMA loads of one tile (slots slot0 .. slot0 + valid - 1; rows
 // past valid repeat the last valid slot, so every LDS byte is defined).
 // Wave w < kChunks loads chunk w (kChunkRows rows) of K and of V.
 template <int D, bool kPaged>
-__device__ __forceinline__ void issue_tile(const CacheView& c, const int32_t* __restrict__ table,
-                                           int b, int kvh, int slot0, int valid, uint32_t stage,
-                                           int wave, int lane, int32_t* err) {
+__device__ __forceinline__ void issue_tile(const CacheView& c, TileBlocks tb, int b, int kvh, int slot0,
+                                           int valid, uint32_t stage, int wave, int lane, int32_t* err) {
     using MC = MainCfg<D>;
     constexpr int P = MC::kPieces;
     if (wave >= MC::kChunks) return;
     const int r_first = min(wave * MC::kChunkRows, valid - 1);
-    int blk_first = 0, blk_last = 0;
-    if (kPaged) {
-        // wave-uniform scalar reads of the (at most two) blocks these rows touch
-        const int r_last = min(wave * MC::kChunkRows + MC::kChunkRows - 1, valid - 1);
-        const int lb0 = (slot0 + r_first) >> 4;
-        const int lb1 = (slot0 + r_last) >> 4;
-        blk_first = lb0 < c.max_blocks ? table[(int64_t)b * c.max_blocks + lb0] : -1;
-        blk_last = lb1 < c.max_blocks ? table[(int64_t)b * c.max_blocks + lb1] : -1;
-        if (blk_first < 0 || blk_first >= c.num_blocks || blk_last < 0 || blk_last >= c.num_blocks) {
-            if (lane == 0) atomicOr(err + b, TTV_ERR_BLOCK_TABLE);
-            blk_first = blk_last = 0;  // load a valid block; the request is flagged
-        }
+    if (kPaged && (tb.first < 0 || tb.first >= c.num_blocks || tb.last < 0 || tb.last >= c.num_blocks)) {
+        if (lane == 0) atomicOr(err + b, TTV_ERR_BLOCK_TABLE);
+        tb.first = tb.last = 0;  // load a valid block; the request is flagged
     }
     const int row = wave * MC::kChunkRows + lane / P;
     const int phys = lane % P;
     const int slot = slot0 + min(row, valid - 1);
-    const int blk = (!kPaged || (slot >> 4) == ((slot0 + r_first) >> 4)) ? blk_first : blk_last;
+    const int blk = (!kPaged || (slot >> 4) == ((slot0 + r_first) >> 4)) ? tb.first : tb.last;
     const uint16_t* krow = kv_row_ptr<D, kPaged>(c, c.k, b, kvh, slot, blk);
     const uint16_t* vrow = kv_row_ptr<D, kPaged>(c, c.v, b, kvh, slot, blk);
     const uint32_t chunk_off = wave * MC::kChunkRows * MC::kRowBytes;
@@ -531,9 +561,9 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
     constexpr int DB = D / 16;   // 16-row blocks of the head dim
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const uint32_t ring = lds_offset(smem);
-    const uint32_t qlo_s = ring + MC::kRingBytes;
-    const uint32_t mask_base = qlo_s + MC::kQloBytes;
-    const uint32_t* mask_s = (const uint32_t*)(smem + MC::kRingBytes + MC::kQloBytes);
+    const uint32_t qlo_s = ring + MC::kQloOffset;
+    const uint32_t mask_base = ring + MC::kMainBytes;
+    const uint32_t* mask_s = (const uint32_t*)(smem + MC::kMainBytes);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -554,8 +584,18 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
     uint32_t koff[KC];  // K operand: row l16 (+16 kb), piece 4kc + g4
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) koff[kc] = l16 * MC::kRowBytes + 16 * swz_k(l16, 4 * kc + g4, P);
-    const int tr_row = 4 * g4 + (l16 >> 2);     // V^T operand rows (16h + tr_row)
-    const int tr_col = 4 * (l16 & 3);          // head-dim offset inside a 16-block
+    // V^T operand: ds_read_b64_tr_b16 at row 16h + 4g4 + l16 / 4, head dim
+    // 16db + 4 (l16 % 4); the XOR swizzle of row + 16 equals that of row.
+    uint32_t voff[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const int row = 4 * g4 + (l16 >> 2);
+        const int d = 16 * db + 4 * (l16 & 3);
+        voff[db] = row * MC::kRowBytes + 16 * swz_v(row, d >> 3, P) + 2 * (d & 7);
+    }
+    // A operand of all ones: 1^T P^T gives the row sums of P.
+    const ttv_bf16x8 kOnes = __builtin_bit_cast(
+        ttv_bf16x8, ttv_u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
     for (int x = vid; x < n_items; x += gridDim.x) {
         const Item it = items[x];
@@ -564,31 +604,58 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
         const int n_ctx_tiles = (it.c1 - it.c0 + kKT - 1) / kKT;
         const int n_tree_tiles = (it.kmax + kKT - 1) / kKT;
         const int n_tiles = n_ctx_tiles + n_tree_tiles;
-        // Tiles where few keys can dominate a row's softmax get Q and P as
-        // bf16 hi + lo pairs (two MFMAs each): tree tiles, and every tile of a
-        // short-context request.
-        const bool precise_ctx = it.ctx < kPreciseCtx;
-        const bool any_precise = n_tree_tiles > 0 || precise_ctx;
+        // Three classes of tiles.  Plain: whole context tiles.  Masked: the
+        // partial context tile and the tree tiles.  Precise: every tile of a
+        // request with a short context, where few keys can dominate a row's
+        // softmax; these are masked and run Q and P as bf16 hi + lo pairs
+        // (two MFMAs each), with the Q low parts in LDS.  An item is either
+        // all precise, or plain tiles [0, n_plain) then masked tiles.
+        const bool precise = it.ctx < kPreciseCtx;
+        const int n_plain = precise ? 0 : (it.c1 - it.c0) / kKT;
+        // Ring depth: precise items share LDS with the Q low parts.
+        const int stages = precise ? MC::kStagesShort : MC::kStagesLong;
+        const int smask = stages - 1;
+        const int ahead = stages - 1;  // tiles issued ahead of the one consumed
         const int node0 = (it.tile * kTileM) / G;
         const int node1 = min(it.n - 1, (it.tile * kTileM + kTileM - 1) / G);
         const int tree_limit = it.ctx + it.kmax;
-        auto tile_slot0 = [&](int tau) {
+        auto tile_slot0 = [&](int tau) __attribute__((always_inline)) {
             return tau < n_ctx_tiles ? it.c0 + tau * kKT : it.ctx + (tau - n_ctx_tiles) * kKT;
         };
-        auto tile_valid = [&](int tau, int slot0) {
+        auto tile_valid = [&](int tau, int slot0) __attribute__((always_inline)) {
             return min(kKT, (tau < n_ctx_tiles ? it.c1 : tree_limit) - slot0);
         };
-        auto issue = [&](int tau) {
+        auto blocks_of = [&](int tau) __attribute__((always_inline)) {
             const int slot0 = tile_slot0(tau);
-            issue_tile<D, kPaged>(cache, table, it.b, it.kvh, slot0, tile_valid(tau, slot0),
-                                  ring + (tau % MC::kStages) * MC::kStageBytes, wave, lane, err);
+            return tile_blocks<D, kPaged>(cache, table, it.b, slot0, tile_valid(tau, slot0), wave);
         };
+        auto issue = [&](int tau, TileBlocks tb) __attribute__((always_inline)) {
+            const int slot0 = tile_slot0(tau);
+            issue_tile<D, kPaged>(cache, tb, it.b, it.kvh, slot0, tile_valid(tau, slot0),
+                                  ring + (tau & smask) * MC::kStageBytes, wave, lane, err);
+        };
+        TileBlocks next_blocks{0, 0};  // blocks of the next tile to issue
 
-        // ---- prologue: Q lo, mask rows and the first tiles go to LDS by DMA,
-        // then Q hi into registers with ordinary loads; one wait covers all of
-        // them (they are in flight together), so the tile loop below starts
-        // with nothing but tiles outstanding.
-        if (any_precise) {
+        // ---- prologue: Q hi into registers (ordinary loads); Q lo, the
+        // tile nodes' mask rows and tiles 0 and 1 into LDS (DMA); one full
+        // wait covers all of them, so the compiler tracks nothing in flight
+        // afterwards.  Tiles 2 .. ahead - 1 are issued after that wait and
+        // stay in flight into the loop.
+        ttv_bf16x8 qreg[kMB][KC];
+        int row_node[kMB];
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) {
+            const int r = row_base + 16 * mb + l16;
+            const bool ok = r < rows;
+            const int rc = min(r, rows - 1);  // rows past the tile end reuse its last row
+            const int node = rc / G, g = rc % G;
+            row_node[mb] = ok ? node - node0 : -1;
+            const uint16_t* src = q_hi + ((int64_t)(it.s + node) * Hq + it.kvh * G + g) * D;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+                qreg[mb][kc] = *(const ttv_bf16x8*)(src + 32 * kc + 8 * g4);
+        }
+        if (precise) {
             // Q low parts, swizzled like K; rows past the tile's last row
             // repeat that row (finite, never written out)
             for (int j = wave; j < MC::kQloChunks; j += kWaves) {
@@ -607,54 +674,29 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
             for (int j = wave; j * 64 < words; j += kWaves)
                 dma4(mask_base + j * 256, src + min(j * 64 + lane, words - 1));
         }
-        constexpr int kAhead = MC::kStages - 1;
-        for (int j = 0; j < kAhead && j < n_tiles; ++j) issue(j);
-        ttv_bf16x8 qreg[kMB][KC];
-        int row_node[kMB];
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
-            const int r = row_base + 16 * mb + l16;
-            const bool ok = r < rows;
-            const int rc = min(r, rows - 1);  // rows past the tile end reuse its last row
-            const int node = rc / G, g = rc % G;
-            row_node[mb] = ok ? node - node0 : -1;
-            const uint16_t* src = q_hi + ((int64_t)(it.s + node) * Hq + it.kvh * G + g) * D;
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc)
-                qreg[mb][kc] = *(const ttv_bf16x8*)(src + 32 * kc + 8 * g4);
-        }
+        for (int j = 0; j < 2 && j < n_tiles; ++j) issue(j, blocks_of(j));
         // A full wait and a fenced barrier (not the loop's raw one, so the two
-        // cannot be merged): Q lo, mask rows and tiles 0..2 are in LDS and Q
-        // hi in registers before the loop, which then carries no compiler
-        // wait on the tiles in flight.
+        // cannot be merged).
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        for (int j = 2; j < ahead && j < n_tiles; ++j) issue(j, blocks_of(j));
+        if (kPaged && ahead < n_tiles) next_blocks = blocks_of(ahead);
 
-        ttv_f32x4 o[DB][kMB];
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int mb = 0; mb < kMB; ++mb) o[db][mb] = ttv_f32x4{0.f, 0.f, 0.f, 0.f};
-        float m_run[kMB], l_run[kMB];
+        ttv_f32x4 o[DB][kMB], lacc[kMB];
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) {
-            m_run[mb] = kNegBig;
-            l_run[mb] = 0.f;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[db][mb] = ttv_f32x4{0.f, 0.f, 0.f, 0.f};
+            lacc[mb] = ttv_f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        float m_run[kMB];
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) m_run[mb] = kNegBig;
 
-        // One tile: scores, mask, online softmax (lazy rescale), P.V.
-        auto consume = [&](auto precise_tag, int tau) {
-            constexpr bool kPrecise = decltype(precise_tag)::value;
-            const uint32_t kst = ring + (tau % MC::kStages) * MC::kStageBytes;
-            const uint32_t vst = kst + MC::kTileBytes;
-            const int valid = tile_valid(tau, tile_slot0(tau));
-            const bool tree = tau >= n_ctx_tiles;
-            // S^T[key][row] for keys 16kb + 4g4 + r, rows 16mb + l16.
-            ttv_f32x4 sacc[2][kMB];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int mb = 0; mb < kMB; ++mb) sacc[kb][mb] = ttv_f32x4{0.f, 0.f, 0.f, 0.f};
+        // S^T[key][row] of tile tau: keys 16kb + 4g4 + r, rows 16mb + l16.
+        auto scores = [&](auto cls, int tau, ttv_f32x4 (&S)[2][kMB]) __attribute__((always_inline)) {
+            constexpr bool kPrecise = decltype(cls)::value == kClassPrecise;
+            const char* kst = smem + (tau & smask) * MC::kStageBytes;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 ttv_bf16x8 qlo[kMB];
@@ -668,65 +710,82 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
                 }
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const ttv_bf16x8 a = *(const ttv_bf16x8*)(smem + (kst - ring) + koff[kc] +
-                                                              kb * 16 * MC::kRowBytes);
+                    const ttv_bf16x8 a = *(const ttv_bf16x8*)(kst + koff[kc] + kb * 16 * MC::kRowBytes);
 #pragma unroll
                     for (int mb = 0; mb < kMB; ++mb) {
-                        sacc[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[mb][kc],
-                                                                               sacc[kb][mb], 0, 0, 0);
+                        S[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            a, qreg[mb][kc], kc == 0 ? ttv_f32x4{0.f, 0.f, 0.f, 0.f} : S[kb][mb], 0, 0, 0);
                         if (kPrecise)
-                            sacc[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[mb],
-                                                                                   sacc[kb][mb], 0, 0, 0);
+                            S[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[mb], S[kb][mb], 0, 0, 0);
                     }
                 }
             }
-            // Mask (in place) on partial and tree tiles only.
-            if (tree || valid < kKT) {
-#pragma unroll
-                for (int mb = 0; mb < kMB; ++mb) {
-                    uint32_t w = valid >= 32 ? 0xFFFFFFFFu : ((1u << valid) - 1u);
-                    if (tree) {
-                        const int nl = row_node[mb];
-                        w &= nl >= 0 ? mask_s[nl * mask_words + (tau - n_ctx_tiles)] : 0u;
-                    }
-                    w >>= 4 * g4;
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (!((w >> (16 * kb + r)) & 1u)) sacc[kb][mb][r] = -INFINITY;
-                }
-            }
-            float tmax[kMB];
-            bool need = false;
+        };
+
+        // Keys a row may not see become -inf: slots past the tile's valid
+        // count and, on tree tiles, keys that are not the row node's
+        // ancestors (or the node itself).  Branch-free.
+        auto mask_scores = [&](int tau, ttv_f32x4 (&S)[2][kMB]) __attribute__((always_inline)) {
+            const int valid = tile_valid(tau, tile_slot0(tau));
+            const bool tree = tau >= n_ctx_tiles;
+            const uint32_t vbits = valid >= 32 ? 0xFFFFFFFFu : ((1u << valid) - 1u);
+            const int word = tree ? tau - n_ctx_tiles : 0;
 #pragma unroll
             for (int mb = 0; mb < kMB; ++mb) {
-                float t = fmaxf(fmaxf(fmaxf(sacc[0][mb][0], sacc[0][mb][1]), fmaxf(sacc[0][mb][2], sacc[0][mb][3])),
-                                fmaxf(fmaxf(sacc[1][mb][0], sacc[1][mb][1]), fmaxf(sacc[1][mb][2], sacc[1][mb][3])));
-                t = group_max(t);
-                tmax[mb] = t;
-                need |= t > m_run[mb] + kLazyRescale;
+                const int nl = row_node[mb];
+                const uint32_t mw = mask_s[max(nl, 0) * mask_words + word];
+                const uint32_t w = (vbits & (tree ? (nl >= 0 ? mw : 0u) : 0xFFFFFFFFu)) >> (4 * g4);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        S[kb][mb][r] = ((w >> (16 * kb + r)) & 1u) ? S[kb][mb][r] : -INFINITY;
             }
-            // Lazy rescale: keep the running max unless some row's max grew by
-            // more than 2^kLazyRescale (then p <= 2^kLazyRescale meanwhile).
-            if (__ballot(need)) {
+        };
+
+        // This lane's part of each row maximum (the other three parts sit in
+        // lanes l ^ 16, l ^ 32, l ^ 48).
+        auto row_max = [&](const ttv_f32x4 (&S)[2][kMB], float (&tmax)[kMB]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb) {
+                const float t0 = __builtin_fmaxf(__builtin_fmaxf(S[0][mb][0], S[0][mb][1]),
+                                                 __builtin_fmaxf(S[0][mb][2], S[0][mb][3]));
+                const float t1 = __builtin_fmaxf(__builtin_fmaxf(S[1][mb][0], S[1][mb][1]),
+                                                 __builtin_fmaxf(S[1][mb][2], S[1][mb][3]));
+                tmax[mb] = __builtin_fmaxf(t0, t1);
+            }
+        };
+
+        // Lazy rescale: the running max moves only when some row of the wave
+        // outgrew it by more than 2^kLazyRescale (p stays below that
+        // meanwhile); rare after the first tile.
+        auto rescale_if_needed = [&](const float (&tmax)[kMB]) __attribute__((always_inline)) {
+            bool need = false;
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb) need |= tmax[mb] > m_run[mb] + kLazyRescale;
+            if (__builtin_expect(__ballot(need) != 0, 0)) {
 #pragma unroll
                 for (int mb = 0; mb < kMB; ++mb) {
-                    const float m_new = fmaxf(m_run[mb], tmax[mb]);
+                    const float m_new = __builtin_fmaxf(m_run[mb], group_max(tmax[mb]));
                     const float alpha = __builtin_amdgcn_exp2f(m_run[mb] - m_new);
                     m_run[mb] = m_new;
-                    l_run[mb] *= alpha;
+                    scale_in_place(lacc[mb], alpha);
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) o[db][mb] *= alpha;
+                    for (int db = 0; db < DB; ++db) scale_in_place(o[db][mb], alpha);
                 }
             }
-            ttv_bf16x8 pb[kMB], pl[kMB];
+        };
+
+        // p = 2^(s - m) as bf16 (plus, when precise, the bf16 of what the
+        // rounding dropped).
+        auto exp_pack = [&](auto cls, const ttv_f32x4 (&S)[2][kMB], ttv_bf16x8 (&pb)[kMB],
+                            ttv_bf16x8 (&pl)[kMB]) __attribute__((always_inline)) {
+            constexpr bool kPrecise = decltype(cls)::value == kClassPrecise;
 #pragma unroll
             for (int mb = 0; mb < kMB; ++mb) {
                 float p[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sacc[e >> 2][mb][e & 3] - m_run[mb]);
-                l_run[mb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+                for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(S[e >> 2][mb][e & 3] - m_run[mb]);
                 uint32_t packed[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) packed[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
@@ -739,48 +798,215 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
                     pl[mb] = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{lo[0], lo[1], lo[2], lo[3]});
                 }
             }
-            // O^T[d][row] += V^T[d][key] P^T[key][row].  MFMA k index 8g4 + j
-            // is key 4g4 + j (j < 4) or 16 + 4g4 + j - 4 (j >= 4); each half
-            // comes from one ds_read_b64_tr_b16 over rows 16h + 4g4 .. +3.
+        };
+
+        // O^T[d][row] += V^T[d][key] P^T[key][row] and l += 1^T P^T (an MFMA
+        // against a ones operand, so l sums the same bf16 P that multiplies
+        // V).  MFMA k index 8g4 + j is key 4g4 + j (j < 4) or 16 + 4g4 + j - 4
+        // (j >= 4); each half comes from one ds_read_b64_tr_b16 over rows
+        // 16h + 4g4 .. +3.
+        auto load_vt = [&](int tau, int db) __attribute__((always_inline)) {
+            const uint32_t vst = ring + (tau & smask) * MC::kStageBytes + MC::kTileBytes;
+            ttv_i16x4 half[2];
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                ttv_i16x4 half[2];
+            for (int h = 0; h < 2; ++h)
+                half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(uintptr_t)(vst + voff[db] + h * 16 * MC::kRowBytes));
+            return __builtin_bit_cast(ttv_bf16x8,
+                                      __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        auto pv_mfma = [&](auto cls, const ttv_bf16x8 (&va)[DB], const ttv_bf16x8 (&pb)[kMB],
+                           const ttv_bf16x8 (&pl)[kMB]) __attribute__((always_inline)) {
+            constexpr bool kPrecise = decltype(cls)::value == kClassPrecise;
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int row = 16 * h + tr_row;
-                    const int d = 16 * db + tr_col;
-                    const uint32_t addr = vst + row * MC::kRowBytes + 16 * swz_v(row, d >> 3, P) + 2 * (d & 7);
-                    half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
-                }
-                const ttv_bf16x8 a = __builtin_bit_cast(
-                    ttv_bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int mb = 0; mb < kMB; ++mb) {
-                    o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[mb], o[db][mb], 0, 0, 0);
+                    o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pb[mb], o[db][mb], 0, 0, 0);
                     if (kPrecise)
-                        o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[mb], o[db][mb], 0, 0, 0);
+                        o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pl[mb], o[db][mb], 0, 0, 0);
+                }
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb) {
+                lacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pb[mb], lacc[mb], 0, 0, 0);
+                if (kPrecise)
+                    lacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pl[mb], lacc[mb], 0, 0, 0);
+            }
+        };
+
+        // Before the scores of tile tau + 1: this wave's loads of that tile
+        // have landed (the later ones up to tile tau + ahead - 1 may stay in
+        // flight) and a barrier publishes them; the barrier also retires
+        // stage (tau - 1) % stages, which the load of tile tau + ahead then
+        // reuses.
+        auto advance = [&](int tau) __attribute__((always_inline)) {
+            if (wave < MC::kChunks) wait_vmcnt_pairs(min(ahead - 2, n_tiles - 2 - tau));
+            raw_barrier();
+            if (tau + ahead < n_tiles) issue(tau + ahead, next_blocks);
+        };
+
+        // Software pipeline: iteration tau computes the scores of tile tau + 1
+        // while it runs the softmax and P.V of tile tau, so the MFMAs of one
+        // overlap the VALU work of the other.
+        ttv_f32x4 S[2][kMB], S_next[2][kMB];
+        float tmax[kMB];
+        ttv_bf16x8 pb[kMB], pl[kMB];
+        constexpr std::integral_constant<int, kClassPlain> cPlain{};
+        constexpr std::integral_constant<int, kClassMasked> cMasked{};
+        constexpr std::integral_constant<int, kClassPrecise> cPrecise{};
+        auto first = [&](auto cls) __attribute__((always_inline)) {
+            scores(cls, 0, S);
+            if (decltype(cls)::value != kClassPlain) mask_scores(0, S);
+            row_max(S, tmax);
+        };
+        // One pipelined iteration: scores of tile tau + 1 (S_nxt), softmax
+        // and P.V of tile tau (S_cur).  The work is cut into phases that the
+        // scheduler may not mix (sched_barrier): each phase pairs one k-chunk
+        // of score MFMAs with a quarter of the exponentials, and the LDS
+        // reads of the next phase are issued one phase ahead; the last phase
+        // runs the P.V MFMAs next to the mask and row maxima of tile tau + 1.
+        auto iteration = [&](auto cur, auto next, int tau, ttv_f32x4 (&S_cur)[2][kMB],
+                             ttv_f32x4 (&S_nxt)[2][kMB]) __attribute__((always_inline)) {
+            constexpr bool kCurPrecise = decltype(cur)::value == kClassPrecise;
+            constexpr bool kNextPrecise = decltype(next)::value == kClassPrecise;
+            constexpr bool kNextMasked = decltype(next)::value != kClassPlain;
+            rescale_if_needed(tmax);
+            advance(tau);
+            const char* kst = smem + ((tau + 1) & smask) * MC::kStageBytes;
+            ttv_bf16x8 ka[KC][2], qlo[KC][kMB], va[DB];
+            auto load_k = [&](int kc) __attribute__((always_inline)) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    ka[kc][kb] = *(const ttv_bf16x8*)(kst + koff[kc] + kb * 16 * MC::kRowBytes);
+                if (kNextPrecise) {
+#pragma unroll
+                    for (int mb = 0; mb < kMB; ++mb) {
+                        const int rl = wave * kRowsPerWave + 16 * mb + l16;
+                        qlo[kc][mb] = *(const ttv_bf16x8*)(smem + (qlo_s - ring) + rl * MC::kRowBytes +
+                                                           16 * swz_k(rl, 4 * kc + g4, P));
+                    }
+                }
+            };
+            auto qk = [&](int kc) __attribute__((always_inline)) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int mb = 0; mb < kMB; ++mb) {
+                        S_nxt[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            ka[kc][kb], qreg[mb][kc], kc == 0 ? ttv_f32x4{0.f, 0.f, 0.f, 0.f} : S_nxt[kb][mb],
+                            0, 0, 0);
+                        if (kNextPrecise)
+                            S_nxt[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kc][kb], qlo[kc][mb],
+                                                                                    S_nxt[kb][mb], 0, 0, 0);
+                    }
+            };
+            float p[kMB][8];
+            uint32_t packed[kMB][4];
+            auto ex = [&](int mb, int half) __attribute__((always_inline)) {
+#pragma unroll
+                for (int e = 4 * half; e < 4 * half + 4; ++e)
+                    p[mb][e] = __builtin_amdgcn_exp2f(S_cur[e >> 2][mb][e & 3] - m_run[mb]);
+#pragma unroll
+                for (int e = 2 * half; e < 2 * half + 2; ++e)
+                    packed[mb][e] = pack_bf16(p[mb][2 * e], p[mb][2 * e + 1]);
+            };
+            auto phase = [] { __builtin_amdgcn_sched_barrier(0); };
+            // Phases for D = 128 (KC = 4); with D = 64 the last two carry no
+            // score MFMAs.
+            static_assert(KC == 2 || KC == 4, "head_dim 64 or 128");
+            load_k(0);
+            load_k(1);
+#pragma unroll
+            for (int db = 0; db < DB / 2; ++db) va[db] = load_vt(tau, db);
+            phase();
+            qk(0);
+            ex(0, 0);
+            if (KC > 2) load_k(2);
+            phase();
+            qk(1);
+            ex(0, 1);
+            if (KC > 2) load_k(3);
+            phase();
+            if (KC > 2) qk(2);
+            ex(1, 0);
+#pragma unroll
+            for (int db = DB / 2; db < DB; ++db) va[db] = load_vt(tau, db);
+            phase();
+            if (KC > 2) qk(3);
+            ex(1, 1);
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb) {
+                pb[mb] = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{packed[mb][0], packed[mb][1], packed[mb][2],
+                                                                  packed[mb][3]});
+                if (kCurPrecise) {
+                    uint32_t lo[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        lo[e] = pack_bf16(p[mb][2 * e] - ttv_bf16_lo(packed[mb][e]),
+                                          p[mb][2 * e + 1] - ttv_bf16_hi(packed[mb][e]));
+                    pl[mb] = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{lo[0], lo[1], lo[2], lo[3]});
                 }
             }
+            phase();
+            pv_mfma(cur, va, pb, pl);
+            if (kNextMasked) mask_scores(tau + 1, S_nxt);
+            row_max(S_nxt, tmax);
+            phase();
+            // A paged cache's block numbers for the tile the next iteration
+            // loads: read now, so the scalar loads return during its barrier.
+            if (kPaged && tau + ahead + 1 < n_tiles) next_blocks = blocks_of(tau + ahead + 1);
         };
-
-        auto step = [&](int tau) {
-            if (tau > 0) {
-                // this wave's loads of tile tau have landed; later tiles may
-                // stay in flight
-                if (wave < MC::kChunks) wait_vmcnt_pairs(min(kAhead - 1, n_tiles - 1 - tau));
-                raw_barrier();  // tile tau visible to all waves; stage of tau-1 free
-            }
-            if (tau + kAhead < n_tiles) issue(tau + kAhead);
-            if (precise_ctx || tau >= n_ctx_tiles)
-                consume(std::integral_constant<bool, true>{}, tau);
-            else
-                consume(std::integral_constant<bool, false>{}, tau);
-        };
-        for (int tau = 0; tau < n_tiles; ++tau) step(tau);
-
-        // Row sums across the 4 lane groups holding a row's keys.
+        auto copy_scores = [&](ttv_f32x4 (&dst)[2][kMB], const ttv_f32x4 (&src)[2][kMB]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) l_run[mb] = group_sum(l_run[mb]);
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int mb = 0; mb < kMB; ++mb) dst[kb][mb] = src[kb][mb];
+        };
+        auto last = [&](auto cur, int tau) __attribute__((always_inline)) {
+            rescale_if_needed(tmax);
+            exp_pack(cur, S, pb, pl);
+            ttv_bf16x8 va[DB];
+#pragma unroll
+            for (int db = 0; db < DB; ++db) va[db] = load_vt(tau, db);
+            pv_mfma(cur, va, pb, pl);
+        };
+        // Runs tiles [tau, end) of one class; the tile after them (if any) is
+        // of class `after`.  Two iterations per trip, so the two score sets
+        // swap roles without copies.
+        auto run = [&](auto cls, auto after, int& tau, int end) __attribute__((always_inline)) {
+            for (; tau + 2 < end; tau += 2) {
+                iteration(cls, cls, tau, S, S_next);
+                iteration(cls, cls, tau + 1, S_next, S);
+            }
+            if (tau + 1 < end) {
+                iteration(cls, cls, tau, S, S_next);
+                copy_scores(S, S_next);
+                ++tau;
+            }
+            if (tau < end) {
+                if (tau + 1 < n_tiles) {
+                    iteration(cls, after, tau, S, S_next);
+                    copy_scores(S, S_next);
+                } else {
+                    last(cls, tau);
+                }
+                ++tau;
+            }
+        };
+        int tau = 0;
+        if (precise) {
+            first(cPrecise);
+            run(cPrecise, cPrecise, tau, n_tiles);
+        } else {
+            if (n_plain > 0) first(cPlain);
+            else first(cMasked);
+            run(cPlain, cMasked, tau, n_plain);
+            run(cMasked, cMasked, tau, n_tiles);
+        }
+
+        float l_run[kMB];
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) l_run[mb] = lacc[mb][0];
         // Lane holds O^T[d = 16db + 4g4 + r][row 16mb + l16].
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) {
@@ -815,7 +1041,7 @@ size_t main_lds_bytes(int G, int mask_words) {
     using MC = MainCfg<D>;
     const int nodes = kTileM / G + 2;
     const size_t mask_bytes = (size_t)((nodes * mask_words + 63) / 64) * 256;
-    return (size_t)MC::kRingBytes + MC::kQloBytes + mask_bytes;
+    return (size_t)MC::kMainBytes + mask_bytes;
 }
 
 // ---------------------------------------------------------------------------
