@@ -242,9 +242,11 @@ TTV_API int tree_greedy_accept(const ttv_batch* bt, const void* logits, int32_t 
  * in : accept_len [B], accepted_nodes [B, max_accept] from tree_greedy_accept
  * out: new_lens int32 [B]; released_blocks int32 [B, max_blocks] and
  *      num_released int32 [B] (paged only; may be NULL for contiguous)
- *      err  OR-ed: TTV_ERR_ACCEPT (accept_len or a node id out of range, or
- *           the ids not a root-down path by increasing index), _CAPACITY,
- *           _BLOCK_TABLE.  A flagged request is left untouched.
+ *      err  OR-ed: TTV_ERR_ACCEPT (accept_len outside [0, min(N_b, max_accept)],
+ *           or the ids not strictly increasing, an id i_d below its depth d,
+ *           or an id >= N_b), _CAPACITY, _BLOCK_TABLE.  The ids are not
+ *           checked against the tree's parent links (tree_greedy_accept
+ *           produces a root-down path).  A flagged request is left untouched.
  */
 TTV_API int tree_kv_commit(const ttv_batch* bt, const ttv_kv_cache* cache,
                            const int32_t* accept_len, const int32_t* accepted_nodes,

@@ -1,0 +1,119 @@
+"""Planted mistakes in the oracle must fail its pins.
+
+Each case swaps one oracle function for a plausible wrong variant (a dropped
+term, a wrong sign or index, an off-by-one) on the CPU, runs the pin tests
+that are meant to guard it, and requires at least one of them to fail.  This
+checks the pins themselves, not the GPU path.
+"""
+
+import numpy as np
+import pytest
+
+import test_oracle_accept_commit as PAC
+import test_oracle_attention as PA
+import test_oracle_tree as PT
+from oracle import accept as AC
+from oracle import attention as A
+from oracle import commit as CM
+from oracle import tree as T
+
+
+def _fails(*pins):
+    """True if at least one pin raises AssertionError."""
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            return True
+    return False
+
+
+def test_unmutated_oracle_passes_these_pins():
+    assert not _fails(PT.test_packed_table_pin, PT.test_positions_pin, PA.test_rope_golden,
+                      PA.test_chain_is_causal_attention, PA.test_star_sees_context_and_self,
+                      PAC.test_verify_tree_example_pin, PAC.test_argmax_ties_and_signed_zero)
+
+
+def test_dropped_self_bit_is_caught(monkeypatch):
+    orig = T.ancestor_path
+    monkeypatch.setattr(T, "ancestor_path", lambda i, parents: orig(i, parents)[:-1])
+    assert _fails(PT.test_packed_table_pin)
+
+
+def test_one_based_depth_is_caught(monkeypatch):
+    orig = T.depth_of
+    monkeypatch.setattr(T, "depth_of", lambda i, parents: orig(i, parents) + 1)
+    assert _fails(PT.test_positions_pin, PT.test_packed_table_pin)
+
+
+def test_rope_sign_error_is_caught(monkeypatch):
+    orig = A.rope
+    # rotating by the opposite angle flips the sign of the sin terms
+    monkeypatch.setattr(A, "rope", lambda x, pos, base=10000.0: orig(x, -np.asarray(pos), base))
+    assert _fails(PA.test_rope_golden, PA.test_rope_matches_complex_rotation)
+
+
+def test_rope_half_split_variant_is_caught(monkeypatch):
+    def rope_neox(x, pos, base=10000.0):
+        x = np.asarray(x, dtype=np.float64)
+        D = x.shape[-1]
+        inv = base ** (-np.arange(D // 2) * 2.0 / D)
+        ang = np.asarray(pos, dtype=np.float64)[..., None] * inv
+        c, s = np.cos(ang), np.sin(ang)
+        a, b = x[..., :D // 2], x[..., D // 2:]
+        return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+    monkeypatch.setattr(A, "rope", rope_neox)
+    assert _fails(PA.test_rope_golden, PA.test_rope_matches_complex_rotation)
+
+
+def test_missing_sqrt_in_scale_is_caught(monkeypatch):
+    orig = A.softmax_attend
+    monkeypatch.setattr(A, "softmax_attend",
+                        lambda qg, kc, vc, kp, vp, scale: orig(qg, kc, vc, kp, vp, scale * scale))
+    assert _fails(PA.test_chain_is_causal_attention)
+
+
+def test_sibling_leak_is_caught(monkeypatch):
+    # every earlier node visible (a lower-triangular mask) instead of ancestors only
+    monkeypatch.setattr(A, "ancestor_path", lambda i, parents: list(range(i + 1)))
+    assert _fails(PA.test_star_sees_context_and_self)
+
+
+def test_argmax_last_tie_is_caught(monkeypatch):
+    def last_argmax(rows):
+        out = []
+        for r in rows:
+            r = np.asarray(r, dtype=np.float64)
+            out.append(int(len(r) - 1 - np.argmax(r[::-1])))
+        return out
+    monkeypatch.setattr(AC, "row_argmax", last_argmax)
+    assert _fails(PAC.test_argmax_ties_and_signed_zero)
+
+
+def test_walk_without_bonus_row_is_caught(monkeypatch):
+    orig = AC.greedy_walk
+
+    def walk_bonus_from_parent_row(choice, tokens, parents, max_accept):
+        w = orig(choice, tokens, parents, max_accept)
+        acc = w["accepted"]
+        # bonus taken from the row before the stop node (an off-by-one in the row index)
+        w["bonus"] = choice[acc[-1]] if acc else choice[0]
+        return w
+    monkeypatch.setattr(AC, "greedy_walk", walk_bonus_from_parent_row)
+    assert _fails(PAC.test_verify_tree_example_pin)
+
+
+def test_commit_off_by_one_slot_is_caught(monkeypatch):
+    def commit_shifted(k_cache, v_cache, ctx_lens, accept_len, accepted_nodes):
+        k = np.array(k_cache, copy=True)
+        v = np.array(v_cache, copy=True)
+        new_lens = []
+        for b, (ctx, a) in enumerate(zip(ctx_lens, accept_len)):
+            for d in range(a):
+                i = accepted_nodes[b][d]
+                k[b, :, ctx + d] = k_cache[b, :, ctx + i - 1 if i > 0 else ctx + i]
+                v[b, :, ctx + d] = v_cache[b, :, ctx + i - 1 if i > 0 else ctx + i]
+            new_lens.append(ctx + a)
+        return k, v, new_lens
+    monkeypatch.setattr(CM, "commit_contiguous", commit_shifted)
+    assert _fails(PAC.test_verify_tree_example_pin)

@@ -577,8 +577,12 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
     const int G = Hq / Hkv;
     // XCD-major virtual id: consecutive ids share an XCD (hardware places
     // workgroup x on XCD x % 8).
-    const int per_xcd = gridDim.x / kNumXcd;
-    const int vid = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
+    // Only as many workgroups as items take part (a multiple of 8, spread
+    // evenly over the XCDs).
+    const int active = min((int)gridDim.x, ((n_items + kNumXcd - 1) / kNumXcd) * kNumXcd);
+    const int per_xcd = active / kNumXcd;
+    const int xcd_slot = blockIdx.x / kNumXcd;
+    const int vid = xcd_slot < per_xcd ? (blockIdx.x % kNumXcd) * per_xcd + xcd_slot : n_items;
 
     // Per-lane LDS byte offsets inside a stage / the Q-lo block.
     uint32_t koff[KC];  // K operand: row l16 (+16 kb), piece 4kc + g4
@@ -597,7 +601,7 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
     const ttv_bf16x8 kOnes = __builtin_bit_cast(
         ttv_bf16x8, ttv_u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-    for (int x = vid; x < n_items; x += gridDim.x) {
+    for (int x = vid; x < n_items; x += active) {
         const Item it = items[x];
         const int rows = it.n * G;
         const int row_base = it.tile * kTileM + wave * kRowsPerWave;
