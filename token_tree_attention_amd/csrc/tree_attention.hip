@@ -46,7 +46,7 @@ constexpr int kTileM = kWaves * kRowsPerWave;
 constexpr int kThreads = kWaves * TTV_WAVE;
 constexpr int kKT = 32;                 // key slots per LDS tile (= one mask word)
 constexpr int kTargetItems = 1024;      // chunking aims at about this many work items
-constexpr int kChunkMin = 256;          // shortest context chunk (slots)
+constexpr int kChunkMin = 128;          // shortest context chunk (slots)
 constexpr int kMaxBatch = 4096;         // plan keeps per-request prefix sums in LDS
 constexpr int kNumXcd = 8;
 constexpr int kPreciseCtx = 256;       // requests with a shorter context run every tile precise
@@ -98,9 +98,9 @@ Layout make_layout(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D) {
     L.off_qlo = off;
     off = align256(off + (size_t)T * Hq * D * 2);
     L.off_po = off;
-    off = align256(off + (size_t)L.max_partials * kTileM * D * 4);
+    off = align256(off + (size_t)L.max_partials * kTileM * D * 2);
     L.off_pml = off;
-    off = align256(off + (size_t)L.max_partials * kTileM * 8);
+    off = align256(off + (size_t)L.max_partials * kTileM * sizeof(float4));
     L.total = off;
     return L;
 }
@@ -463,6 +463,17 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, const void* g) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(g)
                  : "memory", "m0");
 }
+// Same, with a wave-uniform base address and a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16s(uint32_t lds_base, const void* sbase, uint32_t voff) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+    const uint64_t g = (uint64_t)(uintptr_t)sbase;
+    // readfirstlane returns int: widen through uint32_t, never by sign extension
+    const uint32_t g_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)g);
+    const uint32_t g_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(g >> 32));
+    const uint64_t gs = ((uint64_t)g_hi << 32) | (uint64_t)g_lo;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(base), "v"(voff), "s"(gs)
+                 : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(uint32_t lds_base, const void* g) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(base), "v"(g)
@@ -554,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
     const uint16_t* q_hi,  // not __restrict__: keeps its loads ahead of the prologue fence
     const uint16_t* __restrict__ q_lo, const uint32_t* __restrict__ mask, int mask_words,
     CacheView cache, const int32_t* __restrict__ table, int Hq, uint16_t* __restrict__ out,
-    float* __restrict__ part_o, float2* __restrict__ part_ml, int32_t* __restrict__ err) {
+    ttv_f16x4* __restrict__ part_o, float4* __restrict__ part_ml, int32_t* __restrict__ err) {
     using MC = MainCfg<D>;
     constexpr int P = MC::kPieces;
     constexpr int KC = D / 32;   // 32-wide k chunks of the head dim
@@ -639,6 +650,35 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
                                   ring + (tau & smask) * MC::kStageBytes, wave, lane, err);
         };
         TileBlocks next_blocks{0, 0};  // blocks of the next tile to issue
+        // Fast issue path for whole context tiles (slot0 = c0 + 32 tau, no
+        // clamping): this lane's element offsets of its K and V rows, so an
+        // issue is a scalar base plus these.  A wave's rows of such a tile lie
+        // in one paged block (slot0 is a multiple of 32, the rows a wave loads
+        // are a 16-aligned sub-range of a block).
+        const int f_row = wave * MC::kChunkRows + lane / P;
+        const int f_phys = lane % P;
+        const int f_rowb = (kPaged ? (f_row & 15) : f_row) * MC::kRowBytes;
+        const uint32_t f_kb = f_rowb + 16 * swz_k(f_row, f_phys, P);  // byte offsets from the tile base
+        const uint32_t f_vb = f_rowb + 16 * swz_v(f_row, f_phys, P);
+        auto issue_whole = [&](int tau, TileBlocks tb) __attribute__((always_inline)) {
+            if (wave >= MC::kChunks) return;
+            const int slot0 = it.c0 + tau * kKT;
+            int64_t row0;  // element offset of the tile's (first) row of this KV head
+            if (kPaged) {
+                int blk = tb.first;
+                if (blk < 0 || blk >= cache.num_blocks) {
+                    if (lane == 0) atomicOr(err + it.b, TTV_ERR_BLOCK_TABLE);
+                    blk = 0;  // load a valid block; the request is flagged
+                }
+                row0 = ((int64_t)blk * cache.hkv + it.kvh) * TTV_BLOCK_SIZE * D;
+            } else {
+                row0 = (((int64_t)it.b * cache.hkv + it.kvh) * cache.cap + slot0) * D;
+            }
+            const uint32_t stage = ring + (tau & smask) * MC::kStageBytes;
+            const uint32_t chunk_off = wave * MC::kChunkRows * MC::kRowBytes;
+            dma16s(stage + chunk_off, cache.k + row0, f_kb);
+            dma16s(stage + MC::kTileBytes + chunk_off, cache.v + row0, f_vb);
+        };
 
         // ---- prologue: Q hi into registers (ordinary loads); Q lo, the
         // tile nodes' mask rows and tiles 0 and 1 into LDS (DMA); one full
@@ -762,17 +802,29 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
 
         // Lazy rescale: the running max moves only when some row of the wave
         // outgrew it by more than 2^kLazyRescale (p stays below that
-        // meanwhile); rare after the first tile.
-        auto rescale_if_needed = [&](const float (&tmax)[kMB]) __attribute__((always_inline)) {
+        // meanwhile); rare after the first tile.  Plain tiles carry shifted
+        // scores s - m (the score MFMAs start from -m), the others raw ones.
+        auto rescale_if_needed = [&](auto cls, ttv_f32x4 (&S)[2][kMB],
+                                     const float (&tmax)[kMB]) __attribute__((always_inline)) {
+            constexpr bool kShifted = decltype(cls)::value == kClassPlain;
             bool need = false;
 #pragma unroll
-            for (int mb = 0; mb < kMB; ++mb) need |= tmax[mb] > m_run[mb] + kLazyRescale;
+            for (int mb = 0; mb < kMB; ++mb) need |= tmax[mb] > (kShifted ? kLazyRescale : m_run[mb] + kLazyRescale);
             if (__builtin_expect(__ballot(need) != 0, 0)) {
 #pragma unroll
                 for (int mb = 0; mb < kMB; ++mb) {
-                    const float m_new = __builtin_fmaxf(m_run[mb], group_max(tmax[mb]));
-                    const float alpha = __builtin_amdgcn_exp2f(m_run[mb] - m_new);
-                    m_run[mb] = m_new;
+                    float alpha;
+                    if (kShifted) {
+                        const float sh = __builtin_fmaxf(group_max(tmax[mb]), 0.f);
+                        m_run[mb] += sh;
+                        alpha = __builtin_amdgcn_exp2f(-sh);
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) S[kb][mb] -= sh;
+                    } else {
+                        const float m_new = __builtin_fmaxf(m_run[mb], group_max(tmax[mb]));
+                        alpha = __builtin_amdgcn_exp2f(m_run[mb] - m_new);
+                        m_run[mb] = m_new;
+                    }
                     scale_in_place(lacc[mb], alpha);
 #pragma unroll
                     for (int db = 0; db < DB; ++db) scale_in_place(o[db][mb], alpha);
@@ -785,11 +837,13 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
         auto exp_pack = [&](auto cls, const ttv_f32x4 (&S)[2][kMB], ttv_bf16x8 (&pb)[kMB],
                             ttv_bf16x8 (&pl)[kMB]) __attribute__((always_inline)) {
             constexpr bool kPrecise = decltype(cls)::value == kClassPrecise;
+            constexpr bool kShifted = decltype(cls)::value == kClassPlain;
 #pragma unroll
             for (int mb = 0; mb < kMB; ++mb) {
                 float p[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(S[e >> 2][mb][e & 3] - m_run[mb]);
+                for (int e = 0; e < 8; ++e)
+                    p[e] = __builtin_amdgcn_exp2f(kShifted ? S[e >> 2][mb][e & 3] : S[e >> 2][mb][e & 3] - m_run[mb]);
                 uint32_t packed[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) packed[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
@@ -819,6 +873,26 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
             return __builtin_bit_cast(ttv_bf16x8,
                                       __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
         };
+        auto pv_half = [&](auto cls, int half, const ttv_bf16x8 (&va)[DB], const ttv_bf16x8 (&pb)[kMB],
+                           const ttv_bf16x8 (&pl)[kMB]) __attribute__((always_inline)) {
+            constexpr bool kPrecise = decltype(cls)::value == kClassPrecise;
+#pragma unroll
+            for (int db = half * DB / 2; db < (half + 1) * DB / 2; ++db)
+#pragma unroll
+                for (int mb = 0; mb < kMB; ++mb) {
+                    o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pb[mb], o[db][mb], 0, 0, 0);
+                    if (kPrecise)
+                        o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pl[mb], o[db][mb], 0, 0, 0);
+                }
+            if (half == 1) {
+#pragma unroll
+                for (int mb = 0; mb < kMB; ++mb) {
+                    lacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pb[mb], lacc[mb], 0, 0, 0);
+                    if (kPrecise)
+                        lacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pl[mb], lacc[mb], 0, 0, 0);
+                }
+            }
+        };
         auto pv_mfma = [&](auto cls, const ttv_bf16x8 (&va)[DB], const ttv_bf16x8 (&pb)[kMB],
                            const ttv_bf16x8 (&pl)[kMB]) __attribute__((always_inline)) {
             constexpr bool kPrecise = decltype(cls)::value == kClassPrecise;
@@ -843,10 +917,17 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
         // flight) and a barrier publishes them; the barrier also retires
         // stage (tau - 1) % stages, which the load of tile tau + ahead then
         // reuses.
-        auto advance = [&](int tau) __attribute__((always_inline)) {
-            if (wave < MC::kChunks) wait_vmcnt_pairs(min(ahead - 2, n_tiles - 2 - tau));
-            raw_barrier();
-            if (tau + ahead < n_tiles) issue(tau + ahead, next_blocks);
+        auto advance = [&](auto cls, int tau) __attribute__((always_inline)) {
+            constexpr int kA = (decltype(cls)::value == kClassPrecise ? MC::kStagesShort : MC::kStagesLong) - 1;
+            if (tau + kA < n_tiles) {  // steady state: kA - 2 later tiles stay in flight
+                if (MC::kChunks >= kWaves || wave < MC::kChunks) wait_vmcnt<2 * (kA - 2)>();
+                raw_barrier();
+                if (tau + kA < n_plain) issue_whole(tau + kA, next_blocks);
+                else issue(tau + kA, next_blocks);
+            } else {
+                if (MC::kChunks >= kWaves || wave < MC::kChunks) wait_vmcnt_pairs(min(kA - 2, n_tiles - 2 - tau));
+                raw_barrier();
+            }
         };
 
         // Software pipeline: iteration tau computes the scores of tile tau + 1
@@ -862,6 +943,17 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
             scores(cls, 0, S);
             if (decltype(cls)::value != kClassPlain) mask_scores(0, S);
             row_max(S, tmax);
+            if (decltype(cls)::value == kClassPlain) {
+                // whole tile, every key visible: start the running max at the
+                // tile's row max and shift the scores by it
+#pragma unroll
+                for (int mb = 0; mb < kMB; ++mb) {
+                    m_run[mb] = group_max(tmax[mb]);
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) S[kb][mb] -= m_run[mb];
+                    tmax[mb] -= m_run[mb];
+                }
+            }
         };
         // One pipelined iteration: scores of tile tau + 1 (S_nxt), softmax
         // and P.V of tile tau (S_cur).  The work is cut into phases that the
@@ -874,10 +966,18 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
             constexpr bool kCurPrecise = decltype(cur)::value == kClassPrecise;
             constexpr bool kNextPrecise = decltype(next)::value == kClassPrecise;
             constexpr bool kNextMasked = decltype(next)::value != kClassPlain;
-            rescale_if_needed(tmax);
-            advance(tau);
+            constexpr bool kCurShifted = decltype(cur)::value == kClassPlain;
+            rescale_if_needed(cur, S_cur, tmax);
+            advance(cur, tau);
             const char* kst = smem + ((tau + 1) & smask) * MC::kStageBytes;
             ttv_bf16x8 ka[KC][2], qlo[KC][kMB], va[DB];
+            // plain scores start from -m (shifted), the others from 0
+            ttv_f32x4 s_init[kMB];
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb) {
+                const float z = kNextMasked ? 0.f : -m_run[mb];
+                s_init[mb] = ttv_f32x4{z, z, z, z};
+            }
             auto load_k = [&](int kc) __attribute__((always_inline)) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
@@ -897,8 +997,7 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
 #pragma unroll
                     for (int mb = 0; mb < kMB; ++mb) {
                         S_nxt[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            ka[kc][kb], qreg[mb][kc], kc == 0 ? ttv_f32x4{0.f, 0.f, 0.f, 0.f} : S_nxt[kb][mb],
-                            0, 0, 0);
+                            ka[kc][kb], qreg[mb][kc], kc == 0 ? s_init[mb] : S_nxt[kb][mb], 0, 0, 0);
                         if (kNextPrecise)
                             S_nxt[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kc][kb], qlo[kc][mb],
                                                                                     S_nxt[kb][mb], 0, 0, 0);
@@ -909,7 +1008,8 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
             auto ex = [&](int mb, int half) __attribute__((always_inline)) {
 #pragma unroll
                 for (int e = 4 * half; e < 4 * half + 4; ++e)
-                    p[mb][e] = __builtin_amdgcn_exp2f(S_cur[e >> 2][mb][e & 3] - m_run[mb]);
+                    p[mb][e] = __builtin_amdgcn_exp2f(kCurShifted ? S_cur[e >> 2][mb][e & 3]
+                                                                  : S_cur[e >> 2][mb][e & 3] - m_run[mb]);
 #pragma unroll
                 for (int e = 2 * half; e < 2 * half + 2; ++e)
                     packed[mb][e] = pack_bf16(p[mb][2 * e], p[mb][2 * e + 1]);
@@ -933,8 +1033,6 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
             phase();
             if (KC > 2) qk(2);
             ex(1, 0);
-#pragma unroll
-            for (int db = DB / 2; db < DB; ++db) va[db] = load_vt(tau, db);
             phase();
             if (KC > 2) qk(3);
             ex(1, 1);
@@ -952,13 +1050,20 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
                 }
             }
             phase();
-            pv_mfma(cur, va, pb, pl);
+            // P.V in two halves; the V^T operands of the second half load
+            // while the first half runs.
+            pv_half(cur, 0, va, pb, pl);
+#pragma unroll
+            for (int db = DB / 2; db < DB; ++db) va[db] = load_vt(tau, db);
+            phase();
+            pv_half(cur, 1, va, pb, pl);
             if (kNextMasked) mask_scores(tau + 1, S_nxt);
             row_max(S_nxt, tmax);
             phase();
             // A paged cache's block numbers for the tile the next iteration
             // loads: read now, so the scalar loads return during its barrier.
-            if (kPaged && tau + ahead + 1 < n_tiles) next_blocks = blocks_of(tau + ahead + 1);
+            constexpr int kA = (decltype(cur)::value == kClassPrecise ? MC::kStagesShort : MC::kStagesLong) - 1;
+            if (kPaged && tau + kA + 1 < n_tiles) next_blocks = blocks_of(tau + kA + 1);
         };
         auto copy_scores = [&](ttv_f32x4 (&dst)[2][kMB], const ttv_f32x4 (&src)[2][kMB]) __attribute__((always_inline)) {
 #pragma unroll
@@ -967,7 +1072,7 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
                 for (int mb = 0; mb < kMB; ++mb) dst[kb][mb] = src[kb][mb];
         };
         auto last = [&](auto cur, int tau) __attribute__((always_inline)) {
-            rescale_if_needed(tmax);
+            rescale_if_needed(cur, S, tmax);
             exp_pack(cur, S, pb, pl);
             ttv_bf16x8 va[DB];
 #pragma unroll
@@ -1029,11 +1134,24 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
                     *(ttv_u32x2*)(dst + 16 * db + 4 * g4) = w;
                 }
             } else {
-                float* dst = part_o + ((int64_t)it.pslot * kTileM + r_local) * D;
+                // Partial: o / l scaled by a power of two 2^-e that brings the
+                // row's largest |o / l| into [0.5, 1), as fp16 (11-bit
+                // precision relative to that maximum); (m, l, 2^e) beside it.
+                const float inv_l = 1.0f / l_run[mb];
+                float amax = 0.f;
 #pragma unroll
-                for (int db = 0; db < DB; ++db) *(ttv_f32x4*)(dst + 16 * db + 4 * g4) = o[db][mb];
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) amax = __builtin_fmaxf(amax, __builtin_fabsf(o[db][mb][q]));
+                const int e = __builtin_amdgcn_frexp_expf(group_max(amax) * inv_l);
+                const float sc = __builtin_amdgcn_ldexpf(inv_l, -e);
+                ttv_f16x4* dst = part_o + (((int64_t)it.pslot * kTileM + r_local) * D) / 4;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    dst[4 * db + g4] = __builtin_convertvector(o[db][mb] * sc, ttv_f16x4);
                 if (g4 == 0)
-                    part_ml[(int64_t)it.pslot * kTileM + r_local] = make_float2(m_run[mb], l_run[mb]);
+                    part_ml[(int64_t)it.pslot * kTileM + r_local] =
+                        make_float4(m_run[mb], l_run[mb], __builtin_amdgcn_ldexpf(1.0f, e), 0.f);
             }
         }
         __syncthreads();  // LDS (ring, Q-lo, mask) is reused by the next item
@@ -1055,7 +1173,7 @@ size_t main_lds_bytes(int G, int mask_words) {
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(
     const PlanHeader* __restrict__ hdr, const Combine* __restrict__ combine, int Hq, int Hkv,
-    const float* __restrict__ part_o, const float2* __restrict__ part_ml,
+    const ttv_f16x4* __restrict__ part_o, const float4* __restrict__ part_ml,
     uint16_t* __restrict__ out) {
     constexpr int kLanesPerRow = D / 4;                 // each lane: 4 consecutive d
     constexpr int kRowsPerPass = kThreads / kLanesPerRow;
@@ -1076,13 +1194,13 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(
 #pragma unroll 4
         for (int c = 0; c < cb.nc; ++c) {
             const int64_t ps = cb.pslot0 + (int64_t)c * cb.stride;
-            const float2 ml = part_ml[ps * kTileM + r_local];
-            const ttv_f32x4 v = *(const ttv_f32x4*)(part_o + (ps * kTileM + r_local) * D + d);
+            const float4 ml = part_ml[ps * kTileM + r_local];  // m, l, scale of the fp16 o / l
+            const ttv_f32x4 v = __builtin_convertvector(part_o[((ps * kTileM + r_local) * D + d) / 4], ttv_f32x4);
             const float m_new = fmaxf(mmax, ml.x);
             const float a_old = __builtin_amdgcn_exp2f(mmax - m_new);
-            const float a_new = __builtin_amdgcn_exp2f(ml.x - m_new);
-            lsum = lsum * a_old + ml.y * a_new;
-            acc = acc * a_old + v * a_new;
+            const float a_new = __builtin_amdgcn_exp2f(ml.x - m_new) * ml.y;
+            lsum = lsum * a_old + a_new;
+            acc = acc * a_old + v * (a_new * ml.z);
             mmax = m_new;
         }
         const float inv = 1.0f / lsum;
@@ -1145,8 +1263,8 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
     Combine* comb = (Combine*)(ws + L.off_combine);
     uint16_t* q_hi = (uint16_t*)(ws + L.off_q);
     uint16_t* q_lo = (uint16_t*)(ws + L.off_qlo);
-    float* po = (float*)(ws + L.off_po);
-    float2* pml = (float2*)(ws + L.off_pml);
+    ttv_f16x4* po = (ttv_f16x4*)(ws + L.off_po);
+    float4* pml = (float4*)(ws + L.off_pml);
     const double q_mult = scale * 1.4426950408889634074;  // scores come out in log2 units
     dim3 prep_grid(bt->n_max > 0 ? bt->n_max : 1, bt->batch + 1);
     hipLaunchKernelGGL(attn_prep_kernel<D>, prep_grid, dim3(kThreads), 0, stream,

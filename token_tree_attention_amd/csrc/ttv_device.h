@@ -12,6 +12,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 ttv_bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float ttv_f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t ttv_u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t ttv_u32x2;
+typedef _Float16 ttv_f16x4 __attribute__((ext_vector_type(4)));
 
 // ---- bf16 <-> fp32 -------------------------------------------------------
 
