@@ -33,6 +33,7 @@
 //  3. attn_combine_kernel: log-sum-exp merge of the chunks of row tiles whose
 //     context was split; single-chunk tiles are written directly by step 2.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "ttv_device.h"
@@ -56,6 +57,12 @@ constexpr float kNegBig = -1.0e30f;
 constexpr int kClassPlain = 0;
 constexpr int kClassMasked = 1;
 constexpr int kClassPrecise = 2;
+
+// RoPE inverse frequencies base^(-2m/D), m < D/2, computed on the host in
+// double and passed by value.
+struct RopeTable {
+    double inv[64];
+};
 
 struct PlanHeader {
     int32_t n_items;
@@ -134,15 +141,12 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
                            int64_t max_groups, int64_t max_partials, int32_t* err) {
     __shared__ int32_t s_items[kMaxBatch + 1];
     __shared__ int32_t s_parts[kMaxBatch + 1];
-    __shared__ unsigned long long s_work;
-    __shared__ int32_t s_carry_items, s_carry_parts, s_ncomb;
-    __shared__ int32_t t_i[kThreads], t_p[kThreads];
+    __shared__ unsigned long long s_wsum[kWaves];
+    __shared__ int32_t s_wtot[2][kWaves];
+    __shared__ int32_t s_ncomb;
     const int tid = threadIdx.x;
-    if (tid == 0) {
-        s_work = 0;
-        s_ncomb = 0;
-    }
-    __syncthreads();
+    const int lane = tid & 63, wv = tid >> 6;
+    if (tid == 0) s_ncomb = 0;
     // Phase 1: total slot work, W = Hkv * sum over row tiles of (ctx + tree keys).
     unsigned long long my_work = 0;
     for (int b = tid; b < B; b += kThreads) {
@@ -159,21 +163,26 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
         }
     }
     my_work *= (unsigned long long)Hkv;
-    atomicAdd(&s_work, my_work);
+    // workgroup sum: lane shuffles, then one LDS slot per wave
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)my_work, off), hi = __shfl_xor((uint32_t)(my_work >> 32), off);
+        my_work += ((unsigned long long)hi << 32) | lo;
+    }
+    if (lane == 0) s_wsum[wv] = my_work;
     __syncthreads();
-    const unsigned long long W = s_work;
+    unsigned long long W = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) W += s_wsum[w];
     long long cl = (long long)((W + kTargetItems - 1) / kTargetItems);
     cl = ((cl + kKT - 1) / kKT) * kKT;
     if (cl < kChunkMin) cl = kChunkMin;
     if (cl > (1ll << 30)) cl = 1ll << 30;
     const int chunk_len = (int)cl;
 
-    // Phase 2: per-request item and partial counts, exclusive prefix sums.
-    if (tid == 0) {
-        s_carry_items = 0;
-        s_carry_parts = 0;
-    }
-    __syncthreads();
+    // Phase 2: per-request item and partial counts, exclusive prefix sums
+    // (lane scans, then the wave totals; the carry is the same in every thread).
+    int carry_items = 0, carry_parts = 0;
     for (int base = 0; base < B; base += kThreads) {
         const int b = base + tid;
         int ni = 0, np = 0;
@@ -193,32 +202,40 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
                 np = nc > 1 ? ni : 0;
             }
         }
-        // inclusive scan over the workgroup (Hillis-Steele in LDS)
-        t_i[tid] = ni;
-        t_p[tid] = np;
+        int si = ni, sp = np;  // inclusive scans within the wave
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int ti = __shfl_up(si, off), tp = __shfl_up(sp, off);
+            if (lane >= off) {
+                si += ti;
+                sp += tp;
+            }
+        }
+        if (lane == 63) {
+            s_wtot[0][wv] = si;
+            s_wtot[1][wv] = sp;
+        }
         __syncthreads();
-        for (int off = 1; off < kThreads; off <<= 1) {
-            const int ai = tid >= off ? t_i[tid - off] : 0;
-            const int ap = tid >= off ? t_p[tid - off] : 0;
-            __syncthreads();
-            t_i[tid] += ai;
-            t_p[tid] += ap;
-            __syncthreads();
+        int pre_i = carry_items, pre_p = carry_parts;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int vi = s_wtot[0][w], vp = s_wtot[1][w];
+            if (w < wv) {
+                pre_i += vi;
+                pre_p += vp;
+            }
+            carry_items += vi;
+            carry_parts += vp;
         }
         if (b < B) {
-            s_items[b] = s_carry_items + t_i[tid] - ni;
-            s_parts[b] = s_carry_parts + t_p[tid] - np;
+            s_items[b] = pre_i + si - ni;
+            s_parts[b] = pre_p + sp - np;
         }
-        __syncthreads();
-        if (tid == kThreads - 1) {
-            s_carry_items += t_i[tid];
-            s_carry_parts += t_p[tid];
-        }
-        __syncthreads();
+        __syncthreads();  // s_wtot is rewritten by the next block
     }
     if (tid == 0) {
-        s_items[B] = s_carry_items;
-        s_parts[B] = s_carry_parts;
+        s_items[B] = carry_items;
+        s_parts[B] = carry_parts;
     }
     __syncthreads();
     int n_items = s_items[B];
@@ -288,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
     const int32_t* __restrict__ node_offsets, const int32_t* __restrict__ ctx_lens, int B,
     int n_max, int64_t total_nodes, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const int32_t* __restrict__ positions, CacheView cache, int Hq, float rope_base,
+    const int32_t* __restrict__ positions, CacheView cache, int Hq, RopeTable rope,
     double q_mult, uint16_t* __restrict__ q_hi, uint16_t* __restrict__ q_lo, PlanHeader* hdr,
     Item* items, Combine* combine, int64_t max_items, int64_t max_groups, int64_t max_partials,
     int32_t* __restrict__ err) {
@@ -316,11 +333,24 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
     __shared__ double s_cos[D / 2], s_sin[D / 2];
     const int tid = threadIdx.x;
     const int node = s + i;
+    constexpr int kVec = 8;
+    const int q_vecs = Hq * D / kVec;
+    const int kv_vecs = cache.hkv * D / kVec;
+    // This thread's first Q, K and V vectors and cache row are fetched before
+    // the angle work, so their latency overlaps it.
+    ttv_u32x4 q_first = {0u, 0u, 0u, 0u}, k_first = {0u, 0u, 0u, 0u}, v_first = {0u, 0u, 0u, 0u};
+    if (tid < q_vecs) q_first = *(const ttv_u32x4*)(q + (int64_t)node * Hq * D + (int64_t)tid * kVec);
+    int64_t dst_first = -1;
+    if (tid < kv_vecs) {
+        const int64_t e = (int64_t)node * cache.hkv * D + (int64_t)tid * kVec;
+        k_first = *(const ttv_u32x4*)(k_new + e);
+        v_first = *(const ttv_u32x4*)(v_new + e);
+        dst_first = cache_row(cache, b, (tid * kVec) / D, ctx + i, D);
+    }
     const int pos = positions[node];
     if (tid < D / 2) {
-        // inv_freq_m = base^(-2m/D); the angle is reduced modulo 2*pi first.
-        const double inv = exp2(-(2.0 * tid / D) * log2((double)rope_base));
-        const double ang = (double)pos * inv;
+        // the angle is reduced modulo 2*pi before sincos
+        const double ang = (double)pos * rope.inv[tid];
         const double two_pi = 6.283185307179586476925;
         const double red = ang - two_pi * rint(ang / two_pi);
         double sn, cs;
@@ -329,12 +359,10 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
         s_sin[tid] = sn;
     }
     __syncthreads();
-    constexpr int kVec = 8;
     // Q: rotated, scaled by softmax_scale*log2(e), stored as bf16 hi + lo parts.
-    const int q_vecs = Hq * D / kVec;
     for (int v = tid; v < q_vecs; v += kThreads) {
         const int64_t e = (int64_t)node * Hq * D + (int64_t)v * kVec;
-        const ttv_u32x4 in = *(const ttv_u32x4*)(q + e);
+        const ttv_u32x4 in = v == tid ? q_first : *(const ttv_u32x4*)(q + e);
         const int d0 = (v * kVec) % D;
         ttv_u32x4 hi4, lo4;
 #pragma unroll
@@ -354,17 +382,17 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
         *(ttv_u32x4*)(q_lo + e) = lo4;
     }
     // K (rotated, rounded once from fp64) and V (copied) into slot ctx + i.
-    const int kv_vecs = Hkv * D / kVec;
     for (int v = tid; v < kv_vecs; v += kThreads) {
         const int h = (v * kVec) / D;
         const int d0 = (v * kVec) % D;
-        const int64_t dst = cache_row(cache, b, h, ctx + i, D);
+        const bool first = v == tid;
+        const int64_t dst = first ? dst_first : cache_row(cache, b, h, ctx + i, D);
         if (dst < 0) {
             atomicOr(err + b, TTV_ERR_BLOCK_TABLE);
             continue;
         }
         const int64_t e = (int64_t)node * Hkv * D + (int64_t)v * kVec;
-        const ttv_u32x4 kin = *(const ttv_u32x4*)(k_new + e);
+        const ttv_u32x4 kin = first ? k_first : *(const ttv_u32x4*)(k_new + e);
         ttv_u32x4 ko;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -376,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
                     (ttv_f64_to_bf16_bits(x1 * c + x0 * sn) << 16);
         }
         *(ttv_u32x4*)(cache.k + dst + d0) = ko;
-        *(ttv_u32x4*)(cache.v + dst + d0) = *(const ttv_u32x4*)(v_new + e);
+        *(ttv_u32x4*)(cache.v + dst + d0) = first ? v_first : *(const ttv_u32x4*)(v_new + e);
     }
 }
 
@@ -1266,10 +1294,12 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
     ttv_f16x4* po = (ttv_f16x4*)(ws + L.off_po);
     float4* pml = (float4*)(ws + L.off_pml);
     const double q_mult = scale * 1.4426950408889634074;  // scores come out in log2 units
+    RopeTable rope;
+    for (int m = 0; m < 64; ++m) rope.inv[m] = m < D / 2 ? pow((double)rope_base, -2.0 * m / D) : 0.0;
     dim3 prep_grid(bt->n_max > 0 ? bt->n_max : 1, bt->batch + 1);
     hipLaunchKernelGGL(attn_prep_kernel<D>, prep_grid, dim3(kThreads), 0, stream,
                        bt->node_offsets, bt->ctx_lens, bt->batch, bt->n_max, bt->total_nodes, q,
-                       k_new, v_new, positions, cv, n_heads, rope_base, q_mult, q_hi, q_lo, hdr, items,
+                       k_new, v_new, positions, cv, n_heads, rope, q_mult, q_hi, q_lo, hdr, items,
                        comb, L.max_items, L.max_groups, L.max_partials, err);
     if (hipGetLastError() != hipSuccess) return TTV_EHIP;
     const int cus = num_cus();
