@@ -40,10 +40,11 @@
 
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 8;               // prep / combine workgroups: 8 waves
 constexpr int kRowsPerWave = 32;        // query rows per wave: kMB blocks of 16
 constexpr int kMB = kRowsPerWave / 16;
-constexpr int kTileM = kWaves * kRowsPerWave;
+constexpr int kTileM = kWaves * kRowsPerWave;   // largest row tile (8 waves x 32 rows)
+constexpr int kTileMin = 4 * kRowsPerWave;         // smallest row tile (4 waves)
 constexpr int kThreads = kWaves * TTV_WAVE;
 constexpr int kKT = 32;                 // key slots per LDS tile (= one mask word)
 constexpr int kTargetItems = 1024;      // chunking aims at about this many work items
@@ -92,7 +93,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 Layout make_layout(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D) {
     Layout L;
     const int64_t G = Hq / Hkv;
-    L.max_groups = Hkv * ((T * G + kTileM - 1) / kTileM + B);
+    L.max_groups = Hkv * ((T * G + kTileMin - 1) / kTileMin + B);
     L.max_items = kTargetItems + L.max_groups;
     L.max_partials = 2 * kTargetItems;
     size_t off = align256(sizeof(PlanHeader));
@@ -136,9 +137,9 @@ __device__ __forceinline__ int64_t cache_row(const CacheView& c, int b, int h, i
 
 __device__ void build_plan(const int32_t* __restrict__ node_offsets,
                            const int32_t* __restrict__ ctx_lens, int B, int n_max,
-                           int64_t total_nodes, int G, int Hkv, int cap_limit,
-                           PlanHeader* hdr, Item* items, Combine* combine, int64_t max_items,
-                           int64_t max_groups, int64_t max_partials, int32_t* err) {
+                           int64_t total_nodes, int G, int Hkv, int cap_limit, int tile_m,
+                           int target_items, PlanHeader* hdr, Item* items, Combine* combine,
+                           int64_t max_items, int64_t max_groups, int64_t max_partials, int32_t* err) {
     __shared__ int32_t s_items[kMaxBatch + 1];
     __shared__ int32_t s_parts[kMaxBatch + 1];
     __shared__ unsigned long long s_wsum[kWaves];
@@ -156,9 +157,9 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
         if (s < 0 || n < 0 || n > n_max || (int64_t)s + n > total_nodes || ctx < 0) continue;
         if (cap_limit >= 0 && (int64_t)ctx + n > cap_limit) continue;
         const int rows = n * G;
-        const int nt = (rows + kTileM - 1) / kTileM;
+        const int nt = (rows + tile_m - 1) / tile_m;
         for (int t = 0; t < nt; ++t) {
-            const int last_row = min((t + 1) * kTileM, rows) - 1;
+            const int last_row = min((t + 1) * tile_m, rows) - 1;
             my_work += (unsigned long long)(ctx + last_row / G + 1);
         }
     }
@@ -174,7 +175,7 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
     unsigned long long W = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) W += s_wsum[w];
-    long long cl = (long long)((W + kTargetItems - 1) / kTargetItems);
+    long long cl = (long long)((W + target_items - 1) / target_items);
     cl = ((cl + kKT - 1) / kKT) * kKT;
     if (cl < kChunkMin) cl = kChunkMin;
     if (cl > (1ll << 30)) cl = 1ll << 30;
@@ -196,7 +197,7 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
                 atomicOr(err + b, TTV_ERR_CAPACITY);
             }
             if (ok && n > 0) {
-                const int nt = (n * G + kTileM - 1) / kTileM;
+                const int nt = (n * G + tile_m - 1) / tile_m;
                 const int nc = ctx > chunk_len ? (ctx + chunk_len - 1) / chunk_len : 1;
                 ni = Hkv * nt * nc;
                 np = nc > 1 ? ni : 0;
@@ -254,7 +255,7 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
         const int s = node_offsets[b];
         const int n = node_offsets[b + 1] - s;
         const int ctx = ctx_lens[b];
-        const int nt = (n * G + kTileM - 1) / kTileM;
+        const int nt = (n * G + tile_m - 1) / tile_m;
         const int nc = ctx > chunk_len ? (ctx + chunk_len - 1) / chunk_len : 1;
         const int local = x - s_items[b];
         const int t = local % nt;
@@ -270,7 +271,7 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
         it.ctx = ctx;
         it.c0 = chunk * chunk_len;
         it.c1 = min(ctx, it.c0 + chunk_len);
-        const int last_row = min((t + 1) * kTileM, n * G) - 1;
+        const int last_row = min((t + 1) * tile_m, n * G) - 1;
         it.kmax = chunk == nc - 1 ? last_row / G + 1 : 0;
         it.pslot = nc > 1 ? s_parts[b] + local : -1;
         it.nc = nc;
@@ -306,17 +307,17 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
     int n_max, int64_t total_nodes, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ positions, CacheView cache, int Hq, RopeTable rope,
-    double q_mult, uint16_t* __restrict__ q_hi, uint16_t* __restrict__ q_lo, PlanHeader* hdr,
-    Item* items, Combine* combine, int64_t max_items, int64_t max_groups, int64_t max_partials,
-    int32_t* __restrict__ err) {
+    double q_mult, uint16_t* __restrict__ q_hi, uint16_t* __restrict__ q_lo, int tile_m,
+    int target_items, PlanHeader* hdr, Item* items, Combine* combine, int64_t max_items,
+    int64_t max_groups, int64_t max_partials, int32_t* __restrict__ err) {
     const int b = blockIdx.y;
     const int Hkv = cache.hkv;
     const int G = Hq / Hkv;
     if (b == B) {
         if (blockIdx.x == 0)
             build_plan(node_offsets, ctx_lens, B, n_max, total_nodes, G, Hkv,
-                       cache.paged ? -1 : cache.cap, hdr, items, combine, max_items, max_groups,
-                       max_partials, err);
+                       cache.paged ? -1 : cache.cap, tile_m, target_items, hdr, items, combine,
+                       max_items, max_groups, max_partials, err);
         return;
     }
     const int i = blockIdx.x;
@@ -429,23 +430,28 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
 // head-dim column: exactly the V^T operand, no transposing store.
 // ---------------------------------------------------------------------------
 
-template <int D>
+template <int D, int kW>
 struct MainCfg {
+    static constexpr int kTile = kW * kRowsPerWave;        // query rows per work item
     static constexpr int kPieces = D / 8;                  // 16-byte pieces per row
     static constexpr int kRowBytes = D * 2;
     static constexpr int kTileBytes = kKT * kRowBytes;     // one K or V tile
     static constexpr int kChunkRows = 1024 / kRowBytes;    // rows per DMA instruction (64 x 16 B)
     static constexpr int kChunks = kKT / kChunkRows;       // DMA instructions per K (or V) tile
-    static_assert(kChunks <= kWaves, "one K chunk and one V chunk per wave at most");
+    // wave w loads chunks w, w + kW, ...: kCpw chunks (waves >= kChunks none)
+    static constexpr int kCpw = kChunks >= kW ? kChunks / kW : 1;
+    static_assert(kChunks % kW == 0 || kChunks < kW, "chunks spread evenly over the waves");
+    static_assert(kCpw <= 2, "at most two chunks per wave");
+    static constexpr int kOpsPerTile = 2 * kCpw;           // DMA instructions per tile per loading wave
     static constexpr int kStageBytes = 2 * kTileBytes;
     // LDS: 8 stages; precise items use the first 4 and keep their rows' Q
     // low parts in the space of the other 4.
     static constexpr int kStagesShort = 4;
     static constexpr int kStagesLong = 8;
     static constexpr int kQloOffset = kStagesShort * kStageBytes;
-    static constexpr int kQloBytes = kTileM * kRowBytes;
+    static constexpr int kQloBytes = kTile * kRowBytes;
     static constexpr int kMainBytes = kStagesLong * kStageBytes;
-    static_assert(kQloOffset + kQloBytes == kMainBytes, "Q lo fills stages 4..7");
+    static_assert(kQloOffset + kQloBytes <= kMainBytes, "Q lo fits in stages 4..7");
     static constexpr int kQloChunks = kQloBytes / 1024;    // DMA instructions for the Q low parts
 };
 
@@ -458,13 +464,15 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Wait until at most 2*k of this wave's loads are outstanding (k in 0..5).
-__device__ __forceinline__ void wait_vmcnt_pairs(int k) {
-    if (k >= 5) wait_vmcnt<10>();
-    else if (k == 4) wait_vmcnt<8>();
-    else if (k == 3) wait_vmcnt<6>();
-    else if (k == 2) wait_vmcnt<4>();
-    else if (k == 1) wait_vmcnt<2>();
+// Wait until at most k tiles' worth (kOps loads each) of this wave's loads
+// are outstanding (k in 0..5).
+template <int kOps>
+__device__ __forceinline__ void wait_vmcnt_tiles(int k) {
+    if (k >= 5) wait_vmcnt<5 * kOps>();
+    else if (k == 4) wait_vmcnt<4 * kOps>();
+    else if (k == 3) wait_vmcnt<3 * kOps>();
+    else if (k == 2) wait_vmcnt<2 * kOps>();
+    else if (k == 1) wait_vmcnt<kOps>();
     else wait_vmcnt<0>();
 }
 
@@ -539,62 +547,72 @@ __device__ __forceinline__ const uint16_t* kv_row_ptr(const CacheView& c, const 
     return base + (((int64_t)blk * c.hkv + h) * TTV_BLOCK_SIZE + (slot & 15)) * D;
 }
 
-// Physical blocks holding the rows that wave w loads for a tile (slots slot0
-// .. slot0 + valid - 1): the first and the last of those rows, which span at
-// most two blocks.  Wave-uniform scalar reads of the block table; the tile
-// loop fetches them one tile ahead of the loads that use them.
+// Physical blocks holding the rows of each chunk wave w loads for a tile
+// (slots slot0 .. slot0 + valid - 1): the first and the last of those rows,
+// which span at most two blocks.  Wave-uniform scalar reads of the block
+// table; the tile loop fetches them one tile ahead of the loads that use them.
 struct TileBlocks {
-    int32_t first, last;
+    int32_t first[2], last[2];
 };
 
-template <int D, bool kPaged>
+template <int D, int kW, bool kPaged>
 __device__ __forceinline__ TileBlocks tile_blocks(const CacheView& c, const int32_t* __restrict__ table,
                                                   int b, int slot0, int valid, int wave) {
-    using MC = MainCfg<D>;
-    TileBlocks tb{0, 0};
+    using MC = MainCfg<D, kW>;
+    TileBlocks tb{{0, 0}, {0, 0}};
     if (!kPaged || wave >= MC::kChunks) return tb;
-    const int r_first = min(wave * MC::kChunkRows, valid - 1);
-    const int r_last = min(wave * MC::kChunkRows + MC::kChunkRows - 1, valid - 1);
-    const int lb0 = (slot0 + r_first) >> 4;
-    const int lb1 = (slot0 + r_last) >> 4;
-    tb.first = lb0 < c.max_blocks ? table[(int64_t)b * c.max_blocks + lb0] : -1;
-    tb.last = lb1 < c.max_blocks ? table[(int64_t)b * c.max_blocks + lb1] : -1;
+#pragma unroll
+    for (int j = 0; j < MC::kCpw; ++j) {
+        const int ch = wave + j * kW;
+        const int r_first = min(ch * MC::kChunkRows, valid - 1);
+        const int r_last = min(ch * MC::kChunkRows + MC::kChunkRows - 1, valid - 1);
+        const int lb0 = (slot0 + r_first) >> 4;
+        const int lb1 = (slot0 + r_last) >> 4;
+        tb.first[j] = lb0 < c.max_blocks ? table[(int64_t)b * c.max_blocks + lb0] : -1;
+        tb.last[j] = lb1 < c.max_blocks ? table[(int64_t)b * c.max_blocks + lb1] : -1;
+    }
     return tb;
 }
 
 // Issue the LDS-DMA loads of one tile (slots slot0 .. slot0 + valid - 1; rows
 // past valid repeat the last valid slot, so every LDS byte is defined).
-// Wave w < kChunks loads chunk w (kChunkRows rows) of K and of V.
-template <int D, bool kPaged>
+// Wave w loads chunks w, w + kW, ... (kChunkRows rows each) of K and of V.
+template <int D, int kW, bool kPaged>
 __device__ __forceinline__ void issue_tile(const CacheView& c, TileBlocks tb, int b, int kvh, int slot0,
                                            int valid, uint32_t stage, int wave, int lane, int32_t* err) {
-    using MC = MainCfg<D>;
+    using MC = MainCfg<D, kW>;
     constexpr int P = MC::kPieces;
     if (wave >= MC::kChunks) return;
-    const int r_first = min(wave * MC::kChunkRows, valid - 1);
-    if (kPaged && (tb.first < 0 || tb.first >= c.num_blocks || tb.last < 0 || tb.last >= c.num_blocks)) {
-        if (lane == 0) atomicOr(err + b, TTV_ERR_BLOCK_TABLE);
-        tb.first = tb.last = 0;  // load a valid block; the request is flagged
+#pragma unroll
+    for (int j = 0; j < MC::kCpw; ++j) {
+        const int ch = wave + j * kW;
+        const int r_first = min(ch * MC::kChunkRows, valid - 1);
+        int bf = tb.first[j], bl = tb.last[j];
+        if (kPaged && (bf < 0 || bf >= c.num_blocks || bl < 0 || bl >= c.num_blocks)) {
+            if (lane == 0) atomicOr(err + b, TTV_ERR_BLOCK_TABLE);
+            bf = bl = 0;  // load a valid block; the request is flagged
+        }
+        const int row = ch * MC::kChunkRows + lane / P;
+        const int phys = lane % P;
+        const int slot = slot0 + min(row, valid - 1);
+        const int blk = (!kPaged || (slot >> 4) == ((slot0 + r_first) >> 4)) ? bf : bl;
+        const uint16_t* krow = kv_row_ptr<D, kPaged>(c, c.k, b, kvh, slot, blk);
+        const uint16_t* vrow = kv_row_ptr<D, kPaged>(c, c.v, b, kvh, slot, blk);
+        const uint32_t chunk_off = ch * MC::kChunkRows * MC::kRowBytes;
+        dma16(stage + chunk_off, krow + 8 * swz_k(row, phys, P));
+        dma16(stage + MC::kTileBytes + chunk_off, vrow + 8 * swz_v(row, phys, P));
     }
-    const int row = wave * MC::kChunkRows + lane / P;
-    const int phys = lane % P;
-    const int slot = slot0 + min(row, valid - 1);
-    const int blk = (!kPaged || (slot >> 4) == ((slot0 + r_first) >> 4)) ? tb.first : tb.last;
-    const uint16_t* krow = kv_row_ptr<D, kPaged>(c, c.k, b, kvh, slot, blk);
-    const uint16_t* vrow = kv_row_ptr<D, kPaged>(c, c.v, b, kvh, slot, blk);
-    const uint32_t chunk_off = wave * MC::kChunkRows * MC::kRowBytes;
-    dma16(stage + chunk_off, krow + 8 * swz_k(row, phys, P));
-    dma16(stage + MC::kTileBytes + chunk_off, vrow + 8 * swz_v(row, phys, P));
 }
 
-template <int D, bool kPaged>
-__global__ __launch_bounds__(kThreads) void attn_main_kernel(
+template <int D, bool kPaged, int kW>
+__global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
     const PlanHeader* __restrict__ hdr, const Item* __restrict__ items,
     const uint16_t* q_hi,  // not __restrict__: keeps its loads ahead of the prologue fence
     const uint16_t* __restrict__ q_lo, const uint32_t* __restrict__ mask, int mask_words,
     CacheView cache, const int32_t* __restrict__ table, int Hq, uint16_t* __restrict__ out,
     ttv_f16x4* __restrict__ part_o, float4* __restrict__ part_ml, int32_t* __restrict__ err) {
-    using MC = MainCfg<D>;
+    using MC = MainCfg<D, kW>;
+    constexpr int kTileR = MC::kTile;
     constexpr int P = MC::kPieces;
     constexpr int KC = D / 32;   // 32-wide k chunks of the head dim
     constexpr int DB = D / 16;   // 16-row blocks of the head dim
@@ -643,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
     for (int x = vid; x < n_items; x += active) {
         const Item it = items[x];
         const int rows = it.n * G;
-        const int row_base = it.tile * kTileM + wave * kRowsPerWave;
+        const int row_base = it.tile * kTileR + wave * kRowsPerWave;
         const int n_ctx_tiles = (it.c1 - it.c0 + kKT - 1) / kKT;
         const int n_tree_tiles = (it.kmax + kKT - 1) / kKT;
         const int n_tiles = n_ctx_tiles + n_tree_tiles;
@@ -659,8 +677,8 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
         const int stages = precise ? MC::kStagesShort : MC::kStagesLong;
         const int smask = stages - 1;
         const int ahead = stages - 1;  // tiles issued ahead of the one consumed
-        const int node0 = (it.tile * kTileM) / G;
-        const int node1 = min(it.n - 1, (it.tile * kTileM + kTileM - 1) / G);
+        const int node0 = (it.tile * kTileR) / G;
+        const int node1 = min(it.n - 1, (it.tile * kTileR + kTileR - 1) / G);
         const int tree_limit = it.ctx + it.kmax;
         auto tile_slot0 = [&](int tau) __attribute__((always_inline)) {
             return tau < n_ctx_tiles ? it.c0 + tau * kKT : it.ctx + (tau - n_ctx_tiles) * kKT;
@@ -670,42 +688,51 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
         };
         auto blocks_of = [&](int tau) __attribute__((always_inline)) {
             const int slot0 = tile_slot0(tau);
-            return tile_blocks<D, kPaged>(cache, table, it.b, slot0, tile_valid(tau, slot0), wave);
+            return tile_blocks<D, kW, kPaged>(cache, table, it.b, slot0, tile_valid(tau, slot0), wave);
         };
         auto issue = [&](int tau, TileBlocks tb) __attribute__((always_inline)) {
             const int slot0 = tile_slot0(tau);
-            issue_tile<D, kPaged>(cache, tb, it.b, it.kvh, slot0, tile_valid(tau, slot0),
+            issue_tile<D, kW, kPaged>(cache, tb, it.b, it.kvh, slot0, tile_valid(tau, slot0),
                                   ring + (tau & smask) * MC::kStageBytes, wave, lane, err);
         };
-        TileBlocks next_blocks{0, 0};  // blocks of the next tile to issue
+        TileBlocks next_blocks{{0, 0}, {0, 0}};  // blocks of the next tile to issue
         // Fast issue path for whole context tiles (slot0 = c0 + 32 tau, no
-        // clamping): this lane's element offsets of its K and V rows, so an
-        // issue is a scalar base plus these.  A wave's rows of such a tile lie
-        // in one paged block (slot0 is a multiple of 32, the rows a wave loads
-        // are a 16-aligned sub-range of a block).
-        const int f_row = wave * MC::kChunkRows + lane / P;
-        const int f_phys = lane % P;
-        const int f_rowb = (kPaged ? (f_row & 15) : f_row) * MC::kRowBytes;
-        const uint32_t f_kb = f_rowb + 16 * swz_k(f_row, f_phys, P);  // byte offsets from the tile base
-        const uint32_t f_vb = f_rowb + 16 * swz_v(f_row, f_phys, P);
+        // clamping): an issue is a wave-uniform base plus a per-lane byte
+        // offset, kept per chunk this wave loads (from the first row of the
+        // chunk's paged block, or from the tile's first slot).  A chunk's rows
+        // of such a tile lie in one paged block: slot0 is a multiple of 32 and
+        // a chunk is a 16-aligned sub-range of rows.
+        uint32_t f_kb[MC::kCpw], f_vb[MC::kCpw];
+#pragma unroll
+        for (int j = 0; j < MC::kCpw; ++j) {
+            const int f_row = (wave + j * kW) * MC::kChunkRows + lane / P;
+            const int f_phys = lane % P;
+            const int f_rowb = (kPaged ? (f_row & 15) : f_row) * MC::kRowBytes;
+            f_kb[j] = f_rowb + 16 * swz_k(f_row, f_phys, P);
+            f_vb[j] = f_rowb + 16 * swz_v(f_row, f_phys, P);
+        }
         auto issue_whole = [&](int tau, TileBlocks tb) __attribute__((always_inline)) {
             if (wave >= MC::kChunks) return;
             const int slot0 = it.c0 + tau * kKT;
-            int64_t row0;  // element offset of the tile's (first) row of this KV head
-            if (kPaged) {
-                int blk = tb.first;
-                if (blk < 0 || blk >= cache.num_blocks) {
-                    if (lane == 0) atomicOr(err + it.b, TTV_ERR_BLOCK_TABLE);
-                    blk = 0;  // load a valid block; the request is flagged
-                }
-                row0 = ((int64_t)blk * cache.hkv + it.kvh) * TTV_BLOCK_SIZE * D;
-            } else {
-                row0 = (((int64_t)it.b * cache.hkv + it.kvh) * cache.cap + slot0) * D;
-            }
             const uint32_t stage = ring + (tau & smask) * MC::kStageBytes;
-            const uint32_t chunk_off = wave * MC::kChunkRows * MC::kRowBytes;
-            dma16s(stage + chunk_off, cache.k + row0, f_kb);
-            dma16s(stage + MC::kTileBytes + chunk_off, cache.v + row0, f_vb);
+#pragma unroll
+            for (int j = 0; j < MC::kCpw; ++j) {
+                const int ch = wave + j * kW;
+                int64_t row0;  // element offset of the tile's (first) row of this KV head
+                if (kPaged) {
+                    int blk = tb.first[j];
+                    if (blk < 0 || blk >= cache.num_blocks) {
+                        if (lane == 0) atomicOr(err + it.b, TTV_ERR_BLOCK_TABLE);
+                        blk = 0;  // load a valid block; the request is flagged
+                    }
+                    row0 = ((int64_t)blk * cache.hkv + it.kvh) * TTV_BLOCK_SIZE * D;
+                } else {
+                    row0 = (((int64_t)it.b * cache.hkv + it.kvh) * cache.cap + slot0) * D;
+                }
+                const uint32_t chunk_off = ch * MC::kChunkRows * MC::kRowBytes;
+                dma16s(stage + chunk_off, cache.k + row0, f_kb[j]);
+                dma16s(stage + MC::kTileBytes + chunk_off, cache.v + row0, f_vb[j]);
+            }
         };
 
         // ---- prologue: Q hi into registers (ordinary loads); Q lo, the
@@ -730,10 +757,10 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
         if (precise) {
             // Q low parts, swizzled like K; rows past the tile's last row
             // repeat that row (finite, never written out)
-            for (int j = wave; j < MC::kQloChunks; j += kWaves) {
+            for (int j = wave; j < MC::kQloChunks; j += kW) {
                 const int rl = j * MC::kChunkRows + lane / P;
                 const int phys = lane % P;
-                const int r = min(it.tile * kTileM + rl, rows - 1);
+                const int r = min(it.tile * kTileR + rl, rows - 1);
                 const int node = r / G, g = r % G;
                 dma16(qlo_s + j * 1024,
                       q_lo + ((int64_t)(it.s + node) * Hq + it.kvh * G + g) * D + 8 * swz_k(rl, phys, P));
@@ -743,7 +770,7 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
             // the tile nodes' mask rows, copied flat (row stride mask_words)
             const int words = (node1 - node0 + 1) * mask_words;
             const uint32_t* src = mask + (int64_t)(it.s + node0) * mask_words;
-            for (int j = wave; j * 64 < words; j += kWaves)
+            for (int j = wave; j * 64 < words; j += kW)
                 dma4(mask_base + j * 256, src + min(j * 64 + lane, words - 1));
         }
         for (int j = 0; j < 2 && j < n_tiles; ++j) issue(j, blocks_of(j));
@@ -948,12 +975,13 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
         auto advance = [&](auto cls, int tau) __attribute__((always_inline)) {
             constexpr int kA = (decltype(cls)::value == kClassPrecise ? MC::kStagesShort : MC::kStagesLong) - 1;
             if (tau + kA < n_tiles) {  // steady state: kA - 2 later tiles stay in flight
-                if (MC::kChunks >= kWaves || wave < MC::kChunks) wait_vmcnt<2 * (kA - 2)>();
+                if (MC::kChunks >= kW || wave < MC::kChunks) wait_vmcnt<MC::kOpsPerTile * (kA - 2)>();
                 raw_barrier();
                 if (tau + kA < n_plain) issue_whole(tau + kA, next_blocks);
                 else issue(tau + kA, next_blocks);
             } else {
-                if (MC::kChunks >= kWaves || wave < MC::kChunks) wait_vmcnt_pairs(min(kA - 2, n_tiles - 2 - tau));
+                if (MC::kChunks >= kW || wave < MC::kChunks)
+                    wait_vmcnt_tiles<MC::kOpsPerTile>(min(kA - 2, n_tiles - 2 - tau));
                 raw_barrier();
             }
         };
@@ -1148,7 +1176,7 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) {
             const int r_local = wave * kRowsPerWave + 16 * mb + l16;
-            const int r = it.tile * kTileM + r_local;
+            const int r = it.tile * kTileR + r_local;
             if (r >= rows) continue;
             if (it.pslot < 0) {
                 const int node = r / G, g = r % G;
@@ -1173,12 +1201,12 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
                     for (int q = 0; q < 4; ++q) amax = __builtin_fmaxf(amax, __builtin_fabsf(o[db][mb][q]));
                 const int e = __builtin_amdgcn_frexp_expf(group_max(amax) * inv_l);
                 const float sc = __builtin_amdgcn_ldexpf(inv_l, -e);
-                ttv_f16x4* dst = part_o + (((int64_t)it.pslot * kTileM + r_local) * D) / 4;
+                ttv_f16x4* dst = part_o + (((int64_t)it.pslot * kTileR + r_local) * D) / 4;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
                     dst[4 * db + g4] = __builtin_convertvector(o[db][mb] * sc, ttv_f16x4);
                 if (g4 == 0)
-                    part_ml[(int64_t)it.pslot * kTileM + r_local] =
+                    part_ml[(int64_t)it.pslot * kTileR + r_local] =
                         make_float4(m_run[mb], l_run[mb], __builtin_amdgcn_ldexpf(1.0f, e), 0.f);
             }
         }
@@ -1186,10 +1214,10 @@ __global__ __launch_bounds__(kThreads) void attn_main_kernel(
     }
 }
 
-template <int D>
+template <int D, int kW>
 size_t main_lds_bytes(int G, int mask_words) {
-    using MC = MainCfg<D>;
-    const int nodes = kTileM / G + 2;
+    using MC = MainCfg<D, kW>;
+    const int nodes = MC::kTile / G + 2;
     const size_t mask_bytes = (size_t)((nodes * mask_words + 63) / 64) * 256;
     return (size_t)MC::kMainBytes + mask_bytes;
 }
@@ -1198,14 +1226,14 @@ size_t main_lds_bytes(int G, int mask_words) {
 // 3. Combine: merge the chunk partials of split row tiles.
 // ---------------------------------------------------------------------------
 
-template <int D>
+template <int D, int kTileR>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(
     const PlanHeader* __restrict__ hdr, const Combine* __restrict__ combine, int Hq, int Hkv,
     const ttv_f16x4* __restrict__ part_o, const float4* __restrict__ part_ml,
     uint16_t* __restrict__ out) {
     constexpr int kLanesPerRow = D / 4;                 // each lane: 4 consecutive d
     constexpr int kRowsPerPass = kThreads / kLanesPerRow;
-    constexpr int kRowBlocks = kTileM / kRowsPerPass;
+    constexpr int kRowBlocks = kTileR / kRowsPerPass;
     const int n_work = hdr->n_combine * kRowBlocks;
     const int G = Hq / Hkv;
     const int tid = threadIdx.x;
@@ -1213,7 +1241,7 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(
         const Combine cb = combine[wk / kRowBlocks];
         const int r_local = (wk % kRowBlocks) * kRowsPerPass + tid / kLanesPerRow;
         const int d = (tid % kLanesPerRow) * 4;
-        const int r = cb.tile * kTileM + r_local;
+        const int r = cb.tile * kTileR + r_local;
         if (r >= cb.n * G) continue;
         // One pass with a running max; the chunk loads are independent, so the
         // unrolled loop keeps several in flight.
@@ -1222,8 +1250,8 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(
 #pragma unroll 4
         for (int c = 0; c < cb.nc; ++c) {
             const int64_t ps = cb.pslot0 + (int64_t)c * cb.stride;
-            const float4 ml = part_ml[ps * kTileM + r_local];  // m, l, scale of the fp16 o / l
-            const ttv_f32x4 v = __builtin_convertvector(part_o[((ps * kTileM + r_local) * D + d) / 4], ttv_f32x4);
+            const float4 ml = part_ml[ps * kTileR + r_local];  // m, l, scale of the fp16 o / l
+            const ttv_f32x4 v = __builtin_convertvector(part_o[((ps * kTileR + r_local) * D + d) / 4], ttv_f32x4);
             const float m_new = fmaxf(mmax, ml.x);
             const float a_old = __builtin_amdgcn_exp2f(mmax - m_new);
             const float a_new = __builtin_amdgcn_exp2f(ml.x - m_new) * ml.y;
@@ -1296,30 +1324,47 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
     const double q_mult = scale * 1.4426950408889634074;  // scores come out in log2 units
     RopeTable rope;
     for (int m = 0; m < 64; ++m) rope.inv[m] = m < D / 2 ? pow((double)rope_base, -2.0 * m / D) : 0.0;
+    // Few row tiles (a small batch): 128-row items on 4 waves, about one item
+    // per CU; otherwise 256-row items on 8 waves, about four per CU.
+    const int G = n_heads / cache->n_kv_heads;
+    const int64_t tiles256 =
+        (int64_t)bt->batch * cache->n_kv_heads * (((int64_t)bt->n_max * G + kTileM - 1) / kTileM);
+    const bool small = tiles256 < num_cus();
+    const int tile_m = small ? kTileMin : kTileM;
+    const int target_items = small ? num_cus() : kTargetItems;
     dim3 prep_grid(bt->n_max > 0 ? bt->n_max : 1, bt->batch + 1);
     hipLaunchKernelGGL(attn_prep_kernel<D>, prep_grid, dim3(kThreads), 0, stream,
                        bt->node_offsets, bt->ctx_lens, bt->batch, bt->n_max, bt->total_nodes, q,
-                       k_new, v_new, positions, cv, n_heads, rope, q_mult, q_hi, q_lo, hdr, items,
+                       k_new, v_new, positions, cv, n_heads, rope, q_mult, q_hi, q_lo, tile_m,
+                       target_items, hdr, items,
                        comb, L.max_items, L.max_groups, L.max_partials, err);
     if (hipGetLastError() != hipSuccess) return TTV_EHIP;
     const int cus = num_cus();
-    int64_t grid = (int64_t)cus;  // one 256-row workgroup per CU (LDS and registers bound it)
+    int64_t grid = (int64_t)cus;  // one workgroup per CU (LDS and registers bound it)
     if (grid > L.max_items) grid = ((L.max_items + kNumXcd - 1) / kNumXcd) * kNumXcd;
     grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
-    const size_t lds = main_lds_bytes<D>(n_heads / cache->n_kv_heads, mask_words);
-    if (lds > 160 * 1024) return TTV_EINVAL;
-    auto kern = cv.paged ? attn_main_kernel<D, true> : attn_main_kernel<D, false>;
-    static bool attr_set[2] = {false, false};
-    if (!attr_set[cv.paged]) {
-        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr_set[cv.paged] = true;
-    }
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, stream, hdr, items, q_hi,
-                       q_lo, mask, mask_words, cv, cache->block_table, n_heads, out, po, pml, err);
-    if (hipGetLastError() != hipSuccess) return TTV_EHIP;
-    hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((unsigned)(2 * cus)), dim3(kThreads), 0,
-                       stream, hdr, comb, n_heads, cache->n_kv_heads, po, pml, out);
-    return hipGetLastError() == hipSuccess ? TTV_OK : TTV_EHIP;
+    auto run_main = [&](auto waves) -> int {
+        constexpr int kW = decltype(waves)::value;
+        using MC = MainCfg<D, kW>;
+        const size_t lds = main_lds_bytes<D, kW>(n_heads / cache->n_kv_heads, mask_words);
+        if (lds > 160 * 1024) return TTV_EINVAL;
+        auto kern = cv.paged ? attn_main_kernel<D, true, kW> : attn_main_kernel<D, false, kW>;
+        static bool attr_set[2] = {false, false};
+        if (!attr_set[cv.paged]) {
+            if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    160 * 1024) != hipSuccess)
+                return TTV_EHIP;
+            attr_set[cv.paged] = true;
+        }
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kW * TTV_WAVE), lds, stream, hdr, items,
+                           q_hi, q_lo, mask, mask_words, cv, cache->block_table, n_heads, out, po,
+                           pml, err);
+        if (hipGetLastError() != hipSuccess) return TTV_EHIP;
+        hipLaunchKernelGGL((attn_combine_kernel<D, MC::kTile>), dim3((unsigned)(2 * cus)), dim3(kThreads), 0,
+                           stream, hdr, comb, n_heads, cache->n_kv_heads, po, pml, out);
+        return hipGetLastError() == hipSuccess ? TTV_OK : TTV_EHIP;
+    };
+    return small ? run_main(std::integral_constant<int, 4>{}) : run_main(std::integral_constant<int, 8>{});
 }
 
 }  // namespace
