@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kWalkThreads) void greedy_walk_kernel(
     const int32_t* __restrict__ next_sibling, int32_t max_accept, int32_t* __restrict__ accept_len,
     int32_t* __restrict__ accepted_nodes, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ row_argmax, int32_t* __restrict__ err) {
-    __shared__ int32_t s_choice[TTV_MAX_TREE_NODES + 1];
+    __shared__ unsigned long long s_key[TTV_MAX_TREE_NODES + 1];
     __shared__ int32_t s_tok[TTV_MAX_TREE_NODES];
     __shared__ int32_t s_first[TTV_MAX_TREE_NODES];
     __shared__ int32_t s_next[TTV_MAX_TREE_NODES];
@@ -129,6 +129,43 @@ __global__ __launch_bounds__(kWalkThreads) void greedy_walk_kernel(
 
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
+    // Stages every chunk key of rows [s + b, s + b + n] (all loads of a batch
+    // in flight together, then LDS max per row) and the nodes' tokens and
+    // retrieve links.  Keys of one row compare as 64-bit maxima, so repeated
+    // loads of the last key (the clamp below) change nothing.
+    auto stage = [&](int s, int n) {
+        for (int r = tid; r <= n; r += kWalkThreads) s_key[r] = 0ull;
+        for (int i = tid; i < n; i += kWalkThreads) {
+            s_tok[i] = tokens[s + i];
+            s_first[i] = next_token[s + i];
+            s_next[i] = next_sibling[s + i];
+        }
+        __syncthreads();
+        // (n + 1) * n_chunks < 2^31: n <= 1024 and a chunk holds >= 4096 of
+        // fewer than 2^31 vocab entries.
+        const uint32_t nc = (uint32_t)n_chunks;
+        const uint32_t total = (uint32_t)(n + 1) * nc;
+        const uint64_t* pk = partial + ((int64_t)s + b) * n_chunks;
+        constexpr int kBatch = 8;
+        for (uint32_t base = tid; base < total; base += kBatch * kWalkThreads) {
+            uint64_t k[kBatch];
+            uint32_t at[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const uint32_t idx = base + u * kWalkThreads;
+                at[u] = idx < total ? idx : total - 1;
+                k[u] = pk[at[u]];
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) atomicMax(&s_key[at[u] / nc], (unsigned long long)k[u]);
+        }
+        __syncthreads();
+    };
+    // Request 0 starts at node 0 (node_offsets[0] = 0): stage up to n_max
+    // nodes before the offsets arrive, and redo it only if they disagree.
+    const bool spec = b == 0;
+    const int n_spec = (int)min((int64_t)n_max, total_nodes);
+    if (spec) stage(0, n_spec);
     const int s = node_offsets[b];
     const int n = node_offsets[b + 1] - s;
     if (s < 0 || n < 0 || n > n_max || (int64_t)s + n > total_nodes) {  // uniform
@@ -138,25 +175,13 @@ __global__ __launch_bounds__(kWalkThreads) void greedy_walk_kernel(
         }
         return;
     }
+    if (!spec || s != 0) stage(s, n);
     const int64_t row0 = (int64_t)s + b;
-    for (int r = tid; r <= n; r += kWalkThreads) {
-        const uint64_t* pk = partial + (row0 + r) * n_chunks;
-        uint64_t k = pk[0];
-#pragma unroll 8
-        for (int64_t c = 1; c < n_chunks; ++c) k = pk[c] > k ? pk[c] : k;
-        const int32_t choice = (int32_t)ttv_key_index(k);
-        s_choice[r] = choice;
-        if (row_argmax) row_argmax[row0 + r] = choice;
-    }
-    for (int i = tid; i < n; i += kWalkThreads) {
-        s_tok[i] = tokens[s + i];
-        s_first[i] = next_token[s + i];
-        s_next[i] = next_sibling[s + i];
-    }
-    __syncthreads();
+    if (row_argmax)
+        for (int r = tid; r <= n; r += kWalkThreads) row_argmax[row0 + r] = (int32_t)ttv_key_index(s_key[r]);
     if (tid == 0) {
         int a = 0, flags = 0;
-        int target = s_choice[0];
+        int target = (int)ttv_key_index(s_key[0]);
         int j = n > 0 ? 0 : -1;  // node 0 is the root's first child (parent[0] == -1)
         while (j >= 0) {
             // scan the sibling list starting at j for the target token
@@ -170,7 +195,7 @@ __global__ __launch_bounds__(kWalkThreads) void greedy_walk_kernel(
                 break;
             }
             s_path[a++] = j;
-            target = s_choice[1 + j];
+            target = (int)ttv_key_index(s_key[1 + j]);
             const int fc = s_first[j];
             j = (fc > j && fc < n) ? fc : -1;
         }

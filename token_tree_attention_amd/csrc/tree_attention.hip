@@ -51,7 +51,10 @@ constexpr int kTargetItems = 1024;      // chunking aims at about this many work
 constexpr int kChunkMin = 128;          // shortest context chunk (slots)
 constexpr int kMaxBatch = 4096;         // plan keeps per-request prefix sums in LDS
 constexpr int kNumXcd = 8;
-constexpr int kPreciseCtx = 256;       // requests with a shorter context run every tile precise
+constexpr int kMaxGrid = 1024;          // main-kernel workgroups at most (one per CU)
+constexpr int kPreciseCtx = 256;        // requests with a shorter context run every tile precise
+constexpr int kCombThreads = 256;       // combine workgroup
+constexpr int kCombBatch = 8;           // chunk partials a combine thread loads before using any
 constexpr float kLazyRescale = 8.0f;    // log2 headroom before the running max is moved
 constexpr float kNegBig = -1.0e30f;
 // Tile classes of the attention loop (see attn_main_kernel).
@@ -97,8 +100,8 @@ Layout make_layout(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D) {
     L.max_items = kTargetItems + L.max_groups;
     L.max_partials = 2 * kTargetItems;
     size_t off = align256(sizeof(PlanHeader));
-    L.off_items = off;
-    off = align256(off + (size_t)L.max_items * sizeof(Item));
+    L.off_items = off;  // slots in workgroup order: up to max_items + one row of the grid
+    off = align256(off + (size_t)(L.max_items + kMaxGrid) * sizeof(Item));
     L.off_combine = off;
     off = align256(off + (size_t)L.max_groups * sizeof(Combine));
     L.off_q = off;
@@ -138,10 +141,10 @@ __device__ __forceinline__ int64_t cache_row(const CacheView& c, int b, int h, i
 __device__ void build_plan(const int32_t* __restrict__ node_offsets,
                            const int32_t* __restrict__ ctx_lens, int B, int n_max,
                            int64_t total_nodes, int G, int Hkv, int cap_limit, int tile_m,
-                           int target_items, PlanHeader* hdr, Item* items, Combine* combine,
-                           int64_t max_items, int64_t max_groups, int64_t max_partials, int32_t* err) {
-    __shared__ int32_t s_items[kMaxBatch + 1];
-    __shared__ int32_t s_parts[kMaxBatch + 1];
+                           int target_items, int grid, PlanHeader* hdr, Item* items,
+                           Combine* combine, int64_t max_items, int64_t max_groups,
+                           int64_t max_partials, int32_t* err, int32_t* s_items,
+                           int32_t* s_parts) {  // s_items, s_parts: LDS, kMaxBatch + 1 each
     __shared__ unsigned long long s_wsum[kWaves];
     __shared__ int32_t s_wtot[2][kWaves];
     __shared__ int32_t s_ncomb;
@@ -244,6 +247,11 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
     if (n_items > max_items || s_parts[B] > max_partials) n_items = 0;
 
     // Phase 3: item descriptors (request found by binary search on the prefix).
+    // Logical item x goes to workgroup w's k-th slot, k * grid + w, where the
+    // main kernel's workgroup w runs items vid(w) + k * active; so a
+    // workgroup finds its first item at slot w without knowing n_items.
+    const int active = min(grid, ((n_items + kNumXcd - 1) / kNumXcd) * kNumXcd);
+    const int per_xcd = active / kNumXcd;
     for (int x = tid; x < n_items; x += kThreads) {
         int lo = 0, hi = B - 1;
         while (lo < hi) {  // last b with s_items[b] <= x
@@ -276,7 +284,11 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
         it.pslot = nc > 1 ? s_parts[b] + local : -1;
         it.nc = nc;
         it.nt = nt;
-        items[x] = it;
+        {
+            const int kk = x / active, v = x % active;
+            const int w = (v % per_xcd) * kNumXcd + v / per_xcd;
+            items[(int64_t)kk * grid + w] = it;
+        }
         if (nc > 1 && chunk == 0) {
             const int ci = atomicAdd(&s_ncomb, 1);
             if (ci < max_groups) {
@@ -308,47 +320,41 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ positions, CacheView cache, int Hq, RopeTable rope,
     double q_mult, uint16_t* __restrict__ q_hi, uint16_t* __restrict__ q_lo, int tile_m,
-    int target_items, PlanHeader* hdr, Item* items, Combine* combine, int64_t max_items,
+    int target_items, int grid, PlanHeader* hdr, Item* items, Combine* combine, int64_t max_items,
     int64_t max_groups, int64_t max_partials, int32_t* __restrict__ err) {
-    const int b = blockIdx.y;
     const int Hkv = cache.hkv;
     const int G = Hq / Hkv;
-    if (b == B) {
-        if (blockIdx.x == 0)
-            build_plan(node_offsets, ctx_lens, B, n_max, total_nodes, G, Hkv,
-                       cache.paged ? -1 : cache.cap, tile_m, target_items, hdr, items, combine,
-                       max_items, max_groups, max_partials, err);
+    // The plan's prefix sums, or a node workgroup's copy of node_offsets.
+    __shared__ int32_t s_buf[2 * (kMaxBatch + 1)];
+    // Workgroup 0 builds the plan (dispatched first, so it overlaps the
+    // rest); workgroup 1 + t rotates node t of the whole batch.
+    if (blockIdx.x == 0) {
+        build_plan(node_offsets, ctx_lens, B, n_max, total_nodes, G, Hkv,
+                   cache.paged ? -1 : cache.cap, tile_m, target_items, grid, hdr, items, combine,
+                   max_items, max_groups, max_partials, err, s_buf, s_buf + kMaxBatch + 1);
         return;
     }
-    const int i = blockIdx.x;
-    const int s = node_offsets[b];
-    const int n = node_offsets[b + 1] - s;
-    const int ctx = ctx_lens[b];
-    if (s < 0 || n < 0 || n > n_max || (int64_t)s + n > total_nodes || ctx < 0) return;
-    if (i >= n) return;
-    if (!cache.paged && (int64_t)ctx + n > cache.cap) return;  // flagged by the plan
-
+    const int64_t node = (int64_t)blockIdx.x - 1;
+    const int tid = threadIdx.x;
+    constexpr int kVec = 8;
+    const int q_vecs = Hq * D / kVec;
+    const int kv_vecs = cache.hkv * D / kVec;
+    int32_t* s_off = s_buf;
     // Rotation in fp64: with fp32, x0 cos - x1 sin loses absolute accuracy
     // when the two products nearly cancel, which shows up as several bf16
     // ulps on small results.  The work is N_b * (Hq + Hkv) * D/2 pairs.
     __shared__ double s_cos[D / 2], s_sin[D / 2];
-    const int tid = threadIdx.x;
-    const int node = s + i;
-    constexpr int kVec = 8;
-    const int q_vecs = Hq * D / kVec;
-    const int kv_vecs = cache.hkv * D / kVec;
-    // This thread's first Q, K and V vectors and cache row are fetched before
-    // the angle work, so their latency overlaps it.
+    // The node's own loads do not depend on which request owns it, so they
+    // are issued first; the request is then found in the staged offsets.
     ttv_u32x4 q_first = {0u, 0u, 0u, 0u}, k_first = {0u, 0u, 0u, 0u}, v_first = {0u, 0u, 0u, 0u};
-    if (tid < q_vecs) q_first = *(const ttv_u32x4*)(q + (int64_t)node * Hq * D + (int64_t)tid * kVec);
-    int64_t dst_first = -1;
+    if (tid < q_vecs) q_first = *(const ttv_u32x4*)(q + node * Hq * D + (int64_t)tid * kVec);
     if (tid < kv_vecs) {
-        const int64_t e = (int64_t)node * cache.hkv * D + (int64_t)tid * kVec;
+        const int64_t e = node * cache.hkv * D + (int64_t)tid * kVec;
         k_first = *(const ttv_u32x4*)(k_new + e);
         v_first = *(const ttv_u32x4*)(v_new + e);
-        dst_first = cache_row(cache, b, (tid * kVec) / D, ctx + i, D);
     }
     const int pos = positions[node];
+    for (int j = tid; j <= B; j += kThreads) s_off[j] = node_offsets[j];
     if (tid < D / 2) {
         // the angle is reduced modulo 2*pi before sincos
         const double ang = (double)pos * rope.inv[tid];
@@ -360,9 +366,27 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
         s_sin[tid] = sn;
     }
     __syncthreads();
+    // owning request: the last b with node_offsets[b] <= node (offsets are
+    // non-decreasing; the checks below reject anything else)
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_off[mid] <= node) lo = mid;
+        else hi = mid - 1;
+    }
+    const int b = lo;
+    const int s = s_off[b];
+    const int n = s_off[b + 1] - s;
+    const int i = (int)(node - s);
+    const int ctx = ctx_lens[b];
+    const bool ok = s >= 0 && n >= 0 && n <= n_max && (int64_t)s + n <= total_nodes && i >= 0 &&
+                    i < n && ctx >= 0 && (cache.paged || (int64_t)ctx + n <= cache.cap);
+    if (!ok) return;  // uniform; the plan flags the request
+    int64_t dst_first = -1;
+    if (tid < kv_vecs) dst_first = cache_row(cache, b, (tid * kVec) / D, ctx + i, D);
     // Q: rotated, scaled by softmax_scale*log2(e), stored as bf16 hi + lo parts.
     for (int v = tid; v < q_vecs; v += kThreads) {
-        const int64_t e = (int64_t)node * Hq * D + (int64_t)v * kVec;
+        const int64_t e = node * Hq * D + (int64_t)v * kVec;
         const ttv_u32x4 in = v == tid ? q_first : *(const ttv_u32x4*)(q + e);
         const int d0 = (v * kVec) % D;
         ttv_u32x4 hi4, lo4;
@@ -392,7 +416,7 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
             atomicOr(err + b, TTV_ERR_BLOCK_TABLE);
             continue;
         }
-        const int64_t e = (int64_t)node * Hkv * D + (int64_t)v * kVec;
+        const int64_t e = node * Hkv * D + (int64_t)v * kVec;
         const ttv_u32x4 kin = first ? k_first : *(const ttv_u32x4*)(k_new + e);
         ttv_u32x4 ko;
 #pragma unroll
@@ -629,6 +653,9 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15;
     const int g4 = lane >> 4;
+    // The first item sits at slot blockIdx.x (see the plan), so its load
+    // does not wait for n_items.
+    const Item first_item = items[blockIdx.x];
     const int n_items = hdr->n_items;
     const int Hkv = cache.hkv;
     const int G = Hq / Hkv;
@@ -658,8 +685,8 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
     const ttv_bf16x8 kOnes = __builtin_bit_cast(
         ttv_bf16x8, ttv_u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-    for (int x = vid; x < n_items; x += active) {
-        const Item it = items[x];
+    for (int x = vid, slot = blockIdx.x; x < n_items; x += active, slot += gridDim.x) {
+        const Item it = slot == (int)blockIdx.x ? first_item : items[slot];
         const int rows = it.n * G;
         const int row_base = it.tile * kTileR + wave * kRowsPerWave;
         const int n_ctx_tiles = (it.c1 - it.c0 + kKT - 1) / kKT;
@@ -1227,12 +1254,12 @@ size_t main_lds_bytes(int G, int mask_words) {
 // ---------------------------------------------------------------------------
 
 template <int D, int kTileR>
-__global__ __launch_bounds__(kThreads) void attn_combine_kernel(
+__global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(
     const PlanHeader* __restrict__ hdr, const Combine* __restrict__ combine, int Hq, int Hkv,
     const ttv_f16x4* __restrict__ part_o, const float4* __restrict__ part_ml,
     uint16_t* __restrict__ out) {
     constexpr int kLanesPerRow = D / 4;                 // each lane: 4 consecutive d
-    constexpr int kRowsPerPass = kThreads / kLanesPerRow;
+    constexpr int kRowsPerPass = kCombThreads / kLanesPerRow;
     constexpr int kRowBlocks = kTileR / kRowsPerPass;
     const int n_work = hdr->n_combine * kRowBlocks;
     const int G = Hq / Hkv;
@@ -1243,20 +1270,35 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(
         const int d = (tid % kLanesPerRow) * 4;
         const int r = cb.tile * kTileR + r_local;
         if (r >= cb.n * G) continue;
-        // One pass with a running max; the chunk loads are independent, so the
-        // unrolled loop keeps several in flight.
+        // Chunks in batches of kCombBatch: every load of a batch is issued
+        // before any is used, so one memory latency covers the batch; the
+        // batch maximum then rescales the running sums once.  Past the last
+        // chunk the loads repeat it (in bounds, no branch) and count zero.
         float mmax = kNegBig, lsum = 0.f;
         ttv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int c = 0; c < cb.nc; ++c) {
-            const int64_t ps = cb.pslot0 + (int64_t)c * cb.stride;
-            const float4 ml = part_ml[ps * kTileR + r_local];  // m, l, scale of the fp16 o / l
-            const ttv_f32x4 v = __builtin_convertvector(part_o[((ps * kTileR + r_local) * D + d) / 4], ttv_f32x4);
-            const float m_new = fmaxf(mmax, ml.x);
+        for (int c0 = 0; c0 < cb.nc; c0 += kCombBatch) {
+            float4 ml[kCombBatch];  // m, l, scale of the fp16 o / l
+            ttv_f16x4 ov[kCombBatch];
+#pragma unroll
+            for (int j = 0; j < kCombBatch; ++j) {
+                const int c = min(c0 + j, cb.nc - 1);
+                const int64_t ps = cb.pslot0 + (int64_t)c * cb.stride;
+                ml[j] = part_ml[ps * kTileR + r_local];
+                ov[j] = part_o[((ps * kTileR + r_local) * D + d) / 4];
+            }
+            float m_new = mmax;
+#pragma unroll
+            for (int j = 0; j < kCombBatch; ++j) m_new = fmaxf(m_new, ml[j].x);
             const float a_old = __builtin_amdgcn_exp2f(mmax - m_new);
-            const float a_new = __builtin_amdgcn_exp2f(ml.x - m_new) * ml.y;
-            lsum = lsum * a_old + a_new;
-            acc = acc * a_old + v * (a_new * ml.z);
+            lsum *= a_old;
+            acc *= a_old;
+#pragma unroll
+            for (int j = 0; j < kCombBatch; ++j) {
+                const float e = __builtin_amdgcn_exp2f(ml[j].x - m_new) * ml[j].y;
+                const float a = c0 + j < cb.nc ? e : 0.f;
+                lsum += a;
+                acc += __builtin_convertvector(ov[j], ttv_f32x4) * (a * ml[j].z);
+            }
             mmax = m_new;
         }
         const float inv = 1.0f / lsum;
@@ -1332,17 +1374,18 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
     const bool small = tiles256 < num_cus();
     const int tile_m = small ? kTileMin : kTileM;
     const int target_items = small ? num_cus() : kTargetItems;
-    dim3 prep_grid(bt->n_max > 0 ? bt->n_max : 1, bt->batch + 1);
-    hipLaunchKernelGGL(attn_prep_kernel<D>, prep_grid, dim3(kThreads), 0, stream,
-                       bt->node_offsets, bt->ctx_lens, bt->batch, bt->n_max, bt->total_nodes, q,
-                       k_new, v_new, positions, cv, n_heads, rope, q_mult, q_hi, q_lo, tile_m,
-                       target_items, hdr, items,
-                       comb, L.max_items, L.max_groups, L.max_partials, err);
-    if (hipGetLastError() != hipSuccess) return TTV_EHIP;
     const int cus = num_cus();
     int64_t grid = (int64_t)cus;  // one workgroup per CU (LDS and registers bound it)
     if (grid > L.max_items) grid = ((L.max_items + kNumXcd - 1) / kNumXcd) * kNumXcd;
     grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
+    if (grid > kMaxGrid) grid = kMaxGrid;
+    dim3 prep_grid((unsigned)(1 + bt->total_nodes));
+    hipLaunchKernelGGL(attn_prep_kernel<D>, prep_grid, dim3(kThreads), 0, stream,
+                       bt->node_offsets, bt->ctx_lens, bt->batch, bt->n_max, bt->total_nodes, q,
+                       k_new, v_new, positions, cv, n_heads, rope, q_mult, q_hi, q_lo, tile_m,
+                       target_items, (int)grid, hdr, items,
+                       comb, L.max_items, L.max_groups, L.max_partials, err);
+    if (hipGetLastError() != hipSuccess) return TTV_EHIP;
     auto run_main = [&](auto waves) -> int {
         constexpr int kW = decltype(waves)::value;
         using MC = MainCfg<D, kW>;
@@ -1360,7 +1403,7 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
                            q_hi, q_lo, mask, mask_words, cv, cache->block_table, n_heads, out, po,
                            pml, err);
         if (hipGetLastError() != hipSuccess) return TTV_EHIP;
-        hipLaunchKernelGGL((attn_combine_kernel<D, MC::kTile>), dim3((unsigned)(2 * cus)), dim3(kThreads), 0,
+        hipLaunchKernelGGL((attn_combine_kernel<D, MC::kTile>), dim3((unsigned)(4 * cus)), dim3(kCombThreads), 0,
                            stream, hdr, comb, n_heads, cache->n_kv_heads, po, pml, out);
         return hipGetLastError() == hipSuccess ? TTV_OK : TTV_EHIP;
     };

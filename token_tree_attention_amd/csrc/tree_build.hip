@@ -40,6 +40,10 @@ __global__ __launch_bounds__(1024) void tree_build_kernel(
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;  // power of two, >= 64 and >= n_max
 
+    // Request 0 starts at node 0 (node_offsets[0] = 0): its parents load
+    // before the offsets arrive and are used only if the offset read is 0.
+    const bool spec = b == 0 && tid < n_max && tid < total_nodes;
+    const int par_spec = spec ? parents[tid] : -1;
     const int s = node_offsets[b];
     const int e = node_offsets[b + 1];
     const int ctx = ctx_lens[b];
@@ -56,7 +60,7 @@ __global__ __launch_bounds__(1024) void tree_build_kernel(
 
     int par = -1;
     if (tid < n) {
-        par = parents[s + tid];
+        par = (b == 0 && s == 0) ? par_spec : parents[s + tid];
         if (par < -1 || par >= tid) {
             atomicOr(&s_bad, 1);
             par = -1;  // keep every later index in range

@@ -38,6 +38,8 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(
 
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
+    // The path's first entries load with the request's lengths, not after them.
+    const int path_first = tid < max_accept ? accepted_nodes[(int64_t)b * max_accept + tid] : 0;
     const int s = node_offsets[b];
     const int n = node_offsets[b + 1] - s;
     const int ctx = ctx_lens[b];
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(
     // Validate the path (strictly increasing local ids in range) and, for a
     // paged cache, every table entry the request's tentative region uses.
     for (int d = tid; d < a; d += kCommitThreads) {
-        const int i = accepted_nodes[(int64_t)b * max_accept + d];
+        const int i = d == tid ? path_first : accepted_nodes[(int64_t)b * max_accept + d];
         s_path[d] = i;
         if (i < d || i >= n) atomicOr(&s_flags, TTV_ERR_ACCEPT);
     }
