@@ -143,20 +143,26 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
                            int64_t total_nodes, int G, int Hkv, int cap_limit, int tile_m,
                            int target_items, int grid, PlanHeader* hdr, Item* items,
                            Combine* combine, int64_t max_items, int64_t max_groups,
-                           int64_t max_partials, int32_t* err, int32_t* s_items,
-                           int32_t* s_parts) {  // s_items, s_parts: LDS, kMaxBatch + 1 each
+                           int64_t max_partials, int32_t* err, int32_t* s_off, int32_t* s_ctx,
+                           int32_t* s_items, int32_t* s_parts) {  // LDS, B + 1 ints each
     __shared__ unsigned long long s_wsum[kWaves];
     __shared__ int32_t s_wtot[2][kWaves];
     __shared__ int32_t s_ncomb;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     if (tid == 0) s_ncomb = 0;
+    // The offsets and lengths are read once, into LDS.
+    for (int j = tid; j <= B; j += kThreads) {
+        s_off[j] = node_offsets[j];
+        if (j < B) s_ctx[j] = ctx_lens[j];
+    }
+    __syncthreads();
     // Phase 1: total slot work, W = Hkv * sum over row tiles of (ctx + tree keys).
     unsigned long long my_work = 0;
     for (int b = tid; b < B; b += kThreads) {
-        const int s = node_offsets[b];
-        const int n = node_offsets[b + 1] - s;
-        const int ctx = ctx_lens[b];
+        const int s = s_off[b];
+        const int n = s_off[b + 1] - s;
+        const int ctx = s_ctx[b];
         if (s < 0 || n < 0 || n > n_max || (int64_t)s + n > total_nodes || ctx < 0) continue;
         if (cap_limit >= 0 && (int64_t)ctx + n > cap_limit) continue;
         const int rows = n * G;
@@ -191,9 +197,9 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
         const int b = base + tid;
         int ni = 0, np = 0;
         if (b < B) {
-            const int s = node_offsets[b];
-            const int n = node_offsets[b + 1] - s;
-            const int ctx = ctx_lens[b];
+            const int s = s_off[b];
+            const int n = s_off[b + 1] - s;
+            const int ctx = s_ctx[b];
             bool ok = !(s < 0 || n < 0 || n > n_max || (int64_t)s + n > total_nodes || ctx < 0);
             if (ok && cap_limit >= 0 && (int64_t)ctx + n > cap_limit) {
                 ok = false;
@@ -260,9 +266,9 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
             else hi = mid - 1;
         }
         const int b = lo;
-        const int s = node_offsets[b];
-        const int n = node_offsets[b + 1] - s;
-        const int ctx = ctx_lens[b];
+        const int s = s_off[b];
+        const int n = s_off[b + 1] - s;
+        const int ctx = s_ctx[b];
         const int nt = (n * G + tile_m - 1) / tile_m;
         const int nc = ctx > chunk_len ? (ctx + chunk_len - 1) / chunk_len : 1;
         const int local = x - s_items[b];
@@ -324,14 +330,18 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
     int64_t max_groups, int64_t max_partials, int32_t* __restrict__ err) {
     const int Hkv = cache.hkv;
     const int G = Hq / Hkv;
-    // The plan's prefix sums, or a node workgroup's copy of node_offsets.
-    __shared__ int32_t s_buf[2 * (kMaxBatch + 1)];
+    // node_offsets and ctx_lens staged in LDS (B + 1 ints each), then the
+    // plan's prefix sums (B + 1 each, plan workgroup only).
+    extern __shared__ int32_t s_dyn[];
+    int32_t* s_off = s_dyn;
+    int32_t* s_ctx = s_dyn + (B + 1);
     // Workgroup 0 builds the plan (dispatched first, so it overlaps the
     // rest); workgroup 1 + t rotates node t of the whole batch.
     if (blockIdx.x == 0) {
         build_plan(node_offsets, ctx_lens, B, n_max, total_nodes, G, Hkv,
                    cache.paged ? -1 : cache.cap, tile_m, target_items, grid, hdr, items, combine,
-                   max_items, max_groups, max_partials, err, s_buf, s_buf + kMaxBatch + 1);
+                   max_items, max_groups, max_partials, err, s_off, s_ctx, s_dyn + 2 * (B + 1),
+                   s_dyn + 3 * (B + 1));
         return;
     }
     const int64_t node = (int64_t)blockIdx.x - 1;
@@ -339,7 +349,6 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
     constexpr int kVec = 8;
     const int q_vecs = Hq * D / kVec;
     const int kv_vecs = cache.hkv * D / kVec;
-    int32_t* s_off = s_buf;
     // Rotation in fp64: with fp32, x0 cos - x1 sin loses absolute accuracy
     // when the two products nearly cancel, which shows up as several bf16
     // ulps on small results.  The work is N_b * (Hq + Hkv) * D/2 pairs.
@@ -354,7 +363,10 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
         v_first = *(const ttv_u32x4*)(v_new + e);
     }
     const int pos = positions[node];
-    for (int j = tid; j <= B; j += kThreads) s_off[j] = node_offsets[j];
+    for (int j = tid; j <= B; j += kThreads) {
+        s_off[j] = node_offsets[j];
+        if (j < B) s_ctx[j] = ctx_lens[j];
+    }
     if (tid < D / 2) {
         // the angle is reduced modulo 2*pi before sincos
         const double ang = (double)pos * rope.inv[tid];
@@ -378,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
     const int s = s_off[b];
     const int n = s_off[b + 1] - s;
     const int i = (int)(node - s);
-    const int ctx = ctx_lens[b];
+    const int ctx = s_ctx[b];
     const bool ok = s >= 0 && n >= 0 && n <= n_max && (int64_t)s + n <= total_nodes && i >= 0 &&
                     i < n && ctx >= 0 && (cache.paged || (int64_t)ctx + n <= cache.cap);
     if (!ok) return;  // uniform; the plan flags the request
@@ -1380,7 +1392,15 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
     grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
     if (grid > kMaxGrid) grid = kMaxGrid;
     dim3 prep_grid((unsigned)(1 + bt->total_nodes));
-    hipLaunchKernelGGL(attn_prep_kernel<D>, prep_grid, dim3(kThreads), 0, stream,
+    const size_t prep_lds = (size_t)4 * (bt->batch + 1) * sizeof(int32_t);
+    static bool prep_attr_set = false;
+    if (!prep_attr_set) {
+        if (hipFuncSetAttribute((const void*)attn_prep_kernel<D>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024) != hipSuccess)
+            return TTV_EHIP;
+        prep_attr_set = true;
+    }
+    hipLaunchKernelGGL(attn_prep_kernel<D>, prep_grid, dim3(kThreads), prep_lds, stream,
                        bt->node_offsets, bt->ctx_lens, bt->batch, bt->n_max, bt->total_nodes, q,
                        k_new, v_new, positions, cv, n_heads, rope, q_mult, q_hi, q_lo, tile_m,
                        target_items, (int)grid, hdr, items,
