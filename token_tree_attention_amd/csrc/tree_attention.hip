@@ -700,7 +700,6 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
     for (int x = vid, slot = blockIdx.x; x < n_items; x += active, slot += gridDim.x) {
         const Item it = slot == (int)blockIdx.x ? first_item : items[slot];
         const int rows = it.n * G;
-        const int row_base = it.tile * kTileR + wave * kRowsPerWave;
         const int n_ctx_tiles = (it.c1 - it.c0 + kKT - 1) / kKT;
         const int n_tree_tiles = (it.kmax + kKT - 1) / kKT;
         const int n_tiles = n_ctx_tiles + n_tree_tiles;
@@ -783,7 +782,7 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         int row_node[kMB];
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) {
-            const int r = row_base + 16 * mb + l16;
+            const int r = it.tile * kTileR + 16 * (mb * kW + wave) + l16;
             const bool ok = r < rows;
             const int rc = min(r, rows - 1);  // rows past the tile end reuse its last row
             const int node = rc / G, g = rc % G;
@@ -820,434 +819,452 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         for (int j = 2; j < ahead && j < n_tiles; ++j) issue(j, blocks_of(j));
         if (kPaged && ahead < n_tiles) next_blocks = blocks_of(ahead);
 
-        ttv_f32x4 o[DB][kMB], lacc[kMB];
+        // Rows map to waves by 16-row block: rows 16 j .. 16 j + 15 of the
+        // tile belong to wave j % kW as its block mb = j / kW.  A tile with
+        // at most 16 kW rows then needs one block per wave, and the waves
+        // run only NMB blocks (NMB = 0 for a wave without rows).
+        auto body = [&](auto nmb_c) __attribute__((always_inline)) {
+            constexpr int NMB = decltype(nmb_c)::value;
+            ttv_f32x4 o[DB][kMB], lacc[kMB];
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
+            for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
-            for (int db = 0; db < DB; ++db) o[db][mb] = ttv_f32x4{0.f, 0.f, 0.f, 0.f};
-            lacc[mb] = ttv_f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        float m_run[kMB];
+                for (int db = 0; db < DB; ++db) o[db][mb] = ttv_f32x4{0.f, 0.f, 0.f, 0.f};
+                lacc[mb] = ttv_f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            float m_run[kMB];
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) m_run[mb] = kNegBig;
+            for (int mb = 0; mb < NMB; ++mb) m_run[mb] = kNegBig;
 
-        // S^T[key][row] of tile tau: keys 16kb + 4g4 + r, rows 16mb + l16.
-        auto scores = [&](auto cls, int tau, ttv_f32x4 (&S)[2][kMB]) __attribute__((always_inline)) {
-            constexpr bool kPrecise = decltype(cls)::value == kClassPrecise;
-            const char* kst = smem + (tau & smask) * MC::kStageBytes;
+            // S^T[key][row] of tile tau: keys 16kb + 4g4 + r, rows 16mb + l16.
+            auto scores = [&](auto cls, int tau, ttv_f32x4 (&S)[2][kMB]) __attribute__((always_inline)) {
+                constexpr bool kPrecise = decltype(cls)::value == kClassPrecise;
+                const char* kst = smem + (tau & smask) * MC::kStageBytes;
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                ttv_bf16x8 qlo[kMB];
-                if (kPrecise) {
+                for (int kc = 0; kc < KC; ++kc) {
+                    ttv_bf16x8 qlo[kMB];
+                    if (kPrecise) {
 #pragma unroll
-                    for (int mb = 0; mb < kMB; ++mb) {
-                        const int rl = wave * kRowsPerWave + 16 * mb + l16;
-                        qlo[mb] = *(const ttv_bf16x8*)(smem + (qlo_s - ring) + rl * MC::kRowBytes +
-                                                       16 * swz_k(rl, 4 * kc + g4, P));
+                        for (int mb = 0; mb < NMB; ++mb) {
+                            const int rl = 16 * (mb * kW + wave) + l16;
+                            qlo[mb] = *(const ttv_bf16x8*)(smem + (qlo_s - ring) + rl * MC::kRowBytes +
+                                                           16 * swz_k(rl, 4 * kc + g4, P));
+                        }
+                    }
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        const ttv_bf16x8 a = *(const ttv_bf16x8*)(kst + koff[kc] + kb * 16 * MC::kRowBytes);
+#pragma unroll
+                        for (int mb = 0; mb < NMB; ++mb) {
+                            S[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                a, qreg[mb][kc], kc == 0 ? ttv_f32x4{0.f, 0.f, 0.f, 0.f} : S[kb][mb], 0, 0, 0);
+                            if (kPrecise)
+                                S[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[mb], S[kb][mb], 0, 0, 0);
+                        }
                     }
                 }
+            };
+
+            // Keys a row may not see become -inf: slots past the tile's valid
+            // count and, on tree tiles, keys that are not the row node's
+            // ancestors (or the node itself).  Branch-free.
+            auto mask_scores = [&](int tau, ttv_f32x4 (&S)[2][kMB]) __attribute__((always_inline)) {
+                const int valid = tile_valid(tau, tile_slot0(tau));
+                const bool tree = tau >= n_ctx_tiles;
+                const uint32_t vbits = valid >= 32 ? 0xFFFFFFFFu : ((1u << valid) - 1u);
+                const int word = tree ? tau - n_ctx_tiles : 0;
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const ttv_bf16x8 a = *(const ttv_bf16x8*)(kst + koff[kc] + kb * 16 * MC::kRowBytes);
+                for (int mb = 0; mb < NMB; ++mb) {
+                    const int nl = row_node[mb];
+                    const uint32_t mw = mask_s[max(nl, 0) * mask_words + word];
+                    const uint32_t w = (vbits & (tree ? (nl >= 0 ? mw : 0u) : 0xFFFFFFFFu)) >> (4 * g4);
 #pragma unroll
-                    for (int mb = 0; mb < kMB; ++mb) {
-                        S[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            a, qreg[mb][kc], kc == 0 ? ttv_f32x4{0.f, 0.f, 0.f, 0.f} : S[kb][mb], 0, 0, 0);
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            S[kb][mb][r] = ((w >> (16 * kb + r)) & 1u) ? S[kb][mb][r] : -INFINITY;
+                }
+            };
+
+            // This lane's part of each row maximum (the other three parts sit in
+            // lanes l ^ 16, l ^ 32, l ^ 48).
+            auto row_max = [&](const ttv_f32x4 (&S)[2][kMB], float (&tmax)[kMB]) __attribute__((always_inline)) {
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb) {
+                    const float t0 = __builtin_fmaxf(__builtin_fmaxf(S[0][mb][0], S[0][mb][1]),
+                                                     __builtin_fmaxf(S[0][mb][2], S[0][mb][3]));
+                    const float t1 = __builtin_fmaxf(__builtin_fmaxf(S[1][mb][0], S[1][mb][1]),
+                                                     __builtin_fmaxf(S[1][mb][2], S[1][mb][3]));
+                    tmax[mb] = __builtin_fmaxf(t0, t1);
+                }
+            };
+
+            // Lazy rescale: the running max moves only when some row of the wave
+            // outgrew it by more than 2^kLazyRescale (p stays below that
+            // meanwhile); rare after the first tile.  Plain tiles carry shifted
+            // scores s - m (the score MFMAs start from -m), the others raw ones.
+            auto rescale_if_needed = [&](auto cls, ttv_f32x4 (&S)[2][kMB],
+                                         const float (&tmax)[kMB]) __attribute__((always_inline)) {
+                constexpr bool kShifted = decltype(cls)::value == kClassPlain;
+                bool need = false;
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb) need |= tmax[mb] > (kShifted ? kLazyRescale : m_run[mb] + kLazyRescale);
+                if (__builtin_expect(__ballot(need) != 0, 0)) {
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb) {
+                        float alpha;
+                        if (kShifted) {
+                            const float sh = __builtin_fmaxf(group_max(tmax[mb]), 0.f);
+                            m_run[mb] += sh;
+                            alpha = __builtin_amdgcn_exp2f(-sh);
+#pragma unroll
+                            for (int kb = 0; kb < 2; ++kb) S[kb][mb] -= sh;
+                        } else {
+                            const float m_new = __builtin_fmaxf(m_run[mb], group_max(tmax[mb]));
+                            alpha = __builtin_amdgcn_exp2f(m_run[mb] - m_new);
+                            m_run[mb] = m_new;
+                        }
+                        scale_in_place(lacc[mb], alpha);
+#pragma unroll
+                        for (int db = 0; db < DB; ++db) scale_in_place(o[db][mb], alpha);
+                    }
+                }
+            };
+
+            // p = 2^(s - m) as bf16 (plus, when precise, the bf16 of what the
+            // rounding dropped).
+            auto exp_pack = [&](auto cls, const ttv_f32x4 (&S)[2][kMB], ttv_bf16x8 (&pb)[kMB],
+                                ttv_bf16x8 (&pl)[kMB]) __attribute__((always_inline)) {
+                constexpr bool kPrecise = decltype(cls)::value == kClassPrecise;
+                constexpr bool kShifted = decltype(cls)::value == kClassPlain;
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb) {
+                    float p[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        p[e] = __builtin_amdgcn_exp2f(kShifted ? S[e >> 2][mb][e & 3] : S[e >> 2][mb][e & 3] - m_run[mb]);
+                    uint32_t packed[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) packed[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
+                    pb[mb] = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{packed[0], packed[1], packed[2], packed[3]});
+                    if (kPrecise) {
+                        uint32_t lo[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            lo[e] = pack_bf16(p[2 * e] - ttv_bf16_lo(packed[e]), p[2 * e + 1] - ttv_bf16_hi(packed[e]));
+                        pl[mb] = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{lo[0], lo[1], lo[2], lo[3]});
+                    }
+                }
+            };
+
+            // O^T[d][row] += V^T[d][key] P^T[key][row] and l += 1^T P^T (an MFMA
+            // against a ones operand, so l sums the same bf16 P that multiplies
+            // V).  MFMA k index 8g4 + j is key 4g4 + j (j < 4) or 16 + 4g4 + j - 4
+            // (j >= 4); each half comes from one ds_read_b64_tr_b16 over rows
+            // 16h + 4g4 .. +3.
+            auto load_vt = [&](int tau, int db) __attribute__((always_inline)) {
+                const uint32_t vst = ring + (tau & smask) * MC::kStageBytes + MC::kTileBytes;
+                ttv_i16x4 half[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4*)(uintptr_t)(vst + voff[db] + h * 16 * MC::kRowBytes));
+                return __builtin_bit_cast(ttv_bf16x8,
+                                          __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            };
+            auto pv_half = [&](auto cls, int half, const ttv_bf16x8 (&va)[DB], const ttv_bf16x8 (&pb)[kMB],
+                               const ttv_bf16x8 (&pl)[kMB]) __attribute__((always_inline)) {
+                constexpr bool kPrecise = decltype(cls)::value == kClassPrecise;
+#pragma unroll
+                for (int db = half * DB / 2; db < (half + 1) * DB / 2; ++db)
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb) {
+                        o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pb[mb], o[db][mb], 0, 0, 0);
                         if (kPrecise)
-                            S[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[mb], S[kb][mb], 0, 0, 0);
+                            o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pl[mb], o[db][mb], 0, 0, 0);
+                    }
+                if (half == 1) {
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb) {
+                        lacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pb[mb], lacc[mb], 0, 0, 0);
+                        if (kPrecise)
+                            lacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pl[mb], lacc[mb], 0, 0, 0);
                     }
                 }
-            }
-        };
-
-        // Keys a row may not see become -inf: slots past the tile's valid
-        // count and, on tree tiles, keys that are not the row node's
-        // ancestors (or the node itself).  Branch-free.
-        auto mask_scores = [&](int tau, ttv_f32x4 (&S)[2][kMB]) __attribute__((always_inline)) {
-            const int valid = tile_valid(tau, tile_slot0(tau));
-            const bool tree = tau >= n_ctx_tiles;
-            const uint32_t vbits = valid >= 32 ? 0xFFFFFFFFu : ((1u << valid) - 1u);
-            const int word = tree ? tau - n_ctx_tiles : 0;
+            };
+            auto pv_mfma = [&](auto cls, const ttv_bf16x8 (&va)[DB], const ttv_bf16x8 (&pb)[kMB],
+                               const ttv_bf16x8 (&pl)[kMB]) __attribute__((always_inline)) {
+                constexpr bool kPrecise = decltype(cls)::value == kClassPrecise;
 #pragma unroll
-            for (int mb = 0; mb < kMB; ++mb) {
-                const int nl = row_node[mb];
-                const uint32_t mw = mask_s[max(nl, 0) * mask_words + word];
-                const uint32_t w = (vbits & (tree ? (nl >= 0 ? mw : 0u) : 0xFFFFFFFFu)) >> (4 * g4);
+                for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        S[kb][mb][r] = ((w >> (16 * kb + r)) & 1u) ? S[kb][mb][r] : -INFINITY;
-            }
-        };
-
-        // This lane's part of each row maximum (the other three parts sit in
-        // lanes l ^ 16, l ^ 32, l ^ 48).
-        auto row_max = [&](const ttv_f32x4 (&S)[2][kMB], float (&tmax)[kMB]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int mb = 0; mb < kMB; ++mb) {
-                const float t0 = __builtin_fmaxf(__builtin_fmaxf(S[0][mb][0], S[0][mb][1]),
-                                                 __builtin_fmaxf(S[0][mb][2], S[0][mb][3]));
-                const float t1 = __builtin_fmaxf(__builtin_fmaxf(S[1][mb][0], S[1][mb][1]),
-                                                 __builtin_fmaxf(S[1][mb][2], S[1][mb][3]));
-                tmax[mb] = __builtin_fmaxf(t0, t1);
-            }
-        };
-
-        // Lazy rescale: the running max moves only when some row of the wave
-        // outgrew it by more than 2^kLazyRescale (p stays below that
-        // meanwhile); rare after the first tile.  Plain tiles carry shifted
-        // scores s - m (the score MFMAs start from -m), the others raw ones.
-        auto rescale_if_needed = [&](auto cls, ttv_f32x4 (&S)[2][kMB],
-                                     const float (&tmax)[kMB]) __attribute__((always_inline)) {
-            constexpr bool kShifted = decltype(cls)::value == kClassPlain;
-            bool need = false;
-#pragma unroll
-            for (int mb = 0; mb < kMB; ++mb) need |= tmax[mb] > (kShifted ? kLazyRescale : m_run[mb] + kLazyRescale);
-            if (__builtin_expect(__ballot(need) != 0, 0)) {
-#pragma unroll
-                for (int mb = 0; mb < kMB; ++mb) {
-                    float alpha;
-                    if (kShifted) {
-                        const float sh = __builtin_fmaxf(group_max(tmax[mb]), 0.f);
-                        m_run[mb] += sh;
-                        alpha = __builtin_amdgcn_exp2f(-sh);
-#pragma unroll
-                        for (int kb = 0; kb < 2; ++kb) S[kb][mb] -= sh;
-                    } else {
-                        const float m_new = __builtin_fmaxf(m_run[mb], group_max(tmax[mb]));
-                        alpha = __builtin_amdgcn_exp2f(m_run[mb] - m_new);
-                        m_run[mb] = m_new;
+                    for (int mb = 0; mb < NMB; ++mb) {
+                        o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pb[mb], o[db][mb], 0, 0, 0);
+                        if (kPrecise)
+                            o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pl[mb], o[db][mb], 0, 0, 0);
                     }
-                    scale_in_place(lacc[mb], alpha);
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) scale_in_place(o[db][mb], alpha);
-                }
-            }
-        };
-
-        // p = 2^(s - m) as bf16 (plus, when precise, the bf16 of what the
-        // rounding dropped).
-        auto exp_pack = [&](auto cls, const ttv_f32x4 (&S)[2][kMB], ttv_bf16x8 (&pb)[kMB],
-                            ttv_bf16x8 (&pl)[kMB]) __attribute__((always_inline)) {
-            constexpr bool kPrecise = decltype(cls)::value == kClassPrecise;
-            constexpr bool kShifted = decltype(cls)::value == kClassPlain;
-#pragma unroll
-            for (int mb = 0; mb < kMB; ++mb) {
-                float p[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    p[e] = __builtin_amdgcn_exp2f(kShifted ? S[e >> 2][mb][e & 3] : S[e >> 2][mb][e & 3] - m_run[mb]);
-                uint32_t packed[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) packed[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
-                pb[mb] = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{packed[0], packed[1], packed[2], packed[3]});
-                if (kPrecise) {
-                    uint32_t lo[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        lo[e] = pack_bf16(p[2 * e] - ttv_bf16_lo(packed[e]), p[2 * e + 1] - ttv_bf16_hi(packed[e]));
-                    pl[mb] = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{lo[0], lo[1], lo[2], lo[3]});
-                }
-            }
-        };
-
-        // O^T[d][row] += V^T[d][key] P^T[key][row] and l += 1^T P^T (an MFMA
-        // against a ones operand, so l sums the same bf16 P that multiplies
-        // V).  MFMA k index 8g4 + j is key 4g4 + j (j < 4) or 16 + 4g4 + j - 4
-        // (j >= 4); each half comes from one ds_read_b64_tr_b16 over rows
-        // 16h + 4g4 .. +3.
-        auto load_vt = [&](int tau, int db) __attribute__((always_inline)) {
-            const uint32_t vst = ring + (tau & smask) * MC::kStageBytes + MC::kTileBytes;
-            ttv_i16x4 half[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4*)(uintptr_t)(vst + voff[db] + h * 16 * MC::kRowBytes));
-            return __builtin_bit_cast(ttv_bf16x8,
-                                      __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        };
-        auto pv_half = [&](auto cls, int half, const ttv_bf16x8 (&va)[DB], const ttv_bf16x8 (&pb)[kMB],
-                           const ttv_bf16x8 (&pl)[kMB]) __attribute__((always_inline)) {
-            constexpr bool kPrecise = decltype(cls)::value == kClassPrecise;
-#pragma unroll
-            for (int db = half * DB / 2; db < (half + 1) * DB / 2; ++db)
-#pragma unroll
-                for (int mb = 0; mb < kMB; ++mb) {
-                    o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pb[mb], o[db][mb], 0, 0, 0);
-                    if (kPrecise)
-                        o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pl[mb], o[db][mb], 0, 0, 0);
-                }
-            if (half == 1) {
-#pragma unroll
-                for (int mb = 0; mb < kMB; ++mb) {
+                for (int mb = 0; mb < NMB; ++mb) {
                     lacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pb[mb], lacc[mb], 0, 0, 0);
                     if (kPrecise)
                         lacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pl[mb], lacc[mb], 0, 0, 0);
                 }
-            }
-        };
-        auto pv_mfma = [&](auto cls, const ttv_bf16x8 (&va)[DB], const ttv_bf16x8 (&pb)[kMB],
-                           const ttv_bf16x8 (&pl)[kMB]) __attribute__((always_inline)) {
-            constexpr bool kPrecise = decltype(cls)::value == kClassPrecise;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int mb = 0; mb < kMB; ++mb) {
-                    o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pb[mb], o[db][mb], 0, 0, 0);
-                    if (kPrecise)
-                        o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pl[mb], o[db][mb], 0, 0, 0);
-                }
-#pragma unroll
-            for (int mb = 0; mb < kMB; ++mb) {
-                lacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pb[mb], lacc[mb], 0, 0, 0);
-                if (kPrecise)
-                    lacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes, pl[mb], lacc[mb], 0, 0, 0);
-            }
-        };
+            };
 
-        // Before the scores of tile tau + 1: this wave's loads of that tile
-        // have landed (the later ones up to tile tau + ahead - 1 may stay in
-        // flight) and a barrier publishes them; the barrier also retires
-        // stage (tau - 1) % stages, which the load of tile tau + ahead then
-        // reuses.
-        auto advance = [&](auto cls, int tau) __attribute__((always_inline)) {
-            constexpr int kA = (decltype(cls)::value == kClassPrecise ? MC::kStagesShort : MC::kStagesLong) - 1;
-            if (tau + kA < n_tiles) {  // steady state: kA - 2 later tiles stay in flight
-                if (MC::kChunks >= kW || wave < MC::kChunks) wait_vmcnt<MC::kOpsPerTile * (kA - 2)>();
-                raw_barrier();
-                if (tau + kA < n_plain) issue_whole(tau + kA, next_blocks);
-                else issue(tau + kA, next_blocks);
-            } else {
-                if (MC::kChunks >= kW || wave < MC::kChunks)
-                    wait_vmcnt_tiles<MC::kOpsPerTile>(min(kA - 2, n_tiles - 2 - tau));
-                raw_barrier();
-            }
-        };
-
-        // Software pipeline: iteration tau computes the scores of tile tau + 1
-        // while it runs the softmax and P.V of tile tau, so the MFMAs of one
-        // overlap the VALU work of the other.
-        ttv_f32x4 S[2][kMB], S_next[2][kMB];
-        float tmax[kMB];
-        ttv_bf16x8 pb[kMB], pl[kMB];
-        constexpr std::integral_constant<int, kClassPlain> cPlain{};
-        constexpr std::integral_constant<int, kClassMasked> cMasked{};
-        constexpr std::integral_constant<int, kClassPrecise> cPrecise{};
-        auto first = [&](auto cls) __attribute__((always_inline)) {
-            scores(cls, 0, S);
-            if (decltype(cls)::value != kClassPlain) mask_scores(0, S);
-            row_max(S, tmax);
-            if (decltype(cls)::value == kClassPlain) {
-                // whole tile, every key visible: start the running max at the
-                // tile's row max and shift the scores by it
-#pragma unroll
-                for (int mb = 0; mb < kMB; ++mb) {
-                    m_run[mb] = group_max(tmax[mb]);
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) S[kb][mb] -= m_run[mb];
-                    tmax[mb] -= m_run[mb];
-                }
-            }
-        };
-        // One pipelined iteration: scores of tile tau + 1 (S_nxt), softmax
-        // and P.V of tile tau (S_cur).  The work is cut into phases that the
-        // scheduler may not mix (sched_barrier): each phase pairs one k-chunk
-        // of score MFMAs with a quarter of the exponentials, and the LDS
-        // reads of the next phase are issued one phase ahead; the last phase
-        // runs the P.V MFMAs next to the mask and row maxima of tile tau + 1.
-        auto iteration = [&](auto cur, auto next, int tau, ttv_f32x4 (&S_cur)[2][kMB],
-                             ttv_f32x4 (&S_nxt)[2][kMB]) __attribute__((always_inline)) {
-            constexpr bool kCurPrecise = decltype(cur)::value == kClassPrecise;
-            constexpr bool kNextPrecise = decltype(next)::value == kClassPrecise;
-            constexpr bool kNextMasked = decltype(next)::value != kClassPlain;
-            constexpr bool kCurShifted = decltype(cur)::value == kClassPlain;
-            rescale_if_needed(cur, S_cur, tmax);
-            advance(cur, tau);
-            const char* kst = smem + ((tau + 1) & smask) * MC::kStageBytes;
-            ttv_bf16x8 ka[KC][2], qlo[KC][kMB], va[DB];
-            // plain scores start from -m (shifted), the others from 0
-            ttv_f32x4 s_init[kMB];
-#pragma unroll
-            for (int mb = 0; mb < kMB; ++mb) {
-                const float z = kNextMasked ? 0.f : -m_run[mb];
-                s_init[mb] = ttv_f32x4{z, z, z, z};
-            }
-            auto load_k = [&](int kc) __attribute__((always_inline)) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-                    ka[kc][kb] = *(const ttv_bf16x8*)(kst + koff[kc] + kb * 16 * MC::kRowBytes);
-                if (kNextPrecise) {
-#pragma unroll
-                    for (int mb = 0; mb < kMB; ++mb) {
-                        const int rl = wave * kRowsPerWave + 16 * mb + l16;
-                        qlo[kc][mb] = *(const ttv_bf16x8*)(smem + (qlo_s - ring) + rl * MC::kRowBytes +
-                                                           16 * swz_k(rl, 4 * kc + g4, P));
-                    }
-                }
-            };
-            auto qk = [&](int kc) __attribute__((always_inline)) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int mb = 0; mb < kMB; ++mb) {
-                        S_nxt[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            ka[kc][kb], qreg[mb][kc], kc == 0 ? s_init[mb] : S_nxt[kb][mb], 0, 0, 0);
-                        if (kNextPrecise)
-                            S_nxt[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kc][kb], qlo[kc][mb],
-                                                                                    S_nxt[kb][mb], 0, 0, 0);
-                    }
-            };
-            float p[kMB][8];
-            uint32_t packed[kMB][4];
-            auto ex = [&](int mb, int half) __attribute__((always_inline)) {
-#pragma unroll
-                for (int e = 4 * half; e < 4 * half + 4; ++e)
-                    p[mb][e] = __builtin_amdgcn_exp2f(kCurShifted ? S_cur[e >> 2][mb][e & 3]
-                                                                  : S_cur[e >> 2][mb][e & 3] - m_run[mb]);
-#pragma unroll
-                for (int e = 2 * half; e < 2 * half + 2; ++e)
-                    packed[mb][e] = pack_bf16(p[mb][2 * e], p[mb][2 * e + 1]);
-            };
-            auto phase = [] { __builtin_amdgcn_sched_barrier(0); };
-            // Phases for D = 128 (KC = 4); with D = 64 the last two carry no
-            // score MFMAs.
-            static_assert(KC == 2 || KC == 4, "head_dim 64 or 128");
-            load_k(0);
-            load_k(1);
-#pragma unroll
-            for (int db = 0; db < DB / 2; ++db) va[db] = load_vt(tau, db);
-            phase();
-            qk(0);
-            ex(0, 0);
-            if (KC > 2) load_k(2);
-            phase();
-            qk(1);
-            ex(0, 1);
-            if (KC > 2) load_k(3);
-            phase();
-            if (KC > 2) qk(2);
-            ex(1, 0);
-            phase();
-            if (KC > 2) qk(3);
-            ex(1, 1);
-#pragma unroll
-            for (int mb = 0; mb < kMB; ++mb) {
-                pb[mb] = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{packed[mb][0], packed[mb][1], packed[mb][2],
-                                                                  packed[mb][3]});
-                if (kCurPrecise) {
-                    uint32_t lo[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        lo[e] = pack_bf16(p[mb][2 * e] - ttv_bf16_lo(packed[mb][e]),
-                                          p[mb][2 * e + 1] - ttv_bf16_hi(packed[mb][e]));
-                    pl[mb] = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{lo[0], lo[1], lo[2], lo[3]});
-                }
-            }
-            phase();
-            // P.V in two halves; the V^T operands of the second half load
-            // while the first half runs.
-            pv_half(cur, 0, va, pb, pl);
-#pragma unroll
-            for (int db = DB / 2; db < DB; ++db) va[db] = load_vt(tau, db);
-            phase();
-            pv_half(cur, 1, va, pb, pl);
-            if (kNextMasked) mask_scores(tau + 1, S_nxt);
-            row_max(S_nxt, tmax);
-            phase();
-            // A paged cache's block numbers for the tile the next iteration
-            // loads: read now, so the scalar loads return during its barrier.
-            constexpr int kA = (decltype(cur)::value == kClassPrecise ? MC::kStagesShort : MC::kStagesLong) - 1;
-            if (kPaged && tau + kA + 1 < n_tiles) next_blocks = blocks_of(tau + kA + 1);
-        };
-        auto copy_scores = [&](ttv_f32x4 (&dst)[2][kMB], const ttv_f32x4 (&src)[2][kMB]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int mb = 0; mb < kMB; ++mb) dst[kb][mb] = src[kb][mb];
-        };
-        auto last = [&](auto cur, int tau) __attribute__((always_inline)) {
-            rescale_if_needed(cur, S, tmax);
-            exp_pack(cur, S, pb, pl);
-            ttv_bf16x8 va[DB];
-#pragma unroll
-            for (int db = 0; db < DB; ++db) va[db] = load_vt(tau, db);
-            pv_mfma(cur, va, pb, pl);
-        };
-        // Runs tiles [tau, end) of one class; the tile after them (if any) is
-        // of class `after`.  Two iterations per trip, so the two score sets
-        // swap roles without copies.
-        auto run = [&](auto cls, auto after, int& tau, int end) __attribute__((always_inline)) {
-            for (; tau + 2 < end; tau += 2) {
-                iteration(cls, cls, tau, S, S_next);
-                iteration(cls, cls, tau + 1, S_next, S);
-            }
-            if (tau + 1 < end) {
-                iteration(cls, cls, tau, S, S_next);
-                copy_scores(S, S_next);
-                ++tau;
-            }
-            if (tau < end) {
-                if (tau + 1 < n_tiles) {
-                    iteration(cls, after, tau, S, S_next);
-                    copy_scores(S, S_next);
+            // Before the scores of tile tau + 1: this wave's loads of that tile
+            // have landed (the later ones up to tile tau + ahead - 1 may stay in
+            // flight) and a barrier publishes them; the barrier also retires
+            // stage (tau - 1) % stages, which the load of tile tau + ahead then
+            // reuses.
+            auto advance = [&](auto cls, int tau) __attribute__((always_inline)) {
+                constexpr int kA = (decltype(cls)::value == kClassPrecise ? MC::kStagesShort : MC::kStagesLong) - 1;
+                if (tau + kA < n_tiles) {  // steady state: kA - 2 later tiles stay in flight
+                    if (MC::kChunks >= kW || wave < MC::kChunks) wait_vmcnt<MC::kOpsPerTile * (kA - 2)>();
+                    raw_barrier();
+                    if (tau + kA < n_plain) issue_whole(tau + kA, next_blocks);
+                    else issue(tau + kA, next_blocks);
                 } else {
-                    last(cls, tau);
+                    if (MC::kChunks >= kW || wave < MC::kChunks)
+                        wait_vmcnt_tiles<MC::kOpsPerTile>(min(kA - 2, n_tiles - 2 - tau));
+                    raw_barrier();
                 }
-                ++tau;
+            };
+
+            // Software pipeline: iteration tau computes the scores of tile tau + 1
+            // while it runs the softmax and P.V of tile tau, so the MFMAs of one
+            // overlap the VALU work of the other.
+            ttv_f32x4 S[2][kMB], S_next[2][kMB];
+            float tmax[kMB];
+            ttv_bf16x8 pb[kMB], pl[kMB];
+            constexpr std::integral_constant<int, kClassPlain> cPlain{};
+            constexpr std::integral_constant<int, kClassMasked> cMasked{};
+            constexpr std::integral_constant<int, kClassPrecise> cPrecise{};
+            auto first = [&](auto cls) __attribute__((always_inline)) {
+                scores(cls, 0, S);
+                if (decltype(cls)::value != kClassPlain) mask_scores(0, S);
+                row_max(S, tmax);
+                if (decltype(cls)::value == kClassPlain) {
+                    // whole tile, every key visible: start the running max at the
+                    // tile's row max and shift the scores by it
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb) {
+                        m_run[mb] = group_max(tmax[mb]);
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) S[kb][mb] -= m_run[mb];
+                        tmax[mb] -= m_run[mb];
+                    }
+                }
+            };
+            // One pipelined iteration: scores of tile tau + 1 (S_nxt), softmax
+            // and P.V of tile tau (S_cur).  The work is cut into phases that the
+            // scheduler may not mix (sched_barrier): each phase pairs one k-chunk
+            // of score MFMAs with a quarter of the exponentials, and the LDS
+            // reads of the next phase are issued one phase ahead; the last phase
+            // runs the P.V MFMAs next to the mask and row maxima of tile tau + 1.
+            auto iteration = [&](auto cur, auto next, int tau, ttv_f32x4 (&S_cur)[2][kMB],
+                                 ttv_f32x4 (&S_nxt)[2][kMB]) __attribute__((always_inline)) {
+                constexpr bool kCurPrecise = decltype(cur)::value == kClassPrecise;
+                constexpr bool kNextPrecise = decltype(next)::value == kClassPrecise;
+                constexpr bool kNextMasked = decltype(next)::value != kClassPlain;
+                constexpr bool kCurShifted = decltype(cur)::value == kClassPlain;
+                rescale_if_needed(cur, S_cur, tmax);
+                advance(cur, tau);
+                const char* kst = smem + ((tau + 1) & smask) * MC::kStageBytes;
+                ttv_bf16x8 ka[KC][2], qlo[KC][kMB], va[DB];
+                // plain scores start from -m (shifted), the others from 0
+                ttv_f32x4 s_init[kMB];
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb) {
+                    const float z = kNextMasked ? 0.f : -m_run[mb];
+                    s_init[mb] = ttv_f32x4{z, z, z, z};
+                }
+                auto load_k = [&](int kc) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+                        ka[kc][kb] = *(const ttv_bf16x8*)(kst + koff[kc] + kb * 16 * MC::kRowBytes);
+                    if (kNextPrecise) {
+#pragma unroll
+                        for (int mb = 0; mb < NMB; ++mb) {
+                            const int rl = 16 * (mb * kW + wave) + l16;
+                            qlo[kc][mb] = *(const ttv_bf16x8*)(smem + (qlo_s - ring) + rl * MC::kRowBytes +
+                                                               16 * swz_k(rl, 4 * kc + g4, P));
+                        }
+                    }
+                };
+                auto qk = [&](int kc) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int mb = 0; mb < NMB; ++mb) {
+                            S_nxt[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                ka[kc][kb], qreg[mb][kc], kc == 0 ? s_init[mb] : S_nxt[kb][mb], 0, 0, 0);
+                            if (kNextPrecise)
+                                S_nxt[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kc][kb], qlo[kc][mb],
+                                                                                        S_nxt[kb][mb], 0, 0, 0);
+                        }
+                };
+                float p[kMB][8];
+                uint32_t packed[kMB][4];
+                auto ex = [&](int mb, int half) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int e = 4 * half; e < 4 * half + 4; ++e)
+                        p[mb][e] = __builtin_amdgcn_exp2f(kCurShifted ? S_cur[e >> 2][mb][e & 3]
+                                                                      : S_cur[e >> 2][mb][e & 3] - m_run[mb]);
+#pragma unroll
+                    for (int e = 2 * half; e < 2 * half + 2; ++e)
+                        packed[mb][e] = pack_bf16(p[mb][2 * e], p[mb][2 * e + 1]);
+                };
+                auto phase = [] { __builtin_amdgcn_sched_barrier(0); };
+                // Phases for D = 128 (KC = 4); with D = 64 the last two carry no
+                // score MFMAs.
+                static_assert(KC == 2 || KC == 4, "head_dim 64 or 128");
+                load_k(0);
+                load_k(1);
+#pragma unroll
+                for (int db = 0; db < DB / 2; ++db) va[db] = load_vt(tau, db);
+                phase();
+                qk(0);
+                if (NMB > 0) ex(0, 0);
+                if (KC > 2) load_k(2);
+                phase();
+                qk(1);
+                if (NMB > 0) ex(0, 1);
+                if (KC > 2) load_k(3);
+                phase();
+                if (KC > 2) qk(2);
+                if (NMB > 1) ex(1, 0);
+                phase();
+                if (KC > 2) qk(3);
+                if (NMB > 1) ex(1, 1);
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb) {
+                    pb[mb] = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{packed[mb][0], packed[mb][1], packed[mb][2],
+                                                                      packed[mb][3]});
+                    if (kCurPrecise) {
+                        uint32_t lo[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            lo[e] = pack_bf16(p[mb][2 * e] - ttv_bf16_lo(packed[mb][e]),
+                                              p[mb][2 * e + 1] - ttv_bf16_hi(packed[mb][e]));
+                        pl[mb] = __builtin_bit_cast(ttv_bf16x8, ttv_u32x4{lo[0], lo[1], lo[2], lo[3]});
+                    }
+                }
+                phase();
+                // P.V in two halves; the V^T operands of the second half load
+                // while the first half runs.
+                pv_half(cur, 0, va, pb, pl);
+#pragma unroll
+                for (int db = DB / 2; db < DB; ++db) va[db] = load_vt(tau, db);
+                phase();
+                pv_half(cur, 1, va, pb, pl);
+                if (kNextMasked) mask_scores(tau + 1, S_nxt);
+                row_max(S_nxt, tmax);
+                phase();
+                // A paged cache's block numbers for the tile the next iteration
+                // loads: read now, so the scalar loads return during its barrier.
+                constexpr int kA = (decltype(cur)::value == kClassPrecise ? MC::kStagesShort : MC::kStagesLong) - 1;
+                if (kPaged && tau + kA + 1 < n_tiles) next_blocks = blocks_of(tau + kA + 1);
+            };
+            auto copy_scores = [&](ttv_f32x4 (&dst)[2][kMB], const ttv_f32x4 (&src)[2][kMB]) __attribute__((always_inline)) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb) dst[kb][mb] = src[kb][mb];
+            };
+            auto last = [&](auto cur, int tau) __attribute__((always_inline)) {
+                rescale_if_needed(cur, S, tmax);
+                exp_pack(cur, S, pb, pl);
+                ttv_bf16x8 va[DB];
+#pragma unroll
+                for (int db = 0; db < DB; ++db) va[db] = load_vt(tau, db);
+                pv_mfma(cur, va, pb, pl);
+            };
+            // Runs tiles [tau, end) of one class; the tile after them (if any) is
+            // of class `after`.  Two iterations per trip, so the two score sets
+            // swap roles without copies.
+            auto run = [&](auto cls, auto after, int& tau, int end) __attribute__((always_inline)) {
+                for (; tau + 2 < end; tau += 2) {
+                    iteration(cls, cls, tau, S, S_next);
+                    iteration(cls, cls, tau + 1, S_next, S);
+                }
+                if (tau + 1 < end) {
+                    iteration(cls, cls, tau, S, S_next);
+                    copy_scores(S, S_next);
+                    ++tau;
+                }
+                if (tau < end) {
+                    if (tau + 1 < n_tiles) {
+                        iteration(cls, after, tau, S, S_next);
+                        copy_scores(S, S_next);
+                    } else {
+                        last(cls, tau);
+                    }
+                    ++tau;
+                }
+            };
+            int tau = 0;
+            if (precise) {
+                first(cPrecise);
+                run(cPrecise, cPrecise, tau, n_tiles);
+            } else {
+                if (n_plain > 0) first(cPlain);
+                else first(cMasked);
+                run(cPlain, cMasked, tau, n_plain);
+                run(cMasked, cMasked, tau, n_tiles);
+            }
+
+            float l_run[kMB];
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) l_run[mb] = lacc[mb][0];
+            // Lane holds O^T[d = 16db + 4g4 + r][row 16mb + l16].
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) {
+                const int r_local = 16 * (mb * kW + wave) + l16;
+                const int r = it.tile * kTileR + r_local;
+                if (r >= rows) continue;
+                if (it.pslot < 0) {
+                    const int node = r / G, g = r % G;
+                    uint16_t* dst = out + ((int64_t)(it.s + node) * Hq + it.kvh * G + g) * D;
+                    const float inv_l = 1.0f / l_run[mb];
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        ttv_u32x2 w;
+                        w[0] = pack_bf16(o[db][mb][0] * inv_l, o[db][mb][1] * inv_l);
+                        w[1] = pack_bf16(o[db][mb][2] * inv_l, o[db][mb][3] * inv_l);
+                        *(ttv_u32x2*)(dst + 16 * db + 4 * g4) = w;
+                    }
+                } else {
+                    // Partial: o / l scaled by a power of two 2^-e that brings the
+                    // row's largest |o / l| into [0.5, 1), as fp16 (11-bit
+                    // precision relative to that maximum); (m, l, 2^e) beside it.
+                    const float inv_l = 1.0f / l_run[mb];
+                    float amax = 0.f;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) amax = __builtin_fmaxf(amax, __builtin_fabsf(o[db][mb][q]));
+                    const int e = __builtin_amdgcn_frexp_expf(group_max(amax) * inv_l);
+                    const float sc = __builtin_amdgcn_ldexpf(inv_l, -e);
+                    ttv_f16x4* dst = part_o + (((int64_t)it.pslot * kTileR + r_local) * D) / 4;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        dst[4 * db + g4] = __builtin_convertvector(o[db][mb] * sc, ttv_f16x4);
+                    if (g4 == 0)
+                        part_ml[(int64_t)it.pslot * kTileR + r_local] =
+                            make_float4(m_run[mb], l_run[mb], __builtin_amdgcn_ldexpf(1.0f, e), 0.f);
+                }
             }
         };
-        int tau = 0;
-        if (precise) {
-            first(cPrecise);
-            run(cPrecise, cPrecise, tau, n_tiles);
-        } else {
-            if (n_plain > 0) first(cPlain);
-            else first(cMasked);
-            run(cPlain, cMasked, tau, n_plain);
-            run(cMasked, cMasked, tau, n_tiles);
-        }
-
-        float l_run[kMB];
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) l_run[mb] = lacc[mb][0];
-        // Lane holds O^T[d = 16db + 4g4 + r][row 16mb + l16].
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
-            const int r_local = wave * kRowsPerWave + 16 * mb + l16;
-            const int r = it.tile * kTileR + r_local;
-            if (r >= rows) continue;
-            if (it.pslot < 0) {
-                const int node = r / G, g = r % G;
-                uint16_t* dst = out + ((int64_t)(it.s + node) * Hq + it.kvh * G + g) * D;
-                const float inv_l = 1.0f / l_run[mb];
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    ttv_u32x2 w;
-                    w[0] = pack_bf16(o[db][mb][0] * inv_l, o[db][mb][1] * inv_l);
-                    w[1] = pack_bf16(o[db][mb][2] * inv_l, o[db][mb][3] * inv_l);
-                    *(ttv_u32x2*)(dst + 16 * db + 4 * g4) = w;
-                }
-            } else {
-                // Partial: o / l scaled by a power of two 2^-e that brings the
-                // row's largest |o / l| into [0.5, 1), as fp16 (11-bit
-                // precision relative to that maximum); (m, l, 2^e) beside it.
-                const float inv_l = 1.0f / l_run[mb];
-                float amax = 0.f;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) amax = __builtin_fmaxf(amax, __builtin_fabsf(o[db][mb][q]));
-                const int e = __builtin_amdgcn_frexp_expf(group_max(amax) * inv_l);
-                const float sc = __builtin_amdgcn_ldexpf(inv_l, -e);
-                ttv_f16x4* dst = part_o + (((int64_t)it.pslot * kTileR + r_local) * D) / 4;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    dst[4 * db + g4] = __builtin_convertvector(o[db][mb] * sc, ttv_f16x4);
-                if (g4 == 0)
-                    part_ml[(int64_t)it.pslot * kTileR + r_local] =
-                        make_float4(m_run[mb], l_run[mb], __builtin_amdgcn_ldexpf(1.0f, e), 0.f);
-            }
+        {
+            const int tile_rows = min(kTileR, rows - it.tile * kTileR);
+            const int nblk = (tile_rows + 15) / 16;
+            // One block count for every busy wave of the item: waves that
+            // share a SIMD and run different counts were measured slower
+            // than both running two.
+            const int nmb = wave < nblk ? (nblk > kW ? 2 : 1) : 0;
+            if (nmb == 2) body(std::integral_constant<int, 2>{});
+            else if (nmb == 1) body(std::integral_constant<int, 1>{});
+            else body(std::integral_constant<int, 0>{});
         }
         __syncthreads();  // LDS (ring, Q-lo, mask) is reused by the next item
     }
