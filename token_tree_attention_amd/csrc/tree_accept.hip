@@ -129,35 +129,47 @@ __global__ __launch_bounds__(kWalkThreads) void greedy_walk_kernel(
 
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    // Stages every chunk key of rows [s + b, s + b + n] (all loads of a batch
-    // in flight together, then LDS max per row) and the nodes' tokens and
-    // retrieve links.  Keys of one row compare as 64-bit maxima, so repeated
-    // loads of the last key (the clamp below) change nothing.
+    // Stages the argmax key of rows [s + b, s + b + n] (the maximum of each
+    // row's chunk keys) and the nodes' tokens and retrieve links in LDS.
     auto stage = [&](int s, int n) {
-        for (int r = tid; r <= n; r += kWalkThreads) s_key[r] = 0ull;
-        for (int i = tid; i < n; i += kWalkThreads) {
+        const int64_t nc = n_chunks;
+        const uint64_t* pk = partial + ((int64_t)s + b) * nc;
+        // This thread's node links load first; then each row's chunk keys,
+        // up to NB of them in flight before any is compared (past the last
+        // chunk the loads repeat it, which leaves the maximum unchanged).
+        int tok = 0, fc = -1, nx = -1;
+        if (tid < n) {
+            tok = tokens[s + tid];
+            fc = next_token[s + tid];
+            nx = next_sibling[s + tid];
+        }
+        auto reduce_rows = [&](auto nb_c) {
+            constexpr int NB = decltype(nb_c)::value;
+            for (int r = tid; r <= n; r += kWalkThreads) {
+                const uint64_t* row = pk + (int64_t)r * nc;
+                uint64_t best = 0ull;
+                for (int64_t c0 = 0; c0 < nc; c0 += NB) {
+                    uint64_t k[NB];
+#pragma unroll
+                    for (int u = 0; u < NB; ++u) k[u] = row[min(c0 + u, nc - 1)];
+#pragma unroll
+                    for (int u = 0; u < NB; ++u) best = k[u] > best ? k[u] : best;
+                }
+                s_key[r] = best;
+            }
+        };
+        if (nc <= 4) reduce_rows(std::integral_constant<int, 4>{});
+        else if (nc <= 8) reduce_rows(std::integral_constant<int, 8>{});
+        else reduce_rows(std::integral_constant<int, 32>{});
+        if (tid < n) {
+            s_tok[tid] = tok;
+            s_first[tid] = fc;
+            s_next[tid] = nx;
+        }
+        for (int i = tid + kWalkThreads; i < n; i += kWalkThreads) {
             s_tok[i] = tokens[s + i];
             s_first[i] = next_token[s + i];
             s_next[i] = next_sibling[s + i];
-        }
-        __syncthreads();
-        // (n + 1) * n_chunks < 2^31: n <= 1024 and a chunk holds >= 4096 of
-        // fewer than 2^31 vocab entries.
-        const uint32_t nc = (uint32_t)n_chunks;
-        const uint32_t total = (uint32_t)(n + 1) * nc;
-        const uint64_t* pk = partial + ((int64_t)s + b) * n_chunks;
-        constexpr int kBatch = 8;
-        for (uint32_t base = tid; base < total; base += kBatch * kWalkThreads) {
-            uint64_t k[kBatch];
-            uint32_t at[kBatch];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const uint32_t idx = base + u * kWalkThreads;
-                at[u] = idx < total ? idx : total - 1;
-                k[u] = pk[at[u]];
-            }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) atomicMax(&s_key[at[u] / nc], (unsigned long long)k[u]);
         }
         __syncthreads();
     };

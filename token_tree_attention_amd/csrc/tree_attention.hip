@@ -1299,37 +1299,43 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(
         const int d = (tid % kLanesPerRow) * 4;
         const int r = cb.tile * kTileR + r_local;
         if (r >= cb.n * G) continue;
-        // Chunks in batches of kCombBatch: every load of a batch is issued
-        // before any is used, so one memory latency covers the batch; the
-        // batch maximum then rescales the running sums once.  Past the last
-        // chunk the loads repeat it (in bounds, no branch) and count zero.
+        // Chunks in batches of NB: every load of a batch is issued before any
+        // is used, so one memory latency covers the batch; the batch maximum
+        // then rescales the running sums once.  Past the last chunk the
+        // loads repeat it (in bounds, no branch) and count zero; NB = 4 for
+        // tiles of at most 4 chunks keeps those repeats few.
         float mmax = kNegBig, lsum = 0.f;
         ttv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int c0 = 0; c0 < cb.nc; c0 += kCombBatch) {
-            float4 ml[kCombBatch];  // m, l, scale of the fp16 o / l
-            ttv_f16x4 ov[kCombBatch];
+        auto merge = [&](auto nb_c) __attribute__((always_inline)) {
+            constexpr int NB = decltype(nb_c)::value;
+            for (int c0 = 0; c0 < cb.nc; c0 += NB) {
+                float4 ml[NB];  // m, l, scale of the fp16 o / l
+                ttv_f16x4 ov[NB];
 #pragma unroll
-            for (int j = 0; j < kCombBatch; ++j) {
-                const int c = min(c0 + j, cb.nc - 1);
-                const int64_t ps = cb.pslot0 + (int64_t)c * cb.stride;
-                ml[j] = part_ml[ps * kTileR + r_local];
-                ov[j] = part_o[((ps * kTileR + r_local) * D + d) / 4];
+                for (int j = 0; j < NB; ++j) {
+                    const int c = min(c0 + j, cb.nc - 1);
+                    const int64_t ps = cb.pslot0 + (int64_t)c * cb.stride;
+                    ml[j] = part_ml[ps * kTileR + r_local];
+                    ov[j] = part_o[((ps * kTileR + r_local) * D + d) / 4];
+                }
+                float m_new = mmax;
+#pragma unroll
+                for (int j = 0; j < NB; ++j) m_new = fmaxf(m_new, ml[j].x);
+                const float a_old = __builtin_amdgcn_exp2f(mmax - m_new);
+                lsum *= a_old;
+                acc *= a_old;
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const float e = __builtin_amdgcn_exp2f(ml[j].x - m_new) * ml[j].y;
+                    const float a = c0 + j < cb.nc ? e : 0.f;
+                    lsum += a;
+                    acc += __builtin_convertvector(ov[j], ttv_f32x4) * (a * ml[j].z);
+                }
+                mmax = m_new;
             }
-            float m_new = mmax;
-#pragma unroll
-            for (int j = 0; j < kCombBatch; ++j) m_new = fmaxf(m_new, ml[j].x);
-            const float a_old = __builtin_amdgcn_exp2f(mmax - m_new);
-            lsum *= a_old;
-            acc *= a_old;
-#pragma unroll
-            for (int j = 0; j < kCombBatch; ++j) {
-                const float e = __builtin_amdgcn_exp2f(ml[j].x - m_new) * ml[j].y;
-                const float a = c0 + j < cb.nc ? e : 0.f;
-                lsum += a;
-                acc += __builtin_convertvector(ov[j], ttv_f32x4) * (a * ml[j].z);
-            }
-            mmax = m_new;
-        }
+        };
+        if (cb.nc <= 4) merge(std::integral_constant<int, 4>{});
+        else merge(std::integral_constant<int, kCombBatch>{});
         const float inv = 1.0f / lsum;
         const int node = r / G, g = r % G;
         uint16_t* dst = out + ((int64_t)(cb.s + node) * Hq + cb.kvh * G + g) * D + d;
