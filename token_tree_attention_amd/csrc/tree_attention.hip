@@ -40,12 +40,13 @@
 
 namespace {
 
-constexpr int kWaves = 8;               // prep / combine workgroups: 8 waves
+constexpr int kWaves = 8;               // waves of the largest row tile
 constexpr int kRowsPerWave = 32;        // query rows per wave: kMB blocks of 16
 constexpr int kMB = kRowsPerWave / 16;
 constexpr int kTileM = kWaves * kRowsPerWave;   // largest row tile (8 waves x 32 rows)
 constexpr int kTileMin = 4 * kRowsPerWave;         // smallest row tile (4 waves)
-constexpr int kThreads = kWaves * TTV_WAVE;
+constexpr int kPrepWaves = 8;           // prep workgroups (plan and node rotation)
+constexpr int kPrepThreads = kPrepWaves * TTV_WAVE;
 constexpr int kKT = 32;                 // key slots per LDS tile (= one mask word)
 constexpr int kTargetItems = 1024;      // chunking aims at about this many work items
 constexpr int kChunkMin = 128;          // shortest context chunk (slots)
@@ -145,21 +146,21 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
                            Combine* combine, int64_t max_items, int64_t max_groups,
                            int64_t max_partials, int32_t* err, int32_t* s_off, int32_t* s_ctx,
                            int32_t* s_items, int32_t* s_parts) {  // LDS, B + 1 ints each
-    __shared__ unsigned long long s_wsum[kWaves];
-    __shared__ int32_t s_wtot[2][kWaves];
+    __shared__ unsigned long long s_wsum[kPrepWaves];
+    __shared__ int32_t s_wtot[2][kPrepWaves];
     __shared__ int32_t s_ncomb;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     if (tid == 0) s_ncomb = 0;
     // The offsets and lengths are read once, into LDS.
-    for (int j = tid; j <= B; j += kThreads) {
+    for (int j = tid; j <= B; j += kPrepThreads) {
         s_off[j] = node_offsets[j];
         if (j < B) s_ctx[j] = ctx_lens[j];
     }
     __syncthreads();
     // Phase 1: total slot work, W = Hkv * sum over row tiles of (ctx + tree keys).
     unsigned long long my_work = 0;
-    for (int b = tid; b < B; b += kThreads) {
+    for (int b = tid; b < B; b += kPrepThreads) {
         const int s = s_off[b];
         const int n = s_off[b + 1] - s;
         const int ctx = s_ctx[b];
@@ -183,7 +184,7 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
     __syncthreads();
     unsigned long long W = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) W += s_wsum[w];
+    for (int w = 0; w < kPrepWaves; ++w) W += s_wsum[w];
     long long cl = (long long)((W + target_items - 1) / target_items);
     cl = ((cl + kKT - 1) / kKT) * kKT;
     if (cl < kChunkMin) cl = kChunkMin;
@@ -193,7 +194,7 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
     // Phase 2: per-request item and partial counts, exclusive prefix sums
     // (lane scans, then the wave totals; the carry is the same in every thread).
     int carry_items = 0, carry_parts = 0;
-    for (int base = 0; base < B; base += kThreads) {
+    for (int base = 0; base < B; base += kPrepThreads) {
         const int b = base + tid;
         int ni = 0, np = 0;
         if (b < B) {
@@ -228,7 +229,7 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
         __syncthreads();
         int pre_i = carry_items, pre_p = carry_parts;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < kPrepWaves; ++w) {
             const int vi = s_wtot[0][w], vp = s_wtot[1][w];
             if (w < wv) {
                 pre_i += vi;
@@ -258,7 +259,7 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
     // workgroup finds its first item at slot w without knowing n_items.
     const int active = min(grid, ((n_items + kNumXcd - 1) / kNumXcd) * kNumXcd);
     const int per_xcd = active / kNumXcd;
-    for (int x = tid; x < n_items; x += kThreads) {
+    for (int x = tid; x < n_items; x += kPrepThreads) {
         int lo = 0, hi = B - 1;
         while (lo < hi) {  // last b with s_items[b] <= x
             const int mid = (lo + hi + 1) >> 1;
@@ -320,7 +321,7 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_prep_kernel(
+__global__ __launch_bounds__(kPrepThreads) void attn_prep_kernel(
     const int32_t* __restrict__ node_offsets, const int32_t* __restrict__ ctx_lens, int B,
     int n_max, int64_t total_nodes, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
@@ -355,15 +356,18 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
     __shared__ double s_cos[D / 2], s_sin[D / 2];
     // The node's own loads do not depend on which request owns it, so they
     // are issued first; the request is then found in the staged offsets.
-    ttv_u32x4 q_first = {0u, 0u, 0u, 0u}, k_first = {0u, 0u, 0u, 0u}, v_first = {0u, 0u, 0u, 0u};
+    ttv_u32x4 q_first = {0u, 0u, 0u, 0u}, q_second = {0u, 0u, 0u, 0u};
+    ttv_u32x4 k_first = {0u, 0u, 0u, 0u}, v_first = {0u, 0u, 0u, 0u};
     if (tid < q_vecs) q_first = *(const ttv_u32x4*)(q + node * Hq * D + (int64_t)tid * kVec);
+    if (tid + kPrepThreads < q_vecs)
+        q_second = *(const ttv_u32x4*)(q + node * Hq * D + (int64_t)(tid + kPrepThreads) * kVec);
     if (tid < kv_vecs) {
         const int64_t e = node * cache.hkv * D + (int64_t)tid * kVec;
         k_first = *(const ttv_u32x4*)(k_new + e);
         v_first = *(const ttv_u32x4*)(v_new + e);
     }
     const int pos = positions[node];
-    for (int j = tid; j <= B; j += kThreads) {
+    for (int j = tid; j <= B; j += kPrepThreads) {
         s_off[j] = node_offsets[j];
         if (j < B) s_ctx[j] = ctx_lens[j];
     }
@@ -397,9 +401,10 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
     int64_t dst_first = -1;
     if (tid < kv_vecs) dst_first = cache_row(cache, b, (tid * kVec) / D, ctx + i, D);
     // Q: rotated, scaled by softmax_scale*log2(e), stored as bf16 hi + lo parts.
-    for (int v = tid; v < q_vecs; v += kThreads) {
+    for (int v = tid; v < q_vecs; v += kPrepThreads) {
         const int64_t e = node * Hq * D + (int64_t)v * kVec;
-        const ttv_u32x4 in = v == tid ? q_first : *(const ttv_u32x4*)(q + e);
+        const ttv_u32x4 in = v == tid ? q_first
+                           : v == tid + kPrepThreads ? q_second : *(const ttv_u32x4*)(q + e);
         const int d0 = (v * kVec) % D;
         ttv_u32x4 hi4, lo4;
 #pragma unroll
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void attn_prep_kernel(
         *(ttv_u32x4*)(q_lo + e) = lo4;
     }
     // K (rotated, rounded once from fp64) and V (copied) into slot ctx + i.
-    for (int v = tid; v < kv_vecs; v += kThreads) {
+    for (int v = tid; v < kv_vecs; v += kPrepThreads) {
         const int h = (v * kVec) / D;
         const int d0 = (v * kVec) % D;
         const bool first = v == tid;
@@ -1423,7 +1428,7 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
             return TTV_EHIP;
         prep_attr_set = true;
     }
-    hipLaunchKernelGGL(attn_prep_kernel<D>, prep_grid, dim3(kThreads), prep_lds, stream,
+    hipLaunchKernelGGL(attn_prep_kernel<D>, prep_grid, dim3(kPrepThreads), prep_lds, stream,
                        bt->node_offsets, bt->ctx_lens, bt->batch, bt->n_max, bt->total_nodes, q,
                        k_new, v_new, positions, cv, n_heads, rope, q_mult, q_hi, q_lo, tile_m,
                        target_items, (int)grid, hdr, items,
