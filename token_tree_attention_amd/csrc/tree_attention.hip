@@ -471,9 +471,9 @@ __global__ __launch_bounds__(kPrepThreads) void attn_prep_kernel(
 // head-dim column: exactly the V^T operand, no transposing store.
 // ---------------------------------------------------------------------------
 
-template <int D, int kW>
+template <int D, int kW, int kRows = kW * kRowsPerWave>
 struct MainCfg {
-    static constexpr int kTile = kW * kRowsPerWave;        // query rows per work item
+    static constexpr int kTile = kRows;                    // query rows per work item
     static constexpr int kPieces = D / 8;                  // 16-byte pieces per row
     static constexpr int kRowBytes = D * 2;
     static constexpr int kTileBytes = kKT * kRowBytes;     // one K or V tile
@@ -645,15 +645,18 @@ __device__ __forceinline__ void issue_tile(const CacheView& c, TileBlocks tb, in
     }
 }
 
-template <int D, bool kPaged, int kW>
+template <int D, bool kPaged, int kW, int kRows>
 __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
     const PlanHeader* __restrict__ hdr, const Item* __restrict__ items,
     const uint16_t* q_hi,  // not __restrict__: keeps its loads ahead of the prologue fence
     const uint16_t* __restrict__ q_lo, const uint32_t* __restrict__ mask, int mask_words,
     CacheView cache, const int32_t* __restrict__ table, int Hq, uint16_t* __restrict__ out,
     ttv_f16x4* __restrict__ part_o, float4* __restrict__ part_ml, int32_t* __restrict__ err) {
-    using MC = MainCfg<D, kW>;
+    using MC = MainCfg<D, kW, kRows>;
     constexpr int kTileR = MC::kTile;
+    // 16-row blocks per wave that a full tile fills (1 or 2)
+    constexpr int kMBr = (kTileR + 16 * kW - 1) / (16 * kW);
+    static_assert(kMBr >= 1 && kMBr <= kMB, "one or two row blocks per wave");
     constexpr int P = MC::kPieces;
     constexpr int KC = D / 32;   // 32-wide k chunks of the head dim
     constexpr int DB = D / 16;   // 16-row blocks of the head dim
@@ -786,7 +789,7 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         ttv_bf16x8 qreg[kMB][KC];
         int row_node[kMB];
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
+        for (int mb = 0; mb < kMBr; ++mb) {
             const int r = it.tile * kTileR + 16 * (mb * kW + wave) + l16;
             const bool ok = r < rows;
             const int rc = min(r, rows - 1);  // rows past the tile end reuse its last row
@@ -1267,17 +1270,22 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
             // share a SIMD and run different counts were measured slower
             // than both running two.
             const int nmb = wave < nblk ? (nblk > kW ? 2 : 1) : 0;
-            if (nmb == 2) body(std::integral_constant<int, 2>{});
-            else if (nmb == 1) body(std::integral_constant<int, 1>{});
-            else body(std::integral_constant<int, 0>{});
+            if constexpr (kMBr == 2) {
+                if (nmb == 2) body(std::integral_constant<int, 2>{});
+                else if (nmb == 1) body(std::integral_constant<int, 1>{});
+                else body(std::integral_constant<int, 0>{});
+            } else {
+                if (nmb >= 1) body(std::integral_constant<int, 1>{});
+                else body(std::integral_constant<int, 0>{});
+            }
         }
         __syncthreads();  // LDS (ring, Q-lo, mask) is reused by the next item
     }
 }
 
-template <int D, int kW>
+template <int D, int kW, int kRows>
 size_t main_lds_bytes(int G, int mask_words) {
-    using MC = MainCfg<D, kW>;
+    using MC = MainCfg<D, kW, kRows>;
     const int nodes = MC::kTile / G + 2;
     const size_t mask_bytes = (size_t)((nodes * mask_words + 63) / 64) * 256;
     return (size_t)MC::kMainBytes + mask_bytes;
@@ -1434,12 +1442,13 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
                        target_items, (int)grid, hdr, items,
                        comb, L.max_items, L.max_groups, L.max_partials, err);
     if (hipGetLastError() != hipSuccess) return TTV_EHIP;
-    auto run_main = [&](auto waves) -> int {
-        constexpr int kW = decltype(waves)::value;
-        using MC = MainCfg<D, kW>;
-        const size_t lds = main_lds_bytes<D, kW>(n_heads / cache->n_kv_heads, mask_words);
+    auto run_main = [&](auto rows) -> int {
+        constexpr int kW = 8;
+        constexpr int kRows = decltype(rows)::value;
+        using MC = MainCfg<D, kW, kRows>;
+        const size_t lds = main_lds_bytes<D, kW, kRows>(n_heads / cache->n_kv_heads, mask_words);
         if (lds > 160 * 1024) return TTV_EINVAL;
-        auto kern = cv.paged ? attn_main_kernel<D, true, kW> : attn_main_kernel<D, false, kW>;
+        auto kern = cv.paged ? attn_main_kernel<D, true, kW, kRows> : attn_main_kernel<D, false, kW, kRows>;
         static bool attr_set[2] = {false, false};
         if (!attr_set[cv.paged]) {
             if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1455,7 +1464,8 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
                            stream, hdr, comb, n_heads, cache->n_kv_heads, po, pml, out);
         return hipGetLastError() == hipSuccess ? TTV_OK : TTV_EHIP;
     };
-    return small ? run_main(std::integral_constant<int, 4>{}) : run_main(std::integral_constant<int, 8>{});
+    return small ? run_main(std::integral_constant<int, kTileMin>{})
+                 : run_main(std::integral_constant<int, kTileM>{});
 }
 
 }  // namespace
