@@ -786,11 +786,22 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         // wait covers all of them, so the compiler tracks nothing in flight
         // afterwards.  Tiles 2 .. ahead - 1 are issued after that wait and
         // stay in flight into the loop.
+        // Row blocks of 16 rows: a tile with more than 16 kW rows gives wave w
+        // blocks 2w and 2w + 1 (NMB = 2); a tile with at most 16 kW rows
+        // gives wave w block w alone (NMB = 1, or 0 past the last row), so a
+        // partly filled tile runs one block per busy wave.  Every busy wave
+        // of an item runs the same count: waves that share a SIMD and run
+        // different counts were measured slower than both running two.
+        const int nblk = (min(kTileR, rows - it.tile * kTileR) + 15) / 16;
+        const int nmb = wave < nblk ? (nblk > kW ? 2 : 1) : 0;
+        int rblk[kMB];
+        rblk[0] = nmb == 2 ? 2 * wave : wave;
+        rblk[1] = 2 * wave + 1;
         ttv_bf16x8 qreg[kMB][KC];
         int row_node[kMB];
 #pragma unroll
         for (int mb = 0; mb < kMBr; ++mb) {
-            const int r = it.tile * kTileR + 16 * (mb * kW + wave) + l16;
+            const int r = it.tile * kTileR + 16 * rblk[mb] + l16;
             const bool ok = r < rows;
             const int rc = min(r, rows - 1);  // rows past the tile end reuse its last row
             const int node = rc / G, g = rc % G;
@@ -827,10 +838,7 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         for (int j = 2; j < ahead && j < n_tiles; ++j) issue(j, blocks_of(j));
         if (kPaged && ahead < n_tiles) next_blocks = blocks_of(ahead);
 
-        // Rows map to waves by 16-row block: rows 16 j .. 16 j + 15 of the
-        // tile belong to wave j % kW as its block mb = j / kW.  A tile with
-        // at most 16 kW rows then needs one block per wave, and the waves
-        // run only NMB blocks (NMB = 0 for a wave without rows).
+        // The item body, compiled for NMB = 2, 1 and 0 row blocks per wave.
         auto body = [&](auto nmb_c) __attribute__((always_inline)) {
             constexpr int NMB = decltype(nmb_c)::value;
             ttv_f32x4 o[DB][kMB], lacc[kMB];
@@ -854,7 +862,7 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                     if (kPrecise) {
 #pragma unroll
                         for (int mb = 0; mb < NMB; ++mb) {
-                            const int rl = 16 * (mb * kW + wave) + l16;
+                            const int rl = 16 * rblk[mb] + l16;
                             qlo[mb] = *(const ttv_bf16x8*)(smem + (qlo_s - ring) + rl * MC::kRowBytes +
                                                            16 * swz_k(rl, 4 * kc + g4, P));
                         }
@@ -1093,7 +1101,7 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                     if (kNextPrecise) {
 #pragma unroll
                         for (int mb = 0; mb < NMB; ++mb) {
-                            const int rl = 16 * (mb * kW + wave) + l16;
+                            const int rl = 16 * rblk[mb] + l16;
                             qlo[kc][mb] = *(const ttv_bf16x8*)(smem + (qlo_s - ring) + rl * MC::kRowBytes +
                                                                16 * swz_k(rl, 4 * kc + g4, P));
                         }
@@ -1227,7 +1235,7 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
             // Lane holds O^T[d = 16db + 4g4 + r][row 16mb + l16].
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) {
-                const int r_local = 16 * (mb * kW + wave) + l16;
+                const int r_local = 16 * rblk[mb] + l16;
                 const int r = it.tile * kTileR + r_local;
                 if (r >= rows) continue;
                 if (it.pslot < 0) {
@@ -1264,12 +1272,6 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
             }
         };
         {
-            const int tile_rows = min(kTileR, rows - it.tile * kTileR);
-            const int nblk = (tile_rows + 15) / 16;
-            // One block count for every busy wave of the item: waves that
-            // share a SIMD and run different counts were measured slower
-            // than both running two.
-            const int nmb = wave < nblk ? (nblk > kW ? 2 : 1) : 0;
             if constexpr (kMBr == 2) {
                 if (nmb == 2) body(std::integral_constant<int, 2>{});
                 else if (nmb == 1) body(std::integral_constant<int, 1>{});
