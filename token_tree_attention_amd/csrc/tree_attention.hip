@@ -1130,7 +1130,19 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                     for (int e = 2 * half; e < 2 * half + 2; ++e)
                         packed[mb][e] = pack_bf16(p[mb][2 * e], p[mb][2 * e + 1]);
                 };
-                auto phase = [] { __builtin_amdgcn_sched_barrier(0); };
+                // A phase ends in a scheduling fence; inside it, the scheduler is
+                // asked to alternate one MFMA with two VALU instructions and one
+                // LDS read, so the wave issues VALU work and operand reads while
+                // each MFMA runs (MFMA and VALU co-issue only when interleaved).
+                auto phase = [] {
+#pragma unroll
+                    for (int i = 0; i < 9; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                };
                 // Phases for D = 128 (KC = 4); with D = 64 the last two carry no
                 // score MFMAs.
                 static_assert(KC == 2 || KC == 4, "head_dim 64 or 128");
