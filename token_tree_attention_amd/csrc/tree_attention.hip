@@ -12,24 +12,27 @@
 // into one tentative region in node order).
 //
 // How, on gfx950:
-//  1. attn_prep_kernel, one workgroup per node: rotates that node's Q (all
-//     query heads, pre-multiplied by scale*log2(e), bf16) into the workspace
-//     and its K (bf16) plus V into the tentative cache slots ctx + i.  Angles
-//     are reduced in fp64 before the fp32 sin/cos.  One extra workgroup
-//     builds the work plan on the device (no host round trip).
-//  2. attn_main_kernel, persistent: a work item is (request, KV head, row
-//     tile of 256 query rows, slot chunk).  Rows are (node, query head of the
-//     GQA group) pairs, node-major, so every context K/V byte feeds all rows
-//     of its KV head.  Each of 4 waves owns 64 rows and keeps their Q in
-//     registers.  K and V tiles of 32 slots are staged in LDS (V transposed)
-//     with one tile in flight while the previous one is consumed.  S^T = K Q^T
-//     and O^T += V^T P^T run on v_mfma_f32_16x16x32_bf16, so P^T comes out of
-//     the score accumulators already in the B-operand layout.  Online softmax
-//     in fp32 (exp2 domain).  The tree part of a row tile is the last chunk:
-//     tree keys 32 at a time, masked by one word of each row's ancestor mask.
+//  1. attn_prep_kernel: workgroup 0 builds the work plan on the device (no
+//     host round trip); workgroup 1 + t handles node t of the batch.  It
+//     rotates the node's Q for every query head in fp64 (angles reduced
+//     modulo 2 pi before sincos), multiplies by scale * log2(e) and stores it
+//     as bf16 hi + bf16 lo parts in the workspace; it rotates K in fp64,
+//     rounds it once to bf16 and writes it with V into slot ctx + i.
+//  2. attn_main_kernel, persistent, 8 waves: a work item is (request, KV
+//     head, row tile of 128 or 256 query rows, slot chunk).  Rows are (node,
+//     query head of the GQA group) pairs, node-major, so every context K/V
+//     byte feeds all rows of its KV head.  A wave owns one or two 16-row
+//     blocks and keeps their Q in registers.  K and V tiles of 32 slots
+//     stream through an LDS ring (up to 6 tiles in flight) by direct
+//     global->LDS loads; V stays row-major and is read transposed by
+//     ds_read_b64_tr_b16.  S^T = K Q^T and O^T += V^T P^T run on
+//     v_mfma_f32_16x16x32_bf16, so P^T comes out of the score accumulators
+//     already in the B-operand layout.  Online softmax in fp32 (exp2
+//     domain).  The tree part of a row tile rides with its last chunk: tree
+//     keys 32 at a time, masked by one word of each row's ancestor mask.
 //     Items are laid out so that the row tiles of one slot chunk are
 //     consecutive and land on one XCD (blockIdx -> XCD-major virtual id),
-//     where their repeated K/V reads hit that XCD's L2.
+//     where their repeated K/V reads can hit that XCD's L2.
 //  3. attn_combine_kernel: log-sum-exp merge of the chunks of row tiles whose
 //     context was split; single-chunk tiles are written directly by step 2.
 
@@ -44,7 +47,7 @@ constexpr int kWaves = 8;               // waves of the largest row tile
 constexpr int kRowsPerWave = 32;        // query rows per wave: kMB blocks of 16
 constexpr int kMB = kRowsPerWave / 16;
 constexpr int kTileM = kWaves * kRowsPerWave;   // largest row tile (8 waves x 32 rows)
-constexpr int kTileMin = 4 * kRowsPerWave;         // smallest row tile (4 waves)
+constexpr int kTileMin = 128;                       // row tile of small batches (16 rows per wave)
 constexpr int kPrepWaves = 8;           // prep workgroups (plan and node rotation)
 constexpr int kPrepThreads = kPrepWaves * TTV_WAVE;
 constexpr int kKT = 32;                 // key slots per LDS tile (= one mask word)
@@ -1428,8 +1431,8 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
     const double q_mult = scale * 1.4426950408889634074;  // scores come out in log2 units
     RopeTable rope;
     for (int m = 0; m < 64; ++m) rope.inv[m] = m < D / 2 ? pow((double)rope_base, -2.0 * m / D) : 0.0;
-    // Few row tiles (a small batch): 128-row items on 4 waves, about one item
-    // per CU; otherwise 256-row items on 8 waves, about four per CU.
+    // Few row tiles (a small batch): 128-row items, about one item per CU;
+    // otherwise 256-row items, a few per CU.
     const int G = n_heads / cache->n_kv_heads;
     const int64_t tiles256 =
         (int64_t)bt->batch * cache->n_kv_heads * (((int64_t)bt->n_max * G + kTileM - 1) / kTileM);
