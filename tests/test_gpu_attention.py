@@ -1,7 +1,8 @@
 """tree_attention_verify on the GPU against the float64 oracle.
 
-Scaled cases span several 32-slot tiles, several 256-row tiles, split and
-unsplit contexts and ragged tails; outputs must be within 1e-2 + 1e-2|ref|,
+Scaled cases span several 32-slot tiles, 128- and 256-row items (the two
+row-tile sizes of the main kernel), split and unsplit contexts and ragged
+tails; outputs must be within 1e-2 + 1e-2|ref|,
 the tentative K within one bf16 ulp of the rounded rotation, V exact.
 """
 
@@ -40,6 +41,11 @@ SCALED = [
     (4, dict(batch=3, ctx=(40, 900), vocab=64)),
     (5, dict(ctx=(257, 257), vocab=64, ddtree_budget=130, batch=2)),
     (2, dict(batch=3, ctx=(0, 0), vocab=64)),
+    # enough row tiles for the 256-row items: paged, with requests of at most
+    # 128 rows per KV head (one 16-row block per wave) next to larger ones
+    (2, dict(batch=64, ctx=(30, 300), vocab=64)),
+    # 256-row items over a contiguous cache, every tile full
+    (1, dict(batch=40, ctx=(20, 200), vocab=64)),
 ]
 
 
