@@ -101,3 +101,31 @@ def test_attention_softmax_scale_argument():
                                    cache, meta["err"], softmax_scale=1.0 / 8.0)
     torch.cuda.synchronize()
     assert torch.equal(o0, o1)  # 1/sqrt(64) explicitly == default
+
+
+def test_attention_unmapped_block_flags_only_its_request():
+    """A paged request whose tentative block is unmapped (-1) is flagged with
+    ERR_BLOCK_TABLE; its neighbours are unaffected and match the oracle."""
+    require_gpu()
+    import torch
+    from synth.device import to_device
+    wl = synth.make_workload(2, 4, batch=3, ctx=(60, 400), vocab=64)
+    assert wl.layout == "paged"
+    d = to_device(wl)
+    bad = 1
+    c = int(wl.ctx_lens[bad])
+    table = d["block_table"]
+    table[bad, c // 16] = -1  # the block holding the request's first tree slot
+    say(f"tree_attention_verify with block {c // 16} of request {bad} unmapped")
+    bt = tta.Batch(d["node_offsets"], d["ctx_lens"], wl.n_max, total_nodes=wl.total_nodes)
+    meta = tta.tree_build(bt, d["parents"])
+    out = tta.tree_attention_verify(bt, d["q"], d["k_new"], d["v_new"], meta["mask"], meta["positions"],
+                                    tta.KVCache(d["k_cache"], d["v_cache"], table), meta["err"])
+    torch.cuda.synchronize()
+    err = meta["err"].cpu().numpy()
+    assert err[bad] & tta.ERR_BLOCK_TABLE, err
+    for b in range(wl.batch):
+        if b == bad:
+            continue
+        assert err[b] == 0, err
+        check_attention_request(wl, b, bits(out)[wl.request_nodes(b)])

@@ -393,11 +393,13 @@ __global__ __launch_bounds__(kPrepThreads) void attn_prep_kernel(
         if (s_off[mid] <= node) lo = mid;
         else hi = mid - 1;
     }
-    const int b = lo;
-    const int s = s_off[b];
-    const int n = s_off[b + 1] - s;
+    // The request is workgroup-uniform; saying so keeps its values in scalar
+    // registers and lets one lane per wave raise a flag.
+    const int b = __builtin_amdgcn_readfirstlane(lo);
+    const int s = __builtin_amdgcn_readfirstlane(s_off[b]);
+    const int n = __builtin_amdgcn_readfirstlane(s_off[b + 1]) - s;
     const int i = (int)(node - s);
-    const int ctx = s_ctx[b];
+    const int ctx = __builtin_amdgcn_readfirstlane(s_ctx[b]);
     const bool ok = s >= 0 && n >= 0 && n <= n_max && (int64_t)s + n <= total_nodes && i >= 0 &&
                     i < n && ctx >= 0 && (cache.paged || (int64_t)ctx + n <= cache.cap);
     if (!ok) return;  // uniform; the plan flags the request
@@ -432,8 +434,9 @@ __global__ __launch_bounds__(kPrepThreads) void attn_prep_kernel(
         const int d0 = (v * kVec) % D;
         const bool first = v == tid;
         const int64_t dst = first ? dst_first : cache_row(cache, b, h, ctx + i, D);
-        if (dst < 0) {
-            atomicOr(err + b, TTV_ERR_BLOCK_TABLE);
+        if (dst < 0) {  // unmapped slot: one flag per wave, not one per lane
+            const uint64_t bad = __ballot(1);
+            if ((threadIdx.x & 63) == __builtin_ctzll(bad)) atomicOr(err + b, TTV_ERR_BLOCK_TABLE);
             continue;
         }
         const int64_t e = node * Hkv * D + (int64_t)v * kVec;
