@@ -34,6 +34,8 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(
     int32_t* __restrict__ released_blocks, int32_t* __restrict__ num_released,
     int32_t* __restrict__ err) {
     __shared__ int32_t s_path[TTV_MAX_TREE_NODES];
+    // paged: the table entries of the tentative region, read once
+    __shared__ int32_t s_blk[TTV_MAX_TREE_NODES / TTV_BLOCK_SIZE + 2];
     __shared__ int32_t s_flags;
 
     const int b = blockIdx.x;
@@ -82,6 +84,7 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(
         const int last = (ctx + n + block_size - 1) / block_size;
         for (int j = first + tid; j < last; j += kCommitThreads) {
             const int blk = block_table[(int64_t)b * max_blocks + j];
+            s_blk[j - first] = blk;
             if (blk < 0 || blk >= num_blocks) atomicOr(&s_flags, TTV_ERR_BLOCK_TABLE);
         }
     }
@@ -107,7 +110,8 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(
     const int64_t row_stride = head_dim;  // elements
     auto slot_offset = [&](int slot, int h) -> int64_t {
         if (!paged) return (((int64_t)b * n_kv_heads + h) * capacity + slot) * row_stride;
-        const int blk = block_table[(int64_t)b * max_blocks + slot / block_size];
+        // every slot moved lies in the tentative region [ctx, ctx + n)
+        const int blk = s_blk[slot / block_size - ctx / block_size];
         return (((int64_t)blk * n_kv_heads + h) * block_size + slot % block_size) * row_stride;
     };
     for (int d0 = 0; d0 < a; d0 += depths_per_round) {
@@ -149,9 +153,9 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(
         const int first = (new_len + block_size - 1) / block_size;
         const int last = (ctx + n + block_size - 1) / block_size;
         for (int j = first + tid; j < last; j += kCommitThreads) {
-            int32_t* e = block_table + (int64_t)b * max_blocks + j;
-            if (released_blocks) released_blocks[(int64_t)b * max_blocks + (j - first)] = *e;
-            *e = -1;
+            if (released_blocks)  // the staged entry (first >= ctx / block_size)
+                released_blocks[(int64_t)b * max_blocks + (j - first)] = s_blk[j - ctx / block_size];
+            block_table[(int64_t)b * max_blocks + j] = -1;
         }
         if (released_blocks)
             for (int k = (last > first ? last - first : 0) + tid; k < max_blocks; k += kCommitThreads)
