@@ -37,6 +37,7 @@
 //     context was split; single-chunk tiles are written directly by step 2.
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "ttv_device.h"
@@ -1379,15 +1380,44 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(
     }
 }
 
-int g_num_cus = 0;
+// Per-device host state: the CU count and which kernels already had their
+// dynamic-LDS limit raised (a function attribute is set per device).
+// Atomics, so concurrent calls from several host threads stay well defined.
+constexpr int kMaxDevices = 64;
+struct DeviceState {
+    std::atomic<int> cus{0};
+    std::atomic<unsigned> lds_raised{0};
+};
+DeviceState g_device[kMaxDevices];
+
+DeviceState& device_state() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+    return g_device[dev];
+}
 
 int num_cus() {
-    if (g_num_cus > 0) return g_num_cus;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    g_num_cus = cus > 0 ? cus : 256;
-    return g_num_cus;
+    DeviceState& st = device_state();
+    int cus = st.cus.load(std::memory_order_relaxed);
+    if (cus > 0) return cus;
+    int dev = 0;
+    cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    st.cus.store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+// Raises a kernel's dynamic-LDS limit once per device; `bit` names the kernel.
+bool raise_lds_limit(const void* kern, unsigned bit, int bytes) {
+    DeviceState& st = device_state();
+    if (st.lds_raised.load(std::memory_order_acquire) & bit) return true;
+    if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+        return false;
+    st.lds_raised.fetch_or(bit, std::memory_order_release);
+    return true;
 }
 
 bool valid_common(const ttv_batch* bt, const ttv_kv_cache* c, int32_t n_heads) {
@@ -1449,13 +1479,8 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
     if (grid > kMaxGrid) grid = kMaxGrid;
     dim3 prep_grid((unsigned)(1 + bt->total_nodes));
     const size_t prep_lds = (size_t)4 * (bt->batch + 1) * sizeof(int32_t);
-    static bool prep_attr_set = false;
-    if (!prep_attr_set) {
-        if (hipFuncSetAttribute((const void*)attn_prep_kernel<D>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 80 * 1024) != hipSuccess)
-            return TTV_EHIP;
-        prep_attr_set = true;
-    }
+    if (!raise_lds_limit((const void*)attn_prep_kernel<D>, D == 128 ? 1u : 2u, 80 * 1024))
+        return TTV_EHIP;
     hipLaunchKernelGGL(attn_prep_kernel<D>, prep_grid, dim3(kPrepThreads), prep_lds, stream,
                        bt->node_offsets, bt->ctx_lens, bt->batch, bt->n_max, bt->total_nodes, q,
                        k_new, v_new, positions, cv, n_heads, rope, q_mult, q_hi, q_lo, tile_m,
@@ -1469,13 +1494,9 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
         const size_t lds = main_lds_bytes<D, kW, kRows>(n_heads / cache->n_kv_heads, mask_words);
         if (lds > 160 * 1024) return TTV_EINVAL;
         auto kern = cv.paged ? attn_main_kernel<D, true, kW, kRows> : attn_main_kernel<D, false, kW, kRows>;
-        static bool attr_set[2] = {false, false};
-        if (!attr_set[cv.paged]) {
-            if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    160 * 1024) != hipSuccess)
-                return TTV_EHIP;
-            attr_set[cv.paged] = true;
-        }
+        // one bit per main-kernel variant (head dim, layout, row tile)
+        const unsigned bit = 4u << ((D == 128 ? 0 : 4) + (cv.paged ? 0 : 2) + (kRows == kTileM ? 0 : 1));
+        if (!raise_lds_limit((const void*)kern, bit, 160 * 1024)) return TTV_EHIP;
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kW * TTV_WAVE), lds, stream, hdr, items,
                            q_hi, q_lo, mask, mask_words, cv, cache->block_table, n_heads, out, po,
                            pml, err);
