@@ -1,8 +1,8 @@
 """tree_attention_verify on the GPU against the float64 oracle.
 
 Scaled cases span several 32-slot tiles, 128- and 256-row items (the two
-row-tile sizes of the main kernel), split and unsplit contexts and ragged
-tails; outputs must be within 1e-2 + 1e-2|ref|,
+row-tile sizes of the main kernel), requests of one to five row tiles,
+split and unsplit contexts and ragged tails; outputs must be within 1e-2 + 1e-2|ref|,
 the tentative K within one bf16 ulp of the rounded rotation, V exact.
 """
 
@@ -46,6 +46,12 @@ SCALED = [
     (2, dict(batch=64, ctx=(30, 300), vocab=64)),
     # 256-row items over a contiguous cache, every tile full
     (1, dict(batch=40, ctx=(20, 200), vocab=64)),
+    # five 256-row tiles per request and KV head (220-node trees, 5 query
+    # heads per KV head), the last one partial
+    (4, dict(batch=8, ctx=(40, 700), vocab=64)),
+    # one or two 256-row tiles per request and KV head (8 query heads per KV
+    # head, 16..64-node trees)
+    (2, dict(batch=40, ctx=(30, 400), vocab=64, heads=(64, 8, 128))),
 ]
 
 
