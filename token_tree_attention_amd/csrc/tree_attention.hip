@@ -80,6 +80,16 @@ struct PlanHeader {
     int32_t reserved[61];
 };
 
+typedef __bf16 ttv_bf16x2v __attribute__((ext_vector_type(2)));
+typedef float ttv_f32x2v __attribute__((ext_vector_type(2)));
+
+// Two fp64 values to packed bf16 (a in the low half), nearest-even: rounded
+// to odd in fp32, then the hardware's packed fp32 -> bf16 conversion.
+__device__ __forceinline__ uint32_t pack_bf16_f64(double a, double b) {
+    const ttv_f32x2v f = {ttv_f64_to_f32_odd(a), ttv_f64_to_f32_odd(b)};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, ttv_bf16x2v));
+}
+
 struct Item {
     int32_t b, kvh, tile, s;
     int32_t n, ctx, c0, c1;
@@ -406,13 +416,16 @@ __global__ __launch_bounds__(kPrepThreads) void attn_prep_kernel(
     if (!ok) return;  // uniform; the plan flags the request
     int64_t dst_first = -1;
     if (tid < kv_vecs) dst_first = cache_row(cache, b, (tid * kVec) / D, ctx + i, D);
-    // Q: rotated, scaled by softmax_scale*log2(e), stored as bf16 hi + lo parts.
+    // Q: rotated, scaled by softmax_scale*log2(e), stored as bf16 hi + lo
+    // parts; the low parts only where the main kernel reads them (requests
+    // whose items run precise).
+    const bool need_lo = ctx < kPreciseCtx;
     for (int v = tid; v < q_vecs; v += kPrepThreads) {
         const int64_t e = node * Hq * D + (int64_t)v * kVec;
         const ttv_u32x4 in = v == tid ? q_first
                            : v == tid + kPrepThreads ? q_second : *(const ttv_u32x4*)(q + e);
         const int d0 = (v * kVec) % D;
-        ttv_u32x4 hi4, lo4;
+        ttv_u32x4 hi4, lo4 = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const double x0 = ttv_bf16_bits_to_f64(in[w] & 0xFFFFu);
@@ -421,13 +434,13 @@ __global__ __launch_bounds__(kPrepThreads) void attn_prep_kernel(
             const double c = s_cos[m], sn = s_sin[m];
             const double r0 = (x0 * c - x1 * sn) * q_mult;
             const double r1 = (x1 * c + x0 * sn) * q_mult;
-            const uint32_t h0 = ttv_f64_to_bf16_bits(r0), h1 = ttv_f64_to_bf16_bits(r1);
-            hi4[w] = h0 | (h1 << 16);
-            lo4[w] = ttv_f64_to_bf16_bits(r0 - ttv_bf16_bits_to_f64(h0)) |
-                     (ttv_f64_to_bf16_bits(r1 - ttv_bf16_bits_to_f64(h1)) << 16);
+            hi4[w] = pack_bf16_f64(r0, r1);
+            if (need_lo)
+                lo4[w] = pack_bf16_f64(r0 - ttv_bf16_bits_to_f64(hi4[w] & 0xFFFFu),
+                                       r1 - ttv_bf16_bits_to_f64(hi4[w] >> 16));
         }
         *(ttv_u32x4*)(q_hi + e) = hi4;
-        *(ttv_u32x4*)(q_lo + e) = lo4;
+        if (need_lo) *(ttv_u32x4*)(q_lo + e) = lo4;
     }
     // K (rotated, rounded once from fp64) and V (copied) into slot ctx + i.
     for (int v = tid; v < kv_vecs; v += kPrepThreads) {
@@ -449,8 +462,7 @@ __global__ __launch_bounds__(kPrepThreads) void attn_prep_kernel(
             const double x1 = ttv_bf16_bits_to_f64(kin[w] >> 16);
             const int m = (d0 >> 1) + w;
             const double c = s_cos[m], sn = s_sin[m];
-            ko[w] = ttv_f64_to_bf16_bits(x0 * c - x1 * sn) |
-                    (ttv_f64_to_bf16_bits(x1 * c + x0 * sn) << 16);
+            ko[w] = pack_bf16_f64(x0 * c - x1 * sn, x1 * c + x0 * sn);
         }
         *(ttv_u32x4*)(cache.k + dst + d0) = ko;
         *(ttv_u32x4*)(cache.v + dst + d0) = first ? v_first : *(const ttv_u32x4*)(v_new + e);
@@ -532,8 +544,6 @@ __device__ __forceinline__ void raw_barrier() {
 
 typedef short ttv_i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) ttv_i16x4 lds_i16x4;
-typedef __bf16 ttv_bf16x2v __attribute__((ext_vector_type(2)));
-typedef float ttv_f32x2v __attribute__((ext_vector_type(2)));
 
 // Byte address of an LDS location, as the ds_* instructions take it.
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {

@@ -26,13 +26,24 @@ __device__ __forceinline__ uint32_t ttv_f32_to_bf16_bits(float f) {
     return u >> 16;
 }
 
-// Round fp64 to bf16, nearest-even, without double rounding: truncate to fp32,
-// set the sticky bit when inexact (round to odd), then round fp32 -> bf16.
-__device__ __forceinline__ uint32_t ttv_f64_to_bf16_bits(double d) {
-    const float f = __double2float_rz(d);
+// Round fp64 to fp32 to odd: nearest-even first, one step back toward zero
+// where that went away from zero, and the lowest bit set whenever the result
+// is inexact.  Rounding this to bf16 (nearest-even) equals rounding d to bf16
+// directly, since fp32 keeps 16 more fraction bits (no double rounding).
+__device__ __forceinline__ float ttv_f64_to_f32_odd(double d) {
+    const float f = (float)d;
+    const double back = (double)f;
     uint32_t u = __float_as_uint(f);
-    if ((double)f != d) u |= 1u;
-    return ttv_f32_to_bf16_bits(__uint_as_float(u));
+    if (back != d) {
+        if (fabs(back) > fabs(d)) u -= 1u;
+        u |= 1u;
+    }
+    return __uint_as_float(u);
+}
+
+// Round fp64 to bf16, nearest-even.
+__device__ __forceinline__ uint32_t ttv_f64_to_bf16_bits(double d) {
+    return ttv_f32_to_bf16_bits(ttv_f64_to_f32_odd(d));
 }
 
 __device__ __forceinline__ double ttv_bf16_bits_to_f64(uint32_t h) {
