@@ -38,9 +38,11 @@
  *   walk's root) and row 1 + i the prediction after node i.
  * - bf16 is the upper half of an IEEE float32 (uint16 storage).
  * - Ownership: the caller allocates every buffer, including workspaces.  The
- *   library allocates nothing, frees nothing, keeps no state between calls
- *   and keeps no pointer once the call returns.  Calls are asynchronous on
- *   the given stream, reentrant and thread-safe.
+ *   library allocates nothing, frees nothing and keeps no pointer once the
+ *   call returns.  The only state it keeps between calls is per device and
+ *   read-only after the first call there: the compute-unit count and which
+ *   kernels already have their shared-memory limit raised.  Calls are
+ *   asynchronous on the given stream, reentrant and thread-safe.
  * - Host-level errors: the return value is TTV_OK, or TTV_EINVAL (a null
  *   pointer, a size out of range, an unsupported head_dim / head ratio /
  *   dtype / layout; nothing is launched), TTV_ENOSPC (workspace too small;
