@@ -57,6 +57,7 @@ constexpr int kChunkMin = 128;          // shortest context chunk (slots)
 constexpr int kMaxBatch = 4096;         // plan keeps per-request prefix sums in LDS
 constexpr int kNumXcd = 8;
 constexpr int kMaxGrid = 1024;          // main-kernel workgroups at most (one per CU)
+constexpr int kCostBuckets = 1024;      // plan's bucket sort of item costs (32 per octave)
 constexpr int kPreciseCtx = 256;        // requests with a shorter context run every tile precise
 constexpr int kCombThreads = 256;       // combine workgroup
 constexpr int kCombBatch = 8;           // chunk partials a combine thread loads before using any
@@ -162,6 +163,7 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
                            int32_t* s_items, int32_t* s_parts) {  // LDS, B + 1 ints each
     __shared__ unsigned long long s_wsum[kPrepWaves];
     __shared__ int32_t s_wtot[2][kPrepWaves];
+    __shared__ int32_t s_bucket[kCostBuckets];  // counts, then placement cursors
     __shared__ int32_t s_ncomb;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
@@ -268,12 +270,7 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
     if (n_items > max_items || s_parts[B] > max_partials) n_items = 0;
 
     // Phase 3: item descriptors (request found by binary search on the prefix).
-    // Logical item x goes to workgroup w's k-th slot, k * grid + w, where the
-    // main kernel's workgroup w runs items vid(w) + k * active; so a
-    // workgroup finds its first item at slot w without knowing n_items.
-    const int active = min(grid, ((n_items + kNumXcd - 1) / kNumXcd) * kNumXcd);
-    const int per_xcd = active / kNumXcd;
-    for (int x = tid; x < n_items; x += kPrepThreads) {
+    auto make_item = [&](int x, Item& it) __attribute__((always_inline)) {
         int lo = 0, hi = B - 1;
         while (lo < hi) {  // last b with s_items[b] <= x
             const int mid = (lo + hi + 1) >> 1;
@@ -290,10 +287,8 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
         const int t = local % nt;
         const int rest = local / nt;
         const int chunk = rest % nc;
-        const int kvh = rest / nc;
-        Item it;
         it.b = b;
-        it.kvh = kvh;
+        it.kvh = rest / nc;
         it.tile = t;
         it.s = s;
         it.n = n;
@@ -305,24 +300,106 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
         it.pslot = nc > 1 ? s_parts[b] + local : -1;
         it.nc = nc;
         it.nt = nt;
-        {
-            const int kk = x / active, v = x % active;
-            const int w = (v % per_xcd) * kNumXcd + v / per_xcd;
-            items[(int64_t)kk * grid + w] = it;
+        return chunk;
+    };
+    // Estimated cost of an item, in tenths of a microsecond per 32-key tile
+    // (measured: about 1.3 us with two 16-row blocks per wave, 0.8 us with
+    // one, twice that when precise) plus about 7 us of prologue and
+    // epilogue; bucketed on a log scale, 32 buckets per octave.
+    auto cost_bucket = [&](const Item& it) __attribute__((always_inline)) {
+        const int rows = min(tile_m, it.n * G - it.tile * tile_m);
+        const int per_tile = ((rows + 15) / 16 > kWaves ? 13 : 8) * (it.ctx < kPreciseCtx ? 2 : 1);
+        const int tiles = (it.c1 - it.c0 + kKT - 1) / kKT + (it.kmax + kKT - 1) / kKT;
+        const uint32_t key = 70u + (uint32_t)tiles * (uint32_t)per_tile;
+        const int msb = 31 - __builtin_clz(key);
+        return 32 * msb + (int)((key >> (msb - 5)) & 31u);  // key >= 70, so msb >= 6
+    };
+    // Placement: the main kernel's workgroup w runs the items at slots w,
+    // grid + w, 2 grid + w, ...; virtual workgroup v is workgroup
+    // (v % per_xcd) * 8 + v / per_xcd, so consecutive virtual ids share an
+    // XCD (hardware places workgroup w on XCD w % 8).
+    // - At most one item per workgroup: item x on virtual workgroup x, over a
+    //   multiple of 8 workgroups, so the row tiles of one chunk (consecutive
+    //   items, the same K/V) run side by side on one XCD.
+    // - More: whole (request, KV head, chunk) groups, largest estimated cost
+    //   first, each group's row tiles at consecutive positions, dealt in
+    //   snake order -- round r of `grid` positions goes to virtual
+    //   workgroups 0 .. grid-1 for even r and grid-1 .. 0 for odd r -- so
+    //   each workgroup's total comes out close to the mean and a group's
+    //   tiles still run side by side (the order inside a cost bucket is
+    //   arbitrary).
+    const bool snake = n_items > grid;
+    if (snake) {
+        for (int k = tid; k < kCostBuckets; k += kPrepThreads) s_bucket[k] = 0;
+        __syncthreads();
+        for (int x = tid; x < n_items; x += kPrepThreads) {
+            Item it;
+            make_item(x, it);
+            if (it.tile == 0) atomicAdd(&s_bucket[cost_bucket(it)], it.nt);
         }
-        if (nc > 1 && chunk == 0) {
-            const int ci = atomicAdd(&s_ncomb, 1);
-            if (ci < max_groups) {
-                Combine cb;
-                cb.b = b;
-                cb.kvh = kvh;
-                cb.tile = t;
-                cb.s = s;
-                cb.n = n;
-                cb.pslot0 = it.pslot;
-                cb.stride = nt;
-                cb.nc = nc;
-                combine[ci] = cb;
+        __syncthreads();
+        // cursors: bucket k starts after every item of the buckets above it
+        // (thread i owns buckets 1023 - 2i and 1022 - 2i)
+        static_assert(kCostBuckets == 2 * kPrepThreads, "two buckets per thread");
+        const int k_hi = kCostBuckets - 1 - 2 * tid;
+        const int c_hi = s_bucket[k_hi], c_lo = s_bucket[k_hi - 1];
+        int sc = c_hi + c_lo;  // inclusive scan within the wave
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int tv = __shfl_up(sc, off);
+            if (lane >= off) sc += tv;
+        }
+        if (lane == 63) s_wtot[0][wv] = sc;
+        __syncthreads();
+        int pre = sc - c_hi - c_lo;
+#pragma unroll
+        for (int w = 0; w < kPrepWaves; ++w)
+            if (w < wv) pre += s_wtot[0][w];
+        s_bucket[k_hi] = pre;
+        s_bucket[k_hi - 1] = pre + c_hi;
+        __syncthreads();
+    }
+    auto add_combine = [&](const Item& it) __attribute__((always_inline)) {
+        const int ci = atomicAdd(&s_ncomb, 1);
+        if (ci < max_groups) {
+            Combine cb;
+            cb.b = it.b;
+            cb.kvh = it.kvh;
+            cb.tile = it.tile;
+            cb.s = it.s;
+            cb.n = it.n;
+            cb.pslot0 = it.pslot;
+            cb.stride = it.nt;
+            cb.nc = it.nc;
+            combine[ci] = cb;
+        }
+    };
+    if (!snake) {
+        const int per_xcd = (n_items + kNumXcd - 1) / kNumXcd;
+        for (int x = tid; x < n_items; x += kPrepThreads) {
+            Item it;
+            const int chunk = make_item(x, it);
+            items[(x % per_xcd) * kNumXcd + x / per_xcd] = it;
+            if (it.nc > 1 && chunk == 0) add_combine(it);
+        }
+    } else {
+        const int per_xcd = grid / kNumXcd;
+        for (int x = tid; x < n_items; x += kPrepThreads) {
+            Item it;
+            const int chunk = make_item(x, it);
+            if (it.nc > 1 && chunk == 0) add_combine(it);
+            if (it.tile != 0) continue;
+            // the group's first tile places the group's nt tiles
+            const int p0 = atomicAdd(&s_bucket[cost_bucket(it)], it.nt);
+            for (int t = 0; t < it.nt; ++t) {
+                Item u = it;
+                u.tile = t;
+                const int last_row = min((t + 1) * tile_m, it.n * G) - 1;
+                u.kmax = chunk == it.nc - 1 ? last_row / G + 1 : 0;
+                u.pslot = it.nc > 1 ? it.pslot + t : -1;
+                const int p = p0 + t, r = p / grid, k = p % grid;
+                const int v = (r & 1) ? grid - 1 - k : k;
+                items[r * grid + (v % per_xcd) * kNumXcd + v / per_xcd] = u;
             }
         }
     }
@@ -690,20 +767,27 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15;
     const int g4 = lane >> 4;
-    // The first item sits at slot blockIdx.x (see the plan), so its load
-    // does not wait for n_items.
+    // This workgroup's items sit at slots blockIdx.x + k * gridDim.x (see
+    // the plan), so the first one's load does not wait for n_items.
     const Item first_item = items[blockIdx.x];
     const int n_items = hdr->n_items;
     const int Hkv = cache.hkv;
     const int G = Hq / Hkv;
-    // XCD-major virtual id: consecutive ids share an XCD (hardware places
-    // workgroup x on XCD x % 8).
-    // Only as many workgroups as items take part (a multiple of 8, spread
-    // evenly over the XCDs).
-    const int active = min((int)gridDim.x, ((n_items + kNumXcd - 1) / kNumXcd) * kNumXcd);
-    const int per_xcd = active / kNumXcd;
-    const int xcd_slot = blockIdx.x / kNumXcd;
-    const int vid = xcd_slot < per_xcd ? (blockIdx.x % kNumXcd) * per_xcd + xcd_slot : n_items;
+    const int grid = gridDim.x, wg = blockIdx.x;
+    int n_mine;
+    if (n_items > grid) {
+        // snake rounds: full ones, then m items on virtual workgroups
+        // 0 .. m-1 (even round) or grid-m .. grid-1 (odd round)
+        const int r = n_items / grid, m = n_items % grid;
+        const int v = (wg % kNumXcd) * (grid / kNumXcd) + wg / kNumXcd;
+        n_mine = r + ((r & 1) ? (v >= grid - m) : (v < m));
+    } else {
+        // one item each on as many workgroups as items, a multiple of 8,
+        // consecutive items on one XCD: workgroup wg holds item vid(wg)
+        const int active = ((n_items + kNumXcd - 1) / kNumXcd) * kNumXcd;
+        const int per_xcd = active / kNumXcd, xcd_slot = wg / kNumXcd;
+        n_mine = xcd_slot < per_xcd && (wg % kNumXcd) * per_xcd + xcd_slot < n_items;
+    }
 
     // Per-lane LDS byte offsets inside a stage / the Q-lo block.
     uint32_t koff[KC];  // K operand: row l16 (+16 kb), piece 4kc + g4
@@ -722,8 +806,8 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
     const ttv_bf16x8 kOnes = __builtin_bit_cast(
         ttv_bf16x8, ttv_u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-    for (int x = vid, slot = blockIdx.x; x < n_items; x += active, slot += gridDim.x) {
-        const Item it = slot == (int)blockIdx.x ? first_item : items[slot];
+    for (int k = 0, slot = wg; k < n_mine; ++k, slot += grid) {
+        const Item it = k == 0 ? first_item : items[slot];
         const int rows = it.n * G;
         const int n_ctx_tiles = (it.c1 - it.c0 + kKT - 1) / kKT;
         const int n_tree_tiles = (it.kmax + kKT - 1) / kKT;
@@ -761,25 +845,46 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         TileBlocks next_blocks{{0, 0}, {0, 0}};  // blocks of the next tile to issue
         // Fast issue path for whole context tiles (slot0 = c0 + 32 tau, no
         // clamping): an issue is a wave-uniform base plus a per-lane byte
-        // offset, kept per chunk this wave loads (from the first row of the
-        // chunk's paged block, or from the tile's first slot).  A chunk's rows
-        // of such a tile lie in one paged block: slot0 is a multiple of 32 and
-        // a chunk is a 16-aligned sub-range of rows.
-        uint32_t f_kb[MC::kCpw], f_vb[MC::kCpw];
-#pragma unroll
-        for (int j = 0; j < MC::kCpw; ++j) {
-            const int f_row = (wave + j * kW) * MC::kChunkRows + lane / P;
-            const int f_phys = lane % P;
+        // offset per chunk this wave loads (from the first row of the chunk's
+        // paged block, or from the tile's first slot).  A chunk's rows of such
+        // a tile lie in one paged block: slot0 is a multiple of 32 and a chunk
+        // is a 16-aligned sub-range of rows.
+        auto lane_offsets = [&](int ln, int j, uint32_t& kb, uint32_t& vb) __attribute__((always_inline)) {
+            const int f_row = (wave + j * kW) * MC::kChunkRows + ln / P;
+            const int f_phys = ln % P;
             const int f_rowb = (kPaged ? (f_row & 15) : f_row) * MC::kRowBytes;
-            f_kb[j] = f_rowb + 16 * swz_k(f_row, f_phys, P);
-            f_vb[j] = f_rowb + 16 * swz_v(f_row, f_phys, P);
+            kb = f_rowb + 16 * swz_k(f_row, f_phys, P);
+            vb = f_rowb + 16 * swz_v(f_row, f_phys, P);
+        };
+        // With two row blocks per wave the registers run out and the compiler
+        // spills; offsets held across the tile loop would be among the spilled
+        // values, and the vmcnt wait it then puts for their reload between
+        // these DMAs also waits for every tile still in flight (its count
+        // cannot see the DMAs, issued through asm).  So there they are
+        // recomputed at each issue from a lane id that a volatile asm
+        // produces (not hoisted); with one row block they are kept.
+        constexpr bool kOffsetsAtIssue = kMBr == 2;
+        uint32_t f_kb[MC::kCpw], f_vb[MC::kCpw];
+        if constexpr (!kOffsetsAtIssue) {
+#pragma unroll
+            for (int j = 0; j < MC::kCpw; ++j) lane_offsets(lane, j, f_kb[j], f_vb[j]);
         }
         auto issue_whole = [&](int tau, TileBlocks tb) __attribute__((always_inline)) {
             if (wave >= MC::kChunks) return;
             const int slot0 = it.c0 + tau * kKT;
             const uint32_t stage = ring + (tau & smask) * MC::kStageBytes;
+            uint32_t ln = lane;
+            if constexpr (kOffsetsAtIssue)
+                asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
 #pragma unroll
             for (int j = 0; j < MC::kCpw; ++j) {
+                uint32_t kb, vb;
+                if constexpr (kOffsetsAtIssue) {
+                    lane_offsets((int)ln, j, kb, vb);
+                } else {
+                    kb = f_kb[j];
+                    vb = f_vb[j];
+                }
                 const int ch = wave + j * kW;
                 int64_t row0;  // element offset of the tile's (first) row of this KV head
                 if (kPaged) {
@@ -793,8 +898,8 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                     row0 = (((int64_t)it.b * cache.hkv + it.kvh) * cache.cap + slot0) * D;
                 }
                 const uint32_t chunk_off = ch * MC::kChunkRows * MC::kRowBytes;
-                dma16s(stage + chunk_off, cache.k + row0, f_kb[j]);
-                dma16s(stage + MC::kTileBytes + chunk_off, cache.v + row0, f_vb[j]);
+                dma16s(stage + chunk_off, cache.k + row0, kb);
+                dma16s(stage + MC::kTileBytes + chunk_off, cache.v + row0, vb);
             }
         };
 
