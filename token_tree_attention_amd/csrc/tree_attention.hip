@@ -16,8 +16,9 @@
 //     host round trip); workgroup 1 + t handles node t of the batch.  It
 //     rotates the node's Q for every query head in fp64 (angles reduced
 //     modulo 2 pi before sincos), multiplies by scale * log2(e) and stores it
-//     as bf16 hi + bf16 lo parts in the workspace; it rotates K in fp64,
-//     rounds it once to bf16 and writes it with V into slot ctx + i.
+//     as bf16 hi (+ bf16 lo for short contexts) in the workspace; it rotates
+//     K in fp64, rounds it once to bf16 and writes it with V into slot
+//     ctx + i.
 //  2. attn_main_kernel, persistent, 8 waves: a work item is (request, KV
 //     head, row tile of 128 or 256 query rows, slot chunk).  Rows are (node,
 //     query head of the GQA group) pairs, node-major, so every context K/V
@@ -30,9 +31,11 @@
 //     already in the B-operand layout.  Online softmax in fp32 (exp2
 //     domain).  The tree part of a row tile rides with its last chunk: tree
 //     keys 32 at a time, masked by one word of each row's ancestor mask.
-//     Items are laid out so that the row tiles of one slot chunk are
-//     consecutive and land on one XCD (blockIdx -> XCD-major virtual id),
-//     where their repeated K/V reads can hit that XCD's L2.
+//     The plan deals items to workgroups largest estimated cost first, in
+//     snake order, so the workgroups finish close together; the row tiles of
+//     one slot chunk stay consecutive and land on one XCD (blockIdx ->
+//     XCD-major virtual id), where their repeated K/V reads can hit that
+//     XCD's L2.
 //  3. attn_combine_kernel: log-sum-exp merge of the chunks of row tiles whose
 //     context was split; single-chunk tiles are written directly by step 2.
 
