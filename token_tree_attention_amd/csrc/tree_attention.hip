@@ -852,9 +852,9 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         // paged block, or from the tile's first slot).  A chunk's rows of such
         // a tile lie in one paged block: slot0 is a multiple of 32 and a chunk
         // is a 16-aligned sub-range of rows.
-        auto lane_offsets = [&](int ln, int j, uint32_t& kb, uint32_t& vb) __attribute__((always_inline)) {
-            const int f_row = (wave + j * kW) * MC::kChunkRows + ln / P;
-            const int f_phys = ln % P;
+        auto lane_offsets = [&](uint32_t ln, int j, uint32_t& kb, uint32_t& vb) __attribute__((always_inline)) {
+            const int f_row = (wave + j * kW) * MC::kChunkRows + (int)(ln / P);
+            const int f_phys = (int)(ln % P);
             const int f_rowb = (kPaged ? (f_row & 15) : f_row) * MC::kRowBytes;
             kb = f_rowb + 16 * swz_k(f_row, f_phys, P);
             vb = f_rowb + 16 * swz_v(f_row, f_phys, P);
@@ -883,7 +883,7 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
             for (int j = 0; j < MC::kCpw; ++j) {
                 uint32_t kb, vb;
                 if constexpr (kOffsetsAtIssue) {
-                    lane_offsets((int)ln, j, kb, vb);
+                    lane_offsets(ln, j, kb, vb);
                 } else {
                     kb = f_kb[j];
                     vb = f_vb[j];
@@ -891,11 +891,12 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                 const int ch = wave + j * kW;
                 int64_t row0;  // element offset of the tile's (first) row of this KV head
                 if (kPaged) {
-                    int blk = tb.first[j];
-                    if (blk < 0 || blk >= cache.num_blocks) {
-                        if (lane == 0) atomicOr(err + it.b, TTV_ERR_BLOCK_TABLE);
-                        blk = 0;  // load a valid block; the request is flagged
-                    }
+                    // The block id stays wave-uniform (the fallback is chosen
+                    // outside the one-lane flag), so the base is scalar math.
+                    const bool bad = tb.first[j] < 0 || tb.first[j] >= cache.num_blocks;
+                    if (bad && lane == 0) atomicOr(err + it.b, TTV_ERR_BLOCK_TABLE);
+                    // an unmapped block loads block 0 instead; the request is flagged
+                    const int blk = __builtin_amdgcn_readfirstlane(bad ? 0 : tb.first[j]);
                     row0 = ((int64_t)blk * cache.hkv + it.kvh) * TTV_BLOCK_SIZE * D;
                 } else {
                     row0 = (((int64_t)it.b * cache.hkv + it.kvh) * cache.cap + slot0) * D;
