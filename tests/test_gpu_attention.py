@@ -135,3 +135,32 @@ def test_attention_unmapped_block_flags_only_its_request():
             continue
         assert err[b] == 0, err
         check_attention_request(wl, b, bits(out)[wl.request_nodes(b)])
+
+
+def test_attention_unmapped_context_block_in_a_large_batch():
+    """Enough items for cost-ordered placement (40 paged requests): an unmapped
+    block in the middle of one request's context (a whole-tile load) flags
+    only that request; every other request matches the oracle."""
+    require_gpu()
+    import torch
+    from synth.device import to_device
+    wl = synth.make_workload(2, 6, batch=40, ctx=(600, 1500), vocab=64)
+    assert wl.layout == "paged"
+    d = to_device(wl)
+    bad = 7
+    table = d["block_table"]
+    table[bad, 5] = -1  # slots 80..95, inside the committed context
+    say(f"tree_attention_verify, B=40, block 5 of request {bad} unmapped")
+    bt = tta.Batch(d["node_offsets"], d["ctx_lens"], wl.n_max, total_nodes=wl.total_nodes)
+    meta = tta.tree_build(bt, d["parents"])
+    out = tta.tree_attention_verify(bt, d["q"], d["k_new"], d["v_new"], meta["mask"], meta["positions"],
+                                    tta.KVCache(d["k_cache"], d["v_cache"], table), meta["err"])
+    torch.cuda.synchronize()
+    err = meta["err"].cpu().numpy()
+    assert err[bad] & tta.ERR_BLOCK_TABLE, err
+    ob = bits(out)
+    for b in range(wl.batch):
+        if b == bad:
+            continue
+        assert err[b] == 0, (b, err[b])
+        check_attention_request(wl, b, ob[wl.request_nodes(b)])
