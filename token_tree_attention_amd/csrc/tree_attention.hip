@@ -556,9 +556,11 @@ __global__ __launch_bounds__(kPrepThreads) void attn_prep_kernel(
 // context, 4 for precise items, whose rows' Q low parts take the space of
 // the other 4 -- and the tile nodes' mask rows, all filled by direct
 // global->LDS loads (global_load_lds: no registers hold data in flight).  A
-// tile is 32 key slots; wave w < kChunks loads chunk w of K and of V, so each
-// loading wave issues two DMA instructions per tile and waits on its own
-// vmcnt before a barrier publishes the tile.  The DMA is issued through
+// tile is 32 key slots in kChunks chunks of K and of V; waves 0..3 (one per
+// SIMD) load them, wave w chunks w, w + 4, ..., so a loading wave issues
+// 2 kCpw DMA instructions per tile (half as many waves doing the address
+// work as with one chunk per wave) and waits on its own vmcnt before a
+// barrier publishes the tile.  The DMA is issued through
 // inline asm: the compiler then neither counts it nor guards every later LDS
 // read with a wait for all loads in flight; the explicit vmcnt ladder and the
 // raw barriers order it.
@@ -578,9 +580,11 @@ struct MainCfg {
     static constexpr int kTileBytes = kKT * kRowBytes;     // one K or V tile
     static constexpr int kChunkRows = 1024 / kRowBytes;    // rows per DMA instruction (64 x 16 B)
     static constexpr int kChunks = kKT / kChunkRows;       // DMA instructions per K (or V) tile
-    // wave w loads chunks w, w + kW, ...: kCpw chunks (waves >= kChunks none)
-    static constexpr int kCpw = kChunks >= kW ? kChunks / kW : 1;
-    static_assert(kChunks % kW == 0 || kChunks < kW, "chunks spread evenly over the waves");
+    // waves 0 .. kIssueWaves-1 (one per SIMD) load a tile: wave w loads
+    // chunks w, w + kIssueWaves, ... (kCpw of them); the other waves none
+    static constexpr int kIssueWaves = kChunks < 4 ? kChunks : 4;
+    static constexpr int kCpw = kChunks / kIssueWaves;
+    static_assert(kChunks % kIssueWaves == 0 && kIssueWaves <= kW, "chunks spread evenly over the issuing waves");
     static_assert(kCpw <= 2, "at most two chunks per wave");
     static constexpr int kOpsPerTile = 2 * kCpw;           // DMA instructions per tile per loading wave
     static constexpr int kStageBytes = 2 * kTileBytes;
@@ -698,10 +702,10 @@ __device__ __forceinline__ TileBlocks tile_blocks(const CacheView& c, const int3
                                                   int b, int slot0, int valid, int wave) {
     using MC = MainCfg<D, kW>;
     TileBlocks tb{{0, 0}, {0, 0}};
-    if (!kPaged || wave >= MC::kChunks) return tb;
+    if (!kPaged || wave >= MC::kIssueWaves) return tb;
 #pragma unroll
     for (int j = 0; j < MC::kCpw; ++j) {
-        const int ch = wave + j * kW;
+        const int ch = wave + j * MC::kIssueWaves;
         const int r_first = min(ch * MC::kChunkRows, valid - 1);
         const int r_last = min(ch * MC::kChunkRows + MC::kChunkRows - 1, valid - 1);
         const int lb0 = (slot0 + r_first) >> 4;
@@ -720,10 +724,10 @@ __device__ __forceinline__ void issue_tile(const CacheView& c, TileBlocks tb, in
                                            int valid, uint32_t stage, int wave, int lane, int32_t* err) {
     using MC = MainCfg<D, kW>;
     constexpr int P = MC::kPieces;
-    if (wave >= MC::kChunks) return;
+    if (wave >= MC::kIssueWaves) return;
 #pragma unroll
     for (int j = 0; j < MC::kCpw; ++j) {
-        const int ch = wave + j * kW;
+        const int ch = wave + j * MC::kIssueWaves;
         const int r_first = min(ch * MC::kChunkRows, valid - 1);
         int bf = tb.first[j], bl = tb.last[j];
         if (kPaged && (bf < 0 || bf >= c.num_blocks || bl < 0 || bl >= c.num_blocks)) {
@@ -853,7 +857,7 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         // a tile lie in one paged block: slot0 is a multiple of 32 and a chunk
         // is a 16-aligned sub-range of rows.
         auto lane_offsets = [&](uint32_t ln, int j, uint32_t& kb, uint32_t& vb) __attribute__((always_inline)) {
-            const int f_row = (wave + j * kW) * MC::kChunkRows + (int)(ln / P);
+            const int f_row = (wave + j * MC::kIssueWaves) * MC::kChunkRows + (int)(ln / P);
             const int f_phys = (int)(ln % P);
             const int f_rowb = (kPaged ? (f_row & 15) : f_row) * MC::kRowBytes;
             kb = f_rowb + 16 * swz_k(f_row, f_phys, P);
@@ -873,7 +877,7 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
             for (int j = 0; j < MC::kCpw; ++j) lane_offsets(lane, j, f_kb[j], f_vb[j]);
         }
         auto issue_whole = [&](int tau, TileBlocks tb) __attribute__((always_inline)) {
-            if (wave >= MC::kChunks) return;
+            if (wave >= MC::kIssueWaves) return;
             const int slot0 = it.c0 + tau * kKT;
             const uint32_t stage = ring + (tau & smask) * MC::kStageBytes;
             uint32_t ln = lane;
@@ -888,7 +892,7 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                     kb = f_kb[j];
                     vb = f_vb[j];
                 }
-                const int ch = wave + j * kW;
+                const int ch = wave + j * MC::kIssueWaves;
                 int64_t row0;  // element offset of the tile's (first) row of this KV head
                 if (kPaged) {
                     // The block id stays wave-uniform (the fallback is chosen
@@ -1161,12 +1165,12 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
             auto advance = [&](auto cls, int tau) __attribute__((always_inline)) {
                 constexpr int kA = (decltype(cls)::value == kClassPrecise ? MC::kStagesShort : MC::kStagesLong) - 1;
                 if (tau + kA < n_tiles) {  // steady state: kA - 2 later tiles stay in flight
-                    if (MC::kChunks >= kW || wave < MC::kChunks) wait_vmcnt<MC::kOpsPerTile * (kA - 2)>();
+                    if (wave < MC::kIssueWaves) wait_vmcnt<MC::kOpsPerTile * (kA - 2)>();
                     raw_barrier();
                     if (tau + kA < n_plain) issue_whole(tau + kA, next_blocks);
                     else issue(tau + kA, next_blocks);
                 } else {
-                    if (MC::kChunks >= kW || wave < MC::kChunks)
+                    if (wave < MC::kIssueWaves)
                         wait_vmcnt_tiles<MC::kOpsPerTile>(min(kA - 2, n_tiles - 2 - tau));
                     raw_barrier();
                 }
