@@ -13,8 +13,9 @@
 //
 // How, on gfx950:
 //  1. attn_prep_kernel: workgroup 0 builds the work plan on the device (no
-//     host round trip); workgroup 1 + t handles node t of the batch.  It
-//     rotates the node's Q for every query head in fp64 (angles reduced
+//     host round trip); workgroup 1 + p handles nodes 2p and 2p + 1 of the
+//     batch, one per 256-thread half.  A half rotates its node's Q for every
+//     query head in fp64 (angles reduced
 //     modulo 2 pi before sincos), multiplies by scale * log2(e) and stores it
 //     as bf16 hi (+ bf16 lo for short contexts) in the workspace; it rotates
 //     K in fp64, rounds it once to bf16 and writes it with V into slot
@@ -431,7 +432,7 @@ __global__ __launch_bounds__(kPrepThreads) void attn_prep_kernel(
     int32_t* s_off = s_dyn;
     int32_t* s_ctx = s_dyn + (B + 1);
     // Workgroup 0 builds the plan (dispatched first, so it overlaps the
-    // rest); workgroup 1 + t rotates node t of the whole batch.
+    // rest); workgroup 1 + p rotates nodes 2p and 2p + 1 of the whole batch.
     if (blockIdx.x == 0) {
         build_plan(node_offsets, ctx_lens, B, n_max, total_nodes, G, Hkv,
                    cache.paged ? -1 : cache.cap, tile_m, target_items, grid, hdr, items, combine,
@@ -439,33 +440,43 @@ __global__ __launch_bounds__(kPrepThreads) void attn_prep_kernel(
                    s_dyn + 3 * (B + 1));
         return;
     }
-    const int64_t node = (int64_t)blockIdx.x - 1;
-    const int tid = threadIdx.x;
+    // Two nodes per workgroup, one per 256-thread half (four waves each), so
+    // a large batch runs its nodes in half as many workgroups.
+    constexpr int kHalf = kPrepThreads / 2;
+    const int half = threadIdx.x / kHalf;
+    const int tid = threadIdx.x % kHalf;
+    const int64_t node = 2 * ((int64_t)blockIdx.x - 1) + half;
+    const bool has_node = node < total_nodes;  // uniform over the half's waves
     constexpr int kVec = 8;
     const int q_vecs = Hq * D / kVec;
     const int kv_vecs = cache.hkv * D / kVec;
     // Rotation in fp64: with fp32, x0 cos - x1 sin loses absolute accuracy
     // when the two products nearly cancel, which shows up as several bf16
     // ulps on small results.  The work is N_b * (Hq + Hkv) * D/2 pairs.
-    __shared__ double s_cos[D / 2], s_sin[D / 2];
+    __shared__ double s_cos2[2][D / 2], s_sin2[2][D / 2];
+    double* s_cos = s_cos2[half];
+    double* s_sin = s_sin2[half];
     // The node's own loads do not depend on which request owns it, so they
     // are issued first; the request is then found in the staged offsets.
     ttv_u32x4 q_first = {0u, 0u, 0u, 0u}, q_second = {0u, 0u, 0u, 0u};
     ttv_u32x4 k_first = {0u, 0u, 0u, 0u}, v_first = {0u, 0u, 0u, 0u};
-    if (tid < q_vecs) q_first = *(const ttv_u32x4*)(q + node * Hq * D + (int64_t)tid * kVec);
-    if (tid + kPrepThreads < q_vecs)
-        q_second = *(const ttv_u32x4*)(q + node * Hq * D + (int64_t)(tid + kPrepThreads) * kVec);
-    if (tid < kv_vecs) {
-        const int64_t e = node * cache.hkv * D + (int64_t)tid * kVec;
-        k_first = *(const ttv_u32x4*)(k_new + e);
-        v_first = *(const ttv_u32x4*)(v_new + e);
+    int pos = 0;
+    if (has_node) {
+        if (tid < q_vecs) q_first = *(const ttv_u32x4*)(q + node * Hq * D + (int64_t)tid * kVec);
+        if (tid + kHalf < q_vecs)
+            q_second = *(const ttv_u32x4*)(q + node * Hq * D + (int64_t)(tid + kHalf) * kVec);
+        if (tid < kv_vecs) {
+            const int64_t e = node * cache.hkv * D + (int64_t)tid * kVec;
+            k_first = *(const ttv_u32x4*)(k_new + e);
+            v_first = *(const ttv_u32x4*)(v_new + e);
+        }
+        pos = positions[node];
     }
-    const int pos = positions[node];
-    for (int j = tid; j <= B; j += kPrepThreads) {
+    for (int j = threadIdx.x; j <= B; j += kPrepThreads) {
         s_off[j] = node_offsets[j];
         if (j < B) s_ctx[j] = ctx_lens[j];
     }
-    if (tid < D / 2) {
+    if (has_node && tid < D / 2) {
         // the angle is reduced modulo 2*pi before sincos
         const double ang = (double)pos * rope.inv[tid];
         const double two_pi = 6.283185307179586476925;
@@ -476,6 +487,7 @@ __global__ __launch_bounds__(kPrepThreads) void attn_prep_kernel(
         s_sin[tid] = sn;
     }
     __syncthreads();
+    if (!has_node) return;  // after the workgroup's only barrier
     // owning request: the last b with node_offsets[b] <= node (offsets are
     // non-decreasing; the checks below reject anything else)
     int lo = 0, hi = B - 1;
@@ -484,8 +496,9 @@ __global__ __launch_bounds__(kPrepThreads) void attn_prep_kernel(
         if (s_off[mid] <= node) lo = mid;
         else hi = mid - 1;
     }
-    // The request is workgroup-uniform; saying so keeps its values in scalar
-    // registers and lets one lane per wave raise a flag.
+    // The request is uniform over the half (a wave lies in one half); saying
+    // so keeps its values in scalar registers and lets one lane per wave
+    // raise a flag.
     const int b = __builtin_amdgcn_readfirstlane(lo);
     const int s = __builtin_amdgcn_readfirstlane(s_off[b]);
     const int n = __builtin_amdgcn_readfirstlane(s_off[b + 1]) - s;
@@ -500,10 +513,10 @@ __global__ __launch_bounds__(kPrepThreads) void attn_prep_kernel(
     // parts; the low parts only where the main kernel reads them (requests
     // whose items run precise).
     const bool need_lo = ctx < kPreciseCtx;
-    for (int v = tid; v < q_vecs; v += kPrepThreads) {
+    for (int v = tid; v < q_vecs; v += kHalf) {
         const int64_t e = node * Hq * D + (int64_t)v * kVec;
         const ttv_u32x4 in = v == tid ? q_first
-                           : v == tid + kPrepThreads ? q_second : *(const ttv_u32x4*)(q + e);
+                           : v == tid + kHalf ? q_second : *(const ttv_u32x4*)(q + e);
         const int d0 = (v * kVec) % D;
         ttv_u32x4 hi4, lo4 = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -523,7 +536,7 @@ __global__ __launch_bounds__(kPrepThreads) void attn_prep_kernel(
         if (need_lo) *(ttv_u32x4*)(q_lo + e) = lo4;
     }
     // K (rotated, rounded once from fp64) and V (copied) into slot ctx + i.
-    for (int v = tid; v < kv_vecs; v += kPrepThreads) {
+    for (int v = tid; v < kv_vecs; v += kHalf) {
         const int h = (v * kVec) / D;
         const int d0 = (v * kVec) % D;
         const bool first = v == tid;
@@ -1600,7 +1613,7 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
     if (grid > L.max_items) grid = ((L.max_items + kNumXcd - 1) / kNumXcd) * kNumXcd;
     grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
     if (grid > kMaxGrid) grid = kMaxGrid;
-    dim3 prep_grid((unsigned)(1 + bt->total_nodes));
+    dim3 prep_grid((unsigned)(1 + (bt->total_nodes + 1) / 2));  // plan + two nodes per workgroup
     const size_t prep_lds = (size_t)4 * (bt->batch + 1) * sizeof(int32_t);
     if (!raise_lds_limit((const void*)attn_prep_kernel<D>, D == 128 ? 1u : 2u, 80 * 1024))
         return TTV_EHIP;
