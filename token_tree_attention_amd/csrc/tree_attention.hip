@@ -158,7 +158,9 @@ __device__ __forceinline__ int64_t cache_row(const CacheView& c, int b, int h, i
 //    (one extra workgroup) the work plan.
 // ---------------------------------------------------------------------------
 
-__device__ void build_plan(const int32_t* __restrict__ node_offsets,
+// Inlined on purpose: called out of line, its register count (over 160)
+// became the prep kernel's and held every node workgroup to one per CU.
+__device__ __attribute__((always_inline)) void build_plan(const int32_t* __restrict__ node_offsets,
                            const int32_t* __restrict__ ctx_lens, int B, int n_max,
                            int64_t total_nodes, int G, int Hkv, int cap_limit, int tile_m,
                            int target_items, int grid, PlanHeader* hdr, Item* items,
@@ -416,7 +418,9 @@ __device__ void build_plan(const int32_t* __restrict__ node_offsets,
 }
 
 template <int D>
-__global__ __launch_bounds__(kPrepThreads) void attn_prep_kernel(
+// At most 64 registers, so eight waves per SIMD (four 512-thread
+// workgroups per CU) keep a large batch's node workgroups in one round.
+__global__ __launch_bounds__(kPrepThreads, 8) void attn_prep_kernel(
     const int32_t* __restrict__ node_offsets, const int32_t* __restrict__ ctx_lens, int B,
     int n_max, int64_t total_nodes, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
