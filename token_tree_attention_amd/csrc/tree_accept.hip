@@ -13,7 +13,9 @@
 // reduces to one 64-bit key (order-preserving value bits, then the
 // complemented index, so a plain max picks the lowest index on ties).
 // Kernel 2 runs one workgroup per request: it reduces the chunk keys of the
-// request's rows, stages tokens and retrieve links in LDS and walks.
+// request's rows, stages tokens and retrieve links in LDS, rebuilds each
+// node's parent from the links (pointer jumping) and walks with all threads
+// searching a depth's children at once.
 
 #include "ttv_device.h"
 
@@ -23,6 +25,7 @@ constexpr int kArgmaxThreads = 256;
 constexpr int64_t kChunkQuantum = 2048;    // elements; keeps 16-byte alignment for fp32 and bf16
 constexpr int64_t kTargetWorkgroups = 2048;
 constexpr int kWalkThreads = 256;
+constexpr int kSerialWalkMax = 256;  // trees up to this many nodes walk on one thread
 
 struct ChunkPlan {
     int64_t chunk_len;
@@ -124,8 +127,10 @@ __global__ __launch_bounds__(kWalkThreads) void greedy_walk_kernel(
     __shared__ int32_t s_first[TTV_MAX_TREE_NODES];
     __shared__ int32_t s_next[TTV_MAX_TREE_NODES];
     __shared__ int32_t s_path[TTV_MAX_TREE_NODES + 1];
-    __shared__ int32_t s_len;
-    __shared__ int32_t s_bonus;
+    __shared__ int32_t s_par[TTV_MAX_TREE_NODES];   // parent rebuilt from the links
+    __shared__ int32_t s_prev[TTV_MAX_TREE_NODES];  // previous sibling, then jumps
+    __shared__ int32_t s_wmin[kWalkThreads / TTV_WAVE];
+    __shared__ int32_t s_walk[3];  // serial walk's result: accepted, bonus, flags
 
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
@@ -191,38 +196,128 @@ __global__ __launch_bounds__(kWalkThreads) void greedy_walk_kernel(
     const int64_t row0 = (int64_t)s + b;
     if (row_argmax)
         for (int r = tid; r <= n; r += kWalkThreads) row_argmax[row0 + r] = (int32_t)ttv_key_index(s_key[r]);
-    if (tid == 0) {
-        int a = 0, flags = 0;
-        int target = (int)ttv_key_index(s_key[0]);
-        int j = n > 0 ? 0 : -1;  // node 0 is the root's first child (parent[0] == -1)
-        while (j >= 0) {
-            // scan the sibling list starting at j for the target token
-            while (j >= 0 && s_tok[j] != target) {
-                const int nx = s_next[j];
-                j = (nx > j && nx < n) ? nx : -1;
+    int a = 0, flags = 0;
+    int target = (int)ttv_key_index(s_key[0]);
+    if (n <= kSerialWalkMax) {
+        // Small trees: thread 0 follows the links (a depth's sibling list is
+        // short; the parallel walk's barriers would cost more).
+        if (tid == 0) {
+            int j = n > 0 ? 0 : -1;  // node 0 is the root's first child (parent[0] == -1)
+            while (j >= 0) {
+                // scan the sibling list starting at j for the target token
+                while (j >= 0 && s_tok[j] != target) {
+                    const int nx = s_next[j];
+                    j = (nx > j && nx < n) ? nx : -1;
+                }
+                if (j < 0) break;
+                if (a == max_accept) {
+                    flags |= TTV_ERR_ACCEPT;
+                    break;
+                }
+                s_path[a++] = j;
+                target = (int)ttv_key_index(s_key[1 + j]);
+                const int fc = s_first[j];
+                j = (fc > j && fc < n) ? fc : -1;
             }
-            if (j < 0) break;
+            s_walk[0] = a;
+            s_walk[1] = target;
+            s_walk[2] = flags;
+        }
+        __syncthreads();
+        a = s_walk[0];
+        target = s_walk[1];
+        flags = s_walk[2];
+    } else {
+        // Parents from the links (forward links only, as the walk follows them):
+        // a first child's parent is the node naming it; a later sibling's is its
+        // previous sibling's, resolved by pointer jumping over the backward
+        // previous-sibling links (about log2 of the longest sibling list rounds).
+        // Node 0 is the root's first child (parent -1).  kUnknown marks a node
+        // no link reaches; such a node is never matched.
+        constexpr int kUnknown = -2;
+        for (int i = tid; i < n; i += kWalkThreads) {
+            s_par[i] = i == 0 ? -1 : kUnknown;
+            s_prev[i] = -1;
+        }
+        __syncthreads();
+        for (int i = tid; i < n; i += kWalkThreads) {
+            const int fc = s_first[i], nx = s_next[i];
+            if (fc > i && fc < n) s_par[fc] = i;
+            if (nx > i && nx < n) s_prev[nx] = i;
+        }
+        __syncthreads();
+        for (;;) {
+            bool open = false;
+            int par_new[(TTV_MAX_TREE_NODES + kWalkThreads - 1) / kWalkThreads];
+            int prev_new[(TTV_MAX_TREE_NODES + kWalkThreads - 1) / kWalkThreads];
+#pragma unroll
+            for (int u = 0; u * kWalkThreads < TTV_MAX_TREE_NODES; ++u) {
+                const int i = tid + u * kWalkThreads;
+                par_new[u] = kUnknown;
+                prev_new[u] = -1;
+                if (i < n) {
+                    par_new[u] = s_par[i];
+                    prev_new[u] = s_prev[i];
+                    if (par_new[u] == kUnknown && prev_new[u] >= 0) {
+                        const int pp = s_par[prev_new[u]];
+                        if (pp != kUnknown) par_new[u] = pp;
+                        else prev_new[u] = s_prev[prev_new[u]];
+                        open = open || (par_new[u] == kUnknown && prev_new[u] >= 0);
+                    }
+                }
+            }
+            __syncthreads();  // every read of this round before any write
+#pragma unroll
+            for (int u = 0; u * kWalkThreads < TTV_MAX_TREE_NODES; ++u) {
+                const int i = tid + u * kWalkThreads;
+                if (i < n) {
+                    s_par[i] = par_new[u];
+                    s_prev[i] = prev_new[u];
+                }
+            }
+            if (!__syncthreads_or(open)) break;
+        }
+        // The walk: from the root, the lowest-index child of the current node
+        // whose token is the current choice, found by all threads at once.
+        constexpr int kNone = 0x7FFFFFFF;
+        int cur = -1;
+        for (;;) {
+            int best = kNone;
+            for (int i = tid; i < n; i += kWalkThreads)
+                if (s_par[i] == cur && s_tok[i] == target) {
+                    best = i;  // i increases, so the first hit is this thread's lowest
+                    break;
+                }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) best = min(best, __shfl_xor(best, off));
+            if ((tid & (TTV_WAVE - 1)) == 0) s_wmin[tid / TTV_WAVE] = best;
+            __syncthreads();
+            int j = kNone;
+#pragma unroll
+            for (int w = 0; w < kWalkThreads / TTV_WAVE; ++w) j = min(j, s_wmin[w]);
+            __syncthreads();  // s_wmin is rewritten by the next depth
+            if (j == kNone) break;
             if (a == max_accept) {
                 flags |= TTV_ERR_ACCEPT;
                 break;
             }
-            s_path[a++] = j;
+            if (tid == 0) s_path[a] = j;
+            ++a;
             target = (int)ttv_key_index(s_key[1 + j]);
-            const int fc = s_first[j];
-            j = (fc > j && fc < n) ? fc : -1;
+            cur = j;
         }
-        s_len = a;
-        s_bonus = target;
+    }
+    // a, target (the bonus) and flags are the same in every thread
+    if (tid == 0) {
         accept_len[b] = a;
         if (flags) atomicOr(err + b, flags);
     }
-    __syncthreads();
-    const int a = s_len;
+    __syncthreads();  // s_path, written by thread 0
     for (int k = tid; k < max_accept; k += kWalkThreads)
         accepted_nodes[(int64_t)b * max_accept + k] = k < a ? s_path[k] : -1;
     for (int k = tid; k <= max_accept; k += kWalkThreads)
         out_tokens[(int64_t)b * (max_accept + 1) + k] =
-            k < a ? s_tok[s_path[k]] : (k == a ? s_bonus : -1);
+            k < a ? s_tok[s_path[k]] : (k == a ? target : -1);
 }
 
 }  // namespace
