@@ -16,9 +16,11 @@ Inputs are uploaded before timing and rotated over enough copies (> 512 MB)
 that each step reads cold HBM rather than the 256 MB Infinity Cache.  W
 eager warm-up steps; then exactly K steps are captured in one HIP graph (the
 way a serving loop replays a verify step per tree-size bucket) and one replay
-is timed between two synchronisations.  The attention call's duration comes
-from a second graph of K attention calls, timed with HIP events on its
-stream.  The eager (host-launched) time per step is reported too.
+is timed between two synchronisations, right after two untimed replays (the
+GPU clock drops while idle and takes tens of milliseconds to recover).  The
+attention call's duration comes from a second graph of K attention calls,
+timed the same way with HIP events on its stream.  The eager (host-launched)
+time per step is reported too.
 
 Prints ONE JSON line: throughput in verified tree tokens/s (tree nodes per
 second), ms and us per step, the attention roofline (algorithmic bytes per
@@ -341,9 +343,16 @@ def main():
         g_step.replay()
         torch.cuda.synchronize()
         check_replay()
+        # The GPU lowers its clock while idle (graph capture, the check above)
+        # and needs tens of milliseconds of work to come back up: two untimed
+        # replays right before the timed one, so it measures steady state.
+        g_step.replay()
+        g_step.replay()
         ms_step = timed(g_step.replay) / args.steps
-        # Attention calls alone: K calls back to back in one replay.
+        # Attention calls alone: K calls back to back in one replay (also
+        # after two untimed ones).
         restore_tables()
+        g_attn.replay()
         g_attn.replay()
         attn_ms = timed(g_attn.replay) / args.steps
         check_replay()
