@@ -164,3 +164,17 @@ def test_attention_unmapped_context_block_in_a_large_batch():
             continue
         assert err[b] == 0, (b, err[b])
         check_attention_request(wl, b, ob[wl.request_nodes(b)])
+
+
+def test_attention_many_small_requests():
+    """600 paged requests of 1..8 nodes, one query head per KV head, head_dim
+    64: thousands of short items dealt in cost order, two nodes per prep
+    workgroup; every request matches the oracle."""
+    require_gpu()
+    wl = synth.make_workload(2, 8, batch=600, ctx=(1, 200), tree=("random", (1, 8)),
+                             heads=(8, 8, 64), vocab=64)
+    say(f"tree_attention_verify B=600 T={wl.total_nodes} heads=8/8/64")
+    d, out, err = run_attention(wl)
+    assert (err == 0).all(), err
+    for b in range(wl.batch):
+        check_attention_request(wl, b, out[wl.request_nodes(b)])
