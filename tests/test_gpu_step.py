@@ -85,3 +85,46 @@ def test_full_round(cfg):
             assert com["num_released"][b] == last - first
             assert com["released_blocks"][b, :last - first].tolist() == table_before[b, first:last].tolist()
     say(f"full round cfg={cfg}: accept lengths {np.bincount(acc['accept_len']).tolist()}")
+
+
+def test_round_with_empty_and_context_free_requests():
+    """A paged batch where some requests have no tree (0 nodes) and some no
+    committed context: every request's metadata, attention, acceptance and
+    commit against the oracle; an empty request accepts nothing and commits
+    nothing."""
+    require_gpu()
+    import torch
+    from synth.device import to_device
+    from token_tree_attention_amd.step import VerifyStep
+    wl = synth.make_workload(2, 3, batch=24, ctx=(0, 300), tree=("random", (0, 5)), vocab=64)
+    sizes = np.diff(wl.node_offsets)
+    assert (sizes == 0).any() and (sizes > 0).any()
+    d = to_device(wl)
+    ctx = d["ctx_lens"].clone()
+    ctx[1] = 0  # a request with a tree but no committed context
+    d["ctx_lens"] = ctx
+    wl.ctx_lens[1] = 0
+    say(f"round with empty requests {np.flatnonzero(sizes == 0).tolist()}, B={wl.batch} T={wl.total_nodes}")
+    bt = tta.Batch(d["node_offsets"], d["ctx_lens"], wl.n_max, total_nodes=wl.total_nodes)
+    cache = tta.KVCache(d["k_cache"], d["v_cache"], d["block_table"])
+    step = VerifyStep(bt, cache, wl.n_heads, wl.vocab, MAX_ACCEPT)
+    step.build(d["parents"])
+    step.attention(d["q"], d["k_new"], d["v_new"])
+    step.accept(d["logits"], d["tokens"])
+    torch.cuda.synchronize()
+    meta = {k: host(v) for k, v in step.meta.items()}
+    assert (meta["err"] == 0).all(), meta["err"]
+    check_build(wl, meta)
+    acc = {k: host(v) for k, v in step.acc.items()}
+    check_accept(wl, acc, MAX_ACCEPT)
+    out = bits(step.out)
+    for b in range(wl.batch):
+        if sizes[b] > 0:
+            check_attention_request(wl, b, out[wl.request_nodes(b)])
+        else:
+            assert acc["accept_len"][b] == 0
+    step.commit()
+    torch.cuda.synchronize()
+    com = {k: host(v) for k, v in step.com.items()}
+    assert (host(step.meta["err"]) == 0).all()
+    np.testing.assert_array_equal(com["new_lens"], wl.ctx_lens + acc["accept_len"])
