@@ -23,7 +23,7 @@ namespace {
 
 constexpr int kArgmaxThreads = 256;
 constexpr int64_t kChunkQuantum = 2048;    // elements; keeps 16-byte alignment for fp32 and bf16
-constexpr int64_t kTargetWorkgroups = 2048;
+constexpr int64_t kTargetWorkgroups = 8192;
 constexpr int kWalkThreads = 256;
 constexpr int kSerialWalkMax = 256;  // trees up to this many nodes walk on one thread
 
