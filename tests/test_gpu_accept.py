@@ -77,6 +77,38 @@ def test_accept_ties_signed_zero_and_unaligned_vocab():
         check_accept(wl, acc, 16)
 
 
+def test_accept_maxima_at_chunk_boundaries_full_vocab():
+    """Full 128256-entry bf16 rows with the maximum planted next to multiples of 2048
+    (every chunk the argmax splits a row into is a multiple of 2048 elements), in the
+    last, shorter chunk, and as exact ties across two such positions."""
+    require_gpu()
+    V = 128256
+    for batch in (1, 8):
+        wl = synth.make_workload(2, 11 + batch, vocab=V, ctx=(4, 9), batch=batch, logits="bf16")
+        rows = wl.logits.copy()
+        rng = np.random.default_rng(batch)
+        edges = [2048 * k + d for k in range(1, V // 2048 + 1) for d in (-1, 0) if 2048 * k + d < V]
+        tail = list(range(V - 2048 // 2, V))
+        for r in range(rows.shape[0]):
+            bits = rows[r].view(np.uint16)
+            hi = synth.bf16_bits_from_f32(
+                np.array([synth.f32_from_bf16_bits(bits).max() + 2.0], np.float32))[0]
+            kind = r % 4
+            if kind == 0:
+                bits[int(rng.choice(edges))] = hi
+            elif kind == 1:
+                bits[int(rng.choice(tail))] = hi
+            elif kind == 2:
+                a, b = sorted(int(x) for x in rng.choice(edges, 2, replace=False))
+                bits[[a, b]] = hi
+            else:
+                bits[[int(rng.choice(edges[:8])), V - 1]] = hi
+        wl.logits = rows
+        say(f"tree_greedy_accept chunk-boundary maxima V={V} batch={batch} rows={rows.shape[0]}")
+        acc, _ = run_accept(wl)
+        check_accept(wl, acc, 16)
+
+
 def test_accept_overflow_flag():
     require_gpu()
     wl = synth.make_workload(2, 4, vocab=64, ctx=(4, 9), batch=3, p=(1.0, 1.0),
