@@ -109,6 +109,28 @@ def test_accept_maxima_at_chunk_boundaries_full_vocab():
         check_accept(wl, acc, 16)
 
 
+def test_accept_chain_and_star_trees_past_the_serial_walk():
+    """Trees above 256 nodes take the parallel walk: a 1000-node chain accepted end to
+    end (and cut at max_accept, which flags the overflow), and a root with 999
+    children, every draft planted as the target's argmax."""
+    require_gpu()
+    chain = list(range(-1, 999))
+    star = [-1] + [0] * 999
+    for name, parents, max_accept in (("chain", chain, 1024), ("chain", chain, 100),
+                                      ("star", star, 16)):
+        wl = synth.make_workload(2, 21, vocab=2048, ctx=(4, 9), batch=2, p=(1.0, 1.0),
+                                 tree=("parents", parents))
+        say(f"tree_greedy_accept {name} tree of {len(parents)} nodes, max_accept={max_accept}")
+        acc, err = run_accept(wl, max_accept=max_accept)
+        check_accept(wl, acc, max_accept)
+        if name == "chain":
+            assert (acc["accept_len"] == min(max_accept, len(parents))).all(), acc["accept_len"]
+            overflow = max_accept < len(parents)
+            assert all(bool(e & tta.ERR_ACCEPT) == overflow for e in err), err
+        else:
+            assert (acc["accept_len"] == 2).all(), acc["accept_len"]  # the root and its matching child
+
+
 def test_accept_overflow_flag():
     require_gpu()
     wl = synth.make_workload(2, 4, vocab=64, ctx=(4, 9), batch=3, p=(1.0, 1.0),
