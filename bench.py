@@ -6,28 +6,33 @@ tree_build -> tree_attention_verify (one layer) -> tree_greedy_accept ->
 tree_kv_commit (plus, for paged caches, restoring the block table that the
 previous round's commit released, i.e. re-mapping the tentative blocks).
 
-Default workload: an EAGLE-style 64-node tree (depth 6, top-4 expansion,
-reranked), batch 1, committed context 4096, 32 query / 8 KV heads, head_dim
-128, bf16 K/V/Q, vocab 128256 bf16 logits, contiguous cache.  ``--workload``
-selects the other shapes (tiny_medusa, batched, ddtree, medusa_long,
-ddtree_deep).
+Headline workload (the JSON line's ``value``): ``medusa_long``, the largest
+of the five verification workloads: 64 requests, each a Medusa cartesian tree
+with top-s (10, 3, 2, 2) = 220 nodes over a committed context drawn from
+U{1024..32768}, 40 query / 8 KV heads, head_dim 128, bf16, paged cache with
+block size 16 and shuffled block tables, vocab 32000 bf16 logits.
+``--workload`` picks another headline.  ``per_config`` in the same line holds
+every workload's step time (median and p10/p90 over replays), per-call
+times, the attention call's roofline fractions and the acceptance stats.
 
-Inputs are uploaded before timing and rotated over enough copies (> 512 MB)
-that each step reads cold HBM rather than the 256 MB Infinity Cache.  W
-eager warm-up steps; then exactly K steps are captured in one HIP graph (the
-way a serving loop replays a verify step per tree-size bucket) and one replay
-is timed between two synchronisations, right after two untimed replays (the
-GPU clock drops while idle and takes tens of milliseconds to recover).  The
-attention call's duration comes from a second graph of K attention calls,
-timed the same way with HIP events on its stream.  The eager (host-launched)
-time per step is reported too.
+Inputs sit in HBM before timing and are rotated over enough copies (> 512 MB
+in play) that each step reads cold HBM rather than the 256 MB Infinity
+Cache.  W eager warm-up steps; then exactly K steps are captured in one HIP
+graph (the way a serving loop replays a verify step per tree-size bucket);
+after two untimed replays (the GPU clock drops while idle and takes tens of
+milliseconds to recover) one replay is timed between two synchronisations
+with HIP events on the stream the kernels run on: that is ``ms_per_step``.
+Further replays give the p10/p50/p90.  Each call's own time comes from a
+graph of K back-to-back calls of it, timed the same way (commit: K
+table-restore + commit pairs minus K restores).
 
 Prints ONE JSON line: throughput in verified tree tokens/s (tree nodes per
-second), ms and us per step, the attention roofline (algorithmic bytes per
-call / measured call time against 8 TB/s HBM, or flops per call / call time
-against the 2.5 PFLOP/s dense bf16 MFMA peak when the call's arithmetic
-intensity is above the ridge of the two), and the CPU oracle's rate on a
-bounded sample of the same workload.
+second) and us per step, the attention roofline of the headline (algorithmic
+bytes per call / call time against 8 TB/s HBM, or flops per call / call
+time against the 2.5 PFLOP/s dense bf16 MFMA peak when the call's
+arithmetic intensity is above the ridge of the two), the achievable
+streaming bandwidth measured on the same GPU, and the CPU oracle's rate on a
+bounded sample of the headline workload, stage by stage.
 """
 
 import argparse
@@ -47,6 +52,9 @@ BF16_PEAK_TFLOPS = 2500.0
 WORKLOADS = {
     "tiny_medusa": 0, "eagle": 1, "batched": 2, "ddtree": 3, "medusa_long": 4, "ddtree_deep": 5,
 }
+# the five verification workloads reported in per_config (ddtree_deep, a
+# deeper-tree stress variant of ddtree, with --deep)
+PER_CONFIG = ("tiny_medusa", "eagle", "batched", "ddtree", "medusa_long")
 
 
 def describe(wl):
@@ -63,6 +71,7 @@ def describe(wl):
         "logits_dtype": wl.logits_dtype,
         "kv_layout": wl.layout,
         "rope_base": wl.rope_base,
+        "seed": wl.seed,
     }
 
 
@@ -90,57 +99,97 @@ def algorithmic(wl):
     return attn_bytes, flops, accept_bytes
 
 
+def blas_info():
+    """(library name, threads) of the BLAS numpy uses."""
+    try:
+        from threadpoolctl import threadpool_info
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            i = infos[0]
+            return f"{i.get('internal_api')} {i.get('version')}", int(i.get("num_threads", 1))
+    except Exception:  # pragma: no cover
+        pass
+    return "unknown", 1
+
+
 def cpu_baseline(wl, budget_s):
-    """Time the oracle on a bounded sample: whole requests' verify rounds."""
+    """Time the oracle stage by stage on a bounded sample of the workload:
+    whole requests in order (build, per-node path attention, argmax + walk,
+    copy commit of the request's own cache region) until the budget is
+    spent."""
     import numpy as np
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from oracle import accept as O_acc
     from oracle import attention as O_att
     from oracle import bf16 as O_bf16
+    from oracle import commit as O_com
     from oracle import tree as O_tree
 
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = 1
+    blas, blas_threads = blas_info()
     cores = min(len(os.sched_getaffinity(0)), max(1, blas_threads))
-    t0 = time.perf_counter()
+    stage = {"build": 0.0, "attention": 0.0, "accept": 0.0, "commit": 0.0}
     nodes_done = 0
     reqs_done = 0
     passes = 0
-    # Whole requests in order, repeated (a small workload) until the budget is
-    # spent; at least one node.
+    t_start = time.perf_counter()
+
+    def spent():
+        return time.perf_counter() - t_start > budget_s
+
     while True:
         for b in range(wl.batch):
             s, e = int(wl.node_offsets[b]), int(wl.node_offsets[b + 1])
             n, ctx = e - s, int(wl.ctx_lens[b])
             sl = slice(s, e)
+            t0 = time.perf_counter()
             O_tree.build(wl.parents[sl], np.array([0, n]), np.array([ctx]), max(1, n), max(1, (n + 31) // 32))
+            stage["build"] += time.perf_counter() - t0
             kc, vc = O_att.context_of(wl.k_cache, wl.v_cache, b, ctx, wl.layout, wl.block_table)
-            done_nodes = 0
+            done = 0
+            t0 = time.perf_counter()
             for i in range(n):
                 O_att.attention_request(wl.q[sl], wl.k_new[sl], wl.v_new[sl], kc, vc, wl.parents[sl], ctx,
                                         nodes=[i])
-                done_nodes += 1
-                if time.perf_counter() - t0 > budget_s:
+                done += 1
+                if spent():
                     break
+            stage["attention"] += time.perf_counter() - t0
+            t0 = time.perf_counter()
             rows = wl.logits[s + b: e + b + 1]
             rows = O_bf16.to_f64(rows) if wl.logits_dtype == "bf16" else rows.astype(np.float64)
             choice = O_acc.row_argmax(rows)
-            O_acc.greedy_walk(choice, wl.tokens[sl], wl.parents[sl], 64)
-            nodes_done += done_nodes
+            walk = O_acc.greedy_walk(choice, wl.tokens[sl], wl.parents[sl], 64)
+            stage["accept"] += time.perf_counter() - t0
+            # the commit copies this request's own cache region (its blocks, for a paged cache)
+            a = len(walk["accepted"])
+            acc_nodes = np.full((1, max(1, a)), -1, np.int32)
+            acc_nodes[0, :a] = walk["accepted"]
+            if wl.layout == "contiguous":
+                kr, vr = wl.k_cache[b:b + 1], wl.v_cache[b:b + 1]
+                t0 = time.perf_counter()
+                O_com.commit_contiguous(kr, vr, [ctx], [a], acc_nodes)
+            else:
+                nblk = -(-(ctx + n) // 16)
+                ids = wl.block_table[b, :nblk]
+                kr, vr = wl.k_cache[ids], wl.v_cache[ids]
+                table = np.arange(nblk, dtype=np.int32)[None, :]
+                t0 = time.perf_counter()
+                O_com.commit_paged(kr, vr, table, [ctx], [n], [a], acc_nodes)
+            stage["commit"] += time.perf_counter() - t0
+            nodes_done += done
             reqs_done += 1
-            if time.perf_counter() - t0 > budget_s:
+            if spent():
                 break
         passes += 1
-        if time.perf_counter() - t0 > budget_s:
+        if spent():
             break
-    dt = time.perf_counter() - t0
+    dt = sum(stage.values())
     return {"value": nodes_done / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{nodes_done} tree nodes in {reqs_done} request round(s) ({passes} pass(es) over the "
-                      f"workload's requests): float64 oracle build, per-node path attention, argmax + walk "
-                      f"of those requests ({dt:.1f} s)"}
+            "blas": blas,
+            "stage_s": {k: round(v, 4) for k, v in stage.items()},
+            "sample": f"{wl.name}: {nodes_done} tree nodes of {reqs_done} request round(s) ({passes} pass(es) over "
+                      f"the workload's requests): float64 oracle build, per-node path attention, argmax + walk "
+                      f"and copy commit of those requests ({dt:.1f} s; {blas}, {blas_threads} threads)"}
 
 
 def copy_reference(args, dev):
@@ -160,6 +209,35 @@ def copy_reference(args, dev):
     dt = (time.perf_counter() - t0) / args.steps
     print(json.dumps({"copy_reference_bytes": nbytes, "steps": args.steps,
                       "us_per_copy": dt * 1e6, "GBps_read_plus_write": 2 * nbytes / dt / 1e9}))
+
+
+def achievable_bandwidth(dev):
+    """Streaming rates of plain library kernels on this GPU (GB/s): a sum over
+    1 GiB (reads only) and a 1 GiB device copy (read + write)."""
+    import torch
+    n = (1 << 30) // 4
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+
+    def best_of(fn, reps=10):
+        ts = []
+        for _ in range(reps + 2):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts = sorted(ts[2:])
+        return ts[len(ts) // 2]
+    read_ms = best_of(lambda: x.sum())
+    copy_ms = best_of(lambda: y.copy_(x))
+    del x, y
+    torch.cuda.empty_cache()
+    return {"read_gbs": (1 << 30) / (read_ms * 1e-3) / 1e9,
+            "copy_gbs": 2 * (1 << 30) / (copy_ms * 1e-3) / 1e9,
+            "kernels": "torch sum over 1 GiB fp32 (read) and a 1 GiB device copy (read + write), median of 10"}
 
 
 def stored_traffic(workload):
@@ -191,7 +269,8 @@ def roofline_entry(wl, attn_bytes, flops, attn_ms):
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     mfma_bound = flops / attn_bytes > ridge
     entry = {
-        "kernel": "tree_attention_verify call (prep + main + combine launches), K calls back to back, HIP events on their stream",
+        "kernel": "tree_attention_verify call (all its launches), K calls back to back in one HIP graph, "
+                  "HIP events on their stream",
         "bound": "mfma" if mfma_bound else "hbm",
         "achieved": tflops if mfma_bound else gbs,
         "peak": BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
@@ -210,52 +289,26 @@ def roofline_entry(wl, attn_bytes, flops, attn_ms):
     return entry
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="eagle", choices=sorted(WORKLOADS))
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--rotate-mb", type=float, default=600.0,
-                    help="rotate input copies until this many MB are in play (defeats the MALL)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle CPU work")
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--eager-only", action="store_true",
-                    help="host-launched steps only, no graph capture (for counter collection)")
-    ap.add_argument("--copy-reference", type=float, default=0.0, metavar="MB",
-                    help="instead of the path, run K device-to-device copies of MB megabytes "
-                         "(the reference kernel for scaling the HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU (asked for --gpus {args.gpus}); the verification path "
-              f"runs on a single GPU and has no multi-GPU mode", file=sys.stderr)
-        sys.exit(2)
+def pct(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
 
+
+def measure(wl, args, dev):
+    """Time one workload: the step, its dispersion and each call; returns a dict."""
     import numpy as np
     import torch
 
-    import synth
     import token_tree_attention_amd as tta
     from synth.device import to_device
     from token_tree_attention_amd.step import VerifyStep
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a ROCm GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.copy_reference > 0:
-        copy_reference(args, dev)
-        return
-    tta.load_library()
-    cfg = WORKLOADS[args.workload]
-    wl = synth.make_workload(cfg, args.seed)
+    K, W = args.steps, args.warmup
     base = to_device(wl, dev)
     per_set = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
     n_sets = int(max(1, min(64, np.ceil(args.rotate_mb * 1e6 / per_set))))
     free = torch.cuda.mem_get_info()[0]
-    n_sets = int(max(1, min(n_sets, (free * 0.6) // max(1, per_set))))
+    n_sets = int(max(1, min(n_sets, (free * 0.5) // max(1, per_set))))
     sets = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()} for _ in range(n_sets - 1)]
     steps = []
     pristine_tables = []
@@ -266,39 +319,28 @@ def main():
         pristine_tables.append(None if d["block_table"] is None else d["block_table"].clone())
     stream = torch.cuda.current_stream()
 
+    def restore(i):
+        if pristine_tables[i % n_sets] is not None:
+            steps[i % n_sets][0]["block_table"].copy_(pristine_tables[i % n_sets], non_blocking=True)
+
     def run(i):
         d, st = steps[i % n_sets]
-        if pristine_tables[i % n_sets] is not None:
-            d["block_table"].copy_(pristine_tables[i % n_sets], non_blocking=True)
+        restore(i)
         st.build(d["parents"])
         st.attention(d["q"], d["k_new"], d["v_new"])
         st.accept(d["logits"], d["tokens"])
         st.commit()
 
-    for i in range(args.warmup):
+    for i in range(W):
         run(i)
     torch.cuda.synchronize()
     errs = steps[0][1].meta["err"].cpu().numpy()
     if (errs != 0).any():
-        print(f"device error bits after warm-up: {errs.tolist()}", file=sys.stderr)
+        print(f"{wl.name}: device error bits after warm-up: {errs.tolist()}", file=sys.stderr)
         sys.exit(1)
     ref_acc = {k: v.clone() for k, v in steps[0][1].acc.items()}
-
-    # Eager timing (host-launched, for reference).
-    t0e = torch.cuda.Event(enable_timing=True)
-    t1e = torch.cuda.Event(enable_timing=True)
-    t0e.record(stream)
-    for k in range(args.steps):
-        run(args.warmup + k)
-    t1e.record(stream)
-    torch.cuda.synchronize()
-    eager_ms = t0e.elapsed_time(t1e) / args.steps
-
-    def check_replay():
-        for key, ref in ref_acc.items():  # a replay reproduces the eager result
-            if not torch.equal(steps[0][1].acc[key], ref):
-                print(f"graph replay differs from eager in {key}", file=sys.stderr)
-                sys.exit(1)
+    num_released = steps[0][1].com.get("num_released")
+    released = None if num_released is None else int(num_released.sum().item())
 
     def timed(fn):
         """fn() between two HIP events on the stream the kernels run on (ms)."""
@@ -311,78 +353,253 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
-    def restore_tables():
-        # Commits release each round's tentative blocks; the attention-only
-        # timing runs on the tables as the rounds found them (untimed copy).
-        for (d, _), t in zip(steps, pristine_tables):
-            if t is not None:
-                d["block_table"].copy_(t)
+    # Eager (host-launched) steps, for reference.
+    eager_ms = timed(lambda: [run(W + k) for k in range(K)]) / K
+
+    def check_replay():
+        for key, ref in ref_acc.items():  # a replay reproduces the eager result
+            if not torch.equal(steps[0][1].acc[key], ref):
+                print(f"{wl.name}: graph replay differs from eager in {key}", file=sys.stderr)
+                sys.exit(1)
+
+    def restore_all():
+        for i in range(n_sets):
+            restore(i)
         torch.cuda.synchronize()
 
-    def attention_calls():
-        for k in range(args.steps):
+    def graph_of(body):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(K):
+                body(k)
+        return g
+
+    def replay_ms(g, reps):
+        """Two untimed replays (steady clocks), then `reps` timed ones (ms per replay)."""
+        g.replay()
+        g.replay()
+        return [timed(g.replay) for _ in range(reps)]
+
+    g_step = graph_of(run)
+    g_step.replay()
+    torch.cuda.synchronize()
+    check_replay()
+    # the timed region: exactly K steps, one replay; then the dispersion replays
+    step_ms = replay_ms(g_step, 1 + args.replays)
+    ms_step = step_ms[0] / K
+    samples = [t / K for t in step_ms]
+    check_replay()
+
+    def call(name):
+        def body(k):
             d, st = steps[k % n_sets]
-            st.attention(d["q"], d["k_new"], d["v_new"])
+            if name == "build":
+                st.build(d["parents"])
+            elif name == "attention":
+                st.attention(d["q"], d["k_new"], d["v_new"])
+            elif name == "accept":
+                st.accept(d["logits"], d["tokens"])
+            elif name == "restore":
+                restore(k)
+            elif name == "restore_commit":
+                restore(k)
+                st.commit()
+            elif name == "commit":
+                st.commit()
+        return body
 
-    if args.eager_only:
-        ms_step = eager_ms
-        restore_tables()
-        attention_calls()
-        attn_ms = timed(attention_calls) / args.steps
-        timing = "host-launched steps"
-    else:
-        # The timed region: exactly K steps captured in one HIP graph (rotating
-        # input sets), replayed once after one untimed replay.
-        g_step = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_step):
-            for k in range(args.steps):
-                run(k)
-        g_attn = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_attn):
-            attention_calls()
-        g_step.replay()
-        torch.cuda.synchronize()
-        check_replay()
-        # The GPU lowers its clock while idle (graph capture, the check above)
-        # and needs tens of milliseconds of work to come back up: two untimed
-        # replays right before the timed one, so it measures steady state.
-        g_step.replay()
-        g_step.replay()
-        ms_step = timed(g_step.replay) / args.steps
-        # Attention calls alone: K calls back to back in one replay (also
-        # after two untimed ones).
-        restore_tables()
-        g_attn.replay()
-        g_attn.replay()
-        attn_ms = timed(g_attn.replay) / args.steps
-        check_replay()
-        timing = "K steps in one HIP graph replay"
+    calls_us = {}
+    attn_samples = None
+    # A paged commit releases the tentative blocks, so each timed commit runs
+    # on restored tables (restore + commit, minus the restores); a contiguous
+    # commit repeats the same moves.
+    paged = wl.layout == "paged"
+    for name in ("build", "attention", "accept") + (("restore", "restore_commit") if paged else ("commit",)):
+        restore_all()
+        g = graph_of(call(name))
+        ts = replay_ms(g, 1 + (args.replays if name == "attention" else 2))
+        calls_us[name] = float(np.median(ts)) / K * 1e3
+        if name == "attention":
+            attn_ms = ts[0] / K
+            attn_samples = [t / K for t in ts]
+        del g
+    restore_all()
+    check_replay()
+    commit_us = max(0.0, calls_us["restore_commit"] - calls_us["restore"]) if paged else calls_us["commit"]
+
     attn_bytes, flops, accept_bytes = algorithmic(wl)
+    roof = roofline_entry(wl, attn_bytes, flops, attn_ms)
     acc_len = steps[0][1].acc["accept_len"].cpu().numpy()
+    res = {
+        "workload": wl.name,
+        "config": describe(wl),
+        "ms_per_step": ms_step,
+        "us_per_step": ms_step * 1e3,
+        "us_per_step_p10_p50_p90": [pct(samples, 10) * 1e3, pct(samples, 50) * 1e3, pct(samples, 90) * 1e3],
+        "replays": len(samples),
+        "tokens_per_s": wl.total_nodes / (ms_step * 1e-3),
+        "eager_us_per_step": eager_ms * 1e3,
+        "calls_us": {"tree_build": calls_us["build"], "tree_attention_verify": calls_us["attention"],
+                     "tree_greedy_accept": calls_us["accept"], "tree_kv_commit": commit_us,
+                     "block_table_restore": calls_us["restore"] if paged else 0.0},
+        "attention_us_p10_p50_p90": [pct(attn_samples, 10) * 1e3, pct(attn_samples, 50) * 1e3,
+                                     pct(attn_samples, 90) * 1e3],
+        "roofline": roof,
+        "accept_gbs": accept_bytes / (calls_us["accept"] * 1e-6) / 1e9,
+        "accept_bytes": accept_bytes,
+        "accept_len_hist": np.bincount(acc_len).tolist(),
+        "mean_accept_len": float(acc_len.mean()),
+        "released_blocks": released,
+        "input_sets_rotated": n_sets,
+    }
+    del steps, sets, base, g_step
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def summary(res):
+    """The per_config entry: the figures a reader compares across workloads."""
+    r = res["roofline"]
+    return {
+        "us_per_step": res["us_per_step"],
+        "us_per_step_p10_p50_p90": res["us_per_step_p10_p50_p90"],
+        "tokens_per_s": res["tokens_per_s"],
+        "calls_us": res["calls_us"],
+        "attention_us_p10_p50_p90": res["attention_us_p10_p50_p90"],
+        "bound": r["bound"],
+        "frac": r["frac"],
+        "hbm_frac": r["hbm_frac"],
+        "mfma_frac": r["mfma_frac"],
+        "attention_gbs": r["attention_gbs"],
+        "attention_tflops": r["attention_tflops"],
+        "arithmetic_intensity": r["arithmetic_intensity"],
+        "accept_gbs": res["accept_gbs"],
+        "mean_accept_len": res["mean_accept_len"],
+        "released_blocks": res["released_blocks"],
+        "nodes": res["config"]["tree_nodes_total"],
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="medusa_long", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--replays", type=int, default=10, help="timed replays for the p10/p50/p90")
+    ap.add_argument("--rotate-mb", type=float, default=600.0,
+                    help="rotate input copies until this many MB are in play (defeats the MALL)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle CPU work")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", action="store_true", help="the headline workload only (no per_config)")
+    ap.add_argument("--deep", action="store_true", help="also ddtree_deep in per_config")
+    ap.add_argument("--eager-only", action="store_true",
+                    help="host-launched steps of the headline only, no graphs (for counter collection)")
+    ap.add_argument("--copy-reference", type=float, default=0.0, metavar="MB",
+                    help="instead of the path, run K device-to-device copies of MB megabytes "
+                         "(the reference kernel for scaling the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU (asked for --gpus {args.gpus}); the verification path "
+              f"runs on a single GPU and has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import token_tree_attention_amd as tta
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_reference > 0:
+        copy_reference(args, dev)
+        return
+    tta.load_library()
+    if args.eager_only:
+        eager_only(args, dev)
+        return
+
+    names = [args.workload] if args.only else list(PER_CONFIG) + (["ddtree_deep"] if args.deep else [])
+    if args.workload not in names:
+        names.append(args.workload)
+    results = {}
+    head_wl = None
+    for name in names:
+        t0 = time.perf_counter()
+        wl = synth.make_workload(WORKLOADS[name], args.seed)
+        t1 = time.perf_counter()
+        results[name] = measure(wl, args, dev)
+        print(f"[bench] {name}: inputs {t1 - t0:.1f} s, timing {time.perf_counter() - t1:.1f} s, "
+              f"{results[name]['us_per_step']:.1f} us/step", file=sys.stderr, flush=True)
+        if name == args.workload:
+            head_wl = wl
+        else:
+            del wl
+    head = results[args.workload]
     result = {
         "metric": METRIC,
-        "value": wl.total_nodes / (ms_step * 1e-3),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "us_per_step": ms_step * 1e3,
-        "eager_us_per_step": eager_ms * 1e3,
+        "ms_per_step": head["ms_per_step"],
+        "us_per_step": head["us_per_step"],
+        "us_per_step_p10_p50_p90": head["us_per_step_p10_p50_p90"],
+        "eager_us_per_step": head["eager_us_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": describe(wl),
-        "roofline": roofline_entry(wl, attn_bytes, flops, attn_ms),
-        "accept_len_hist": np.bincount(acc_len).tolist(),
-        "input_sets_rotated": n_sets,
-        "timing": timing,
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "calls_us": head["calls_us"],
+        "accept_len_hist": head["accept_len_hist"],
+        "released_blocks": head["released_blocks"],
+        "input_sets_rotated": head["input_sets_rotated"],
+        "timing": "K steps in one HIP graph replay (after two untimed replays); p10/p50/p90 over "
+                  f"{head['replays']} replays",
+        "per_config": {name: summary(r) for name, r in results.items()},
+        "achievable_bandwidth": achievable_bandwidth(dev),
     }
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(head_wl, args.cpu_budget)
     print(json.dumps(result))
+
+
+def eager_only(args, dev):
+    """Host-launched steps of one workload (the counter runs need no graphs)."""
+    import torch
+
+    import synth
+    import token_tree_attention_amd as tta
+    from synth.device import to_device
+    from token_tree_attention_amd.step import VerifyStep
+
+    wl = synth.make_workload(WORKLOADS[args.workload], args.seed)
+    d = to_device(wl, dev)
+    bt = tta.Batch(d["node_offsets"], d["ctx_lens"], wl.n_max, total_nodes=wl.total_nodes)
+    cache = tta.KVCache(d["k_cache"], d["v_cache"], d["block_table"])
+    st = VerifyStep(bt, cache, wl.n_heads, wl.vocab, max_accept=64)
+    table = None if d["block_table"] is None else d["block_table"].clone()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for k in range(args.warmup + args.steps):
+        if k == args.warmup:
+            torch.cuda.synchronize()
+            e0.record()
+        if table is not None:
+            d["block_table"].copy_(table)
+        st.run(d["parents"], d["tokens"], d["q"], d["k_new"], d["v_new"], d["logits"])
+    e1.record()
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": wl.name, "eager_us_per_step": e0.elapsed_time(e1) / args.steps * 1e3,
+                      "steps": args.steps}))
 
 
 if __name__ == "__main__":

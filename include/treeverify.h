@@ -182,8 +182,14 @@ TTV_API size_t tree_attention_workspace_bytes(const ttv_batch* bt, const ttv_kv_
  *      rope_base > 0; softmax_scale 0 means 1/sqrt(D)
  * out: out     bf16 [T, n_heads, D]
  *      workspace  device, >= tree_attention_workspace_bytes(), 256-byte aligned
- *      err     OR-ed: TTV_ERR_CAPACITY, TTV_ERR_BLOCK_TABLE, _TOO_MANY_NODES
- * Supported: D in {64, 128}; n_heads % n_kv_heads == 0; n_max <= 1024.
+ *      err     OR-ed: TTV_ERR_CAPACITY, TTV_ERR_BLOCK_TABLE, _TOO_MANY_NODES.
+ *              Should the device-side work plan ever exceed the workspace's
+ *              bounds, nothing is computed and every request gets
+ *              TTV_ERR_CAPACITY.
+ * Supported: D in {64, 128}; n_heads % n_kv_heads == 0 with at most 64 query
+ * heads per KV head; n_max <= 1024 for every head ratio; mask_words in
+ * [ceil(n_max / 32), 32]; B <= 4096.  Anything else returns TTV_EINVAL
+ * before any launch, so a rejected call has no device-side effect.
  */
 TTV_API int tree_attention_verify(const ttv_batch* bt, const void* q, const void* k_new,
                                   const void* v_new, const uint32_t* mask, int32_t mask_words,
@@ -240,6 +246,9 @@ TTV_API int tree_greedy_accept(const ttv_batch* bt, const void* logits, int32_t 
  * Paged: logical blocks j in [ceil(new_len/16), ceil((ctx_b + N_b)/16)) are
  * released: their physical ids go to released_blocks[b*max_blocks + k] in
  * logical order, num_released[b] is set, and block_table entries become -1.
+ *
+ * Any n_kv_heads >= 1 and head_dim in {64, 128}: a request's moves run in
+ * rounds of 2048 sixteen-byte pieces until every piece has moved.
  *
  * in : accept_len [B], accepted_nodes [B, max_accept] from tree_greedy_accept
  * out: new_lens int32 [B]; released_blocks int32 [B, max_blocks] and

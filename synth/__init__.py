@@ -6,8 +6,10 @@ none of the verification arithmetic (no masks, depths, positions, RoPE,
 attention, acceptance walk or commit).  The CPU oracle and the GPU path both
 consume what it returns, and neither imports the other.
 
-Every draw comes from ``np.random.default_rng([seed, cfg_id, stream])`` with a
-separate stream per kind of input, so any one input can be regenerated alone.
+Every draw comes from ``np.random.default_rng([seed, cfg_id, stream, ...])``
+with a separate stream per kind of input, so any one input can be regenerated
+alone; the large normal arrays (Q/K/V, caches) are drawn in 2^24-value slabs,
+each seeded by its index, so several threads can draw them.
 
 Workload shapes follow the five verification workloads of the pages' setting:
 
@@ -91,18 +93,37 @@ def _f32_round_up(v: float) -> float:
     return float(f)
 
 
-def _normal_bf16(rng: np.random.Generator, shape, scale: float = 1.0) -> np.ndarray:
-    """bf16 bits of N(0, scale^2) float32 draws, drawn in slabs to bound memory."""
+_SLAB = 1 << 24  # values per independently seeded slab of a normal draw
+
+
+def _normal_bf16(key, shape, scale: float = 1.0) -> np.ndarray:
+    """bf16 bits of N(0, scale^2) float32 draws.
+
+    ``key`` is a list of ints; slab i of 2^24 values comes from
+    ``np.random.default_rng(key + [i])``, so the slabs can be drawn by
+    several threads and the result depends only on the key and the shape.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
     shape = tuple(int(s) for s in shape)
     n = int(np.prod(shape)) if shape else 1
     out = np.empty(n, dtype=np.uint16)
-    slab = 1 << 24
-    for s in range(0, n, slab):
-        e = min(n, s + slab)
-        x = rng.standard_normal(e - s, dtype=np.float32)
+
+    def slab(i):
+        s = i * _SLAB
+        e = min(n, s + _SLAB)
+        x = np.random.default_rng(list(key) + [i]).standard_normal(e - s, dtype=np.float32)
         if scale != 1.0:
             x *= np.float32(scale)
         out[s:e] = bf16_bits_from_f32(x)
+
+    n_slabs = (n + _SLAB - 1) // _SLAB
+    if n_slabs <= 1:
+        for i in range(n_slabs):
+            slab(i)
+    else:
+        with ThreadPoolExecutor(max_workers=min(8, n_slabs)) as ex:
+            list(ex.map(slab, range(n_slabs)))
     return out.reshape(shape)
 
 
@@ -314,23 +335,31 @@ CONFIGS = {
 }
 
 
+def _small_alphabet_tokens(rng: np.random.Generator, parents: np.ndarray, alphabet: int) -> np.ndarray:
+    """Uniform tokens from [0, alphabet): siblings often share a token."""
+    return rng.integers(0, alphabet, size=len(parents)).astype(np.int32)
+
+
 def _tree_for(cfg: dict, rng_tree, rng_tok, vocab, draft_vocab, ddtree_budget):
     kind, arg = cfg["tree"]
+    dup = int(cfg.get("dup_alphabet", 0))  # > 0: sibling tokens drawn from a tiny alphabet
+    tok_of = ((lambda p: _small_alphabet_tokens(rng_tok, p, dup)) if dup > 0
+              else (lambda p: _distinct_sibling_tokens(rng_tok, p, vocab)))
     if kind == "medusa":
         return medusa_tree(arg), medusa_tokens(rng_tok, arg, vocab)
     if kind == "eagle":
         p = eagle_tree(rng_tree, budget=int(arg))
-        return p, _distinct_sibling_tokens(rng_tok, p, vocab)
+        return p, tok_of(p)
     if kind == "random":
         lo, hi = arg
         p = random_tree(rng_tree, int(rng_tree.integers(lo, hi + 1)))
-        return p, _distinct_sibling_tokens(rng_tok, p, vocab)
+        return p, tok_of(p)
     if kind == "ddtree":
         return ddtree_tree(rng_tree, draft_vocab, topk=min(1024, draft_vocab),
                            budget=ddtree_budget, sigma=float(arg))
     if kind == "parents":  # explicit parent list
         p = np.asarray(arg, dtype=np.int32)
-        return p, _distinct_sibling_tokens(rng_tok, p, vocab)
+        return p, tok_of(p)
     raise ValueError(kind)
 
 
@@ -396,7 +425,9 @@ def make_workload(cfg_id: int, seed: int = 0, **over) -> Workload:
 
     ``over`` may replace any CONFIGS field (``batch``, ``ctx``, ``tree``,
     ``heads``, ``vocab``, ``logits``, ``p``, ``layout``) to draw a scaled-down
-    case of the same structure, plus ``ddtree_budget`` and ``spare_slots``.
+    case of the same structure, plus ``ddtree_budget``, ``spare_slots`` and
+    ``dup_alphabet`` (draw non-Medusa node tokens from that many ids, so
+    siblings share tokens; the planted choice is still a child's token).
     """
     ddtree_budget = int(over.pop("ddtree_budget", 1024))
     spare = int(over.pop("spare_slots", 0))
@@ -409,17 +440,17 @@ def make_workload(cfg_id: int, seed: int = 0, **over) -> Workload:
     sizes = np.diff(tb.node_offsets)
     ctx = tb.ctx_lens
 
-    r_qkv = _rng(seed, cfg_id, _S_QKV)
-    q = _normal_bf16(r_qkv, (T, hq, D))
-    k_new = _normal_bf16(r_qkv, (T, hkv, D))
-    v_new = _normal_bf16(r_qkv, (T, hkv, D))
+    qkv = [int(seed), int(cfg_id), _S_QKV]
+    q = _normal_bf16(qkv + [0], (T, hq, D))
+    k_new = _normal_bf16(qkv + [1], (T, hkv, D))
+    v_new = _normal_bf16(qkv + [2], (T, hkv, D))
 
-    r_cache = _rng(seed, cfg_id, _S_CACHE)
+    kv = [int(seed), int(cfg_id), _S_CACHE]
     need = ctx + sizes.astype(np.int32)
     if cfg["layout"] == "contiguous":
         cap = int(-(-(int(need.max(initial=1)) + spare) // BLOCK_SIZE) * BLOCK_SIZE)
-        k_cache = _normal_bf16(r_cache, (B, hkv, cap, D))
-        v_cache = _normal_bf16(r_cache, (B, hkv, cap, D))
+        k_cache = _normal_bf16(kv + [0], (B, hkv, cap, D))
+        v_cache = _normal_bf16(kv + [1], (B, hkv, cap, D))
         block_table = None
     else:
         nblk = [-(-(int(n) + spare) // BLOCK_SIZE) for n in need]
@@ -431,8 +462,8 @@ def make_workload(cfg_id: int, seed: int = 0, **over) -> Workload:
         for b, nb in enumerate(nblk):
             block_table[b, :nb] = perm[off:off + nb]
             off += nb
-        k_cache = _normal_bf16(r_cache, (total, hkv, BLOCK_SIZE, D))
-        v_cache = _normal_bf16(r_cache, (total, hkv, BLOCK_SIZE, D))
+        k_cache = _normal_bf16(kv + [0], (total, hkv, BLOCK_SIZE, D))
+        v_cache = _normal_bf16(kv + [1], (total, hkv, BLOCK_SIZE, D))
         cap = 0
 
     logits, planted = _planted_logits(_rng(seed, cfg_id, _S_LOGITS), _rng(seed, cfg_id, _S_PLANT),

@@ -128,3 +128,84 @@ def test_commit_rejects(lib):
     assert call(_cache(layout=1, bs=16, max_blocks=4, nb=10, table=None)) == tta.TTV_EINVAL
     assert call(_cache(layout=1, bs=16, max_blocks=4, nb=10, table=FAKE), rel=None) == tta.TTV_EINVAL
     assert call(_cache(layout=5)) == tta.TTV_EINVAL
+
+
+def test_attention_rejects_oversized_mask_stride(lib):
+    b = _batch()
+    ok = _cache()
+    ws = lib.tree_attention_workspace_bytes(ctypes.byref(b), ctypes.byref(ok), 8)
+    # a mask row stride above 32 words (1024 nodes) is refused before any launch
+    assert lib.tree_attention_verify(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, 33, FAKE, ctypes.byref(ok), 8,
+                                     10000.0, 0.0, FAKE, FAKE * 16, ws, FAKE, None) == tta.TTV_EINVAL
+
+
+# ---- the Python binding checks shapes before anything reaches the library ----
+
+def _fake_batch(B=2, T=10, n_max=8):
+    from types import SimpleNamespace
+    return SimpleNamespace(batch=B, total_nodes=T, n_max=n_max, mask_words=max(1, (n_max + 31) // 32))
+
+
+def _fake_cache(B=2, hkv=2, D=128, paged=False, table_rows=2):
+    import torch
+    from types import SimpleNamespace
+    k = torch.zeros((B, hkv, 4, D), dtype=torch.bfloat16)
+    return SimpleNamespace(k=k, v=k, n_kv_heads=hkv, head_dim=D,
+                           layout=tta.KV_PAGED if paged else tta.KV_CONTIGUOUS,
+                           block_table=torch.zeros((table_rows, 3), dtype=torch.int32) if paged else None)
+
+
+def _attn_args(T=10, Hq=8, D=128, W=1):
+    import torch
+    bf = dict(dtype=torch.bfloat16)
+    return dict(q=torch.zeros((T, Hq, D), **bf), k_new=torch.zeros((T, 2, 128), **bf),
+                v_new=torch.zeros((T, 2, 128), **bf), mask=torch.zeros((T, W), dtype=torch.int32),
+                positions=torch.zeros(T, dtype=torch.int32), err=torch.zeros(2, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("bad, match", [
+    (dict(q=(10, 8, 64)), "q must be"),          # head_dim differs from the cache's
+    (dict(q=(9, 8, 128)), "q must be"),          # rows differ from T
+    (dict(mask=(9, 1)), "mask must be"),         # mask rows differ from T
+    (dict(mask=(10, 33)), "mask must be"),       # stride over 32 words
+    (dict(out=(10, 8, 64)), "out must have"),    # out smaller than q
+])
+def test_binding_attention_shape_mismatch_raises(lib, bad, match):
+    import torch
+    a = _attn_args()
+    out = None
+    for k, shape in bad.items():
+        t = torch.zeros(shape, dtype=torch.int32 if k == "mask" else torch.bfloat16)
+        if k == "out":
+            out = t
+        else:
+            a[k] = t
+    with pytest.raises(ValueError, match=match):
+        tta.tree_attention_verify(_fake_batch(), a["q"], a["k_new"], a["v_new"], a["mask"], a["positions"],
+                                  _fake_cache(), a["err"], out=out)
+
+
+def test_binding_cache_rows_must_match_batch(lib):
+    a = _attn_args()
+    with pytest.raises(ValueError, match="contiguous cache"):
+        tta.tree_attention_verify(_fake_batch(), a["q"], a["k_new"], a["v_new"], a["mask"], a["positions"],
+                                  _fake_cache(B=3), a["err"])
+    with pytest.raises(ValueError, match="block_table"):
+        tta.tree_attention_verify(_fake_batch(), a["q"], a["k_new"], a["v_new"], a["mask"], a["positions"],
+                                  _fake_cache(paged=True, table_rows=5), a["err"])
+
+
+def test_binding_commit_shapes(lib):
+    import torch
+    z = lambda *s: torch.zeros(s, dtype=torch.int32)
+    with pytest.raises(ValueError, match="accepted_nodes"):
+        tta.tree_kv_commit(_fake_batch(), _fake_cache(), z(2), z(3, 4), z(2))
+    with pytest.raises(ValueError, match="block_table"):
+        tta.tree_kv_commit(_fake_batch(), _fake_cache(paged=True, table_rows=1), z(2), z(2, 4), z(2))
+
+
+def test_binding_refuses_host_tensors(lib):
+    a = _attn_args()
+    with pytest.raises(ValueError, match="ROCm device"):
+        tta.tree_attention_verify(_fake_batch(), a["q"], a["k_new"], a["v_new"], a["mask"], a["positions"],
+                                  _fake_cache(), a["err"])

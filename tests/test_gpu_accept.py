@@ -141,3 +141,26 @@ def test_accept_overflow_flag():
     for b in range(wl.batch):
         if acc["accept_len"][b] == 3:
             assert err[b] & tta.ERR_ACCEPT
+
+
+@pytest.mark.parametrize("n, seed", [(200, 0), (200, 1), (700, 0), (1000, 2)])
+def test_accept_duplicate_sibling_tokens(n, seed):
+    """Sibling tokens drawn from 3 ids, so most nodes share their token with a
+    sibling: the walk must take the lowest-index matching child.  Trees of at
+    most 256 nodes take the one-lane walk, larger ones the parallel walk."""
+    require_gpu()
+    wl = synth.make_workload(2, seed, batch=4, tree=("random", (n, n)), vocab=64, ctx=(4, 9),
+                             p=(0.95, 0.95), dup_alphabet=3)
+    seen = set()
+    dups = 0
+    for b in range(wl.batch):
+        sl = wl.request_nodes(b)
+        for p, t in zip(wl.parents[sl], wl.tokens[sl]):
+            dups += (b, int(p), int(t)) in seen
+            seen.add((b, int(p), int(t)))
+    assert dups > 0
+    say(f"tree_greedy_accept duplicate sibling tokens n={n} seed={seed}")
+    acc, err = run_accept(wl, max_accept=64)
+    assert (err == 0).all(), err
+    ref = check_accept(wl, acc, 64)
+    assert ref["accept_len"].max() >= 2  # the walks do go down the tree

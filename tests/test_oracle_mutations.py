@@ -53,6 +53,30 @@ def test_rope_sign_error_is_caught(monkeypatch):
     assert _fails(PA.test_rope_golden, PA.test_rope_matches_complex_rotation)
 
 
+def test_rope_ignoring_base_is_caught(monkeypatch):
+    orig = A.rope
+    # a rope that always uses the default base passes every base-10000 case,
+    # so only the goldens at bases 16, 100 and 500000 can catch it
+    monkeypatch.setattr(A, "rope", lambda x, pos, base=10000.0: orig(x, pos, 10000.0))
+    assert _fails(PA.test_rope_golden)
+
+
+def test_rope_base_exponent_off_by_two_is_caught(monkeypatch):
+    def rope_wrong_exponent(x, pos, base=10000.0):
+        # inv_freq base^(-m/D) instead of base^(-2m/D)
+        x = np.asarray(x, dtype=np.float64)
+        D = x.shape[-1]
+        inv = float(base) ** (-np.arange(D // 2) / D)
+        ang = np.asarray(pos, dtype=np.float64)[..., None] * inv
+        c, s = np.cos(ang), np.sin(ang)
+        out = np.empty_like(x)
+        out[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+        out[..., 1::2] = x[..., 1::2] * c + x[..., 0::2] * s
+        return out
+    monkeypatch.setattr(A, "rope", rope_wrong_exponent)
+    assert _fails(PA.test_rope_golden)
+
+
 def test_rope_half_split_variant_is_caught(monkeypatch):
     def rope_neox(x, pos, base=10000.0):
         x = np.asarray(x, dtype=np.float64)

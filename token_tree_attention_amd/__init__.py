@@ -194,6 +194,16 @@ class KVCache:
         return 0 if self.block_table is None else int(self.block_table.shape[1])
 
 
+def _check_cache_rows(bt: Batch, cache: "KVCache") -> None:
+    """A contiguous cache holds B requests; a paged block table has B rows."""
+    if cache.layout == KV_CONTIGUOUS:
+        if int(cache.k.shape[0]) != bt.batch:
+            raise ValueError(f"contiguous cache must be [B={bt.batch}, Hkv, capacity, D], "
+                             f"got {tuple(cache.k.shape)}")
+    elif int(cache.block_table.shape[0]) != bt.batch:
+        raise ValueError(f"block_table must have B={bt.batch} rows, got {tuple(cache.block_table.shape)}")
+
+
 def tree_build(bt: Batch, parents, out: Optional[Dict] = None, stream=None) -> Dict:
     """Masks, depths, positions and retrieve indices for every request's tree."""
     torch = _torch()
@@ -226,22 +236,30 @@ def tree_attention_verify(bt: Batch, q, k_new, v_new, mask, positions, cache: KV
     torch = _torch()
     lib = load_library()
     T = bt.total_nodes
-    if q.dim() != 3 or q.shape[0] != T:
-        raise ValueError("q must be [T, n_heads, D]")
+    # Shapes first (they need no device), then dtype / device / layout.
+    if q.dim() != 3 or q.shape[0] != T or q.shape[2] != cache.head_dim:
+        raise ValueError(f"q must be [T={T}, n_heads, D={cache.head_dim}], got {tuple(q.shape)}")
     n_heads = int(q.shape[1])
+    if mask.dim() != 2 or mask.shape[0] != T or not (bt.mask_words <= mask.shape[1] <= MAX_TREE_NODES // 32):
+        raise ValueError(f"mask must be [T={T}, W] with {bt.mask_words} <= W <= {MAX_TREE_NODES // 32}, "
+                         f"got {tuple(mask.shape)}")
+    _check_cache_rows(bt, cache)
+    if out is not None and tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out must have q's shape {tuple(q.shape)}, got {tuple(out.shape)}")
     _dev(q, torch.bfloat16, "q")
     _dev(k_new, torch.bfloat16, "k_new", T * cache.n_kv_heads * cache.head_dim)
     _dev(v_new, torch.bfloat16, "v_new", T * cache.n_kv_heads * cache.head_dim)
     _dev(mask, torch.int32, "mask")
     _dev(positions, torch.int32, "positions", T)
     _dev(err, torch.int32, "err", bt.batch)
-    W = int(mask.shape[1]) if mask.dim() == 2 else bt.mask_words
+    W = int(mask.shape[1])
     if out is None:
         out = torch.empty_like(q)
-    _dev(out, torch.bfloat16, "out", q.numel())
+    _dev(out, torch.bfloat16, "out")
     need = tree_attention_workspace_bytes(bt, cache, n_heads)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, torch.uint8, "workspace")
     st = lib.tree_attention_verify(ctypes.byref(bt._c), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(mask), W,
                                    _ptr(positions), ctypes.byref(cache._c), n_heads, float(rope_base),
                                    float(softmax_scale), _ptr(out), _ptr(workspace), workspace.numel(),
@@ -285,6 +303,8 @@ def tree_greedy_accept(bt: Batch, logits, tokens, retrieve_next_token, retrieve_
     need = tree_greedy_accept_workspace_bytes(bt, vocab)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _dev(workspace, torch.uint8, "workspace")
+    _check_accept_outputs(out, B, int(max_accept), T)
     st = lib.tree_greedy_accept(ctypes.byref(bt._c), _ptr(logits), dt, vocab, _ptr(tokens),
                                 _ptr(retrieve_next_token), _ptr(retrieve_next_sibling), int(max_accept),
                                 _ptr(out["accept_len"]), _ptr(out["accepted_nodes"]), _ptr(out["out_tokens"]),
@@ -294,12 +314,24 @@ def tree_greedy_accept(bt: Batch, logits, tokens, retrieve_next_token, retrieve_
     return out
 
 
+def _check_accept_outputs(out: Dict, B: int, max_accept: int, T: int) -> None:
+    torch = _torch()
+    _dev(out["accept_len"], torch.int32, "accept_len", B)
+    _dev(out["accepted_nodes"], torch.int32, "accepted_nodes", B * max_accept)
+    _dev(out["out_tokens"], torch.int32, "out_tokens", B * (max_accept + 1))
+    if out.get("row_argmax") is not None:
+        _dev(out["row_argmax"], torch.int32, "row_argmax", T + B)
+
+
 def tree_kv_commit(bt: Batch, cache: KVCache, accept_len, accepted_nodes, err,
                    out: Optional[Dict] = None, stream=None) -> Dict:
     """Move the accepted nodes' K/V into place; paged caches also release blocks."""
     torch = _torch()
     lib = load_library()
     B = bt.batch
+    if accepted_nodes.dim() != 2 or accepted_nodes.shape[0] != B:
+        raise ValueError(f"accepted_nodes must be [B={B}, max_accept], got {tuple(accepted_nodes.shape)}")
+    _check_cache_rows(bt, cache)
     _dev(accept_len, torch.int32, "accept_len", B)
     _dev(accepted_nodes, torch.int32, "accepted_nodes")
     max_accept = int(accepted_nodes.shape[1])

@@ -272,8 +272,13 @@ __device__ __attribute__((always_inline)) void build_plan(const int32_t* __restr
     }
     __syncthreads();
     int n_items = s_items[B];
-    // Both bounds hold by construction of chunk_len (see make_layout); stay safe anyway.
-    if (n_items > max_items || s_parts[B] > max_partials) n_items = 0;
+    // Both bounds hold by construction of chunk_len (see make_layout).  Should
+    // either ever trip, nothing runs and every request is flagged, so no
+    // caller reads outputs the call never wrote.
+    if (n_items > max_items || s_parts[B] > max_partials) {
+        n_items = 0;
+        for (int b = tid; b < B; b += kPrepThreads) atomicOr(err + b, TTV_ERR_CAPACITY);
+    }
 
     // Phase 3: item descriptors (request found by binary search on the prefix).
     auto make_item = [&](int x, Item& it) __attribute__((always_inline)) {
@@ -1609,7 +1614,13 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
     const int G = n_heads / cache->n_kv_heads;
     const int64_t tiles256 =
         (int64_t)bt->batch * cache->n_kv_heads * (((int64_t)bt->n_max * G + kTileM - 1) / kTileM);
-    const bool small = tiles256 < num_cus();
+    // 256-row items need the mask rows of up to 256 / G + 2 nodes beside the
+    // 128 KB ring; when those do not fit in 160 KB of LDS (one query head per
+    // KV head with trees over 992 nodes) the 128-row items run instead.
+    constexpr size_t kLdsLimit = 160 * 1024;
+    const bool small = tiles256 < num_cus() || main_lds_bytes<D, 8, kTileM>(G, mask_words) > kLdsLimit;
+    // Checked before anything is launched, so a rejected call has no effect.
+    if (main_lds_bytes<D, 8, kTileMin>(G, mask_words) > kLdsLimit) return TTV_EINVAL;
     const int tile_m = small ? kTileMin : kTileM;
     const int target_items = small ? num_cus() : kTargetItems;
     const int cus = num_cus();
@@ -1632,7 +1643,6 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
         constexpr int kRows = decltype(rows)::value;
         using MC = MainCfg<D, kW, kRows>;
         const size_t lds = main_lds_bytes<D, kW, kRows>(n_heads / cache->n_kv_heads, mask_words);
-        if (lds > 160 * 1024) return TTV_EINVAL;
         auto kern = cv.paged ? attn_main_kernel<D, true, kW, kRows> : attn_main_kernel<D, false, kW, kRows>;
         // one bit per main-kernel variant (head dim, layout, row tile)
         const unsigned bit = 4u << ((D == 128 ? 0 : 4) + (cv.paged ? 0 : 2) + (kRows == kTileM ? 0 : 1));
@@ -1668,7 +1678,7 @@ extern "C" TTV_API int tree_attention_verify(const ttv_batch* bt, const void* q,
                                              int32_t* err, hipStream_t stream) {
     if (!valid_common(bt, cache, n_heads)) return TTV_EINVAL;
     if (!(rope_base > 0.f) || softmax_scale < 0.f) return TTV_EINVAL;
-    if (mask_words < (bt->n_max + 31) / 32) return TTV_EINVAL;
+    if (mask_words < (bt->n_max + 31) / 32 || mask_words > TTV_MAX_TREE_NODES / 32) return TTV_EINVAL;
     if (bt->batch == 0) return TTV_OK;
     if (!bt->node_offsets || !bt->ctx_lens || !cache->k || !cache->v || !err || !workspace)
         return TTV_EINVAL;

@@ -14,8 +14,9 @@
 // the node at depth d has local index i_d >= d (its d ancestors come first),
 // so destination slot ctx+d never equals a later source ctx+i_d' (d' > d),
 // only possibly an earlier one.  The moves run in rounds over increasing
-// depth ranges; each round loads all its rows before a barrier and stores
-// after it, and later rounds only read slots no earlier round writes.
+// (depth, 16-byte piece) ranges, any number of KV heads and head dims; each
+// round loads all its pieces before a barrier and stores after it, and later
+// rounds only read bytes no earlier round writes.
 
 #include "ttv_device.h"
 
@@ -101,12 +102,19 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(
         return;
     }
 
-    // Moves: a unit is (depth d, KV head h, K or V): head_dim bf16 = head_dim/8 pieces.
+    // Moves: a unit is (depth d, KV head h, K or V): head_dim bf16 = head_dim/8
+    // pieces.  The a * pieces_per_depth pieces are taken in increasing
+    // (depth, piece) order, kCommitThreads * kPiecesPerThread per round; a
+    // round loads all its pieces, then a barrier, then stores them.  A round
+    // never stores over a piece a later round still reads: a later round
+    // reads sources ctx + i_d' with d' at least the depths stored so far, and
+    // i_d' >= d' > every destination depth d stored before it (or the same
+    // depth, whose source differs from its destination unless i_d = d, which
+    // is not moved).
     const int pieces_per_row = head_dim / 8;
     const int units_per_depth = n_kv_heads * 2;
-    const int pieces_per_depth = units_per_depth * pieces_per_row;
-    const int depths_per_round =
-        max(1, (kCommitThreads * kPiecesPerThread) / max(1, pieces_per_depth));
+    const int64_t pieces_per_depth = (int64_t)units_per_depth * pieces_per_row;
+    constexpr int kRound = kCommitThreads * kPiecesPerThread;
     const int64_t row_stride = head_dim;  // elements
     auto slot_offset = [&](int slot, int h) -> int64_t {
         if (!paged) return (((int64_t)b * n_kv_heads + h) * capacity + slot) * row_stride;
@@ -114,19 +122,18 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(
         const int blk = s_blk[slot / block_size - ctx / block_size];
         return (((int64_t)blk * n_kv_heads + h) * block_size + slot % block_size) * row_stride;
     };
-    for (int d0 = 0; d0 < a; d0 += depths_per_round) {
-        const int d1 = min(a, d0 + depths_per_round);
-        const int total = (d1 - d0) * pieces_per_depth;
+    const int64_t total = (int64_t)a * pieces_per_depth;
+    for (int64_t p0 = 0; p0 < total; p0 += kRound) {
         ttv_u32x4 held[kPiecesPerThread];
         int64_t dst_off[kPiecesPerThread];
         uint16_t* dst_base[kPiecesPerThread];
 #pragma unroll
         for (int k = 0; k < kPiecesPerThread; ++k) {
             dst_base[k] = nullptr;
-            const int p = tid + k * kCommitThreads;
+            const int64_t p = p0 + tid + k * kCommitThreads;
             if (p < total) {
-                const int d = d0 + p / pieces_per_depth;
-                const int r = p % pieces_per_depth;
+                const int d = (int)(p / pieces_per_depth);
+                const int r = (int)(p % pieces_per_depth);
                 const int unit = r / pieces_per_row;
                 const int piece = r % pieces_per_row;
                 const int h = unit >> 1;
