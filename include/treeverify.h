@@ -234,6 +234,32 @@ TTV_API int tree_greedy_accept(const ttv_batch* bt, const void* logits, int32_t 
                                int32_t* err, hipStream_t stream);
 
 /*
+ * tree_greedy_accept_noalloc -- tree_greedy_accept for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and device error
+ * bits as tree_greedy_accept, without the workspace: the argmax keys go to a
+ * static 4 MiB scratch array the library holds on each device it runs on
+ * until the process ends.  The call allocates and frees nothing.
+ *
+ * Limit: tree_greedy_accept_workspace_bytes(bt, vocab) <= 4 MiB, else
+ * TTV_ENOSPC before any device call (every workload of up to 14144 logits
+ * rows of 32000 or 4100 rows of 151936 needs well under 1 MiB).
+ * Concurrency: every call on one GPU shares that GPU's scratch, so calls that
+ * overlap on one GPU (different streams or host threads without ordering)
+ * race and give undefined results; calls ordered on one stream are safe.
+ * Nothing in the scratch needs clearing between calls: each call writes
+ * every key its walk reads.
+ */
+TTV_API int tree_greedy_accept_noalloc(const ttv_batch* bt, const void* logits,
+                                       int32_t logits_dtype, int64_t vocab,
+                                       const int32_t* tokens,
+                                       const int32_t* retrieve_next_token,
+                                       const int32_t* retrieve_next_sibling,
+                                       int32_t max_accept, int32_t* accept_len,
+                                       int32_t* accepted_nodes, int32_t* out_tokens,
+                                       int32_t* row_argmax, int32_t* err, hipStream_t stream);
+
+/*
  * tree_kv_commit -- commit the accepted path and roll back the rest
  * ([GLOSSARY] "Tree/Self Speculation": cache [10,11] + accepted [4,7] ->
  * [10,11,4,7]; [ESSAY] KV cache section; [ATLAS] §4 after acceptance).

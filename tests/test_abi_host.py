@@ -209,3 +209,16 @@ def test_binding_refuses_host_tensors(lib):
     with pytest.raises(ValueError, match="ROCm device"):
         tta.tree_attention_verify(_fake_batch(), a["q"], a["k_new"], a["v_new"], a["mask"], a["positions"],
                                   _fake_cache(), a["err"])
+
+
+def test_accept_noalloc_rejects_beyond_its_scratch(lib):
+    # 1000 requests of up to 1024 nodes: (T + B) keys of 8 bytes exceed the 4 MiB scratch
+    big = _batch(B=1000, n_max=1024, T=1000 * 1024)
+    assert lib.tree_greedy_accept_workspace_bytes(ctypes.byref(big), 32000) > (4 << 20)
+    assert lib.tree_greedy_accept_noalloc(ctypes.byref(big), FAKE, 1, 32000, FAKE, FAKE, FAKE, 16,
+                                          FAKE, FAKE, FAKE, None, FAKE, None) == tta.TTV_ENOSPC
+    b = _batch()
+    assert lib.tree_greedy_accept_noalloc(ctypes.byref(b), FAKE, 7, 32000, FAKE, FAKE, FAKE, 16,
+                                          FAKE, FAKE, FAKE, None, FAKE, None) == tta.TTV_EINVAL
+    assert lib.tree_greedy_accept_noalloc(ctypes.byref(b), None, 1, 32000, FAKE, FAKE, FAKE, 16,
+                                          FAKE, FAKE, FAKE, None, FAKE, None) == tta.TTV_EINVAL

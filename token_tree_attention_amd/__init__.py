@@ -26,8 +26,8 @@ from typing import Dict, Optional
 __all__ = [
     "Batch", "KVCache", "library_path", "load_library", "ttv_version", "ttv_status_string",
     "tree_build", "tree_attention_workspace_bytes", "tree_attention_verify",
-    "tree_greedy_accept_workspace_bytes", "tree_greedy_accept", "tree_kv_commit",
-    "TTV_OK", "TTV_EINVAL", "TTV_EHIP", "TTV_ENOSPC", "ERR_BAD_PARENT", "ERR_TOO_MANY_NODES",
+    "tree_greedy_accept_workspace_bytes", "tree_greedy_accept", "tree_greedy_accept_noalloc",
+    "tree_kv_commit", "TTV_OK", "TTV_EINVAL", "TTV_EHIP", "TTV_ENOSPC", "ERR_BAD_PARENT", "ERR_TOO_MANY_NODES",
     "ERR_CAPACITY", "ERR_BLOCK_TABLE", "ERR_ACCEPT", "ERR_BAD_LENGTH", "MAX_TREE_NODES",
     "BLOCK_SIZE", "EXPORTED_SYMBOLS",
 ]
@@ -43,7 +43,7 @@ KV_CONTIGUOUS, KV_PAGED = 0, 1
 EXPORTED_SYMBOLS = (
     "ttv_version", "ttv_status_string", "tree_build", "tree_attention_workspace_bytes",
     "tree_attention_verify", "tree_greedy_accept_workspace_bytes", "tree_greedy_accept",
-    "tree_kv_commit",
+    "tree_greedy_accept_noalloc", "tree_kv_commit",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +93,8 @@ def load_library() -> ctypes.CDLL:
     lib.tree_greedy_accept_workspace_bytes.argtypes = [BP, I64]
     lib.tree_greedy_accept.restype = ctypes.c_int
     lib.tree_greedy_accept.argtypes = [BP, P, I32, I64, P, P, P, I32, P, P, P, P, P, SZ, P, P]
+    lib.tree_greedy_accept_noalloc.restype = ctypes.c_int
+    lib.tree_greedy_accept_noalloc.argtypes = [BP, P, I32, I64, P, P, P, I32, P, P, P, P, P, P]
     lib.tree_kv_commit.restype = ctypes.c_int
     lib.tree_kv_commit.argtypes = [BP, CP, P, P, I32, P, P, P, P, P]
     _LIB = lib
@@ -311,6 +313,37 @@ def tree_greedy_accept(bt: Batch, logits, tokens, retrieve_next_token, retrieve_
                                 _ptr(out.get("row_argmax")), _ptr(workspace), workspace.numel(), _ptr(err),
                                 _stream(stream))
     _check(st, "tree_greedy_accept")
+    return out
+
+
+def tree_greedy_accept_noalloc(bt: Batch, logits, tokens, retrieve_next_token, retrieve_next_sibling,
+                               max_accept: int, err, out: Dict, stream=None) -> Dict:
+    """tree_greedy_accept without a workspace (the library's static device
+    scratch holds the argmax keys); ``out`` must be preallocated, since this
+    entry point exists for callers that cannot allocate."""
+    torch = _torch()
+    lib = load_library()
+    T, B = bt.total_nodes, bt.batch
+    if logits.dim() != 2 or logits.shape[0] != T + B:
+        raise ValueError("logits must be [T + B, vocab]")
+    if logits.dtype == torch.float32:
+        dt = DTYPE_FP32
+    elif logits.dtype == torch.bfloat16:
+        dt = DTYPE_BF16
+    else:
+        raise TypeError("logits must be float32 or bfloat16")
+    _dev(logits, logits.dtype, "logits")
+    _dev(tokens, torch.int32, "tokens", T)
+    _dev(retrieve_next_token, torch.int32, "retrieve_next_token", T)
+    _dev(retrieve_next_sibling, torch.int32, "retrieve_next_sibling", T)
+    _dev(err, torch.int32, "err", B)
+    _check_accept_outputs(out, B, int(max_accept), T)
+    st = lib.tree_greedy_accept_noalloc(ctypes.byref(bt._c), _ptr(logits), dt, int(logits.shape[1]), _ptr(tokens),
+                                        _ptr(retrieve_next_token), _ptr(retrieve_next_sibling), int(max_accept),
+                                        _ptr(out["accept_len"]), _ptr(out["accepted_nodes"]),
+                                        _ptr(out["out_tokens"]), _ptr(out.get("row_argmax")), _ptr(err),
+                                        _stream(stream))
+    _check(st, "tree_greedy_accept_noalloc")
     return out
 
 

@@ -17,7 +17,16 @@
 // node's parent from the links (pointer jumping) and walks with all threads
 // searching a depth's children at once.
 
+#include <atomic>
+
 #include "ttv_device.h"
+
+// Argmax-key scratch of tree_greedy_accept_noalloc: one 64-bit key per
+// (logits row, vocab chunk), 4 MiB per device, held until the process ends.
+// Host code never uses this name as an address: it takes the device address
+// with hipGetSymbolAddress once per device (scratch_of_current_device).
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) uint64_t scratch[kNoAllocScratchBytes / sizeof(uint64_t)];
 
 namespace {
 
@@ -320,6 +329,73 @@ __global__ __launch_bounds__(kWalkThreads) void greedy_walk_kernel(
             k < a ? s_tok[s_path[k]] : (k == a ? target : -1);
 }
 
+// The scratch array's device address on each device, taken once per device
+// with that device current (the array's name is only a host-side stand-in).
+constexpr int kMaxDevices = 64;
+std::atomic<uint64_t*> g_scratch[kMaxDevices];
+
+int scratch_of_current_device(uint64_t** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TTV_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return TTV_EINVAL;
+    uint64_t* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void* addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return TTV_EHIP;
+        p = (uint64_t*)addr;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return TTV_OK;
+}
+
+int check_accept_args(const ttv_batch* bt, int32_t logits_dtype, int64_t vocab, int32_t max_accept) {
+    if (!bt || bt->batch < 0 || bt->n_max < 0 || bt->n_max > TTV_MAX_TREE_NODES ||
+        bt->total_nodes < 0 || bt->total_nodes > (int64_t)bt->batch * bt->n_max)
+        return TTV_EINVAL;
+    if (logits_dtype != TTV_DTYPE_FP32 && logits_dtype != TTV_DTYPE_BF16) return TTV_EINVAL;
+    if (vocab <= 0 || vocab >= (1ll << 31) || max_accept < 1 || max_accept > TTV_MAX_TREE_NODES)
+        return TTV_EINVAL;
+    return TTV_OK;
+}
+
+int check_accept_pointers(const ttv_batch* bt, const void* logits, const int32_t* tokens,
+                          const int32_t* retrieve_next_token, const int32_t* retrieve_next_sibling,
+                          const int32_t* accept_len, const int32_t* accepted_nodes,
+                          const int32_t* out_tokens, const int32_t* err) {
+    if (!bt->node_offsets || !logits || !accept_len || !accepted_nodes || !out_tokens || !err)
+        return TTV_EINVAL;
+    if (bt->total_nodes > 0 && (!tokens || !retrieve_next_token || !retrieve_next_sibling))
+        return TTV_EINVAL;
+    return TTV_OK;
+}
+
+// The two launches of a greedy accept call, with the argmax keys in `partial`.
+int launch_accept(const ttv_batch* bt, const void* logits, int32_t logits_dtype, int64_t vocab,
+                  const int32_t* tokens, const int32_t* retrieve_next_token,
+                  const int32_t* retrieve_next_sibling, int32_t max_accept, int32_t* accept_len,
+                  int32_t* accepted_nodes, int32_t* out_tokens, int32_t* row_argmax,
+                  uint64_t* partial, int32_t* err, hipStream_t stream) {
+    const int64_t rows = bt->total_nodes + bt->batch;
+    const ChunkPlan p = plan_chunks(rows, vocab);
+    const int64_t grid = rows * p.n_chunks;
+    if (grid > 0x7FFFFFFF) return TTV_EINVAL;
+    if (logits_dtype == TTV_DTYPE_BF16)
+        hipLaunchKernelGGL(row_argmax_partial_kernel<true>, dim3((unsigned)grid),
+                           dim3(kArgmaxThreads), 0, stream, logits, vocab, p.chunk_len, p.n_chunks,
+                           partial);
+    else
+        hipLaunchKernelGGL(row_argmax_partial_kernel<false>, dim3((unsigned)grid),
+                           dim3(kArgmaxThreads), 0, stream, logits, vocab, p.chunk_len, p.n_chunks,
+                           partial);
+    if (hipGetLastError() != hipSuccess) return TTV_EHIP;
+    hipLaunchKernelGGL(greedy_walk_kernel, dim3(bt->batch), dim3(kWalkThreads), 0, stream,
+                       bt->node_offsets, bt->n_max, bt->total_nodes, partial, p.n_chunks, tokens,
+                       retrieve_next_token, retrieve_next_sibling, max_accept, accept_len,
+                       accepted_nodes, out_tokens, row_argmax, err);
+    return hipGetLastError() == hipSuccess ? TTV_OK : TTV_EHIP;
+}
+
 }  // namespace
 
 extern "C" TTV_API size_t tree_greedy_accept_workspace_bytes(const ttv_batch* bt, int64_t vocab) {
@@ -337,37 +413,40 @@ extern "C" TTV_API int tree_greedy_accept(
     const int32_t* retrieve_next_sibling, int32_t max_accept, int32_t* accept_len,
     int32_t* accepted_nodes, int32_t* out_tokens, int32_t* row_argmax, void* workspace,
     size_t workspace_bytes, int32_t* err, hipStream_t stream) {
-    if (!bt || bt->batch < 0 || bt->n_max < 0 || bt->n_max > TTV_MAX_TREE_NODES ||
-        bt->total_nodes < 0 || bt->total_nodes > (int64_t)bt->batch * bt->n_max)
-        return TTV_EINVAL;
-    if (logits_dtype != TTV_DTYPE_FP32 && logits_dtype != TTV_DTYPE_BF16) return TTV_EINVAL;
-    if (vocab <= 0 || vocab >= (1ll << 31) || max_accept < 1 || max_accept > TTV_MAX_TREE_NODES)
-        return TTV_EINVAL;
+    int st = check_accept_args(bt, logits_dtype, vocab, max_accept);
+    if (st != TTV_OK) return st;
     if (bt->batch == 0) return TTV_OK;
-    if (!bt->node_offsets || !logits || !accept_len || !accepted_nodes || !out_tokens || !err ||
-        !workspace)
-        return TTV_EINVAL;
-    if (bt->total_nodes > 0 && (!tokens || !retrieve_next_token || !retrieve_next_sibling))
-        return TTV_EINVAL;
+    st = check_accept_pointers(bt, logits, tokens, retrieve_next_token, retrieve_next_sibling,
+                               accept_len, accepted_nodes, out_tokens, err);
+    if (st != TTV_OK) return st;
+    if (!workspace) return TTV_EINVAL;
     const size_t need = tree_greedy_accept_workspace_bytes(bt, vocab);
     if (workspace_bytes < need) return TTV_ENOSPC;
-    const int64_t rows = bt->total_nodes + bt->batch;
-    const ChunkPlan p = plan_chunks(rows, vocab);
-    const int64_t grid = rows * p.n_chunks;
-    if (grid > 0x7FFFFFFF) return TTV_EINVAL;
-    uint64_t* partial = (uint64_t*)workspace;
-    if (logits_dtype == TTV_DTYPE_BF16)
-        hipLaunchKernelGGL(row_argmax_partial_kernel<true>, dim3((unsigned)grid),
-                           dim3(kArgmaxThreads), 0, stream, logits, vocab, p.chunk_len, p.n_chunks,
-                           partial);
-    else
-        hipLaunchKernelGGL(row_argmax_partial_kernel<false>, dim3((unsigned)grid),
-                           dim3(kArgmaxThreads), 0, stream, logits, vocab, p.chunk_len, p.n_chunks,
-                           partial);
-    if (hipGetLastError() != hipSuccess) return TTV_EHIP;
-    hipLaunchKernelGGL(greedy_walk_kernel, dim3(bt->batch), dim3(kWalkThreads), 0, stream,
-                       bt->node_offsets, bt->n_max, bt->total_nodes, partial, p.n_chunks, tokens,
-                       retrieve_next_token, retrieve_next_sibling, max_accept, accept_len,
-                       accepted_nodes, out_tokens, row_argmax, err);
-    return hipGetLastError() == hipSuccess ? TTV_OK : TTV_EHIP;
+    return launch_accept(bt, logits, logits_dtype, vocab, tokens, retrieve_next_token,
+                         retrieve_next_sibling, max_accept, accept_len, accepted_nodes, out_tokens,
+                         row_argmax, (uint64_t*)workspace, err, stream);
+}
+
+extern "C" TTV_API int tree_greedy_accept_noalloc(
+    const ttv_batch* bt, const void* logits, int32_t logits_dtype, int64_t vocab,
+    const int32_t* tokens, const int32_t* retrieve_next_token,
+    const int32_t* retrieve_next_sibling, int32_t max_accept, int32_t* accept_len,
+    int32_t* accepted_nodes, int32_t* out_tokens, int32_t* row_argmax, int32_t* err,
+    hipStream_t stream) {
+    int st = check_accept_args(bt, logits_dtype, vocab, max_accept);
+    if (st != TTV_OK) return st;
+    // The keys must fit the static scratch: checked before any device call.
+    if (tree_greedy_accept_workspace_bytes(bt, vocab) > kNoAllocScratchBytes) return TTV_ENOSPC;
+    if (bt->batch == 0) return TTV_OK;
+    st = check_accept_pointers(bt, logits, tokens, retrieve_next_token, retrieve_next_sibling,
+                               accept_len, accepted_nodes, out_tokens, err);
+    if (st != TTV_OK) return st;
+    uint64_t* keys = nullptr;
+    st = scratch_of_current_device(&keys);
+    if (st != TTV_OK) return st;
+    // Every key slot the walk reads is written by this call's argmax launch,
+    // so the scratch needs no clearing.
+    return launch_accept(bt, logits, logits_dtype, vocab, tokens, retrieve_next_token,
+                         retrieve_next_sibling, max_accept, accept_len, accepted_nodes, out_tokens,
+                         row_argmax, keys, err, stream);
 }
