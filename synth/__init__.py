@@ -43,6 +43,7 @@ import numpy as np
 __all__ = [
     "CONFIGS", "Workload", "make_workload", "bf16_bits_from_f32", "f32_from_bf16_bits",
     "medusa_tree", "eagle_tree", "random_tree", "ddtree_tree", "BLOCK_SIZE", "make_trees", "TreeBatch",
+    "gumbel_noise", "draft_distributions", "uniforms",
 ]
 
 BLOCK_SIZE = 16
@@ -474,6 +475,39 @@ def make_workload(cfg_id: int, seed: int = 0, **over) -> Workload:
                     tokens=tb.tokens, node_offsets=tb.node_offsets, ctx_lens=ctx, accept_p=tb.accept_p,
                     q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, capacity=cap,
                     block_table=block_table, logits=logits, planted=planted)
+
+
+# --------------------------------------------------------------------------
+# Random inputs of the sampled walks (drawing only)
+# --------------------------------------------------------------------------
+
+_S_GUMBEL, _S_DRAFT, _S_UNIFORM = 8, 9, 10
+
+
+def gumbel_noise(seed: int, cfg_id: int, rows: int, vocab: int) -> np.ndarray:
+    """float32 [rows, vocab] standard Gumbel draws (numpy's Gumbel(0, 1) sampler)."""
+    rng = _rng(seed, cfg_id, _S_GUMBEL)
+    return rng.gumbel(0.0, 1.0, size=(rows, vocab)).astype(np.float32)
+
+
+def draft_distributions(seed: int, cfg_id: int, rows: int, vocab: int, tokens_of_row=None,
+                        boost: float = 0.0) -> np.ndarray:
+    """float32 [rows, vocab] probability vectors (flat Dirichlet draws: normalised
+    exponential variates).  ``tokens_of_row(r)`` may name tokens whose weight is
+    multiplied by (1 + boost), so drafted tokens carry visible draft mass."""
+    rng = _rng(seed, cfg_id, _S_DRAFT)
+    x = rng.exponential(1.0, size=(rows, vocab))
+    if tokens_of_row is not None and boost:
+        for r in range(rows):
+            t = tokens_of_row(r)
+            if len(t):
+                x[r, np.asarray(t, dtype=np.int64)] *= 1.0 + boost
+    return (x / x.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def uniforms(seed: int, cfg_id: int, n: int) -> np.ndarray:
+    """float32 [n] U[0, 1) draws."""
+    return _rng(seed, cfg_id, _S_UNIFORM).random(n, dtype=np.float32)
 
 
 def _planted_logits(r_val, r_plant, parents, tokens, accept_p, vocab, dtype):

@@ -11,8 +11,10 @@ import pytest
 
 import test_oracle_accept_commit as PAC
 import test_oracle_attention as PA
+import test_oracle_sampling as PS
 import test_oracle_tree as PT
 from oracle import accept as AC
+from oracle import sampling as SM
 from oracle import attention as A
 from oracle import commit as CM
 from oracle import tree as T
@@ -141,3 +143,74 @@ def test_commit_off_by_one_slot_is_caught(monkeypatch):
         return k, v, new_lens
     monkeypatch.setattr(CM, "commit_contiguous", commit_shifted)
     assert _fails(PAC.test_verify_tree_example_pin)
+
+
+# ---- sampled walks ----
+
+def test_sampling_without_noise_is_caught(monkeypatch):
+    orig = SM.perturbed_rows
+    monkeypatch.setattr(SM, "perturbed_rows", lambda x, T, g: orig(x, T, np.zeros_like(g)))
+    assert _fails(PS.test_gumbel_max_frequencies_match_softmax, PS.test_hand_computed_row)
+
+
+def test_sampling_ignoring_temperature_is_caught(monkeypatch):
+    orig = SM.perturbed_rows
+    monkeypatch.setattr(SM, "perturbed_rows", lambda x, T, g: orig(x, 1.0, g))
+    assert _fails(PS.test_gumbel_max_frequencies_match_softmax)
+
+
+def test_sampling_dividing_noise_by_temperature_is_caught(monkeypatch):
+    # (x + g) / T samples from softmax(x / T) only when T = 1
+    monkeypatch.setattr(SM, "perturbed_rows",
+                        lambda x, T, g: ((np.asarray(x, np.float32) + np.asarray(g, np.float32)) /
+                                         np.float32(T)).astype(np.float32))
+    assert _fails(PS.test_gumbel_max_frequencies_match_softmax)
+
+
+def _walk_variant(residual=True, ratio_swapped=False):
+    """A copy of the stochastic walk with one step changed."""
+    def walk(rows_f32, T, q_rows, u, g_rows, tokens, parents, max_accept):
+        tokens = [int(t) for t in tokens]
+        parents = [int(p) for p in parents]
+        accepted, cur, row = [], -1, 0
+        r = SM.softmax_f64(rows_f32[0], T)
+        while True:
+            q = np.asarray(q_rows[row], dtype=np.float64)
+            nxt = None
+            for j in [j for j in range(len(parents)) if parents[j] == cur]:
+                x = tokens[j]
+                ok = (u[j] * r[x] < q[x]) if ratio_swapped else (u[j] * q[x] < r[x])
+                if ok:
+                    nxt = j
+                    break
+                if residual:
+                    res = np.maximum(r - q, 0.0)
+                    if res.sum() > 0:
+                        r = res / res.sum()
+            if nxt is None:
+                return dict(accepted=accepted, accepted_tokens=[tokens[j] for j in accepted],
+                            bonus=SM.gumbel_sample(r, g_rows[row]), err=0)
+            accepted.append(nxt)
+            cur, row = nxt, 1 + nxt
+            r = SM.softmax_f64(rows_f32[row], T)
+    return walk
+
+
+def test_stochastic_walk_copy_passes():
+    import test_oracle_sampling as P
+    orig = SM.stochastic_walk
+    try:
+        SM.stochastic_walk = _walk_variant()
+        assert not _fails(P.test_stochastic_hand_computed, P.test_q_equal_p_accepts_first_children)
+    finally:
+        SM.stochastic_walk = orig
+
+
+def test_stochastic_walk_without_residual_is_caught(monkeypatch):
+    monkeypatch.setattr(SM, "stochastic_walk", _walk_variant(residual=False))
+    assert _fails(PS.test_stochastic_hand_computed, lambda: PS.test_stochastic_walk_is_lossless(3))
+
+
+def test_stochastic_walk_with_swapped_ratio_is_caught(monkeypatch):
+    monkeypatch.setattr(SM, "stochastic_walk", _walk_variant(ratio_swapped=True))
+    assert _fails(PS.test_stochastic_hand_computed, PS.test_q_equal_p_accepts_first_children)
