@@ -9,6 +9,11 @@
  *   tree_greedy_accept     vocab argmax per node + greedy walk from the root
  *   tree_kv_commit         move accepted K/V into place, release the rest
  *
+ * and two further acceptance rules over the same tree metadata:
+ *
+ *   tree_sample_accept     the walk with temperature-sampled choices
+ *   tree_stochastic_accept the stochastic min(1, p/q) per-edge walk
+ *
  * Pages that define the operations (cited by title and section):
  *   [GLOSSARY] "Beam Search、约束解码与 Tree/Self Speculation"
  *              (llm-glossary.tokens-kit.com, decoding extensions): sections
@@ -21,6 +26,7 @@
  *              verify flow and KV release.
  *   [DDTREE]   "Accelerating Speculative Decoding with Block Diffusion Draft
  *              Trees" notes: §6 worked example, §7 tree attention and walk.
+ *   [DECODING] "解码：采样、束搜索和推测性解码": "Gumbel Max技巧".
  *
  * Conventions shared by every call
  * --------------------------------
@@ -232,6 +238,76 @@ TTV_API int tree_greedy_accept(const ttv_batch* bt, const void* logits, int32_t 
                                int32_t* accept_len, int32_t* accepted_nodes, int32_t* out_tokens,
                                int32_t* row_argmax, void* workspace, size_t workspace_bytes,
                                int32_t* err, hipStream_t stream);
+
+/*
+ * tree_sample_accept -- the verifier walk with temperature sampling instead of
+ * greedy choices ([DDTREE] §7.2: each step picks a token by the target's own
+ * decoding rule, greedy or temperature sampling, and follows the drafted
+ * child carrying it; §7.3: the result is distributed as plain autoregressive
+ * sampling from the target, so the walk is lossless; [DECODING] "Gumbel Max
+ * 技巧": a sample of softmax(h) is argmax_i (h_i + g_i) with precomputed
+ * Gumbel noise g).
+ *
+ * For every logits row: choice = argmax_v fl32(fl32(x_v * fl32(1 / T)) + g_v),
+ * float32 throughout with one rounding per operation (no fused multiply-add),
+ * lowest v on ties, -0.0 equal to +0.0; then exactly tree_greedy_accept's walk
+ * with these choices.  Same outputs and device error bits as
+ * tree_greedy_accept; row_choice (nullable) gets every row's choice.
+ *
+ * in : temperature  finite, > 0 (1 / T must be finite in float32)
+ *      gumbel       float32 [T + B, vocab], row-major like the logits: the
+ *                   caller's Gumbel(0, 1) draws, one per logit
+ *      workspace    >= tree_greedy_accept_workspace_bytes(bt, vocab)
+ */
+TTV_API int tree_sample_accept(const ttv_batch* bt, const void* logits, int32_t logits_dtype,
+                               int64_t vocab, float temperature, const float* gumbel,
+                               const int32_t* tokens, const int32_t* retrieve_next_token,
+                               const int32_t* retrieve_next_sibling, int32_t max_accept,
+                               int32_t* accept_len, int32_t* accepted_nodes, int32_t* out_tokens,
+                               int32_t* row_choice, void* workspace, size_t workspace_bytes,
+                               int32_t* err, hipStream_t stream);
+
+/* Workspace bytes tree_stochastic_accept needs (host call): fp64 [B, vocab]. */
+TTV_API size_t tree_stochastic_accept_workspace_bytes(const ttv_batch* bt, int64_t vocab);
+
+/*
+ * tree_stochastic_accept -- the stochastic per-edge walk ([ATLAS] §4: from the
+ * root, each child of the current node is accepted or rejected by the
+ * min(1, p/q) rule; an accepted child becomes the current node; when every
+ * child is rejected a correction token is sampled at the current node; at a
+ * leaf the bonus token is sampled from the leaf's p).
+ *
+ * Per request, in float64: p_r = softmax(x_r / T) for a visited logits row
+ * r; the target side starts as p_r; the current node's children are tried in
+ * increasing index order: child j (token t) is accepted iff
+ * u_j * q_r(t) < side(t); a rejection replaces the side by
+ * max(0, side - q_r) / sum(max(0, side - q_r)) (kept as it was if that sum
+ * is 0).  When no child is accepted the last token is
+ * argmax_v (log side_v + g_r,v) over side_v > 0 (lowest v on ties): the
+ * correction, or the bonus at a leaf.
+ *
+ * in : logits        fp32 or bf16 [T + B, vocab], rows as in tree_greedy_accept
+ *      temperature   finite, > 0
+ *      draft_probs   float32 [T + B, vocab]: row r is the draft distribution
+ *                    the children of row r's node were proposed from
+ *      uniforms      float32 [T]: node j's uniform draw in [0, 1)
+ *      gumbel        float32 [T + B, vocab]: Gumbel(0, 1) noise per logit
+ *      tokens, retrieve_next_token, retrieve_next_sibling, max_accept as in
+ *      tree_greedy_accept
+ * out: accept_len, accepted_nodes, out_tokens as in tree_greedy_accept (the
+ *      last token is the correction / bonus; -1 for a flagged request)
+ *      workspace     >= tree_stochastic_accept_workspace_bytes(bt, vocab)
+ *      err           OR-ed: TTV_ERR_ACCEPT if an acceptance would exceed
+ *                    max_accept; TTV_ERR_TOO_MANY_NODES for bad offsets
+ */
+TTV_API int tree_stochastic_accept(const ttv_batch* bt, const void* logits, int32_t logits_dtype,
+                                   int64_t vocab, float temperature, const float* draft_probs,
+                                   const float* uniforms, const float* gumbel,
+                                   const int32_t* tokens, const int32_t* retrieve_next_token,
+                                   const int32_t* retrieve_next_sibling, int32_t max_accept,
+                                   int32_t* accept_len, int32_t* accepted_nodes,
+                                   int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                                   int32_t* err, hipStream_t stream);
 
 /*
  * tree_greedy_accept_noalloc -- tree_greedy_accept for callers that cannot

@@ -222,3 +222,30 @@ def test_accept_noalloc_rejects_beyond_its_scratch(lib):
                                           FAKE, FAKE, FAKE, None, FAKE, None) == tta.TTV_EINVAL
     assert lib.tree_greedy_accept_noalloc(ctypes.byref(b), None, 1, 32000, FAKE, FAKE, FAKE, 16,
                                           FAKE, FAKE, FAKE, None, FAKE, None) == tta.TTV_EINVAL
+
+
+def test_sampled_walks_reject(lib):
+    b = _batch()
+    need = lib.tree_greedy_accept_workspace_bytes(ctypes.byref(b), 1000)
+
+    def sample(T=1.0, gumbel=FAKE, ws_bytes=need):
+        return lib.tree_sample_accept(ctypes.byref(b), FAKE, 1, 1000, T, gumbel, FAKE, FAKE, FAKE, 16, FAKE, FAKE,
+                                      FAKE, None, FAKE, ws_bytes, FAKE, None)
+
+    assert sample(T=0.0) == tta.TTV_EINVAL
+    assert sample(T=-2.0) == tta.TTV_EINVAL
+    assert sample(T=float("inf")) == tta.TTV_EINVAL
+    assert sample(T=1e-45) == tta.TTV_EINVAL        # 1 / T overflows float32
+    assert sample(gumbel=None) == tta.TTV_EINVAL
+    assert sample(ws_bytes=need - 1) == tta.TTV_ENOSPC
+    sneed = lib.tree_stochastic_accept_workspace_bytes(ctypes.byref(b), 1000)
+    assert sneed == 2 * 1000 * 8
+
+    def stoch(T=1.0, q=FAKE, u=FAKE, ws_bytes=sneed):
+        return lib.tree_stochastic_accept(ctypes.byref(b), FAKE, 1, 1000, T, q, u, FAKE, FAKE, FAKE, FAKE, 16,
+                                          FAKE, FAKE, FAKE, FAKE, ws_bytes, FAKE, None)
+
+    assert stoch(T=0.0) == tta.TTV_EINVAL
+    assert stoch(q=None) == tta.TTV_EINVAL
+    assert stoch(u=None) == tta.TTV_EINVAL
+    assert stoch(ws_bytes=sneed - 1) == tta.TTV_ENOSPC

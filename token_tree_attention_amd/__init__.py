@@ -27,6 +27,7 @@ __all__ = [
     "Batch", "KVCache", "library_path", "load_library", "ttv_version", "ttv_status_string",
     "tree_build", "tree_attention_workspace_bytes", "tree_attention_verify",
     "tree_greedy_accept_workspace_bytes", "tree_greedy_accept", "tree_greedy_accept_noalloc",
+    "tree_sample_accept", "tree_stochastic_accept_workspace_bytes", "tree_stochastic_accept",
     "tree_kv_commit", "TTV_OK", "TTV_EINVAL", "TTV_EHIP", "TTV_ENOSPC", "ERR_BAD_PARENT", "ERR_TOO_MANY_NODES",
     "ERR_CAPACITY", "ERR_BLOCK_TABLE", "ERR_ACCEPT", "ERR_BAD_LENGTH", "MAX_TREE_NODES",
     "BLOCK_SIZE", "EXPORTED_SYMBOLS",
@@ -43,7 +44,8 @@ KV_CONTIGUOUS, KV_PAGED = 0, 1
 EXPORTED_SYMBOLS = (
     "ttv_version", "ttv_status_string", "tree_build", "tree_attention_workspace_bytes",
     "tree_attention_verify", "tree_greedy_accept_workspace_bytes", "tree_greedy_accept",
-    "tree_greedy_accept_noalloc", "tree_kv_commit",
+    "tree_greedy_accept_noalloc", "tree_sample_accept", "tree_stochastic_accept_workspace_bytes",
+    "tree_stochastic_accept", "tree_kv_commit",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +97,12 @@ def load_library() -> ctypes.CDLL:
     lib.tree_greedy_accept.argtypes = [BP, P, I32, I64, P, P, P, I32, P, P, P, P, P, SZ, P, P]
     lib.tree_greedy_accept_noalloc.restype = ctypes.c_int
     lib.tree_greedy_accept_noalloc.argtypes = [BP, P, I32, I64, P, P, P, I32, P, P, P, P, P, P]
+    lib.tree_sample_accept.restype = ctypes.c_int
+    lib.tree_sample_accept.argtypes = [BP, P, I32, I64, F32, P, P, P, P, I32, P, P, P, P, P, SZ, P, P]
+    lib.tree_stochastic_accept_workspace_bytes.restype = SZ
+    lib.tree_stochastic_accept_workspace_bytes.argtypes = [BP, I64]
+    lib.tree_stochastic_accept.restype = ctypes.c_int
+    lib.tree_stochastic_accept.argtypes = [BP, P, I32, I64, F32, P, P, P, P, P, P, I32, P, P, P, P, SZ, P, P]
     lib.tree_kv_commit.restype = ctypes.c_int
     lib.tree_kv_commit.argtypes = [BP, CP, P, P, I32, P, P, P, P, P]
     _LIB = lib
@@ -344,6 +352,96 @@ def tree_greedy_accept_noalloc(bt: Batch, logits, tokens, retrieve_next_token, r
                                         _ptr(out["out_tokens"]), _ptr(out.get("row_argmax")), _ptr(err),
                                         _stream(stream))
     _check(st, "tree_greedy_accept_noalloc")
+    return out
+
+
+def _logits_dtype(logits, T: int, B: int) -> int:
+    torch = _torch()
+    if logits.dim() != 2 or logits.shape[0] != T + B:
+        raise ValueError("logits must be [T + B, vocab]")
+    if logits.dtype == torch.float32:
+        return DTYPE_FP32
+    if logits.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError("logits must be float32 or bfloat16")
+
+
+def _accept_outputs(out, B: int, max_accept: int, T: int, dev, want_rows: bool) -> Dict:
+    torch = _torch()
+    if out is None:
+        out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+               "accepted_nodes": torch.empty((B, max_accept), dtype=torch.int32, device=dev),
+               "out_tokens": torch.empty((B, max_accept + 1), dtype=torch.int32, device=dev)}
+        if want_rows:
+            out["row_argmax"] = torch.empty(T + B, dtype=torch.int32, device=dev)
+    return out
+
+
+def tree_sample_accept(bt: Batch, logits, gumbel, temperature: float, tokens, retrieve_next_token,
+                       retrieve_next_sibling, max_accept: int, err, out: Optional[Dict] = None,
+                       workspace=None, want_row_choice: bool = True, stream=None) -> Dict:
+    """The verifier walk with temperature-sampled choices: argmax of logits / T +
+    Gumbel noise per row (``out["row_argmax"]`` holds the choices)."""
+    torch = _torch()
+    lib = load_library()
+    T, B = bt.total_nodes, bt.batch
+    dt = _logits_dtype(logits, T, B)
+    _dev(logits, logits.dtype, "logits")
+    vocab = int(logits.shape[1])
+    _dev(gumbel, torch.float32, "gumbel", (T + B) * vocab)
+    _dev(tokens, torch.int32, "tokens", T)
+    _dev(retrieve_next_token, torch.int32, "retrieve_next_token", T)
+    _dev(retrieve_next_sibling, torch.int32, "retrieve_next_sibling", T)
+    _dev(err, torch.int32, "err", B)
+    out = _accept_outputs(out, B, int(max_accept), T, logits.device, want_row_choice)
+    _check_accept_outputs(out, B, int(max_accept), T)
+    if workspace is None:
+        workspace = torch.empty(max(tree_greedy_accept_workspace_bytes(bt, vocab), 256), dtype=torch.uint8,
+                                device=logits.device)
+    _dev(workspace, torch.uint8, "workspace")
+    st = lib.tree_sample_accept(ctypes.byref(bt._c), _ptr(logits), dt, vocab, float(temperature), _ptr(gumbel),
+                                _ptr(tokens), _ptr(retrieve_next_token), _ptr(retrieve_next_sibling),
+                                int(max_accept), _ptr(out["accept_len"]), _ptr(out["accepted_nodes"]),
+                                _ptr(out["out_tokens"]), _ptr(out.get("row_argmax")), _ptr(workspace),
+                                workspace.numel(), _ptr(err), _stream(stream))
+    _check(st, "tree_sample_accept")
+    return out
+
+
+def tree_stochastic_accept_workspace_bytes(bt: Batch, vocab: int) -> int:
+    return int(load_library().tree_stochastic_accept_workspace_bytes(ctypes.byref(bt._c), int(vocab)))
+
+
+def tree_stochastic_accept(bt: Batch, logits, temperature: float, draft_probs, uniforms, gumbel, tokens,
+                           retrieve_next_token, retrieve_next_sibling, max_accept: int, err,
+                           out: Optional[Dict] = None, workspace=None, stream=None) -> Dict:
+    """The stochastic min(1, p/q) walk: draft_probs [T + B, V] (the draft
+    distribution of each row's children), uniforms [T], gumbel [T + B, V]."""
+    torch = _torch()
+    lib = load_library()
+    T, B = bt.total_nodes, bt.batch
+    dt = _logits_dtype(logits, T, B)
+    _dev(logits, logits.dtype, "logits")
+    vocab = int(logits.shape[1])
+    _dev(draft_probs, torch.float32, "draft_probs", (T + B) * vocab)
+    _dev(uniforms, torch.float32, "uniforms", T)
+    _dev(gumbel, torch.float32, "gumbel", (T + B) * vocab)
+    _dev(tokens, torch.int32, "tokens", T)
+    _dev(retrieve_next_token, torch.int32, "retrieve_next_token", T)
+    _dev(retrieve_next_sibling, torch.int32, "retrieve_next_sibling", T)
+    _dev(err, torch.int32, "err", B)
+    out = _accept_outputs(out, B, int(max_accept), T, logits.device, False)
+    _check_accept_outputs(out, B, int(max_accept), T)
+    if workspace is None:
+        workspace = torch.empty(max(tree_stochastic_accept_workspace_bytes(bt, vocab), 256), dtype=torch.uint8,
+                                device=logits.device)
+    _dev(workspace, torch.uint8, "workspace")
+    st = lib.tree_stochastic_accept(ctypes.byref(bt._c), _ptr(logits), dt, vocab, float(temperature),
+                                    _ptr(draft_probs), _ptr(uniforms), _ptr(gumbel), _ptr(tokens),
+                                    _ptr(retrieve_next_token), _ptr(retrieve_next_sibling), int(max_accept),
+                                    _ptr(out["accept_len"]), _ptr(out["accepted_nodes"]), _ptr(out["out_tokens"]),
+                                    _ptr(workspace), workspace.numel(), _ptr(err), _stream(stream))
+    _check(st, "tree_stochastic_accept")
     return out
 
 

@@ -53,10 +53,20 @@ ChunkPlan plan_chunks(int64_t rows, int64_t vocab) {
     return p;
 }
 
-template <bool kBf16>
+// One row's value at index idx: the logit itself (greedy), or, with noise,
+// fl32(fl32(x * inv_t) + g): the temperature-scaled logit plus that element's
+// Gumbel noise, each operation rounded once (no fused multiply-add), so the
+// sampled choice is the argmax of exactly these float32 values.
+template <bool kNoise>
+__device__ __forceinline__ float choice_value(float x, float g, float inv_t) {
+    if (!kNoise) return x;
+    return __fadd_rn(__fmul_rn(x, inv_t), g);
+}
+
+template <bool kBf16, bool kNoise>
 __global__ __launch_bounds__(kArgmaxThreads) void row_argmax_partial_kernel(
-    const void* __restrict__ logits, int64_t vocab, int64_t chunk_len, int64_t n_chunks,
-    uint64_t* __restrict__ partial) {
+    const void* __restrict__ logits, const float* __restrict__ noise, float inv_t, int64_t vocab,
+    int64_t chunk_len, int64_t n_chunks, uint64_t* __restrict__ partial) {
     __shared__ uint64_t s_red[kArgmaxThreads / TTV_WAVE];
     const int64_t row = blockIdx.x / n_chunks;
     const int64_t chunk = blockIdx.x % n_chunks;
@@ -66,11 +76,13 @@ __global__ __launch_bounds__(kArgmaxThreads) void row_argmax_partial_kernel(
     constexpr int kEpv = kBf16 ? 8 : 4;  // elements per 16-byte vector
     const size_t esize = kBf16 ? 2 : 4;
     const char* row_base = (const char*)logits + (size_t)row * (size_t)vocab * esize;
+    const float* noise_row = kNoise ? noise + (size_t)row * (size_t)vocab : nullptr;
 
     // Start from the thread's first element so an all -inf range still names
     // its lowest index; threads with no element report key 0 (below any value).
     float best = -INFINITY;
-    const bool vec_ok = ((vocab * (int64_t)esize) % 16 == 0) && (((uintptr_t)logits & 15) == 0);
+    const bool vec_ok = ((vocab * (int64_t)esize) % 16 == 0) && (((uintptr_t)logits & 15) == 0) &&
+                        (!kNoise || (vocab % 4 == 0 && ((uintptr_t)noise & 15) == 0));
     uint32_t best_i = 0xFFFFFFFFu;
     {
         const int64_t first = e0 + (int64_t)tid * (vec_ok ? kEpv : 1);
@@ -78,13 +90,20 @@ __global__ __launch_bounds__(kArgmaxThreads) void row_argmax_partial_kernel(
     }
     if (vec_ok) {
         const ttv_u32x4* vbase = (const ttv_u32x4*)row_base;
+        const ttv_u32x4* nbase = (const ttv_u32x4*)noise_row;
+        constexpr int kNv = kNoise ? kEpv / 4 : 0;  // 16-byte noise vectors per logits vector
         const int64_t stride = (int64_t)kArgmaxThreads * kEpv;
         for (int64_t base = e0 + (int64_t)tid * kEpv; base < e1; base += 4 * stride) {
             ttv_u32x4 v[4];
+            ttv_u32x4 nz[4][kNv > 0 ? kNv : 1];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int64_t idx = base + u * stride;
-                if (idx < e1) v[u] = __builtin_nontemporal_load(vbase + idx / kEpv);
+                if (idx < e1) {
+                    v[u] = __builtin_nontemporal_load(vbase + idx / kEpv);
+#pragma unroll
+                    for (int k = 0; k < kNv; ++k) nz[u][k] = __builtin_nontemporal_load(nbase + idx / 4 + k);
+                }
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -93,12 +112,15 @@ __global__ __launch_bounds__(kArgmaxThreads) void row_argmax_partial_kernel(
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
                         if (kBf16) {
-                            const float f0 = ttv_bf16_lo(v[u][w]);
-                            const float f1 = ttv_bf16_hi(v[u][w]);
+                            const float g0 = kNoise ? __uint_as_float(nz[u][w / 2][2 * (w % 2)]) : 0.f;
+                            const float g1 = kNoise ? __uint_as_float(nz[u][w / 2][2 * (w % 2) + 1]) : 0.f;
+                            const float f0 = choice_value<kNoise>(ttv_bf16_lo(v[u][w]), g0, inv_t);
+                            const float f1 = choice_value<kNoise>(ttv_bf16_hi(v[u][w]), g1, inv_t);
                             if (f0 > best) { best = f0; best_i = (uint32_t)(idx + 2 * w); }
                             if (f1 > best) { best = f1; best_i = (uint32_t)(idx + 2 * w + 1); }
                         } else {
-                            const float f = __uint_as_float(v[u][w]);
+                            const float g = kNoise ? __uint_as_float(nz[u][0][w]) : 0.f;
+                            const float f = choice_value<kNoise>(__uint_as_float(v[u][w]), g, inv_t);
                             if (f > best) { best = f; best_i = (uint32_t)(idx + w); }
                         }
                     }
@@ -110,6 +132,7 @@ __global__ __launch_bounds__(kArgmaxThreads) void row_argmax_partial_kernel(
             float f;
             if (kBf16) f = __uint_as_float((uint32_t)((const uint16_t*)row_base)[idx] << 16);
             else f = ((const float*)row_base)[idx];
+            f = choice_value<kNoise>(f, kNoise ? noise_row[idx] : 0.f, inv_t);
             if (f > best) { best = f; best_i = (uint32_t)idx; }
         }
     }
@@ -370,24 +393,30 @@ int check_accept_pointers(const ttv_batch* bt, const void* logits, const int32_t
     return TTV_OK;
 }
 
-// The two launches of a greedy accept call, with the argmax keys in `partial`.
+// The two launches of an accept call, with the argmax keys in `partial`:
+// greedy when noise is null, else the temperature-sampled choice.
 int launch_accept(const ttv_batch* bt, const void* logits, int32_t logits_dtype, int64_t vocab,
-                  const int32_t* tokens, const int32_t* retrieve_next_token,
-                  const int32_t* retrieve_next_sibling, int32_t max_accept, int32_t* accept_len,
-                  int32_t* accepted_nodes, int32_t* out_tokens, int32_t* row_argmax,
-                  uint64_t* partial, int32_t* err, hipStream_t stream) {
+                  const float* noise, float inv_t, const int32_t* tokens,
+                  const int32_t* retrieve_next_token, const int32_t* retrieve_next_sibling,
+                  int32_t max_accept, int32_t* accept_len, int32_t* accepted_nodes,
+                  int32_t* out_tokens, int32_t* row_argmax, uint64_t* partial, int32_t* err,
+                  hipStream_t stream) {
     const int64_t rows = bt->total_nodes + bt->batch;
     const ChunkPlan p = plan_chunks(rows, vocab);
     const int64_t grid = rows * p.n_chunks;
     if (grid > 0x7FFFFFFF) return TTV_EINVAL;
-    if (logits_dtype == TTV_DTYPE_BF16)
-        hipLaunchKernelGGL(row_argmax_partial_kernel<true>, dim3((unsigned)grid),
-                           dim3(kArgmaxThreads), 0, stream, logits, vocab, p.chunk_len, p.n_chunks,
-                           partial);
-    else
-        hipLaunchKernelGGL(row_argmax_partial_kernel<false>, dim3((unsigned)grid),
-                           dim3(kArgmaxThreads), 0, stream, logits, vocab, p.chunk_len, p.n_chunks,
-                           partial);
+    auto argmax = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kArgmaxThreads), 0, stream, logits, noise,
+                           inv_t, vocab, p.chunk_len, p.n_chunks, partial);
+    };
+    const bool bf16 = logits_dtype == TTV_DTYPE_BF16;
+    if (noise) {
+        if (bf16) argmax(row_argmax_partial_kernel<true, true>);
+        else argmax(row_argmax_partial_kernel<false, true>);
+    } else {
+        if (bf16) argmax(row_argmax_partial_kernel<true, false>);
+        else argmax(row_argmax_partial_kernel<false, false>);
+    }
     if (hipGetLastError() != hipSuccess) return TTV_EHIP;
     hipLaunchKernelGGL(greedy_walk_kernel, dim3(bt->batch), dim3(kWalkThreads), 0, stream,
                        bt->node_offsets, bt->n_max, bt->total_nodes, partial, p.n_chunks, tokens,
@@ -422,9 +451,9 @@ extern "C" TTV_API int tree_greedy_accept(
     if (!workspace) return TTV_EINVAL;
     const size_t need = tree_greedy_accept_workspace_bytes(bt, vocab);
     if (workspace_bytes < need) return TTV_ENOSPC;
-    return launch_accept(bt, logits, logits_dtype, vocab, tokens, retrieve_next_token,
-                         retrieve_next_sibling, max_accept, accept_len, accepted_nodes, out_tokens,
-                         row_argmax, (uint64_t*)workspace, err, stream);
+    return launch_accept(bt, logits, logits_dtype, vocab, nullptr, 1.0f, tokens,
+                         retrieve_next_token, retrieve_next_sibling, max_accept, accept_len,
+                         accepted_nodes, out_tokens, row_argmax, (uint64_t*)workspace, err, stream);
 }
 
 extern "C" TTV_API int tree_greedy_accept_noalloc(
@@ -446,7 +475,29 @@ extern "C" TTV_API int tree_greedy_accept_noalloc(
     if (st != TTV_OK) return st;
     // Every key slot the walk reads is written by this call's argmax launch,
     // so the scratch needs no clearing.
-    return launch_accept(bt, logits, logits_dtype, vocab, tokens, retrieve_next_token,
-                         retrieve_next_sibling, max_accept, accept_len, accepted_nodes, out_tokens,
-                         row_argmax, keys, err, stream);
+    return launch_accept(bt, logits, logits_dtype, vocab, nullptr, 1.0f, tokens,
+                         retrieve_next_token, retrieve_next_sibling, max_accept, accept_len,
+                         accepted_nodes, out_tokens, row_argmax, keys, err, stream);
+}
+
+extern "C" TTV_API int tree_sample_accept(
+    const ttv_batch* bt, const void* logits, int32_t logits_dtype, int64_t vocab,
+    float temperature, const float* gumbel, const int32_t* tokens,
+    const int32_t* retrieve_next_token, const int32_t* retrieve_next_sibling, int32_t max_accept,
+    int32_t* accept_len, int32_t* accepted_nodes, int32_t* out_tokens, int32_t* row_choice,
+    void* workspace, size_t workspace_bytes, int32_t* err, hipStream_t stream) {
+    int st = check_accept_args(bt, logits_dtype, vocab, max_accept);
+    if (st != TTV_OK) return st;
+    if (!(temperature > 0.f) || !(temperature < INFINITY)) return TTV_EINVAL;
+    const float inv_t = 1.0f / temperature;  // fl32(1 / T): the float32 scale of every logit
+    if (!(inv_t < INFINITY)) return TTV_EINVAL;
+    if (bt->batch == 0) return TTV_OK;
+    st = check_accept_pointers(bt, logits, tokens, retrieve_next_token, retrieve_next_sibling,
+                               accept_len, accepted_nodes, out_tokens, err);
+    if (st != TTV_OK) return st;
+    if (!gumbel || !workspace) return TTV_EINVAL;
+    if (tree_greedy_accept_workspace_bytes(bt, vocab) > workspace_bytes) return TTV_ENOSPC;
+    return launch_accept(bt, logits, logits_dtype, vocab, gumbel, inv_t, tokens,
+                         retrieve_next_token, retrieve_next_sibling, max_accept, accept_len,
+                         accepted_nodes, out_tokens, row_choice, (uint64_t*)workspace, err, stream);
 }

@@ -1,0 +1,248 @@
+// tree_stochastic_accept: the stochastic per-edge acceptance walk.
+//
+// "02 · Token Tree 与 Tree Attention" §4: one target pass gives every node a
+// distribution p; from the root each child of the current node is accepted
+// or rejected by the min(1, p/q) rule (speculative sampling's: a draft token
+// x proposed from q is kept with probability min(1, p(x)/q(x)), and after a
+// rejection the target side continues from the residual norm(max(0, p - q)));
+// an accepted child becomes the current node; when every child is rejected a
+// correction token is sampled at the current node and the walk ends; at a
+// leaf the bonus token is sampled from the leaf's p.
+//
+// Choices made where the page is open: siblings are tried in increasing
+// index order, each rejection replacing the target side by the residual; p
+// of a row is softmax(logits / T) in float64; node j's accept test is
+// u_j * q(x_j) < r(x_j) in float64 (u_j the caller's uniform draw for node j,
+// q the draft distribution the children of the current node came from, r the
+// current target side); the correction / bonus is the Gumbel-max sample
+// argmax_v (log r_v + g_v) over r_v > 0 with the caller's noise g of that row.
+//
+// One workgroup per request walks the tree; each step that needs the whole
+// distribution (a visited row's softmax, a residual, the final sample) is a
+// pass of the workgroup over the vocab with fp64 block reductions.  The
+// current target side is kept as r_v = buf[v] / den: the row's exp values and
+// their sum right after a visit, the unnormalised residual and its sum after
+// a rejection (buf in the caller's workspace, fp64 [B, vocab]); r_v is formed
+// by that one division wherever it is used, as in p = e / sum(e) and
+// r = res / sum(res).
+
+#include "ttv_device.h"
+
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / TTV_WAVE;
+
+__device__ __forceinline__ double shfl_xor_f64(double v, int off) {
+    const uint64_t u = __double_as_longlong(v);
+    const uint32_t lo = __shfl_xor((uint32_t)u, off, TTV_WAVE);
+    const uint32_t hi = __shfl_xor((uint32_t)(u >> 32), off, TTV_WAVE);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+template <bool kMax>
+__device__ double block_reduce(double v, double* s_red) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const double o = shfl_xor_f64(v, off);
+        v = kMax ? fmax(v, o) : v + o;
+    }
+    const int tid = threadIdx.x;
+    __syncthreads();  // s_red may still be read by the previous reduction
+    if ((tid & (TTV_WAVE - 1)) == 0) s_red[tid / TTV_WAVE] = v;
+    __syncthreads();
+    double r = s_red[0];
+    for (int w = 1; w < kWaves; ++w) r = kMax ? fmax(r, s_red[w]) : r + s_red[w];
+    return r;
+}
+
+// (score, index) maximum, lowest index on equal scores.
+__device__ int block_argmax(double v, int idx, double* s_val, int* s_idx) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const double ov = shfl_xor_f64(v, off);
+        const int oi = __shfl_xor(idx, off, TTV_WAVE);
+        if (ov > v || (ov == v && oi < idx)) {
+            v = ov;
+            idx = oi;
+        }
+    }
+    const int tid = threadIdx.x;
+    __syncthreads();
+    if ((tid & (TTV_WAVE - 1)) == 0) {
+        s_val[tid / TTV_WAVE] = v;
+        s_idx[tid / TTV_WAVE] = idx;
+    }
+    __syncthreads();
+    double bv = s_val[0];
+    int bi = s_idx[0];
+    for (int w = 1; w < kWaves; ++w)
+        if (s_val[w] > bv || (s_val[w] == bv && s_idx[w] < bi)) {
+            bv = s_val[w];
+            bi = s_idx[w];
+        }
+    return bi;
+}
+
+template <bool kBf16>
+__device__ __forceinline__ double logit_at(const void* logits, int64_t row, int64_t vocab, int64_t v) {
+    if (kBf16) return (double)__uint_as_float((uint32_t)((const uint16_t*)logits)[row * vocab + v] << 16);
+    return (double)((const float*)logits)[row * vocab + v];
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(kThreads) void stochastic_walk_kernel(
+    const int32_t* __restrict__ node_offsets, int32_t n_max, int64_t total_nodes,
+    const void* __restrict__ logits, int64_t vocab, double temperature,
+    const float* __restrict__ draft_probs, const float* __restrict__ uniforms,
+    const float* __restrict__ gumbel, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ next_token, const int32_t* __restrict__ next_sibling,
+    int32_t max_accept, int32_t* __restrict__ accept_len, int32_t* __restrict__ accepted_nodes,
+    int32_t* __restrict__ out_tokens, double* __restrict__ work, int32_t* __restrict__ err) {
+    __shared__ int32_t s_path[TTV_MAX_TREE_NODES + 1];
+    __shared__ double s_red[kWaves];
+    __shared__ int32_t s_ired[kWaves];
+
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int s = node_offsets[b];
+    const int n = node_offsets[b + 1] - s;
+    if (s < 0 || n < 0 || n > n_max || (int64_t)s + n > total_nodes) {  // uniform
+        if (tid == 0) {
+            accept_len[b] = 0;
+            atomicOr(err + b, TTV_ERR_TOO_MANY_NODES);
+        }
+        return;
+    }
+    double* buf = work + (int64_t)b * vocab;
+    const int64_t row0 = (int64_t)s + b;  // the request's root row
+
+    // Visit a row: buf = exp((x - max) / T), den = their sum.
+    auto visit = [&](int64_t row) -> double {
+        double m = -INFINITY;
+        for (int64_t v = tid; v < vocab; v += kThreads) m = fmax(m, logit_at<kBf16>(logits, row, vocab, v));
+        m = block_reduce<true>(m, s_red);
+        double sum = 0.0;
+        for (int64_t v = tid; v < vocab; v += kThreads) {
+            const double e = exp((logit_at<kBf16>(logits, row, vocab, v) - m) / temperature);
+            buf[v] = e;
+            sum += e;
+        }
+        __syncthreads();  // buf written before any thread reads another's entry
+        return block_reduce<false>(sum, s_red);
+    };
+
+    int a = 0, flags = 0, final_token = -1;
+    int cur = -1;
+    int64_t row = row0;
+    double den = visit(row);
+    for (;;) {
+        // children of the current node, lowest index first
+        int j = cur < 0 ? (n > 0 ? 0 : -1) : next_token[s + cur];
+        if (j >= 0 && (j <= cur || j >= n)) j = -1;
+        const float* q = draft_probs + row * vocab;
+        int accepted = -1;
+        while (j >= 0) {
+            const int x = tokens[s + j];
+            const double r_x = (x >= 0 && x < vocab) ? buf[x] / den : 0.0;
+            const double qx = (x >= 0 && x < vocab) ? (double)q[x] : 0.0;
+            const bool take = (double)uniforms[s + j] * qx < r_x;
+            __syncthreads();  // every thread has read buf[x] before the residual rewrites it
+            if (take) {
+                accepted = j;
+                break;
+            }
+            // rejected: the target side becomes norm(max(0, r - q)); left as it
+            // was when nothing remains above q (r == q up to rounding)
+            double z = 0.0;
+            for (int64_t v = tid; v < vocab; v += kThreads) z += fmax(buf[v] / den - (double)q[v], 0.0);
+            z = block_reduce<false>(z, s_red);
+            if (z > 0.0) {
+                for (int64_t v = tid; v < vocab; v += kThreads) buf[v] = fmax(buf[v] / den - (double)q[v], 0.0);
+                den = z;
+                __syncthreads();
+            }
+            const int nx = next_sibling[s + j];
+            j = (nx > j && nx < n) ? nx : -1;
+        }
+        if (accepted < 0) {
+            // correction / bonus: Gumbel-max sample of the current side
+            const float* g = gumbel + row * vocab;
+            double best = -INFINITY;
+            int best_i = 0x7FFFFFFF;
+            for (int64_t v = tid; v < vocab; v += kThreads) {
+                const double r = buf[v] / den;
+                if (r > 0.0) {
+                    const double sc = log(r) + (double)g[v];
+                    if (sc > best) {  // v increases per thread: the first maximum is the lowest index
+                        best = sc;
+                        best_i = (int)v;
+                    }
+                }
+            }
+            final_token = block_argmax(best, best_i, s_red, s_ired);
+            if (final_token == 0x7FFFFFFF) final_token = -1;
+            break;
+        }
+        if (a == max_accept) {
+            flags |= TTV_ERR_ACCEPT;
+            break;
+        }
+        if (tid == 0) s_path[a] = accepted;
+        ++a;
+        cur = accepted;
+        row = row0 + 1 + accepted;
+        __syncthreads();  // every thread has read buf before the next visit rewrites it
+        den = visit(row);
+    }
+    if (tid == 0) {
+        accept_len[b] = a;
+        if (flags) atomicOr(err + b, flags);
+    }
+    __syncthreads();  // s_path, written by thread 0
+    for (int k = tid; k < max_accept; k += kThreads)
+        accepted_nodes[(int64_t)b * max_accept + k] = k < a ? s_path[k] : -1;
+    for (int k = tid; k <= max_accept; k += kThreads)
+        out_tokens[(int64_t)b * (max_accept + 1) + k] =
+            k < a ? tokens[s + s_path[k]] : (k == a ? final_token : -1);
+}
+
+}  // namespace
+
+extern "C" TTV_API size_t tree_stochastic_accept_workspace_bytes(const ttv_batch* bt, int64_t vocab) {
+    if (!bt || bt->batch < 0 || vocab <= 0 || vocab >= (1ll << 31)) return 0;
+    const size_t bytes = (size_t)bt->batch * (size_t)vocab * sizeof(double);
+    return bytes > 0 ? bytes : 256;
+}
+
+extern "C" TTV_API int tree_stochastic_accept(
+    const ttv_batch* bt, const void* logits, int32_t logits_dtype, int64_t vocab, float temperature,
+    const float* draft_probs, const float* uniforms, const float* gumbel, const int32_t* tokens,
+    const int32_t* retrieve_next_token, const int32_t* retrieve_next_sibling, int32_t max_accept,
+    int32_t* accept_len, int32_t* accepted_nodes, int32_t* out_tokens, void* workspace,
+    size_t workspace_bytes, int32_t* err, hipStream_t stream) {
+    if (!bt || bt->batch < 0 || bt->n_max < 0 || bt->n_max > TTV_MAX_TREE_NODES ||
+        bt->total_nodes < 0 || bt->total_nodes > (int64_t)bt->batch * bt->n_max)
+        return TTV_EINVAL;
+    if (logits_dtype != TTV_DTYPE_FP32 && logits_dtype != TTV_DTYPE_BF16) return TTV_EINVAL;
+    if (vocab <= 0 || vocab >= (1ll << 31) || max_accept < 1 || max_accept > TTV_MAX_TREE_NODES)
+        return TTV_EINVAL;
+    if (!(temperature > 0.f) || !(temperature < INFINITY)) return TTV_EINVAL;
+    if (bt->batch == 0) return TTV_OK;
+    if (!bt->node_offsets || !logits || !draft_probs || !gumbel || !accept_len || !accepted_nodes ||
+        !out_tokens || !err || !workspace)
+        return TTV_EINVAL;
+    if (bt->total_nodes > 0 && (!tokens || !uniforms || !retrieve_next_token || !retrieve_next_sibling))
+        return TTV_EINVAL;
+    if (workspace_bytes < tree_stochastic_accept_workspace_bytes(bt, vocab)) return TTV_ENOSPC;
+    auto launch = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(bt->batch), dim3(kThreads), 0, stream, bt->node_offsets,
+                           bt->n_max, bt->total_nodes, logits, vocab, (double)temperature,
+                           draft_probs, uniforms, gumbel, tokens, retrieve_next_token,
+                           retrieve_next_sibling, max_accept, accept_len, accepted_nodes,
+                           out_tokens, (double*)workspace, err);
+    };
+    if (logits_dtype == TTV_DTYPE_BF16) launch(stochastic_walk_kernel<true>);
+    else launch(stochastic_walk_kernel<false>);
+    return hipGetLastError() == hipSuccess ? TTV_OK : TTV_EHIP;
+}
