@@ -14,6 +14,8 @@
  *   tree_sample_accept     the walk with temperature-sampled choices
  *   tree_stochastic_accept the stochastic min(1, p/q) per-edge walk
  *
+ * and the dense mask forms for interop (tree_expand_mask, tree_pack_mask).
+ *
  * Pages that define the operations (cited by title and section):
  *   [GLOSSARY] "Beam Search、约束解码与 Tree/Self Speculation"
  *              (llm-glossary.tokens-kit.com, decoding extensions): sections
@@ -84,6 +86,7 @@ extern "C" {
 #define TTV_ERR_BLOCK_TABLE     8   /* a needed block-table entry is -1 or >= num_blocks */
 #define TTV_ERR_ACCEPT          16  /* the walk would exceed max_accept, or commit got a bad path */
 #define TTV_ERR_BAD_LENGTH      32  /* ctx_lens[b] < 0 */
+#define TTV_ERR_BAD_MASK        64  /* tree_pack_mask: a dense row the attention cannot run */
 
 /* Limits. */
 #define TTV_MAX_TREE_NODES 1024     /* N_b <= 1024, so mask rows need <= 32 words */
@@ -92,6 +95,10 @@ extern "C" {
 /* Logits dtypes. */
 #define TTV_DTYPE_FP32 0
 #define TTV_DTYPE_BF16 1
+
+/* Dense mask modes (tree_expand_mask / tree_pack_mask). */
+#define TTV_MASK_QLEN_ONLY 0        /* one byte per tree column */
+#define TTV_MASK_FULL      1        /* one byte per column of context + tree */
 
 /* KV cache layouts. */
 #define TTV_KV_CONTIGUOUS 0         /* k, v: bf16 [B, n_kv_heads, capacity, head_dim] */
@@ -238,6 +245,43 @@ TTV_API int tree_greedy_accept(const ttv_batch* bt, const void* logits, int32_t 
                                int32_t* accept_len, int32_t* accepted_nodes, int32_t* out_tokens,
                                int32_t* row_argmax, void* workspace, size_t workspace_bytes,
                                int32_t* err, hipStream_t stream);
+
+/*
+ * tree_expand_mask -- the bit-packed mask rows in one of the two dense forms
+ * ([ATLAS] §3: build_tree_kernel_efficient emits FULL_MASK, QLEN_ONLY or the
+ * bit-packed form; [GLOSSARY] packed-vs-branch experiment: tree_mask
+ * [N, prefix + N] with the prefix always visible), for callers whose
+ * attention takes a dense mask.
+ *
+ * in : mask, mask_words     bit-packed rows as tree_build writes them
+ *      mode                 TTV_MASK_QLEN_ONLY: byte j of node i's row = bit j;
+ *                           TTV_MASK_FULL: bytes 0 .. ctx_b - 1 = 1, byte
+ *                           ctx_b + j = bit j
+ *      row_stride           bytes per dense row, >= n_max (QLEN_ONLY) and
+ *                           >= ctx_b + N_b for every request (FULL)
+ * out: dense  uint8 [T, row_stride]; bytes past the row's columns are 0
+ *      err    OR-ed: TTV_ERR_CAPACITY (FULL row longer than row_stride; the
+ *             request's rows are not written), _TOO_MANY_NODES
+ */
+TTV_API int tree_expand_mask(const ttv_batch* bt, const uint32_t* mask, int32_t mask_words,
+                             int32_t mode, uint8_t* dense, int64_t row_stride, int32_t* err,
+                             hipStream_t stream);
+
+/*
+ * tree_pack_mask -- a caller's dense mask (either mode, nonzero byte =
+ * visible) packed into the bit-packed rows tree_attention_verify reads.
+ * A request is refused with TTV_ERR_BAD_MASK (its packed rows undefined)
+ * when a row is not a tree mask the attention can run: a FULL row with a
+ * context column zero, a nonzero byte in the column of a later node or past
+ * the tree, or the node's own column zero.
+ *
+ * in : dense uint8 [T, row_stride]; mode; row_stride as in tree_expand_mask
+ * out: mask uint32 [T, mask_words], mask_words in [ceil(n_max / 32), 32]
+ *      err  OR-ed: TTV_ERR_BAD_MASK, _CAPACITY, _TOO_MANY_NODES
+ */
+TTV_API int tree_pack_mask(const ttv_batch* bt, const uint8_t* dense, int64_t row_stride,
+                           int32_t mode, uint32_t* mask, int32_t mask_words, int32_t* err,
+                           hipStream_t stream);
 
 /*
  * tree_sample_accept -- the verifier walk with temperature sampling instead of

@@ -39,6 +39,11 @@ import numpy as np
 
 ERR_BAD_PARENT = 1
 ERR_TOO_MANY_NODES = 2
+ERR_CAPACITY = 4
+ERR_BAD_MASK = 64
+
+MASK_QLEN_ONLY = 0   # dense [N_b] columns: the tree only
+MASK_FULL = 1        # dense [ctx_b + N_b] columns: committed context, then the tree
 
 
 def parents_valid(parents) -> bool:
@@ -124,3 +129,77 @@ def mask_bool(mask_rows: np.ndarray, n: int) -> np.ndarray:
         for j in range(n):
             dense[i, j] = bool((int(mask_rows[i, j // 32]) >> (j % 32)) & 1)
     return dense
+
+
+def dense_mask(parents_all, node_offsets, ctx_lens, mode: int, row_stride: int):
+    """The dense (one byte per column) masks of "02 · Token Tree 与 Tree
+    Attention" §3's other two modes, in one [T, row_stride] uint8 array.
+
+    QLEN_ONLY: byte j of node i's row is 1 iff j is i or an ancestor of i.
+    FULL (the mask over the whole sequence, as the glossary's packed-vs-branch
+    experiment's tree_mask [N, prefix + N]): bytes 0 .. ctx-1 are 1 (the
+    committed context is always visible), byte ctx + j as QLEN_ONLY's byte j.
+    Unused bytes are 0.  A request whose row does not fit row_stride gets
+    err bit 4 and zero rows; bad parents / sizes as in ``build``.
+    Returns (mask, err).
+    """
+    node_offsets = np.asarray(node_offsets)
+    B = len(node_offsets) - 1
+    T = int(node_offsets[-1])
+    mask = np.zeros((T, row_stride), dtype=np.uint8)
+    err = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        s, e = int(node_offsets[b]), int(node_offsets[b + 1])
+        par = [int(p) for p in parents_all[s:e]]
+        ctx = int(ctx_lens[b])
+        if not parents_valid(par):
+            err[b] |= ERR_BAD_PARENT
+            continue
+        base = ctx if mode == MASK_FULL else 0
+        if base + (e - s) > row_stride:
+            err[b] |= ERR_CAPACITY
+            continue
+        for i in range(e - s):
+            mask[s + i, :base] = 1
+            for j in ancestor_path(i, par):
+                mask[s + i, base + j] = 1
+    return mask, err
+
+
+def pack_dense(dense, node_offsets, ctx_lens, mode: int, mask_words: int):
+    """A caller's dense mask (either mode) packed into the bit-packed
+    QLEN-only rows the attention reads: bit j of node i's row = byte j (or
+    ctx + j) of its dense row.  A row is refused (err bit 64, row left zero)
+    when it is not a mask the attention can run: a FULL row hiding a context
+    column, a bit above the diagonal (a later node) or past the tree, or the
+    node's own column clear.  Returns (packed, err)."""
+    node_offsets = np.asarray(node_offsets)
+    B = len(node_offsets) - 1
+    T = int(node_offsets[-1])
+    dense = np.asarray(dense)
+    packed = np.zeros((T, mask_words), dtype=np.uint32)
+    err = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        s, e = int(node_offsets[b]), int(node_offsets[b + 1])
+        n, ctx = e - s, int(ctx_lens[b])
+        base = ctx if mode == MASK_FULL else 0
+        if base + n > dense.shape[1]:
+            err[b] |= ERR_CAPACITY
+            continue
+        ok = True
+        for i in range(n):
+            row = dense[s + i]
+            if mode == MASK_FULL and not all(row[:ctx] != 0):
+                ok = False
+            tree = row[base:base + n] != 0
+            if not tree[i] or tree[i + 1:].any() or (row[base + n:] != 0).any():
+                ok = False
+        if not ok:
+            err[b] |= ERR_BAD_MASK
+            continue
+        for i in range(n):
+            row = dense[s + i]
+            for j in range(n):
+                if row[base + j]:
+                    packed[s + i, j // 32] |= np.uint32(1 << (j % 32))
+    return packed, err

@@ -249,3 +249,16 @@ def test_sampled_walks_reject(lib):
     assert stoch(q=None) == tta.TTV_EINVAL
     assert stoch(u=None) == tta.TTV_EINVAL
     assert stoch(ws_bytes=sneed - 1) == tta.TTV_ENOSPC
+
+
+def test_mask_interop_rejects(lib):
+    b = _batch()
+    assert lib.tree_expand_mask(ctypes.byref(b), FAKE, 1, 2, FAKE, 64, FAKE, None) == tta.TTV_EINVAL   # mode
+    assert lib.tree_expand_mask(ctypes.byref(b), FAKE, 0, 0, FAKE, 64, FAKE, None) == tta.TTV_EINVAL   # words
+    assert lib.tree_expand_mask(ctypes.byref(b), FAKE, 33, 0, FAKE, 64, FAKE, None) == tta.TTV_EINVAL  # words > 32
+    assert lib.tree_expand_mask(ctypes.byref(b), FAKE, 1, 0, FAKE, 4, FAKE, None) == tta.TTV_EINVAL    # stride < n_max
+    assert lib.tree_expand_mask(ctypes.byref(b), None, 1, 0, FAKE, 64, FAKE, None) == tta.TTV_EINVAL
+    assert lib.tree_pack_mask(ctypes.byref(b), FAKE, 64, 5, FAKE, 1, FAKE, None) == tta.TTV_EINVAL
+    assert lib.tree_pack_mask(ctypes.byref(b), None, 64, 1, FAKE, 1, FAKE, None) == tta.TTV_EINVAL
+    empty = _batch(B=0, T=0)
+    assert lib.tree_pack_mask(ctypes.byref(empty), None, 64, 1, None, 1, None, None) == tta.TTV_OK

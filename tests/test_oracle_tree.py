@@ -5,6 +5,7 @@ import itertools
 import numpy as np
 import pytest
 
+import synth
 from oracle import tree as T
 from conftest import golden
 
@@ -132,3 +133,69 @@ def test_empty_request_and_retrieve_rows():
     assert out["err"].tolist() == [0, 0, 0]
     assert out["retrieve_index"].tolist() == [1, 2, 5, 6, 7]
     assert out["positions"].tolist() == [4, 5, 0, 0, 1]
+
+
+# ---- dense mask modes (FULL_MASK / QLEN_ONLY) and packing a caller's dense mask ----
+
+def test_full_mask_pin():
+    """The glossary's packed node table: tree_mask is [8, 10] (prefix 2 + 8 nodes)
+    and each row sees 3, 3, 4, 4, 4, 5, 5, 5 columns (prefix included)."""
+    g = golden("packed_table.json")
+    par, P = g["parents"], g["prefix_length"]
+    full, err = T.dense_mask(par, [0, len(par)], [P], T.MASK_FULL, P + len(par))
+    assert list(full.shape) == g["shapes"]["tree_mask"] and not err.any()
+    assert full.sum(axis=1).tolist() == g["tree_mask_visible_counts_with_prefix"]
+    for i, anc in enumerate(g["visible_candidate_ancestors"]):
+        assert np.flatnonzero(full[i, P:]).tolist() == anc
+        assert full[i, :P].all()
+    qlen, _ = T.dense_mask(par, [0, len(par)], [P], T.MASK_QLEN_ONLY, len(par))
+    assert np.array_equal(qlen, full[:, P:])
+
+
+def test_full_mask_of_a_chain_is_causal_and_of_a_star_is_diagonal():
+    n, ctx = 9, 4
+    chain = [-1] + list(range(n - 1))
+    full, _ = T.dense_mask(chain, [0, n], [ctx], T.MASK_FULL, ctx + n)
+    # the rows of the last n positions of a causal mask over ctx + n tokens
+    assert np.array_equal(full, np.tril(np.ones((ctx + n, ctx + n), np.uint8))[ctx:])
+    star = [-1] * n
+    full, _ = T.dense_mask(star, [0, n], [ctx], T.MASK_FULL, ctx + n)
+    assert np.array_equal(full, np.concatenate([np.ones((n, ctx), np.uint8), np.eye(n, dtype=np.uint8)], 1))
+
+
+def test_dense_mask_stride_and_errors():
+    par = [-1, 0, 0, 1]
+    full, err = T.dense_mask(par + [-1, 5], [0, 4, 6], [3, 2], T.MASK_FULL, 8)
+    assert err.tolist() == [0, T.ERR_BAD_PARENT]
+    assert (full[:4, 7] == 0).all() and full[0, :4].tolist() == [1, 1, 1, 1]
+    _, err = T.dense_mask(par, [0, 4], [5], T.MASK_FULL, 8)
+    assert err.tolist() == [T.ERR_CAPACITY]
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_pack_dense_round_trip_and_refusals(mode):
+    rng = np.random.default_rng(9)
+    sizes = [5, 40, 1, 0, 33]
+    pars = [synth.random_tree(rng, k) if k else np.zeros(0, np.int32) for k in sizes]
+    par_all = np.concatenate(pars).astype(np.int32)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    ctx = np.array([3, 0, 7, 2, 1], np.int32)
+    stride = 64
+    dense, err = T.dense_mask(par_all, offs, ctx, mode, stride)
+    assert not err.any()
+    packed, err = T.pack_dense(dense, offs, ctx, mode, 2)
+    assert not err.any()
+    assert np.array_equal(packed, T.build(par_all, offs, ctx, 40, 2)["mask"])
+    base = (lambda b: int(ctx[b])) if mode == 1 else (lambda b: 0)
+    # a later node's column set (a sibling or child), and the own column cleared
+    for b, (row, col) in ((1, (5, 9)), (4, (2, 2))):
+        bad = dense.copy()
+        i = offs[b] + row
+        bad[i, base(b) + col] ^= 1
+        _, err = T.pack_dense(bad, offs, ctx, mode, 2)
+        assert err[b] == T.ERR_BAD_MASK and err.sum() == T.ERR_BAD_MASK
+    if mode == 1:  # a hidden context column
+        bad = dense.copy()
+        bad[offs[0] + 1, 0] = 0
+        _, err = T.pack_dense(bad, offs, ctx, mode, 2)
+        assert err[0] == T.ERR_BAD_MASK

@@ -28,14 +28,16 @@ __all__ = [
     "tree_build", "tree_attention_workspace_bytes", "tree_attention_verify",
     "tree_greedy_accept_workspace_bytes", "tree_greedy_accept", "tree_greedy_accept_noalloc",
     "tree_sample_accept", "tree_stochastic_accept_workspace_bytes", "tree_stochastic_accept",
-    "tree_kv_commit", "TTV_OK", "TTV_EINVAL", "TTV_EHIP", "TTV_ENOSPC", "ERR_BAD_PARENT", "ERR_TOO_MANY_NODES",
+    "tree_kv_commit", "tree_expand_mask", "tree_pack_mask", "MASK_QLEN_ONLY", "MASK_FULL", "ERR_BAD_MASK",
+    "TTV_OK", "TTV_EINVAL", "TTV_EHIP", "TTV_ENOSPC", "ERR_BAD_PARENT", "ERR_TOO_MANY_NODES",
     "ERR_CAPACITY", "ERR_BLOCK_TABLE", "ERR_ACCEPT", "ERR_BAD_LENGTH", "MAX_TREE_NODES",
     "BLOCK_SIZE", "EXPORTED_SYMBOLS",
 ]
 
 TTV_OK, TTV_EINVAL, TTV_EHIP, TTV_ENOSPC = 0, -1, -2, -3
 ERR_BAD_PARENT, ERR_TOO_MANY_NODES, ERR_CAPACITY = 1, 2, 4
-ERR_BLOCK_TABLE, ERR_ACCEPT, ERR_BAD_LENGTH = 8, 16, 32
+ERR_BLOCK_TABLE, ERR_ACCEPT, ERR_BAD_LENGTH, ERR_BAD_MASK = 8, 16, 32, 64
+MASK_QLEN_ONLY, MASK_FULL = 0, 1
 MAX_TREE_NODES = 1024
 BLOCK_SIZE = 16
 DTYPE_FP32, DTYPE_BF16 = 0, 1
@@ -45,7 +47,7 @@ EXPORTED_SYMBOLS = (
     "ttv_version", "ttv_status_string", "tree_build", "tree_attention_workspace_bytes",
     "tree_attention_verify", "tree_greedy_accept_workspace_bytes", "tree_greedy_accept",
     "tree_greedy_accept_noalloc", "tree_sample_accept", "tree_stochastic_accept_workspace_bytes",
-    "tree_stochastic_accept", "tree_kv_commit",
+    "tree_stochastic_accept", "tree_kv_commit", "tree_expand_mask", "tree_pack_mask",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -103,6 +105,10 @@ def load_library() -> ctypes.CDLL:
     lib.tree_stochastic_accept_workspace_bytes.argtypes = [BP, I64]
     lib.tree_stochastic_accept.restype = ctypes.c_int
     lib.tree_stochastic_accept.argtypes = [BP, P, I32, I64, F32, P, P, P, P, P, P, I32, P, P, P, P, SZ, P, P]
+    lib.tree_expand_mask.restype = ctypes.c_int
+    lib.tree_expand_mask.argtypes = [BP, P, I32, I32, P, I64, P, P]
+    lib.tree_pack_mask.restype = ctypes.c_int
+    lib.tree_pack_mask.argtypes = [BP, P, I64, I32, P, I32, P, P]
     lib.tree_kv_commit.restype = ctypes.c_int
     lib.tree_kv_commit.argtypes = [BP, CP, P, P, I32, P, P, P, P, P]
     _LIB = lib
@@ -478,4 +484,41 @@ def tree_kv_commit(bt: Batch, cache: KVCache, accept_len, accepted_nodes, err,
                             _ptr(out.get("released_blocks")), _ptr(out.get("num_released")),
                             _ptr(err), _stream(stream))
     _check(st, "tree_kv_commit")
+    return out
+
+
+def tree_expand_mask(bt: Batch, mask, mode: int, row_stride: int, err, out=None, stream=None):
+    """Dense uint8 [T, row_stride] mask (MASK_QLEN_ONLY or MASK_FULL) from tree_build's packed rows."""
+    torch = _torch()
+    lib = load_library()
+    T = bt.total_nodes
+    if mask.dim() != 2 or mask.shape[0] != T:
+        raise ValueError(f"mask must be [T={T}, W]")
+    _dev(mask, torch.int32, "mask")
+    _dev(err, torch.int32, "err", bt.batch)
+    if out is None:
+        out = torch.empty((T, int(row_stride)), dtype=torch.uint8, device=mask.device)
+    _dev(out, torch.uint8, "dense", T * int(row_stride))
+    st = lib.tree_expand_mask(ctypes.byref(bt._c), _ptr(mask), int(mask.shape[1]), int(mode), _ptr(out),
+                              int(row_stride), _ptr(err), _stream(stream))
+    _check(st, "tree_expand_mask")
+    return out
+
+
+def tree_pack_mask(bt: Batch, dense, mode: int, err, mask_words: Optional[int] = None, out=None, stream=None):
+    """Bit-packed int32 [T, W] rows (the attention's input) from a dense uint8 [T, row_stride] mask."""
+    torch = _torch()
+    lib = load_library()
+    T = bt.total_nodes
+    if dense.dim() != 2 or dense.shape[0] != T:
+        raise ValueError(f"dense must be [T={T}, row_stride]")
+    _dev(dense, torch.uint8, "dense")
+    _dev(err, torch.int32, "err", bt.batch)
+    W = bt.mask_words if mask_words is None else int(mask_words)
+    if out is None:
+        out = torch.empty((T, W), dtype=torch.int32, device=dense.device)
+    _dev(out, torch.int32, "mask", T * W)
+    st = lib.tree_pack_mask(ctypes.byref(bt._c), _ptr(dense), int(dense.shape[1]), int(mode), _ptr(out), W,
+                            _ptr(err), _stream(stream))
+    _check(st, "tree_pack_mask")
     return out
