@@ -214,3 +214,39 @@ def test_stochastic_walk_without_residual_is_caught(monkeypatch):
 def test_stochastic_walk_with_swapped_ratio_is_caught(monkeypatch):
     monkeypatch.setattr(SM, "stochastic_walk", _walk_variant(ratio_swapped=True))
     assert _fails(PS.test_stochastic_hand_computed, PS.test_q_equal_p_accepts_first_children)
+
+
+# ---- DDTree construction ----
+
+def test_ddtree_without_sibling_push_is_caught(monkeypatch):
+    import heapq
+    import test_oracle_ddtree as PD
+    from oracle import ddtree as DD
+
+    def no_siblings(logq, budget):
+        heap = [(-logq[0][0], (0,))]
+        popped = []
+        while heap and len(popped) < budget:
+            negs, ranks = heapq.heappop(heap)
+            popped.append(ranks)
+            d = len(ranks) - 1
+            if d + 1 < len(logq):
+                heapq.heappush(heap, (-(-negs + logq[d + 1][0]), ranks + (0,)))
+        return popped
+    monkeypatch.setattr(DD, "best_first", no_siblings)
+    assert _fails(PD.test_worked_example_tree, lambda: PD.test_top_b_against_brute_force(0, 5, 3, 8))
+
+
+def test_ddtree_unsorted_topk_is_caught(monkeypatch):
+    import test_oracle_ddtree as PD
+    from oracle import ddtree as DD
+    orig = DD.depth_topk
+
+    def first_k(z_row, K):  # the first K tokens instead of the K largest
+        z = np.asarray(z_row, dtype=np.float64)
+        toks, _ = orig(z, len(z))
+        sel = np.sort(toks[:K])
+        lq = z[sel] - np.log(np.exp(z[sel]).sum())
+        return sel, lq
+    monkeypatch.setattr(DD, "depth_topk", first_k)
+    assert _fails(PD.test_depth_topk_order_and_normalisation, PD.test_worked_example_tree)
