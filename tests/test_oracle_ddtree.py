@@ -26,6 +26,7 @@ def test_worked_example_tree():
                   [0.45, 0.55, 1e-3, 1e-3],   # position 2
                   [1e-3, 1e-3, 0.75, 0.2]])   # position 3
     par, tok = DD.build_tree(np.log(q), 6)
+    assert len(par) == 6
     paths = set()
     for i in range(6):
         paths.add(tuple(int(tok[j]) for j in T.ancestor_path(i, par)))
