@@ -14,7 +14,8 @@
  *   tree_sample_accept     the walk with temperature-sampled choices
  *   tree_stochastic_accept the stochastic min(1, p/q) per-edge walk
  *
- * and the dense mask forms for interop (tree_expand_mask, tree_pack_mask).
+ * the dense mask forms for interop (tree_expand_mask, tree_pack_mask), and
+ * DDTree's draft-tree construction (tree_ddtree_build) that feeds tree_build.
  *
  * Pages that define the operations (cited by title and section):
  *   [GLOSSARY] "Beam Search、约束解码与 Tree/Self Speculation"
@@ -282,6 +283,39 @@ TTV_API int tree_expand_mask(const ttv_batch* bt, const uint32_t* mask, int32_t 
 TTV_API int tree_pack_mask(const ttv_batch* bt, const uint8_t* dense, int64_t row_stride,
                            int32_t mode, uint32_t* mask, int32_t mask_words, int32_t* err,
                            hipStream_t stream);
+
+/* Workspace bytes tree_ddtree_build needs (host call); 0 for invalid sizes. */
+TTV_API size_t tree_ddtree_workspace_bytes(int32_t requests, int32_t depths, int64_t vocab,
+                                           int32_t budget);
+
+/*
+ * tree_ddtree_build -- DDTree's draft tree, the step before tree_build
+ * ([DDTREE] §4.2: the top-B prefixes of a factorised draft are the optimal,
+ * prefix-closed tree; §4.3 Lemma 1: each depth's top-min(B, V) tokens
+ * suffice; §5 Algorithm 1: a best-first heap over rank tuples, popping a
+ * prefix and pushing its next sibling and its first child).
+ *
+ * Per request and depth d: the top K = min(budget, vocab) tokens by logit
+ * (descending, then token id ascending), log q = z - lse over those K (lse =
+ * z_1 + log(sum_r exp(z_r - z_1)), summed in rank order, float64).  Then
+ * Algorithm 1 with float64 scores (a sibling's score = parent entry's score -
+ * log q(rank) + log q(rank + 1), a child's = score + log q(rank 1 of the next
+ * depth)); equal scores pop in increasing rank-tuple order, a tuple before
+ * its extensions.  Node i is the i-th popped prefix.
+ *
+ * in : draft_logits  float32 [requests, depths, vocab] (finite)
+ *      depths in [1, 20]; budget in [1, 1024]; requests <= 65535
+ * out: parents int32 [requests, budget]   -1 at depth 1, else an earlier node
+ *      tokens  int32 [requests, budget]
+ *      n_nodes int32 [requests]           min(budget, number of prefixes);
+ *                                         entries past it are -1
+ *      workspace  device, 256-byte aligned, >= tree_ddtree_workspace_bytes()
+ * The parents / tokens rows feed tree_build directly (topological order).
+ */
+TTV_API int tree_ddtree_build(int32_t requests, int32_t depths, int64_t vocab, int32_t budget,
+                              const float* draft_logits, int32_t* parents, int32_t* tokens,
+                              int32_t* n_nodes, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
 
 /*
  * tree_sample_accept -- the verifier walk with temperature sampling instead of

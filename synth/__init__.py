@@ -43,7 +43,7 @@ import numpy as np
 __all__ = [
     "CONFIGS", "Workload", "make_workload", "bf16_bits_from_f32", "f32_from_bf16_bits",
     "medusa_tree", "eagle_tree", "random_tree", "ddtree_tree", "BLOCK_SIZE", "make_trees", "TreeBatch",
-    "gumbel_noise", "draft_distributions", "uniforms",
+    "gumbel_noise", "draft_distributions", "uniforms", "draft_logits",
 ]
 
 BLOCK_SIZE = 16
@@ -481,7 +481,7 @@ def make_workload(cfg_id: int, seed: int = 0, **over) -> Workload:
 # Random inputs of the sampled walks (drawing only)
 # --------------------------------------------------------------------------
 
-_S_GUMBEL, _S_DRAFT, _S_UNIFORM = 8, 9, 10
+_S_GUMBEL, _S_DRAFT, _S_UNIFORM, _S_DDRAFT = 8, 9, 10, 11
 
 
 def gumbel_noise(seed: int, cfg_id: int, rows: int, vocab: int) -> np.ndarray:
@@ -503,6 +503,16 @@ def draft_distributions(seed: int, cfg_id: int, rows: int, vocab: int, tokens_of
             if len(t):
                 x[r, np.asarray(t, dtype=np.int64)] *= 1.0 + boost
     return (x / x.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def draft_logits(seed: int, cfg_id: int, requests: int, depths: int, vocab: int, sigma: float = 2.0,
+                 levels: int = 0) -> np.ndarray:
+    """float32 [requests, depths, vocab] per-depth drafter logits, N(0, sigma^2);
+    with ``levels`` > 0 rounded to multiples of 1 / levels (many exact ties)."""
+    x = _rng(seed, cfg_id, _S_DDRAFT).standard_normal((requests, depths, vocab)) * sigma
+    if levels:
+        x = np.round(x * levels) / levels
+    return x.astype(np.float32)
 
 
 def uniforms(seed: int, cfg_id: int, n: int) -> np.ndarray:

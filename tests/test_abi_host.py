@@ -262,3 +262,14 @@ def test_mask_interop_rejects(lib):
     assert lib.tree_pack_mask(ctypes.byref(b), None, 64, 1, FAKE, 1, FAKE, None) == tta.TTV_EINVAL
     empty = _batch(B=0, T=0)
     assert lib.tree_pack_mask(ctypes.byref(empty), None, 64, 1, None, 1, None, None) == tta.TTV_OK
+
+
+def test_ddtree_build_rejects(lib):
+    assert lib.tree_ddtree_workspace_bytes(4, 16, 151936, 1024) == 4 * 16 * 1024 * 12 + 256
+    assert lib.tree_ddtree_workspace_bytes(4, 21, 1000, 64) == 0      # depths > 20
+    assert lib.tree_ddtree_workspace_bytes(4, 16, 1000, 1025) == 0    # budget > 1024
+    need = lib.tree_ddtree_workspace_bytes(2, 3, 50, 20)
+    assert lib.tree_ddtree_build(2, 3, 50, 20, None, FAKE, FAKE, FAKE, FAKE * 16, need, None) == tta.TTV_EINVAL
+    assert lib.tree_ddtree_build(2, 3, 50, 20, FAKE, FAKE, FAKE, FAKE, FAKE * 16 + 8, need, None) == tta.TTV_EINVAL
+    assert lib.tree_ddtree_build(2, 3, 50, 20, FAKE, FAKE, FAKE, FAKE, FAKE * 16, need - 1, None) == tta.TTV_ENOSPC
+    assert lib.tree_ddtree_build(0, 3, 50, 20, None, None, None, None, None, 0, None) == tta.TTV_OK

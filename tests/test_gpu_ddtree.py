@@ -1,0 +1,63 @@
+"""tree_ddtree_build on the GPU against the oracle, bit-exact: the pop order
+(node numbering), parents, tokens and node count of every request, including
+logits with many exact ties and a budget larger than the number of prefixes;
+and the trees feed tree_build as they come out."""
+
+import numpy as np
+import pytest
+
+import synth
+import token_tree_attention_amd as tta
+from gpu_helpers import host, require_gpu, say
+from oracle import ddtree as O_dd
+from oracle import tree as O_tree
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (requests, depths, vocab, budget, sigma, levels)
+    (2, 3, 50, 20, 2.0, 0),
+    (2, 2, 3, 20, 2.0, 0),          # 3 + 9 prefixes: the heap empties before the budget
+    (3, 16, 4096, 300, 2.0, 0),
+    (3, 16, 4096, 300, 8.0, 0),     # deep trees
+    (2, 6, 2000, 500, 1.0, 2),      # logits on a 0.5 grid: ties in the top-K and in the scores
+    (4, 16, 151936, 1024, 2.0, 0),  # the DDTree workload's shape
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_ddtree_build_matches_oracle(case):
+    require_gpu()
+    import torch
+    R, L, V, budget, sigma, levels = CASES[case]
+    z = synth.draft_logits(case, 3, R, L, V, sigma, levels)
+    say(f"tree_ddtree_build R={R} L={L} V={V} budget={budget} sigma={sigma} levels={levels}")
+    out = tta.tree_ddtree_build(torch.from_numpy(z).cuda(), budget)
+    torch.cuda.synchronize()
+    par, tok, nn = host(out["parents"]), host(out["tokens"]), host(out["n_nodes"])
+    for r in range(R):
+        rp, rt = O_dd.build_tree(z[r], budget)
+        assert nn[r] == len(rp)
+        np.testing.assert_array_equal(par[r, :nn[r]], rp, err_msg=f"parents of request {r}")
+        np.testing.assert_array_equal(tok[r, :nn[r]], rt, err_msg=f"tokens of request {r}")
+        assert (par[r, nn[r]:] == -1).all() and (tok[r, nn[r]:] == -1).all()
+
+
+def test_ddtree_trees_feed_tree_build():
+    require_gpu()
+    import torch
+    R, L, V, budget = 3, 16, 8192, 1024
+    z = synth.draft_logits(9, 3, R, L, V, 4.0)
+    out = tta.tree_ddtree_build(torch.from_numpy(z).cuda(), budget)
+    nn = host(out["n_nodes"])
+    offs = np.concatenate([[0], np.cumsum(nn)]).astype(np.int32)
+    parents = torch.cat([out["parents"][r, :nn[r]] for r in range(R)]).contiguous()
+    ctx = np.array([100, 0, 5000], np.int32)
+    bt = tta.Batch(torch.from_numpy(offs).cuda(), torch.from_numpy(ctx).cuda(), int(nn.max()),
+                   total_nodes=int(offs[-1]))
+    meta = tta.tree_build(bt, parents)
+    torch.cuda.synchronize()
+    assert (host(meta["err"]) == 0).all()
+    ref = O_tree.build(host(parents), offs, ctx, int(nn.max()), meta["mask"].shape[1])
+    np.testing.assert_array_equal(host(meta["mask"]).view(np.uint32), ref["mask"])
+    np.testing.assert_array_equal(host(meta["positions"]), ref["positions"])

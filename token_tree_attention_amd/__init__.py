@@ -28,7 +28,8 @@ __all__ = [
     "tree_build", "tree_attention_workspace_bytes", "tree_attention_verify",
     "tree_greedy_accept_workspace_bytes", "tree_greedy_accept", "tree_greedy_accept_noalloc",
     "tree_sample_accept", "tree_stochastic_accept_workspace_bytes", "tree_stochastic_accept",
-    "tree_kv_commit", "tree_expand_mask", "tree_pack_mask", "MASK_QLEN_ONLY", "MASK_FULL", "ERR_BAD_MASK",
+    "tree_kv_commit", "tree_expand_mask", "tree_pack_mask", "tree_ddtree_workspace_bytes",
+    "tree_ddtree_build", "MASK_QLEN_ONLY", "MASK_FULL", "ERR_BAD_MASK",
     "TTV_OK", "TTV_EINVAL", "TTV_EHIP", "TTV_ENOSPC", "ERR_BAD_PARENT", "ERR_TOO_MANY_NODES",
     "ERR_CAPACITY", "ERR_BLOCK_TABLE", "ERR_ACCEPT", "ERR_BAD_LENGTH", "MAX_TREE_NODES",
     "BLOCK_SIZE", "EXPORTED_SYMBOLS",
@@ -48,6 +49,7 @@ EXPORTED_SYMBOLS = (
     "tree_attention_verify", "tree_greedy_accept_workspace_bytes", "tree_greedy_accept",
     "tree_greedy_accept_noalloc", "tree_sample_accept", "tree_stochastic_accept_workspace_bytes",
     "tree_stochastic_accept", "tree_kv_commit", "tree_expand_mask", "tree_pack_mask",
+    "tree_ddtree_workspace_bytes", "tree_ddtree_build",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -109,6 +111,10 @@ def load_library() -> ctypes.CDLL:
     lib.tree_expand_mask.argtypes = [BP, P, I32, I32, P, I64, P, P]
     lib.tree_pack_mask.restype = ctypes.c_int
     lib.tree_pack_mask.argtypes = [BP, P, I64, I32, P, I32, P, P]
+    lib.tree_ddtree_workspace_bytes.restype = SZ
+    lib.tree_ddtree_workspace_bytes.argtypes = [I32, I32, I64, I32]
+    lib.tree_ddtree_build.restype = ctypes.c_int
+    lib.tree_ddtree_build.argtypes = [I32, I32, I64, I32, P, P, P, P, P, SZ, P]
     lib.tree_kv_commit.restype = ctypes.c_int
     lib.tree_kv_commit.argtypes = [BP, CP, P, P, I32, P, P, P, P, P]
     _LIB = lib
@@ -521,4 +527,37 @@ def tree_pack_mask(bt: Batch, dense, mode: int, err, mask_words: Optional[int] =
     st = lib.tree_pack_mask(ctypes.byref(bt._c), _ptr(dense), int(dense.shape[1]), int(mode), _ptr(out), W,
                             _ptr(err), _stream(stream))
     _check(st, "tree_pack_mask")
+    return out
+
+
+def tree_ddtree_workspace_bytes(requests: int, depths: int, vocab: int, budget: int) -> int:
+    return int(load_library().tree_ddtree_workspace_bytes(int(requests), int(depths), int(vocab), int(budget)))
+
+
+def tree_ddtree_build(draft_logits, budget: int, out: Optional[Dict] = None, workspace=None, stream=None) -> Dict:
+    """DDTree draft trees from float32 draft logits [R, L, V]: parents / tokens
+    [R, budget] (pop order) and n_nodes [R]."""
+    torch = _torch()
+    lib = load_library()
+    if draft_logits.dim() != 3:
+        raise ValueError("draft_logits must be [requests, depths, vocab]")
+    _dev(draft_logits, torch.float32, "draft_logits")
+    R, L, V = (int(x) for x in draft_logits.shape)
+    dev = draft_logits.device
+    if out is None:
+        out = {"parents": torch.empty((R, budget), dtype=torch.int32, device=dev),
+               "tokens": torch.empty((R, budget), dtype=torch.int32, device=dev),
+               "n_nodes": torch.empty(R, dtype=torch.int32, device=dev)}
+    _dev(out["parents"], torch.int32, "parents", R * budget)
+    _dev(out["tokens"], torch.int32, "tokens", R * budget)
+    _dev(out["n_nodes"], torch.int32, "n_nodes", R)
+    need = tree_ddtree_workspace_bytes(R, L, V, budget)
+    if need == 0:
+        raise ValueError("unsupported DDTree sizes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _dev(workspace, torch.uint8, "workspace")
+    st = lib.tree_ddtree_build(R, L, V, int(budget), _ptr(draft_logits), _ptr(out["parents"]), _ptr(out["tokens"]),
+                               _ptr(out["n_nodes"]), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "tree_ddtree_build")
     return out
