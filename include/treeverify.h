@@ -15,7 +15,9 @@
  *   tree_stochastic_accept the stochastic min(1, p/q) per-edge walk
  *
  * the dense mask forms for interop (tree_expand_mask, tree_pack_mask), and
- * DDTree's draft-tree construction (tree_ddtree_build) that feeds tree_build.
+ * the draft-tree construction that feeds tree_build: DDTree's best-first
+ * top-B tree (tree_ddtree_build) and SpecInfer's prefix merge
+ * (tree_merge_sequences).
  *
  * Pages that define the operations (cited by title and section):
  *   [GLOSSARY] "Beam Search、约束解码与 Tree/Self Speculation"
@@ -316,6 +318,30 @@ TTV_API int tree_ddtree_build(int32_t requests, int32_t depths, int64_t vocab, i
                               const float* draft_logits, int32_t* parents, int32_t* tokens,
                               int32_t* n_nodes, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/*
+ * tree_merge_sequences -- SpecInfer's tree: the distinct prefixes of each
+ * request's independent draft sequences ([ATLAS] §3: SpecInfer merges
+ * independent drafts along common prefixes, bottom-up; [GLOSSARY] packed
+ * node table: branches [4,5,6], [4,7,8], [9,0,1] become 8 unique nodes,
+ * tokens [4,9,5,7,0,6,8,1], parents [-1,-1,0,0,1,2,3,4]).
+ *
+ * A sequence ends at its first negative entry.  Nodes are numbered level by
+ * level (depth 0 first), within a level in the order the sequences, by
+ * index, first reach them, so the output is topological (it feeds
+ * tree_build).
+ *
+ * in : seqs int32 [requests, n_seqs, seq_len]; n_seqs <= 1024;
+ *      seq_len <= 1024; max_nodes <= 1024 (row length of the outputs)
+ * out: parents, tokens int32 [requests, max_nodes] (-1 past n_nodes)
+ *      n_nodes int32 [requests]
+ *      err     int32 [requests] OR-ed: TTV_ERR_TOO_MANY_NODES when the
+ *              distinct prefixes exceed max_nodes (n_nodes = 0, rows undefined)
+ */
+TTV_API int tree_merge_sequences(int32_t requests, int32_t n_seqs, int32_t seq_len,
+                                 const int32_t* seqs, int32_t max_nodes, int32_t* parents,
+                                 int32_t* tokens, int32_t* n_nodes, int32_t* err,
+                                 hipStream_t stream);
 
 /*
  * tree_sample_accept -- the verifier walk with temperature sampling instead of

@@ -203,3 +203,36 @@ def pack_dense(dense, node_offsets, ctx_lens, mode: int, mask_words: int):
                 if row[base + j]:
                     packed[s + i, j // 32] |= np.uint32(1 << (j % 32))
     return packed, err
+
+
+def merge_sequences(seqs):
+    """Draft sequences merged into one tree of their distinct prefixes
+    (test infrastructure only).
+
+    "02 · Token Tree 与 Tree Attention" §3: SpecInfer builds the tree bottom-up,
+    merging independent drafts along their common prefixes; the glossary's
+    packed node table shows three branches [4,5,6], [4,7,8], [9,0,1] becoming
+    8 unique nodes.  Readings: a sequence ends at its first negative entry;
+    nodes are numbered level by level (depth 0 first), and within a level in
+    the order the sequences first reach them (sequence index, then nothing
+    else: a sequence adds at most one node per level).  Returns (parents,
+    tokens, node_of) with node_of[m][d] the node of sequence m's prefix of
+    length d + 1 (-1 past its end).
+    """
+    M = len(seqs)
+    L = max((len(s) for s in seqs), default=0)
+    node_of = [[-1] * L for _ in range(M)]
+    parents: List[int] = []
+    tokens: List[int] = []
+    for d in range(L):
+        seen = {}
+        for m in range(M):
+            if d >= len(seqs[m]) or seqs[m][d] < 0 or (d > 0 and node_of[m][d - 1] < 0):
+                continue
+            key = (node_of[m][d - 1] if d > 0 else -1, int(seqs[m][d]))
+            if key not in seen:
+                seen[key] = len(parents)
+                parents.append(key[0])
+                tokens.append(key[1])
+            node_of[m][d] = seen[key]
+    return parents, tokens, node_of

@@ -273,3 +273,10 @@ def test_ddtree_build_rejects(lib):
     assert lib.tree_ddtree_build(2, 3, 50, 20, FAKE, FAKE, FAKE, FAKE, FAKE * 16 + 8, need, None) == tta.TTV_EINVAL
     assert lib.tree_ddtree_build(2, 3, 50, 20, FAKE, FAKE, FAKE, FAKE, FAKE * 16, need - 1, None) == tta.TTV_ENOSPC
     assert lib.tree_ddtree_build(0, 3, 50, 20, None, None, None, None, None, 0, None) == tta.TTV_OK
+
+
+def test_merge_sequences_rejects(lib):
+    assert lib.tree_merge_sequences(1, 1025, 4, FAKE, 64, FAKE, FAKE, FAKE, FAKE, None) == tta.TTV_EINVAL
+    assert lib.tree_merge_sequences(1, 4, 4, FAKE, 1025, FAKE, FAKE, FAKE, FAKE, None) == tta.TTV_EINVAL
+    assert lib.tree_merge_sequences(1, 4, 4, None, 64, FAKE, FAKE, FAKE, FAKE, None) == tta.TTV_EINVAL
+    assert lib.tree_merge_sequences(0, 4, 4, None, 64, None, None, None, None, None) == tta.TTV_OK

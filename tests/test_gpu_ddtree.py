@@ -61,3 +61,41 @@ def test_ddtree_trees_feed_tree_build():
     ref = O_tree.build(host(parents), offs, ctx, int(nn.max()), meta["mask"].shape[1])
     np.testing.assert_array_equal(host(meta["mask"]).view(np.uint32), ref["mask"])
     np.testing.assert_array_equal(host(meta["positions"]), ref["positions"])
+
+
+@pytest.mark.parametrize("seed, R, M, L, alphabet", [(0, 1, 3, 3, 10), (1, 4, 16, 8, 3), (2, 3, 200, 6, 4),
+                                                     (3, 2, 1024, 12, 2), (4, 5, 64, 40, 2)])
+def test_merge_sequences_matches_oracle(seed, R, M, L, alphabet):
+    require_gpu()
+    import torch
+    rng = np.random.default_rng(seed)
+    seqs = rng.integers(0, alphabet, size=(R, M, L)).astype(np.int32)
+    ends = rng.integers(0, L + 1, size=(R, M))
+    for r in range(R):
+        for m in range(M):
+            seqs[r, m, ends[r, m]:] = -1
+    if seed == 0:  # the glossary's three branches
+        seqs[0] = np.array([[4, 5, 6], [4, 7, 8], [9, 0, 1]], np.int32)
+    say(f"tree_merge_sequences R={R} M={M} L={L} alphabet={alphabet}")
+    out = tta.tree_merge_sequences(torch.from_numpy(seqs).cuda(), 1024)
+    torch.cuda.synchronize()
+    par, tok, nn, err = (host(out[k]) for k in ("parents", "tokens", "n_nodes", "err"))
+    for r in range(R):
+        rp, rt, _ = O_tree.merge_sequences([[int(x) for x in s] for s in seqs[r]])
+        if len(rp) > 1024:
+            assert err[r] & tta.ERR_TOO_MANY_NODES and nn[r] == 0
+            continue
+        assert err[r] == 0 and nn[r] == len(rp)
+        np.testing.assert_array_equal(par[r, :nn[r]], rp)
+        np.testing.assert_array_equal(tok[r, :nn[r]], rt)
+    if seed == 0:
+        assert par[0, :8].tolist() == [-1, -1, 0, 0, 1, 2, 3, 4] and tok[0, :8].tolist() == [4, 9, 5, 7, 0, 6, 8, 1]
+
+
+def test_merge_sequences_overflow_flag():
+    require_gpu()
+    import torch
+    seqs = np.arange(2 * 30 * 5, dtype=np.int32).reshape(2, 30, 5)  # 150 distinct prefixes per request
+    out = tta.tree_merge_sequences(torch.from_numpy(seqs).cuda(), 100)
+    torch.cuda.synchronize()
+    assert (host(out["err"]) & tta.ERR_TOO_MANY_NODES).all() and (host(out["n_nodes"]) == 0).all()

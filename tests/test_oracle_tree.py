@@ -199,3 +199,33 @@ def test_pack_dense_round_trip_and_refusals(mode):
         bad[offs[0] + 1, 0] = 0
         _, err = T.pack_dense(bad, offs, ctx, mode, 2)
         assert err[0] == T.ERR_BAD_MASK
+
+
+def test_merge_sequences_pin():
+    """The glossary's three branches merge into its packed node table."""
+    g = golden("packed_table.json")
+    par, tok, node_of = T.merge_sequences(g["branches"])
+    assert par == g["parents"] and tok == g["tokens"]
+    assert len(par) == g["unique_tree_nodes"]
+    assert sum(len(b) for b in g["branches"]) == g["branch_expanded_nodes"]
+    # every sequence's last node spells the sequence from the root
+    for m, br in enumerate(g["branches"]):
+        assert [tok[j] for j in T.ancestor_path(node_of[m][-1], par)] == br
+
+
+def test_merge_sequences_against_prefix_set():
+    rng = np.random.default_rng(4)
+    for _ in range(20):
+        M, L = int(rng.integers(1, 12)), int(rng.integers(1, 6))
+        seqs = rng.integers(0, 3, size=(M, L)).tolist()
+        for s in seqs:  # ragged ends
+            cut = int(rng.integers(0, L + 1))
+            for d in range(cut, L):
+                s[d] = -1
+        par, tok, node_of = T.merge_sequences(seqs)
+        assert T.parents_valid(par)
+        prefixes = {tuple(s[:d + 1]) for s in seqs for d in range(L) if all(x >= 0 for x in s[:d + 1])}
+        paths = [tuple(tok[j] for j in T.ancestor_path(i, par)) for i in range(len(par))]
+        assert len(paths) == len(set(paths)) and set(paths) == prefixes
+        depth = [T.depth_of(i, par) for i in range(len(par))]
+        assert depth == sorted(depth)  # level order

@@ -29,7 +29,7 @@ __all__ = [
     "tree_greedy_accept_workspace_bytes", "tree_greedy_accept", "tree_greedy_accept_noalloc",
     "tree_sample_accept", "tree_stochastic_accept_workspace_bytes", "tree_stochastic_accept",
     "tree_kv_commit", "tree_expand_mask", "tree_pack_mask", "tree_ddtree_workspace_bytes",
-    "tree_ddtree_build", "MASK_QLEN_ONLY", "MASK_FULL", "ERR_BAD_MASK",
+    "tree_ddtree_build", "tree_merge_sequences", "MASK_QLEN_ONLY", "MASK_FULL", "ERR_BAD_MASK",
     "TTV_OK", "TTV_EINVAL", "TTV_EHIP", "TTV_ENOSPC", "ERR_BAD_PARENT", "ERR_TOO_MANY_NODES",
     "ERR_CAPACITY", "ERR_BLOCK_TABLE", "ERR_ACCEPT", "ERR_BAD_LENGTH", "MAX_TREE_NODES",
     "BLOCK_SIZE", "EXPORTED_SYMBOLS",
@@ -49,7 +49,7 @@ EXPORTED_SYMBOLS = (
     "tree_attention_verify", "tree_greedy_accept_workspace_bytes", "tree_greedy_accept",
     "tree_greedy_accept_noalloc", "tree_sample_accept", "tree_stochastic_accept_workspace_bytes",
     "tree_stochastic_accept", "tree_kv_commit", "tree_expand_mask", "tree_pack_mask",
-    "tree_ddtree_workspace_bytes", "tree_ddtree_build",
+    "tree_ddtree_workspace_bytes", "tree_ddtree_build", "tree_merge_sequences",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -115,6 +115,8 @@ def load_library() -> ctypes.CDLL:
     lib.tree_ddtree_workspace_bytes.argtypes = [I32, I32, I64, I32]
     lib.tree_ddtree_build.restype = ctypes.c_int
     lib.tree_ddtree_build.argtypes = [I32, I32, I64, I32, P, P, P, P, P, SZ, P]
+    lib.tree_merge_sequences.restype = ctypes.c_int
+    lib.tree_merge_sequences.argtypes = [I32, I32, I32, P, I32, P, P, P, P, P]
     lib.tree_kv_commit.restype = ctypes.c_int
     lib.tree_kv_commit.argtypes = [BP, CP, P, P, I32, P, P, P, P, P]
     _LIB = lib
@@ -560,4 +562,30 @@ def tree_ddtree_build(draft_logits, budget: int, out: Optional[Dict] = None, wor
     st = lib.tree_ddtree_build(R, L, V, int(budget), _ptr(draft_logits), _ptr(out["parents"]), _ptr(out["tokens"]),
                                _ptr(out["n_nodes"]), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "tree_ddtree_build")
+    return out
+
+
+def tree_merge_sequences(seqs, max_nodes: int, err=None, out: Optional[Dict] = None, stream=None) -> Dict:
+    """SpecInfer's merged tree of int32 draft sequences [R, M, L] (negative = ended):
+    parents / tokens [R, max_nodes] in level order, n_nodes [R], err [R]."""
+    torch = _torch()
+    lib = load_library()
+    if seqs.dim() != 3:
+        raise ValueError("seqs must be [requests, n_seqs, seq_len]")
+    _dev(seqs, torch.int32, "seqs")
+    R, M, L = (int(x) for x in seqs.shape)
+    dev = seqs.device
+    if out is None:
+        out = {"parents": torch.empty((R, max_nodes), dtype=torch.int32, device=dev),
+               "tokens": torch.empty((R, max_nodes), dtype=torch.int32, device=dev),
+               "n_nodes": torch.empty(R, dtype=torch.int32, device=dev)}
+    if err is None:
+        err = torch.zeros(R, dtype=torch.int32, device=dev)
+    out["err"] = _dev(err, torch.int32, "err", R)
+    for k in ("parents", "tokens"):
+        _dev(out[k], torch.int32, k, R * max_nodes)
+    _dev(out["n_nodes"], torch.int32, "n_nodes", R)
+    st = lib.tree_merge_sequences(R, M, L, _ptr(seqs), int(max_nodes), _ptr(out["parents"]), _ptr(out["tokens"]),
+                                  _ptr(out["n_nodes"]), _ptr(err), _stream(stream))
+    _check(st, "tree_merge_sequences")
     return out

@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libtreeverify.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["abi.hip", "tree_build.hip", "tree_attention.hip", "tree_accept.hip", "tree_commit.hip",
-           "tree_stochastic.hip", "tree_mask.hip", "tree_ddtree.hip"]
+           "tree_stochastic.hip", "tree_mask.hip", "tree_ddtree.hip",
+           "tree_merge.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
