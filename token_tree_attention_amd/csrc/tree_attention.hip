@@ -987,8 +987,17 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         // cannot be merged).
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        for (int j = 2; j < ahead && j < n_tiles; ++j) issue(j, blocks_of(j));
-        if (kPaged && ahead < n_tiles) next_blocks = blocks_of(ahead);
+        // Long-context items over a contiguous cache (8 stages) issue two
+        // tiles per barrier from the loop, so their prologue leaves tiles 6
+        // and 7 to the loop's first barrier.  Paged and precise items issue
+        // one tile per barrier: with a paged cache the pair's block numbers,
+        // prefetched a tile ahead, pushed the kernel into spilling, which ran
+        // it 30-50 % slower (measured on the batched and long Medusa
+        // workloads); contiguous items gained 2-4 %.
+        const bool pairs = !kPaged && !precise;
+        const int pro_end = pairs ? MC::kStagesLong - 2 : ahead;
+        for (int j = 2; j < pro_end && j < n_tiles; ++j) issue(j, blocks_of(j));
+        if (kPaged && pro_end < n_tiles) next_blocks = blocks_of(pro_end);
 
         // The item body, compiled for NMB = 2, 1 and 0 row blocks per wave.
         auto body = [&](auto nmb_c) __attribute__((always_inline)) {
@@ -1184,17 +1193,39 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
             // flight) and a barrier publishes them; the barrier also retires
             // stage (tau - 1) % stages, which the load of tile tau + ahead then
             // reuses.
+            // Long-context classes (8 stages): at even tau, tiles tau + 1 and
+            // tau + 2 must have landed (their scores are computed in iterations
+            // tau and tau + 1); at most tiles tau + 3 .. tau + 5 stay in flight;
+            // the barrier retires tiles tau - 2 and tau - 1, whose stages take
+            // tiles tau + 6 and tau + 7.  Odd tau needs neither wait nor barrier.
             auto advance = [&](auto cls, int tau) __attribute__((always_inline)) {
-                constexpr int kA = (decltype(cls)::value == kClassPrecise ? MC::kStagesShort : MC::kStagesLong) - 1;
-                if (tau + kA < n_tiles) {  // steady state: kA - 2 later tiles stay in flight
-                    if (wave < MC::kIssueWaves) wait_vmcnt<MC::kOpsPerTile * (kA - 2)>();
-                    raw_barrier();
-                    if (tau + kA < n_plain) issue_whole(tau + kA, next_blocks);
-                    else issue(tau + kA, next_blocks);
-                } else {
+                constexpr bool kPrecise = decltype(cls)::value == kClassPrecise;
+                if constexpr (!kPrecise && !kPaged) {
+                    if (tau & 1) return;
                     if (wave < MC::kIssueWaves)
-                        wait_vmcnt_tiles<MC::kOpsPerTile>(min(kA - 2, n_tiles - 2 - tau));
+                        wait_vmcnt_tiles<MC::kOpsPerTile>(min(3, max(0, n_tiles - 3 - tau)));
                     raw_barrier();
+                    const int t0 = tau + MC::kStagesLong - 2;
+                    if (t0 < n_tiles) {
+                        if (t0 < n_plain) issue_whole(t0, next_blocks);
+                        else issue(t0, next_blocks);
+                    }
+                    if (t0 + 1 < n_tiles) {
+                        if (t0 + 1 < n_plain) issue_whole(t0 + 1, next_blocks);
+                        else issue(t0 + 1, next_blocks);
+                    }
+                } else {
+                    constexpr int kA = (kPrecise ? MC::kStagesShort : MC::kStagesLong) - 1;
+                    if (tau + kA < n_tiles) {  // steady state: kA - 2 later tiles stay in flight
+                        if (wave < MC::kIssueWaves) wait_vmcnt<MC::kOpsPerTile * (kA - 2)>();
+                        raw_barrier();
+                        if (tau + kA < n_plain) issue_whole(tau + kA, next_blocks);
+                        else issue(tau + kA, next_blocks);
+                    } else {
+                        if (wave < MC::kIssueWaves)
+                            wait_vmcnt_tiles<MC::kOpsPerTile>(min(kA - 2, n_tiles - 2 - tau));
+                        raw_barrier();
+                    }
                 }
             };
 
@@ -1342,8 +1373,10 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                 phase();
                 // A paged cache's block numbers for the tile the next iteration
                 // loads: read now, so the scalar loads return during its barrier.
-                constexpr int kA = (decltype(cur)::value == kClassPrecise ? MC::kStagesShort : MC::kStagesLong) - 1;
-                if (kPaged && tau + kA + 1 < n_tiles) next_blocks = blocks_of(tau + kA + 1);
+                if constexpr (kPaged) {
+                    const int t = tau + (kCurPrecise ? MC::kStagesShort : MC::kStagesLong);
+                    if (t < n_tiles) next_blocks = blocks_of(t);
+                }
             };
             auto copy_scores = [&](ttv_f32x4 (&dst)[2][kMB], const ttv_f32x4 (&src)[2][kMB]) __attribute__((always_inline)) {
 #pragma unroll
