@@ -987,17 +987,18 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         // cannot be merged).
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        // Long-context items over a contiguous cache (8 stages) issue two
-        // tiles per barrier from the loop, so their prologue leaves tiles 6
-        // and 7 to the loop's first barrier.  Paged and precise items issue
-        // one tile per barrier: with a paged cache the pair's block numbers,
-        // prefetched a tile ahead, pushed the kernel into spilling, which ran
-        // it 30-50 % slower (measured on the batched and long Medusa
-        // workloads); contiguous items gained 2-4 %.
-        const bool pairs = !kPaged && !precise;
+        // Long-context items (8 stages) issue two tiles per barrier from the
+        // loop, so their prologue leaves tiles 6 and 7 to the loop's first
+        // barrier; precise items (4 stages) issue one tile per barrier.
+        // Measured against one tile per barrier: contiguous 2-4 % faster,
+        // paged about 3 % on the long Medusa workload.  A paged pair reads
+        // its block numbers right before the wait that precedes its issue:
+        // holding them from the previous iteration instead pushed the kernel
+        // into spilling and ran it 30-50 % slower.
+        const bool pairs = !precise;
         const int pro_end = pairs ? MC::kStagesLong - 2 : ahead;
         for (int j = 2; j < pro_end && j < n_tiles; ++j) issue(j, blocks_of(j));
-        if (kPaged && pro_end < n_tiles) next_blocks = blocks_of(pro_end);
+        if (kPaged && precise && pro_end < n_tiles) next_blocks = blocks_of(pro_end);
 
         // The item body, compiled for NMB = 2, 1 and 0 row blocks per wave.
         auto body = [&](auto nmb_c) __attribute__((always_inline)) {
@@ -1200,19 +1201,24 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
             // tiles tau + 6 and tau + 7.  Odd tau needs neither wait nor barrier.
             auto advance = [&](auto cls, int tau) __attribute__((always_inline)) {
                 constexpr bool kPrecise = decltype(cls)::value == kClassPrecise;
-                if constexpr (!kPrecise && !kPaged) {
+                if constexpr (!kPrecise) {
                     if (tau & 1) return;
+                    const int t0 = tau + MC::kStagesLong - 2;
+                    // paged: the pair's block numbers are read here, right
+                    // before the wait, so their latency hides behind it
+                    TileBlocks b0 = next_blocks, b1 = next_blocks;
+                    if (kPaged && t0 < n_tiles) b0 = blocks_of(t0);
+                    if (kPaged && t0 + 1 < n_tiles) b1 = blocks_of(t0 + 1);
                     if (wave < MC::kIssueWaves)
                         wait_vmcnt_tiles<MC::kOpsPerTile>(min(3, max(0, n_tiles - 3 - tau)));
                     raw_barrier();
-                    const int t0 = tau + MC::kStagesLong - 2;
                     if (t0 < n_tiles) {
-                        if (t0 < n_plain) issue_whole(t0, next_blocks);
-                        else issue(t0, next_blocks);
+                        if (t0 < n_plain) issue_whole(t0, b0);
+                        else issue(t0, b0);
                     }
                     if (t0 + 1 < n_tiles) {
-                        if (t0 + 1 < n_plain) issue_whole(t0 + 1, next_blocks);
-                        else issue(t0 + 1, next_blocks);
+                        if (t0 + 1 < n_plain) issue_whole(t0 + 1, b1);
+                        else issue(t0 + 1, b1);
                     }
                 } else {
                     constexpr int kA = (kPrecise ? MC::kStagesShort : MC::kStagesLong) - 1;
@@ -1373,8 +1379,8 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                 phase();
                 // A paged cache's block numbers for the tile the next iteration
                 // loads: read now, so the scalar loads return during its barrier.
-                if constexpr (kPaged) {
-                    const int t = tau + (kCurPrecise ? MC::kStagesShort : MC::kStagesLong);
+                if constexpr (kPaged && kCurPrecise) {
+                    const int t = tau + MC::kStagesShort;
                     if (t < n_tiles) next_blocks = blocks_of(t);
                 }
             };
