@@ -57,7 +57,9 @@ _LIB: Optional[ctypes.CDLL] = None
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "libtreeverify.so")
+    """The built library next to this file, or the one TTV_LIBRARY names (for
+    instance the host-sanitized build the argument-checking tests load)."""
+    return os.environ.get("TTV_LIBRARY") or os.path.join(_HERE, "libtreeverify.so")
 
 
 class _CBatch(ctypes.Structure):

@@ -62,5 +62,52 @@ def build(verbose: bool = False, jobs: int = 5) -> str:
     return OUT
 
 
+SANITIZED = os.path.join(BUILD, "san", "libtreeverify_san.so")
+CLANGXX = os.environ.get("CLANGXX", "/opt/rocm/llvm/bin/clang++")
+
+
+def build_host_sanitized() -> str:
+    """The library's host code with AddressSanitizer and UndefinedBehaviorSanitizer,
+    for argument-checking tests on a machine without a GPU.
+
+    Each source is compiled with the sanitizers on the host pass only (the
+    device code is built as usual, uninstrumented) and linked with clang++
+    against the shared sanitizer runtime.  Load it with that runtime
+    preloaded (``sanitizer_runtime()``) and TTV_LIBRARY set to its path.
+    """
+    out_dir = os.path.dirname(SANITIZED)
+    os.makedirs(out_dir, exist_ok=True)
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(out_dir, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmd = [HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-fvisibility=hidden", "-fno-omit-frame-pointer",
+               "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+               "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for cmd, p in procs:
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            failed.append(" ".join(cmd) + "\n" + out)
+    if failed:
+        raise RuntimeError("sanitized host build failed:\n" + "\n\n".join(failed))
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "lib")
+    _run([CLANGXX, "-shared", "-fPIC", "-shared-libsan", "-fsanitize=address,undefined", "-o", SANITIZED, *objs,
+          "-L" + rocm_lib, "-Wl,-rpath," + rocm_lib, "-lamdhip64"])
+    return SANITIZED
+
+
+def sanitizer_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime the sanitized library links."""
+    r = subprocess.run([CLANGXX, "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE, text=True)
+    return r.stdout.strip()
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized())
+    else:
+        print(build(verbose="-v" in sys.argv))
