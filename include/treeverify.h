@@ -16,8 +16,9 @@
  *
  * the dense mask forms for interop (tree_expand_mask, tree_pack_mask), and
  * the draft-tree construction that feeds tree_build: DDTree's best-first
- * top-B tree (tree_ddtree_build) and SpecInfer's prefix merge
- * (tree_merge_sequences).
+ * top-B tree (tree_ddtree_build), SpecInfer's prefix merge
+ * (tree_merge_sequences) and EAGLE's layer-by-layer growth with a global
+ * rerank (tree_eagle_grow).
  *
  * Pages that define the operations (cited by title and section):
  *   [GLOSSARY] "Beam Search、约束解码与 Tree/Self Speculation"
@@ -342,6 +343,33 @@ TTV_API int tree_merge_sequences(int32_t requests, int32_t n_seqs, int32_t seq_l
                                  const int32_t* seqs, int32_t max_nodes, int32_t* parents,
                                  int32_t* tokens, int32_t* n_nodes, int32_t* err,
                                  hipStream_t stream);
+
+/*
+ * tree_eagle_grow -- EAGLE's dynamic tree ([ATLAS] §3: grown layer by layer,
+ * each step expanding the current layer's top-k nodes by top-k children;
+ * §5: a node scores its prefix survival probability, the product of the
+ * draft confidences on its path, and the N_tree most promising nodes are
+ * kept).
+ *
+ * Per request: layer 0 is the k candidates (root_tokens, root_conf); for
+ * each further layer l the k best nodes of layer l - 1, by (score
+ * descending, creation index ascending), are expanded, the j-th of them by
+ * the drafter's row j of k children (child_tokens / child_conf [l - 1][j]);
+ * a child's score is its parent's times its confidence (float64).  The
+ * budget best of all created nodes in the same order (prefix-closed: a
+ * parent precedes its children) are kept and numbered in creation order
+ * (topological: the rows feed tree_build).
+ *
+ * in : root_tokens int32 [requests, k], root_conf float32 [requests, k]
+ *      child_tokens int32 / child_conf float32 [requests, layers - 1, k, k]
+ *      k in [1, 16]; layers in [1, 16]; budget in [1, 1024]
+ * out: parents, tokens int32 [requests, budget] (-1 past n_nodes);
+ *      n_nodes int32 [requests] = min(budget, k + (layers - 1) k^2)
+ */
+TTV_API int tree_eagle_grow(int32_t requests, int32_t k, int32_t layers, const int32_t* root_tokens,
+                            const float* root_conf, const int32_t* child_tokens,
+                            const float* child_conf, int32_t budget, int32_t* parents,
+                            int32_t* tokens, int32_t* n_nodes, hipStream_t stream);
 
 /*
  * tree_sample_accept -- the verifier walk with temperature sampling instead of

@@ -236,3 +236,43 @@ def merge_sequences(seqs):
                 tokens.append(key[1])
             node_of[m][d] = seen[key]
     return parents, tokens, node_of
+
+
+def eagle_grow(root_tokens, root_conf, child_tokens, child_conf, budget: int):
+    """EAGLE-style dynamic tree: layer-by-layer top-k expansion, then a global
+    rerank (test infrastructure only).
+
+    "02 · Token Tree 与 Tree Attention" §3: EAGLE grows the tree layer by layer,
+    expanding the current layer's top-k nodes by top-k children ("layer x
+    topk"); §5: the dynamic tree scores a node by its prefix survival
+    probability (the product of the draft confidences along its path) and
+    keeps the N_tree most promising nodes overall.
+
+    Inputs: root_tokens / root_conf [k]: the first layer's k candidates;
+    child_tokens / child_conf [L-1, k, k]: at layer l (1-based), the drafter's
+    k children of the j-th expanded node of the previous layer.
+    Readings: a node's score is its parent's score times its confidence
+    (float64, in that order); a layer's expanded nodes are its k best by
+    (score descending, creation index ascending), in that order; the kept
+    nodes are the ``budget`` best of all created nodes by the same order (a
+    parent comes before its children in that order, so the kept set is
+    prefix-closed); they are renumbered in creation order.
+    Returns (parents, tokens) of the kept tree.
+    """
+    k = len(root_tokens)
+    par: List[int] = [-1] * k
+    tok: List[int] = [int(t) for t in root_tokens]
+    score: List[float] = [float(c) for c in root_conf]
+    layer = list(range(k))
+    for l in range(len(child_tokens)):
+        expanded = sorted(layer, key=lambda i: (-score[i], i))[:k]
+        layer = []
+        for j, p in enumerate(expanded):
+            for c in range(k):
+                layer.append(len(par))
+                par.append(p)
+                tok.append(int(child_tokens[l][j][c]))
+                score.append(score[p] * float(child_conf[l][j][c]))
+    keep = sorted(sorted(range(len(par)), key=lambda i: (-score[i], i))[:budget])
+    remap = {old: new for new, old in enumerate(keep)}
+    return [-1 if par[i] < 0 else remap[par[i]] for i in keep], [tok[i] for i in keep]

@@ -280,3 +280,11 @@ def test_merge_sequences_rejects(lib):
     assert lib.tree_merge_sequences(1, 4, 4, FAKE, 1025, FAKE, FAKE, FAKE, FAKE, None) == tta.TTV_EINVAL
     assert lib.tree_merge_sequences(1, 4, 4, None, 64, FAKE, FAKE, FAKE, FAKE, None) == tta.TTV_EINVAL
     assert lib.tree_merge_sequences(0, 4, 4, None, 64, None, None, None, None, None) == tta.TTV_OK
+
+
+def test_eagle_grow_rejects(lib):
+    assert lib.tree_eagle_grow(1, 17, 6, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, None) == tta.TTV_EINVAL
+    assert lib.tree_eagle_grow(1, 4, 17, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, None) == tta.TTV_EINVAL
+    assert lib.tree_eagle_grow(1, 4, 6, FAKE, FAKE, FAKE, FAKE, 1025, FAKE, FAKE, FAKE, None) == tta.TTV_EINVAL
+    assert lib.tree_eagle_grow(1, 4, 6, FAKE, FAKE, None, FAKE, 64, FAKE, FAKE, FAKE, None) == tta.TTV_EINVAL
+    assert lib.tree_eagle_grow(0, 4, 6, None, None, None, None, 64, None, None, None, None) == tta.TTV_OK

@@ -99,3 +99,30 @@ def test_merge_sequences_overflow_flag():
     out = tta.tree_merge_sequences(torch.from_numpy(seqs).cuda(), 100)
     torch.cuda.synchronize()
     assert (host(out["err"]) & tta.ERR_TOO_MANY_NODES).all() and (host(out["n_nodes"]) == 0).all()
+
+
+@pytest.mark.parametrize("seed, R, k, L, budget, tie", [(0, 1, 4, 6, 64, False), (1, 5, 4, 6, 64, False),
+                                                        (2, 3, 8, 5, 200, False), (3, 2, 16, 16, 1024, False),
+                                                        (4, 4, 4, 4, 1024, False), (5, 3, 6, 5, 100, True)])
+def test_eagle_grow_matches_oracle(seed, R, k, L, budget, tie):
+    require_gpu()
+    import torch
+    rng = np.random.default_rng(seed)
+    rt = rng.integers(0, 32000, size=(R, k)).astype(np.int32)
+    rc = rng.uniform(0.01, 0.99, size=(R, k)).astype(np.float32)
+    ct = rng.integers(0, 32000, size=(R, L - 1, k, k)).astype(np.int32)
+    cc = rng.uniform(0.01, 0.99, size=(R, L - 1, k, k)).astype(np.float32)
+    if tie:  # confidences on a coarse grid: many equal path products
+        rc = (np.round(rc * 4) / 4 + 0.25).clip(0.25, 0.75).astype(np.float32)
+        cc = (np.round(cc * 2) / 2).clip(0.5, 0.5).astype(np.float32)
+    say(f"tree_eagle_grow R={R} k={k} L={L} budget={budget} tie={tie}")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    out = tta.tree_eagle_grow(t(rt), t(rc), t(ct), t(cc), budget)
+    torch.cuda.synchronize()
+    par, tok, nn = host(out["parents"]), host(out["tokens"]), host(out["n_nodes"])
+    for r in range(R):
+        rp, rtk = O_tree.eagle_grow(rt[r], rc[r], ct[r], cc[r], budget)
+        assert nn[r] == len(rp)
+        np.testing.assert_array_equal(par[r, :nn[r]], rp, err_msg=f"parents {r}")
+        np.testing.assert_array_equal(tok[r, :nn[r]], rtk, err_msg=f"tokens {r}")
+        assert (par[r, nn[r]:] == -1).all()

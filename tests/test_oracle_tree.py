@@ -229,3 +229,54 @@ def test_merge_sequences_against_prefix_set():
         assert len(paths) == len(set(paths)) and set(paths) == prefixes
         depth = [T.depth_of(i, par) for i in range(len(par))]
         assert depth == sorted(depth)  # level order
+
+
+def test_eagle_grow_hand_case():
+    # k = 2, two layers: roots A (0.9), B (0.5); layer 1 expands both:
+    # A -> C (0.9 * 0.8 = 0.72), D (0.9 * 0.1 = 0.09); B -> E (0.5 * 0.6 = 0.30), F (0.05)
+    A, B, C, D, E, F = 10, 11, 12, 13, 14, 15
+    par, tok = T.eagle_grow([A, B], [0.9, 0.5], [[[C, D], [E, F]]], [[[0.8, 0.1], [0.6, 0.1]]], 4)
+    # best four: A 0.9, C 0.72, B 0.5, E 0.30; creation order A, B, C, E
+    assert tok == [A, B, C, E] and par == [-1, -1, 0, 1]
+    # the second layer expands only the two best of layer 1 (C, E), in score order
+    par, tok = T.eagle_grow([A, B], [0.9, 0.5], [[[C, D], [E, F]], [[1, 2], [3, 4]]],
+                            [[[0.8, 0.1], [0.6, 0.1]], [[0.9, 0.5], [0.99, 0.2]]], 7)
+    assert tok == [A, B, C, E, 1, 2, 3] and par == [-1, -1, 0, 1, 2, 2, 3]
+
+
+def test_eagle_grow_selection_by_path_product():
+    """Every kept node's path product (recomputed from the inputs along its
+    path) is at least every dropped node's; with the whole budget the tree
+    holds k roots and k * k children per further layer, each layer's children
+    hanging off the k best nodes of the layer before."""
+    rng = np.random.default_rng(6)
+    for _ in range(30):
+        k, L = int(rng.integers(1, 5)), int(rng.integers(1, 5))
+        rt = np.arange(k)
+        rc = rng.uniform(0.01, 0.99, size=k)
+        ct = rng.integers(0, 1000, size=(L - 1, k, k)) + 1000 * np.arange(1, L)[:, None, None]
+        cc = rng.uniform(0.01, 0.99, size=(L - 1, k, k))
+        total = k + (L - 1) * k * k
+        par, tok = T.eagle_grow(rt, rc, ct, cc, total)
+        assert len(par) == total and T.parents_valid(par)
+        # path product of every node: the confidence of each (layer, expanded slot, child)
+        conf = {}
+        for i in range(k):
+            conf[i] = rc[i]
+        depth = [T.depth_of(i, par) for i in range(total)]
+        score = [0.0] * total
+        for i in range(total):
+            if par[i] < 0:
+                score[i] = rc[tok[i]]
+                continue
+            l = depth[i]
+            # siblings of i are the children of par[i]; their slot j is par[i]'s rank in its layer
+            layer_prev = [x for x in range(total) if depth[x] == l - 1]
+            ranked = sorted(layer_prev, key=lambda x: (-score[x], x))[:k]
+            j = ranked.index(par[i])
+            c = [x for x in range(total) if par[x] == par[i]].index(i)
+            score[i] = score[par[i]] * cc[l - 1][j][c]
+        for budget in range(1, total + 1):
+            kp, kt = T.eagle_grow(rt, rc, ct, cc, budget)
+            kept = sorted(range(total), key=lambda x: (-score[x], x))[:budget]
+            assert sorted(tok[x] for x in kept) == sorted(kt)

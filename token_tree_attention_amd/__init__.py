@@ -29,7 +29,7 @@ __all__ = [
     "tree_greedy_accept_workspace_bytes", "tree_greedy_accept", "tree_greedy_accept_noalloc",
     "tree_sample_accept", "tree_stochastic_accept_workspace_bytes", "tree_stochastic_accept",
     "tree_kv_commit", "tree_expand_mask", "tree_pack_mask", "tree_ddtree_workspace_bytes",
-    "tree_ddtree_build", "tree_merge_sequences", "MASK_QLEN_ONLY", "MASK_FULL", "ERR_BAD_MASK",
+    "tree_ddtree_build", "tree_merge_sequences", "tree_eagle_grow", "MASK_QLEN_ONLY", "MASK_FULL", "ERR_BAD_MASK",
     "TTV_OK", "TTV_EINVAL", "TTV_EHIP", "TTV_ENOSPC", "ERR_BAD_PARENT", "ERR_TOO_MANY_NODES",
     "ERR_CAPACITY", "ERR_BLOCK_TABLE", "ERR_ACCEPT", "ERR_BAD_LENGTH", "MAX_TREE_NODES",
     "BLOCK_SIZE", "EXPORTED_SYMBOLS",
@@ -49,7 +49,7 @@ EXPORTED_SYMBOLS = (
     "tree_attention_verify", "tree_greedy_accept_workspace_bytes", "tree_greedy_accept",
     "tree_greedy_accept_noalloc", "tree_sample_accept", "tree_stochastic_accept_workspace_bytes",
     "tree_stochastic_accept", "tree_kv_commit", "tree_expand_mask", "tree_pack_mask",
-    "tree_ddtree_workspace_bytes", "tree_ddtree_build", "tree_merge_sequences",
+    "tree_ddtree_workspace_bytes", "tree_ddtree_build", "tree_merge_sequences", "tree_eagle_grow",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -119,6 +119,8 @@ def load_library() -> ctypes.CDLL:
     lib.tree_ddtree_build.argtypes = [I32, I32, I64, I32, P, P, P, P, P, SZ, P]
     lib.tree_merge_sequences.restype = ctypes.c_int
     lib.tree_merge_sequences.argtypes = [I32, I32, I32, P, I32, P, P, P, P, P]
+    lib.tree_eagle_grow.restype = ctypes.c_int
+    lib.tree_eagle_grow.argtypes = [I32, I32, I32, P, P, P, P, I32, P, P, P, P]
     lib.tree_kv_commit.restype = ctypes.c_int
     lib.tree_kv_commit.argtypes = [BP, CP, P, P, I32, P, P, P, P, P]
     _LIB = lib
@@ -590,4 +592,35 @@ def tree_merge_sequences(seqs, max_nodes: int, err=None, out: Optional[Dict] = N
     st = lib.tree_merge_sequences(R, M, L, _ptr(seqs), int(max_nodes), _ptr(out["parents"]), _ptr(out["tokens"]),
                                   _ptr(out["n_nodes"]), _ptr(err), _stream(stream))
     _check(st, "tree_merge_sequences")
+    return out
+
+
+def tree_eagle_grow(root_tokens, root_conf, child_tokens, child_conf, budget: int, out: Optional[Dict] = None,
+                    stream=None) -> Dict:
+    """EAGLE's layer-by-layer tree: root_tokens / root_conf [R, k], child_tokens /
+    child_conf [R, L-1, k, k] -> parents / tokens [R, budget], n_nodes [R]."""
+    torch = _torch()
+    lib = load_library()
+    if root_tokens.dim() != 2 or child_tokens.dim() != 4:
+        raise ValueError("root_tokens must be [R, k] and child_tokens [R, L-1, k, k]")
+    R, k = (int(x) for x in root_tokens.shape)
+    L = int(child_tokens.shape[1]) + 1
+    if tuple(child_tokens.shape) != (R, L - 1, k, k) or tuple(child_conf.shape) != tuple(child_tokens.shape):
+        raise ValueError("child_tokens and child_conf must be [R, L-1, k, k]")
+    _dev(root_tokens, torch.int32, "root_tokens")
+    _dev(root_conf, torch.float32, "root_conf", R * k)
+    _dev(child_tokens, torch.int32, "child_tokens")
+    _dev(child_conf, torch.float32, "child_conf")
+    dev = root_tokens.device
+    if out is None:
+        out = {"parents": torch.empty((R, budget), dtype=torch.int32, device=dev),
+               "tokens": torch.empty((R, budget), dtype=torch.int32, device=dev),
+               "n_nodes": torch.empty(R, dtype=torch.int32, device=dev)}
+    for key in ("parents", "tokens"):
+        _dev(out[key], torch.int32, key, R * budget)
+    _dev(out["n_nodes"], torch.int32, "n_nodes", R)
+    st = lib.tree_eagle_grow(R, k, L, _ptr(root_tokens), _ptr(root_conf), _ptr(child_tokens), _ptr(child_conf),
+                             int(budget), _ptr(out["parents"]), _ptr(out["tokens"]), _ptr(out["n_nodes"]),
+                             _stream(stream))
+    _check(st, "tree_eagle_grow")
     return out
