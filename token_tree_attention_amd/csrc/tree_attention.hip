@@ -1320,14 +1320,17 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                         packed[mb][e] = pack_bf16(p[mb][2 * e], p[mb][2 * e + 1]);
                 };
                 // A phase ends in a scheduling fence; inside it, the scheduler is
-                // asked to alternate one MFMA with two VALU instructions and one
+                // asked to alternate one MFMA with one VALU instruction and one
                 // LDS read, so the wave issues VALU work and operand reads while
                 // each MFMA runs (MFMA and VALU co-issue only when interleaved).
+                // Measured against one MFMA per two VALU: about 2 % faster on the
+                // long Medusa workload, the same elsewhere; three VALU, no
+                // pattern, or a raised wave priority in the loop body were slower.
                 auto phase = [] {
 #pragma unroll
                     for (int i = 0; i < 9; ++i) {
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+                        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
                         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
                     }
                     __builtin_amdgcn_sched_barrier(0);
