@@ -488,6 +488,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="medusa_long", choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--seeds", default="0,1,2",
+                    help="input seeds the headline workload is also measured with (reported per seed)")
     ap.add_argument("--replays", type=int, default=10, help="timed replays for the p10/p50/p90")
     ap.add_argument("--rotate-mb", type=float, default=600.0,
                     help="rotate input copies until this many MB are in play (defeats the MALL)")
@@ -541,6 +543,18 @@ def main():
         else:
             del wl
     head = results[args.workload]
+    per_seed = []
+    for sd in [int(x) for x in args.seeds.split(",") if x.strip()]:
+        if sd == args.seed:
+            r = head
+        else:
+            t0 = time.perf_counter()
+            r = measure(synth.make_workload(WORKLOADS[args.workload], sd), args, dev)
+            print(f"[bench] {args.workload} seed {sd}: {time.perf_counter() - t0:.1f} s, "
+                  f"{r['us_per_step']:.1f} us/step", file=sys.stderr, flush=True)
+        per_seed.append({"seed": sd, "us_per_step": r["us_per_step"], "tokens_per_s": r["tokens_per_s"],
+                         "attention_us": r["roofline"]["attention_us"], "frac": r["roofline"]["frac"],
+                         "nodes": r["config"]["tree_nodes_total"], "ctx_tokens": r["config"]["ctx_tokens"]})
     result = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
@@ -566,6 +580,7 @@ def main():
         "timing": "K steps in one HIP graph replay (after two untimed replays); p10/p50/p90 over "
                   f"{head['replays']} replays",
         "per_config": {name: summary(r) for name, r in results.items()},
+        "seeds": per_seed,
         "achievable_bandwidth": achievable_bandwidth(dev),
     }
     if not args.no_cpu:
