@@ -458,6 +458,174 @@ def measure(wl, args, dev):
     return res
 
 
+def graph_call_us(fn, K, reps=3):
+    """fn() K times in one HIP graph: two untimed replays, then the median of
+    `reps` timed ones (HIP events on the capture stream), in us per call."""
+    import numpy as np
+    import torch
+    stream = torch.cuda.current_stream()
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(K):
+            fn()
+    g.replay()
+    g.replay()
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del g
+    return float(np.median(ts)) / K * 1e3
+
+
+def measure_next(args, dev):
+    """The calls beyond the four-step round, each timed like the round's calls
+    (K back to back in a HIP graph) on seeded inputs of a workload's shape,
+    with its algorithmic bytes against the 8 TB/s HBM peak where it streams
+    memory, else its latency:
+    - tree_sample_accept (Gumbel-max temperature sampling) and
+      tree_stochastic_accept (min(1, p/q) walk) on the batched workload;
+    - tree_ddtree_build on the DDTree workload's draft logits (4 requests, 16
+      depths, vocab 151936, budget 1024);
+    - tree_eagle_grow (32 requests of the EAGLE tree: 4 roots, 6 layers,
+      budget 64) and tree_merge_sequences (32 requests of 64 drafts of 8
+      tokens over 4 symbols);
+    - tree_expand_mask / tree_pack_mask of the DDTree workload (T = 4096) in
+      both dense forms."""
+    import numpy as np
+    import torch
+
+    import synth
+    import token_tree_attention_amd as tta
+    from synth.device import to_device
+
+    K = max(1, args.steps)
+    res = {}
+
+    def hbm(name, us, nbytes, **extra):
+        res[name] = {"us": us, "algorithmic_bytes": int(nbytes), "gbs": nbytes / (us * 1e-6) / 1e9,
+                     "hbm_frac": nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), **extra}
+
+    # -- acceptance variants on the batched workload
+    cfg = WORKLOADS["batched"]
+    wl = synth.make_workload(cfg, args.seed)
+    d = to_device(wl, dev)
+    T, B, V = wl.total_nodes, wl.batch, wl.vocab
+    R = T + B
+    esz = 4 if wl.logits_dtype == "fp32" else 2
+    bt = tta.Batch(d["node_offsets"], d["ctx_lens"], wl.n_max, total_nodes=T)
+    meta = tta.tree_build(bt, d["parents"])
+    g = torch.from_numpy(synth.gumbel_noise(args.seed, cfg, R, V)).to(dev)
+    kids = {}
+    for b in range(B):
+        s0, e0 = int(wl.node_offsets[b]), int(wl.node_offsets[b + 1])
+        for i in range(s0, e0):
+            p = int(wl.parents[i])
+            kids.setdefault(s0 + b + (0 if p < 0 else 1 + p), []).append(int(wl.tokens[i]))
+    q = torch.from_numpy(synth.draft_distributions(args.seed, cfg, R, V, lambda r: kids.get(r, []), 20.0)).to(dev)
+    u = torch.from_numpy(synth.uniforms(args.seed, cfg, T)).to(dev)
+    max_accept = 64
+    out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+           "accepted_nodes": torch.empty((B, max_accept), dtype=torch.int32, device=dev),
+           "out_tokens": torch.empty((B, max_accept + 1), dtype=torch.int32, device=dev),
+           "row_argmax": torch.empty(R, dtype=torch.int32, device=dev)}
+    ws = torch.empty(max(256, tta.tree_greedy_accept_workspace_bytes(bt, V)), dtype=torch.uint8, device=dev)
+    sws = torch.empty(max(256, tta.tree_stochastic_accept_workspace_bytes(bt, V)), dtype=torch.uint8, device=dev)
+    err = meta["err"]
+
+    def sample():
+        tta.tree_sample_accept(bt, d["logits"], g, 0.8, d["tokens"], meta["retrieve_next_token"],
+                               meta["retrieve_next_sibling"], max_accept, err, out=out, workspace=ws)
+    hbm("tree_sample_accept", graph_call_us(sample, K), R * V * (esz + 4), workload="batched", temperature=0.8)
+    sout = {k: v for k, v in out.items() if k != "row_argmax"}
+
+    def stochastic():
+        tta.tree_stochastic_accept(bt, d["logits"], 1.0, q, u, g, d["tokens"], meta["retrieve_next_token"],
+                                   meta["retrieve_next_sibling"], max_accept, err, out=sout, workspace=sws)
+    us = graph_call_us(stochastic, K)
+    a = sout["accept_len"].cpu().numpy()
+    if (err.cpu().numpy() != 0).any():
+        raise RuntimeError("device error bits in the acceptance variants")
+    # visited rows: a_b + 1 per request (logits and draft row each), the final row's noise, the uniforms
+    hbm("tree_stochastic_accept", us, int(((a + 1) * V * (esz + 4)).sum() + B * V * 4 + T * 4),
+        workload="batched", temperature=1.0, draft_boost=20.0, mean_accept_len=float(a.mean()),
+        bound_note="one workgroup per request walks its visited rows: latency of dependent full-vocab passes")
+    del g, q, u, ws, sws, d
+
+    # -- DDTree construction
+    cfg = WORKLOADS["ddtree"]
+    Rq, L, Vd, budget = 4, 16, 151936, 1024
+    z = torch.from_numpy(synth.draft_logits(args.seed, cfg, Rq, L, Vd)).to(dev)
+    dd_out = {"parents": torch.empty((Rq, budget), dtype=torch.int32, device=dev),
+              "tokens": torch.empty((Rq, budget), dtype=torch.int32, device=dev),
+              "n_nodes": torch.empty(Rq, dtype=torch.int32, device=dev)}
+    dd_ws = torch.empty(tta.tree_ddtree_workspace_bytes(Rq, L, Vd, budget), dtype=torch.uint8, device=dev)
+    hbm("tree_ddtree_build", graph_call_us(lambda: tta.tree_ddtree_build(z, budget, out=dd_out, workspace=dd_ws), K),
+        Rq * L * Vd * 4 + Rq * budget * 8, requests=Rq, depths=L, vocab=Vd, budget=budget)
+    del z, dd_ws
+
+    # -- EAGLE growth and SpecInfer merge (latency)
+    rng = np.random.default_rng([args.seed, 1, 99])
+    Re, k, Le, be = 32, 4, 6, 64
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    rt = t(rng.integers(0, 128256, size=(Re, k)).astype(np.int32))
+    rc = t(rng.uniform(0.01, 0.99, size=(Re, k)).astype(np.float32))
+    ct = t(rng.integers(0, 128256, size=(Re, Le - 1, k, k)).astype(np.int32))
+    cc = t(rng.uniform(0.01, 0.99, size=(Re, Le - 1, k, k)).astype(np.float32))
+    eg = {"parents": torch.empty((Re, be), dtype=torch.int32, device=dev),
+          "tokens": torch.empty((Re, be), dtype=torch.int32, device=dev),
+          "n_nodes": torch.empty(Re, dtype=torch.int32, device=dev)}
+    res["tree_eagle_grow"] = {"us": graph_call_us(lambda: tta.tree_eagle_grow(rt, rc, ct, cc, be, out=eg), K),
+                              "requests": Re, "k": k, "layers": Le, "budget": be, "bound": "latency"}
+    Rm, M, Lm = 32, 64, 8
+    seqs = rng.integers(0, 4, size=(Rm, M, Lm)).astype(np.int32)
+    ends = rng.integers(1, Lm + 1, size=(Rm, M))
+    for r in range(Rm):
+        for m in range(M):
+            seqs[r, m, ends[r, m]:] = -1
+    seqs = t(seqs)
+    mg = {"parents": torch.empty((Rm, 1024), dtype=torch.int32, device=dev),
+          "tokens": torch.empty((Rm, 1024), dtype=torch.int32, device=dev),
+          "n_nodes": torch.empty(Rm, dtype=torch.int32, device=dev)}
+    merr = torch.zeros(Rm, dtype=torch.int32, device=dev)
+    res["tree_merge_sequences"] = {
+        "us": graph_call_us(lambda: tta.tree_merge_sequences(seqs, 1024, err=merr, out=mg), K),
+        "requests": Rm, "sequences": M, "seq_len": Lm, "alphabet": 4, "bound": "latency",
+        "mean_nodes": float(mg["n_nodes"].float().mean().item())}
+
+    # -- dense mask forms of the DDTree workload
+    wl = synth.make_trees(WORKLOADS["ddtree"], args.seed)
+    i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
+    bt = tta.Batch(i32(wl.node_offsets), i32(wl.ctx_lens), wl.n_max, total_nodes=wl.total_nodes)
+    meta = tta.tree_build(bt, i32(wl.parents))
+    T, W = wl.total_nodes, meta["mask"].shape[1]
+    for mode, name in ((tta.MASK_QLEN_ONLY, "qlen_only"), (tta.MASK_FULL, "full")):
+        stride = wl.n_max if mode == tta.MASK_QLEN_ONLY else int((wl.ctx_lens + np.diff(wl.node_offsets)).max())
+        stride = -(-stride // 16) * 16
+        dense = torch.empty((T, stride), dtype=torch.uint8, device=dev)
+        packed = torch.empty((T, W), dtype=torch.int32, device=dev)
+        hbm(f"tree_expand_mask_{name}",
+            graph_call_us(lambda: tta.tree_expand_mask(bt, meta["mask"], mode, stride, meta["err"], out=dense), K),
+            T * stride + T * W * 4, nodes=T, row_stride=stride)
+        hbm(f"tree_pack_mask_{name}",
+            graph_call_us(lambda: tta.tree_pack_mask(bt, dense, mode, meta["err"], mask_words=W, out=packed), K),
+            T * stride + T * W * 4, nodes=T, row_stride=stride)
+        if (meta["err"].cpu().numpy() != 0).any() or not torch.equal(packed, meta["mask"]):
+            raise RuntimeError(f"dense mask round trip ({name}) failed")
+        del dense, packed
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def summary(res):
     """The per_config entry: the figures a reader compares across workloads."""
     r = res["roofline"]
@@ -497,6 +665,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", action="store_true", help="the headline workload only (no per_config)")
     ap.add_argument("--deep", action="store_true", help="also ddtree_deep in per_config")
+    ap.add_argument("--no-next", action="store_true", help="skip the calls beyond the four-step round")
+    ap.add_argument("--next-only", action="store_true",
+                    help="time only the calls beyond the four-step round (one JSON object)")
     ap.add_argument("--eager-only", action="store_true",
                     help="host-launched steps of the headline only, no graphs (for counter collection)")
     ap.add_argument("--copy-reference", type=float, default=0.0, metavar="MB",
@@ -524,6 +695,9 @@ def main():
     tta.load_library()
     if args.eager_only:
         eager_only(args, dev)
+        return
+    if args.next_only:
+        print(json.dumps({"next": measure_next(args, dev)}))
         return
 
     names = [args.workload] if args.only else list(PER_CONFIG) + (["ddtree_deep"] if args.deep else [])
@@ -583,6 +757,10 @@ def main():
         "seeds": per_seed,
         "achievable_bandwidth": achievable_bandwidth(dev),
     }
+    if not args.no_next:
+        t0 = time.perf_counter()
+        result["next"] = measure_next(args, dev)
+        print(f"[bench] calls beyond the round: {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(head_wl, args.cpu_budget)
     print(json.dumps(result))

@@ -16,29 +16,58 @@
 // extensions; node i is the i-th popped prefix.
 //
 // Kernel 1, one 1024-thread workgroup per (depth, request): radix select of
-// the K-th largest order key over the vocab (four 8-bit histogram passes),
-// a gather of the elements above it plus the lowest-index ties at it, a
-// bitonic sort of the K candidates in LDS, then log q (the sum by one thread
-// in rank order, as the definition adds it).
-// Kernel 2, one workgroup per request: the heap of Algorithm 1 in LDS, run by
-// one lane; an entry holds its score, its rank tuple packed for comparison
-// (11 bits per depth, rank + 1, 5 depths per 64-bit word, depth 0 in the
-// most significant field, so a shorter tuple compares below its
-// extensions), its parent node, depth and last rank.
+// the K-th largest 64-bit key (order key of the logit, then the complement of
+// the token id, so keys are distinct and the lowest ids win ties) in 8-bit
+// digits, the low word's passes only when ties at the K-th logit must be
+// split; a gather of the K keys at or above it; a bitonic sort of them in
+// LDS; then log q, the exponentials in parallel and their sum by one thread
+// in rank order, as the definition adds it.  Every pass over the vocab keeps
+// 32 loads per thread in flight.
+// Kernel 2, one wave per request: Algorithm 1's priority queue as a frontier
+// array in LDS (at most budget + 1 live entries: a popped entry's slot takes
+// its next sibling, its first child takes a new slot), each lane caching the
+// best entry among the slots it owns; a pop is a wave-wide maximum of the
+// cached scores (the rank tuples, packed for comparison, decide exact ties:
+// 11 bits per depth, rank + 1, 5 depths per 64-bit word, depth 0 in the most
+// significant field, so a shorter tuple compares below its extensions).
 
 #include "ttv_device.h"
 
 namespace {
 
 constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / TTV_WAVE;
+constexpr int kBatch = 32;         // loads in flight per thread in a vocab pass
 constexpr int kMaxK = 1024;
 constexpr int kMaxDepths = 20;     // 4 key words x 5 fields
 constexpr int kKeyWords = 4;
-constexpr int kMaxHeap = kMaxK + 2;
+constexpr int kHeapLanes = TTV_WAVE;
+constexpr int kMaxSlots = kMaxK + kHeapLanes;  // live frontier entries: at most budget + 1
 
 __device__ __forceinline__ float key_to_float(uint32_t k) {
     const uint32_t bits = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
     return __uint_as_float(bits);
+}
+
+// f(v, key) for every v < vocab, key = (order key of z[v]) << 32 | ~v; each
+// thread loads kBatch values before using any.
+template <typename F>
+__device__ __forceinline__ void for_each_key(const float* __restrict__ row, int64_t vocab, F&& f) {
+    const int tid = threadIdx.x;
+    for (int64_t base = 0; base < vocab; base += (int64_t)kBatch * kTopkThreads) {
+        float x[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int64_t v = base + (int64_t)j * kTopkThreads + tid;
+            x[j] = v < vocab ? row[v] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int64_t v = base + (int64_t)j * kTopkThreads + tid;
+            if (v < vocab)
+                f(((uint64_t)ttv_order_key(__float_as_uint(x[j])) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v));
+        }
+    }
 }
 
 __global__ __launch_bounds__(kTopkThreads) void ddtree_topk_kernel(
@@ -46,24 +75,27 @@ __global__ __launch_bounds__(kTopkThreads) void ddtree_topk_kernel(
     int32_t* __restrict__ tok_out, double* __restrict__ logq_out) {
     __shared__ uint32_t s_hist[256];
     __shared__ uint32_t s_sel[2];  // digit, count above it
+    __shared__ uint32_t s_count;
     __shared__ uint64_t s_cand[kMaxK];
-    __shared__ uint32_t s_wsum[2][kTopkThreads / TTV_WAVE];
+    __shared__ double s_exp[kMaxK];
     __shared__ double s_lse;
     const int d = blockIdx.x;
     const int r = blockIdx.y;
     const int tid = threadIdx.x;
     const float* row = z + ((int64_t)r * depths + d) * vocab;
 
-    // ---- radix select: the K-th largest order key -------------------------
-    uint32_t prefix = 0, pmask = 0;
+    // ---- radix select of the K-th largest key ----------------------------
+    // High word first; the low word (the token id) only splits ties at the
+    // K-th logit, so its passes run only when the elements equal to the
+    // selected high word outnumber the slots left for them.
+    uint64_t prefix = 0, pmask = 0;
     uint32_t k_rem = (uint32_t)K;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int shift = 56; shift >= 0; shift -= 8) {
         for (int i = tid; i < 256; i += kTopkThreads) s_hist[i] = 0;
         __syncthreads();
-        for (int64_t v = tid; v < vocab; v += kTopkThreads) {
-            const uint32_t u = ttv_order_key(__float_as_uint(row[v]));
-            if ((u & pmask) == prefix) atomicAdd(&s_hist[(u >> shift) & 255u], 1u);
-        }
+        for_each_key(row, vocab, [&](uint64_t key) {
+            if ((key & pmask) == prefix) atomicAdd(&s_hist[(uint32_t)(key >> shift) & 255u], 1u);
+        });
         __syncthreads();
         if (tid == 0) {
             uint32_t above = 0;
@@ -74,56 +106,37 @@ __global__ __launch_bounds__(kTopkThreads) void ddtree_topk_kernel(
             }
             s_sel[0] = (uint32_t)dig;
             s_sel[1] = above;
+            // after the high word: stop when every element at this prefix is kept
+            s_count = (shift == 32 && above + s_hist[dig] == k_rem) ? 1u : 0u;
         }
         __syncthreads();
-        prefix |= s_sel[0] << shift;
-        pmask |= 255u << shift;
+        prefix |= (uint64_t)s_sel[0] << shift;
+        pmask |= (uint64_t)255 << shift;
         k_rem -= s_sel[1];
-        __syncthreads();  // s_sel and s_hist are rewritten by the next pass
+        const bool done = s_count != 0;
+        __syncthreads();  // s_sel, s_count and s_hist are rewritten next
+        if (done) break;
     }
-    const uint32_t vk = prefix;       // the K-th largest key
-    const uint32_t ties = k_rem;      // elements equal to vk that are kept (lowest indices)
-    const uint32_t n_gt = (uint32_t)K - ties;
-
-    // ---- gather: contiguous index segments, block scans of the counts -----
-    const int64_t seg = (vocab + kTopkThreads - 1) / kTopkThreads;
-    const int64_t v0 = (int64_t)tid * seg, v1 = min(vocab, v0 + seg);
-    uint32_t c_gt = 0, c_eq = 0;
-    for (int64_t v = v0; v < v1; ++v) {
-        const uint32_t u = ttv_order_key(__float_as_uint(row[v]));
-        c_gt += u > vk;
-        c_eq += u == vk;
-    }
-    const int lane = tid & 63, wv = tid >> 6;
-    uint32_t sg = c_gt, se = c_eq;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t tg = __shfl_up(sg, off), te = __shfl_up(se, off);
-        if (lane >= off) {
-            sg += tg;
-            se += te;
-        }
-    }
-    if (lane == 63) {
-        s_wsum[0][wv] = sg;
-        s_wsum[1][wv] = se;
-    }
+    // Keys kept: those above `prefix` on the bits of pmask, and those equal to
+    // it there (exactly k_rem of them, all of them when the passes stopped early).
+    if (tid == 0) s_count = 0;
     for (int i = tid; i < kMaxK; i += kTopkThreads) s_cand[i] = 0ull;
     __syncthreads();
-    uint32_t pg = sg - c_gt, pe = se - c_eq;
-    for (int w = 0; w < wv; ++w) {
-        pg += s_wsum[0][w];
-        pe += s_wsum[1][w];
-    }
-    for (int64_t v = v0; v < v1; ++v) {
-        const uint32_t u = ttv_order_key(__float_as_uint(row[v]));
-        const uint64_t key = ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
-        if (u > vk) s_cand[pg++] = key;
-        else if (u == vk) {
-            if (pe < ties) s_cand[n_gt + pe] = key;
-            ++pe;
+    const int lane = tid & 63;
+    for_each_key(row, vocab, [&](uint64_t key) {
+        const bool keep = (key & pmask) >= prefix;
+        // wave-aggregated slot claim (candidate order is irrelevant: sorted next)
+        const uint64_t m = __ballot(keep);
+        if (m == 0) return;
+        uint32_t base = 0;
+        const int leader = __builtin_ctzll(m);
+        if (lane == leader) base = atomicAdd(&s_count, (uint32_t)__builtin_popcountll(m));
+        base = __shfl(base, leader);
+        if (keep) {
+            const uint32_t pos = base + (uint32_t)__builtin_popcountll(m & ((1ull << lane) - 1ull));
+            if (pos < (uint32_t)kMaxK) s_cand[pos] = key;
         }
-    }
+    });
     __syncthreads();
 
     // ---- bitonic sort, descending ------------------------------------------
@@ -144,11 +157,14 @@ __global__ __launch_bounds__(kTopkThreads) void ddtree_topk_kernel(
         }
     }
 
-    // ---- log q over the kept K, the sum in rank order ------------------------
+    // ---- log q over the kept K: exp(z_r - z_1) in parallel, the sum in rank order
+    const double m = (double)key_to_float((uint32_t)(s_cand[0] >> 32));
+    for (int i = tid; i < K; i += kTopkThreads)
+        s_exp[i] = exp((double)key_to_float((uint32_t)(s_cand[i] >> 32)) - m);
+    __syncthreads();
     if (tid == 0) {
-        const double m = (double)key_to_float((uint32_t)(s_cand[0] >> 32));
         double s = 0.0;
-        for (int i = 0; i < K; ++i) s += exp((double)key_to_float((uint32_t)(s_cand[i] >> 32)) - m);
+        for (int i = 0; i < K; ++i) s += s_exp[i];
         s_lse = m + log(s);
     }
     __syncthreads();
@@ -171,97 +187,172 @@ __device__ __forceinline__ bool key_less(const HeapKey& a, const HeapKey& b) {
     return false;
 }
 
+// Field `depth` of the packed tuple := rank + 1.  The word is picked by
+// comparison, not by indexing, so the key stays in registers.
 __device__ __forceinline__ void key_set(HeapKey& k, int depth, int rank) {
     const int w = depth / 5, sh = 11 * (4 - depth % 5);
-    k.w[w] = (k.w[w] & ~((uint64_t)2047 << sh)) | ((uint64_t)(rank + 1) << sh);
+#pragma unroll
+    for (int i = 0; i < kKeyWords; ++i)
+        if (i == w) k.w[i] = (k.w[i] & ~((uint64_t)2047 << sh)) | ((uint64_t)(rank + 1) << sh);
 }
 
-__global__ __launch_bounds__(64) void ddtree_heap_kernel(
+// Wave-wide maximum of a double, in every lane: DPP steps inside each row of
+// 16 lanes, then the cross-row swaps (as 32-bit halves, moved together).
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, kCtrl, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), kCtrl, 0xF, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double wave_max_f64(double v) {
+    v = fmax(v, dpp_f64<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = fmax(v, dpp_f64<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fmax(v, dpp_f64<0x141>(v));  // row_half_mirror
+    v = fmax(v, dpp_f64<0x140>(v));  // row_mirror
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    v = fmax(__longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0])),
+             __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1])));
+    const uint64_t w = (uint64_t)__double_as_longlong(v);
+    auto lo2 = __builtin_amdgcn_permlane32_swap((uint32_t)w, (uint32_t)w, false, false);
+    auto hi2 = __builtin_amdgcn_permlane32_swap((uint32_t)(w >> 32), (uint32_t)(w >> 32), false, false);
+    return fmax(__longlong_as_double((long long)(((uint64_t)hi2[0] << 32) | lo2[0])),
+                __longlong_as_double((long long)(((uint64_t)hi2[1] << 32) | lo2[1])));
+}
+
+__global__ __launch_bounds__(kHeapLanes) void ddtree_heap_kernel(
     const int32_t* __restrict__ toks, const double* __restrict__ logq, int32_t depths, int32_t K,
     int32_t budget, int32_t* __restrict__ parents, int32_t* __restrict__ tokens,
     int32_t* __restrict__ n_nodes) {
-    __shared__ double h_score[kMaxHeap];
-    __shared__ HeapKey h_key[kMaxHeap];
-    __shared__ int16_t h_par[kMaxHeap];
-    __shared__ int16_t h_rank[kMaxHeap];
-    __shared__ int8_t h_depth[kMaxHeap];
+    constexpr int kPerLane = kMaxSlots / kHeapLanes;
+    static_assert(kPerLane * kHeapLanes == kMaxSlots, "whole slots per lane");
+    // Frontier entries; slot i is read by lane i % 64.  Scores are finite
+    // (log q = z - lse with finite z), so -inf marks an empty slot.
+    __shared__ double e_score[kMaxSlots];
+    __shared__ double e_lq[kMaxSlots];  // log q of the entry's own (last) rank
+    __shared__ HeapKey e_key[kMaxSlots];
+    __shared__ int16_t e_par[kMaxSlots];
+    __shared__ int16_t e_rank[kMaxSlots];
+    __shared__ int8_t e_depth[kMaxSlots];
+    // popped nodes, written out after the loop
+    __shared__ int16_t n_par[kMaxK];
+    __shared__ int16_t n_rank[kMaxK];
+    __shared__ int8_t n_depth[kMaxK];
+    __shared__ double s_first[kMaxDepths];  // log q of rank 1 at each depth
     const int r = blockIdx.x;
-    if (threadIdx.x != 0) return;
+    const int lane = threadIdx.x;
     const int32_t* tk = toks + (int64_t)r * depths * K;
     const double* lq = logq + (int64_t)r * depths * K;
-    // entry a pops before entry b
-    auto before = [&](int a, int b) {
-        if (h_score[a] != h_score[b]) return h_score[a] > h_score[b];
-        return key_less(h_key[a], h_key[b]);
-    };
-    auto swap_entries = [&](int a, int b) {
-        const double ts = h_score[a]; h_score[a] = h_score[b]; h_score[b] = ts;
-        const HeapKey tk2 = h_key[a]; h_key[a] = h_key[b]; h_key[b] = tk2;
-        const int16_t tp = h_par[a]; h_par[a] = h_par[b]; h_par[b] = tp;
-        const int16_t tr = h_rank[a]; h_rank[a] = h_rank[b]; h_rank[b] = tr;
-        const int8_t td = h_depth[a]; h_depth[a] = h_depth[b]; h_depth[b] = td;
-    };
-    int size = 0;
-    auto push = [&](double score, const HeapKey& key, int par, int depth, int rank) {
-        int i = size++;
-        h_score[i] = score;
-        h_key[i] = key;
-        h_par[i] = (int16_t)par;
-        h_depth[i] = (int8_t)depth;
-        h_rank[i] = (int16_t)rank;
-        while (i > 0) {
-            const int p = (i - 1) >> 1;
-            if (!before(i, p)) break;
-            swap_entries(i, p);
-            i = p;
-        }
-    };
-    HeapKey k0 = {{0ull, 0ull, 0ull, 0ull}};
-    key_set(k0, 0, 0);
-    push(lq[0], k0, -1, 0, 0);
+    for (int i = lane; i < depths; i += kHeapLanes) s_first[i] = lq[(int64_t)i * K];
+    if (lane == 0) {
+        HeapKey k0 = {{0ull, 0ull, 0ull, 0ull}};
+        key_set(k0, 0, 0);
+        e_score[0] = lq[0];
+        e_lq[0] = lq[0];
+        e_key[0] = k0;
+        e_par[0] = -1;
+        e_rank[0] = 0;
+        e_depth[0] = 0;
+    }
+    __syncthreads();
+    // Each lane caches the best entry among its slots (score, slot; -inf and
+    // -1 when it has none).  Per pop: a wave maximum of the cached scores
+    // picks the entry; the popped slot takes the next sibling and the owner
+    // of that slot rescans its slots with one slot per lane; the lane that
+    // owns the child's new slot compares it with its cached best.
+    double my = lane == 0 ? e_score[0] : -INFINITY;
+    int best = lane == 0 ? 0 : -1;
+    int n_slots = 1;
     int n = 0;
-    while (size > 0 && n < budget) {
-        // pop the top
-        const double s = h_score[0];
-        const HeapKey key = h_key[0];
-        const int par = h_par[0], d = h_depth[0], rk = h_rank[0];
-        --size;
-        if (size > 0) {
-            h_score[0] = h_score[size];
-            h_key[0] = h_key[size];
-            h_par[0] = h_par[size];
-            h_depth[0] = h_depth[size];
-            h_rank[0] = h_rank[size];
-            int i = 0;
-            for (;;) {
-                const int a = 2 * i + 1, b = a + 1;
-                if (a >= size) break;
-                const int c = (b < size && before(b, a)) ? b : a;
-                if (!before(c, i)) break;
-                swap_entries(i, c);
-                i = c;
+    for (; n < budget; ++n) {
+        const double top = wave_max_f64(my);
+        if (top == -INFINITY) break;  // the frontier is empty
+        uint64_t cand = __ballot(my == top);
+        int wslot = __builtin_amdgcn_readlane(best, __builtin_ctzll(cand));
+        cand &= cand - 1;
+        while (cand) {  // exact score ties across lanes: the lowest rank tuple
+            const int cs = __builtin_amdgcn_readlane(best, __builtin_ctzll(cand));
+            cand &= cand - 1;
+            if (key_less(e_key[cs], e_key[wslot])) wslot = cs;
+        }
+        const double s = e_score[wslot];
+        const double lq_cur = e_lq[wslot];
+        const HeapKey key = e_key[wslot];
+        const int par = __builtin_amdgcn_readfirstlane(e_par[wslot]);
+        const int d = __builtin_amdgcn_readfirstlane(e_depth[wslot]);
+        const int rk = __builtin_amdgcn_readfirstlane(e_rank[wslot]);
+        const bool sib = rk + 1 < K;
+        const bool child = d + 1 < depths;
+        // uniform index: a scalar load of the sibling's log q
+        const double lq_next = sib ? lq[(int64_t)d * K + rk + 1] : 0.0;
+        __syncthreads();  // every lane has read the popped entry
+        const int cslot = n_slots;
+        if (lane == 0) {
+            n_par[n] = (int16_t)par;
+            n_depth[n] = (int8_t)d;
+            n_rank[n] = (int16_t)rk;
+            // the next sibling takes the popped slot: score - log q^(rk) + log q^(rk + 1), in that order
+            if (sib) {
+                HeapKey ks = key;
+                key_set(ks, d, rk + 1);
+                e_score[wslot] = s - lq_cur + lq_next;
+                e_lq[wslot] = lq_next;
+                e_key[wslot] = ks;
+                e_rank[wslot] = (int16_t)(rk + 1);
+            } else {
+                e_score[wslot] = -INFINITY;
+            }
+            // the first child, one depth down, in a new slot
+            if (child) {
+                HeapKey kc = key;
+                key_set(kc, d + 1, 0);
+                e_score[cslot] = s + s_first[d + 1];
+                e_lq[cslot] = s_first[d + 1];
+                e_key[cslot] = kc;
+                e_par[cslot] = (int16_t)n;
+                e_rank[cslot] = 0;
+                e_depth[cslot] = (int8_t)(d + 1);
             }
         }
-        const int node = n++;
-        parents[(int64_t)r * budget + node] = par;
-        tokens[(int64_t)r * budget + node] = tk[(int64_t)d * K + rk];
-        // the next sibling: score - log q^(rk) + log q^(rk + 1), in that order
-        if (rk + 1 < K) {
-            HeapKey ks = key;
-            key_set(ks, d, rk + 1);
-            push(s - lq[(int64_t)d * K + rk] + lq[(int64_t)d * K + rk + 1], ks, par, d, rk + 1);
+        if (child) ++n_slots;
+        __syncthreads();  // the new entries are visible to every lane
+        // the popped slot's owner: best of its slots, lane k reading its k-th
+        const int owner = wslot & (kHeapLanes - 1);
+        const int mine = owner + kHeapLanes * lane;
+        const double v = (lane < kPerLane && mine < n_slots) ? e_score[mine] : -INFINITY;
+        const double vmax = wave_max_f64(v);
+        int nb = -1;
+        if (vmax != -INFINITY) {
+            uint64_t c2 = __ballot(v == vmax);
+            nb = owner + kHeapLanes * __builtin_ctzll(c2);
+            c2 &= c2 - 1;
+            while (c2) {
+                const int cs = owner + kHeapLanes * __builtin_ctzll(c2);
+                c2 &= c2 - 1;
+                if (key_less(e_key[cs], e_key[nb])) nb = cs;
+            }
         }
-        // the first child, one depth down
-        if (d + 1 < depths) {
-            HeapKey kc = key;
-            key_set(kc, d + 1, 0);
-            push(s + lq[(int64_t)(d + 1) * K], kc, node, d + 1, 0);
+        if (lane == owner) {
+            my = vmax;
+            best = nb;
+        }
+        // the child's slot, when another lane owns it
+        if (child && lane == (cslot & (kHeapLanes - 1)) && lane != owner) {
+            const double cv = e_score[cslot];
+            if (best < 0 || cv > my || (cv == my && key_less(e_key[cslot], e_key[best]))) {
+                my = cv;
+                best = cslot;
+            }
         }
     }
-    n_nodes[r] = n;
-    for (int i = n; i < budget; ++i) {
-        parents[(int64_t)r * budget + i] = -1;
-        tokens[(int64_t)r * budget + i] = -1;
+    if (lane == 0) n_nodes[r] = n;
+    for (int i = lane; i < budget; i += kHeapLanes) {
+        const bool live = i < n;
+        parents[(int64_t)r * budget + i] = live ? (int32_t)n_par[i] : -1;
+        tokens[(int64_t)r * budget + i] = live ? tk[(int64_t)n_depth[i] * K + n_rank[i]] : -1;
     }
 }
 

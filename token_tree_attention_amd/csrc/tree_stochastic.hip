@@ -17,9 +17,10 @@
 // current target side); the correction / bonus is the Gumbel-max sample
 // argmax_v (log r_v + g_v) over r_v > 0 with the caller's noise g of that row.
 //
-// One workgroup per request walks the tree; each step that needs the whole
-// distribution (a visited row's softmax, a residual, the final sample) is a
-// pass of the workgroup over the vocab with fp64 block reductions.  The
+// One 1024-thread workgroup per request walks the tree; each step that needs
+// the whole distribution (a visited row's softmax, a residual, the final
+// sample) is a pass of the workgroup over the vocab with fp64 block
+// reductions, each thread loading four entries before using any.  The
 // current target side is kept as r_v = buf[v] / den: the row's exp values and
 // their sum right after a visit, the unnormalised residual and its sum after
 // a rejection (buf in the caller's workspace, fp64 [B, vocab]); r_v is formed
@@ -30,8 +31,9 @@
 
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / TTV_WAVE;
+constexpr int kBatch = 4;  // loads in flight per thread in a vocab pass
 
 __device__ __forceinline__ double shfl_xor_f64(double v, int off) {
     const uint64_t u = __double_as_longlong(v);
@@ -90,6 +92,26 @@ __device__ __forceinline__ double logit_at(const void* logits, int64_t row, int6
     return (double)((const float*)logits)[row * vocab + v];
 }
 
+// f(v, j) for the entries v = base + j * kThreads + tid, j < kBatch, of every
+// batch; load(v, j) runs for all of a batch's entries first, so their loads
+// are in flight together.  v increases along each thread's calls.
+template <typename Load, typename Use>
+__device__ __forceinline__ void vocab_pass(int64_t vocab, Load&& load, Use&& use) {
+    const int tid = threadIdx.x;
+    for (int64_t base = 0; base < vocab; base += (int64_t)kBatch * kThreads) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int64_t v = base + (int64_t)j * kThreads + tid;
+            if (v < vocab) load(v, j);
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int64_t v = base + (int64_t)j * kThreads + tid;
+            if (v < vocab) use(v, j);
+        }
+    }
+}
+
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void stochastic_walk_kernel(
     const int32_t* __restrict__ node_offsets, int32_t n_max, int64_t total_nodes,
@@ -118,16 +140,20 @@ __global__ __launch_bounds__(kThreads) void stochastic_walk_kernel(
     const int64_t row0 = (int64_t)s + b;  // the request's root row
 
     // Visit a row: buf = exp((x - max) / T), den = their sum.
+    double xb[kBatch], bb[kBatch];
+    float fb[kBatch];
     auto visit = [&](int64_t row) -> double {
         double m = -INFINITY;
-        for (int64_t v = tid; v < vocab; v += kThreads) m = fmax(m, logit_at<kBf16>(logits, row, vocab, v));
+        vocab_pass(vocab, [&](int64_t v, int j) { xb[j] = logit_at<kBf16>(logits, row, vocab, v); },
+                   [&](int64_t, int j) { m = fmax(m, xb[j]); });
         m = block_reduce<true>(m, s_red);
         double sum = 0.0;
-        for (int64_t v = tid; v < vocab; v += kThreads) {
-            const double e = exp((logit_at<kBf16>(logits, row, vocab, v) - m) / temperature);
-            buf[v] = e;
-            sum += e;
-        }
+        vocab_pass(vocab, [&](int64_t v, int j) { xb[j] = logit_at<kBf16>(logits, row, vocab, v); },
+                   [&](int64_t v, int j) {
+                       const double e = exp((xb[j] - m) / temperature);
+                       buf[v] = e;
+                       sum += e;
+                   });
         __syncthreads();  // buf written before any thread reads another's entry
         return block_reduce<false>(sum, s_red);
     };
@@ -155,10 +181,15 @@ __global__ __launch_bounds__(kThreads) void stochastic_walk_kernel(
             // rejected: the target side becomes norm(max(0, r - q)); left as it
             // was when nothing remains above q (r == q up to rounding)
             double z = 0.0;
-            for (int64_t v = tid; v < vocab; v += kThreads) z += fmax(buf[v] / den - (double)q[v], 0.0);
+            auto load_bq = [&](int64_t v, int jj) {
+                bb[jj] = buf[v];
+                fb[jj] = q[v];
+            };
+            vocab_pass(vocab, load_bq, [&](int64_t, int jj) { z += fmax(bb[jj] / den - (double)fb[jj], 0.0); });
             z = block_reduce<false>(z, s_red);
             if (z > 0.0) {
-                for (int64_t v = tid; v < vocab; v += kThreads) buf[v] = fmax(buf[v] / den - (double)q[v], 0.0);
+                vocab_pass(vocab, load_bq,
+                           [&](int64_t v, int jj) { buf[v] = fmax(bb[jj] / den - (double)fb[jj], 0.0); });
                 den = z;
                 __syncthreads();
             }
@@ -170,16 +201,21 @@ __global__ __launch_bounds__(kThreads) void stochastic_walk_kernel(
             const float* g = gumbel + row * vocab;
             double best = -INFINITY;
             int best_i = 0x7FFFFFFF;
-            for (int64_t v = tid; v < vocab; v += kThreads) {
-                const double r = buf[v] / den;
-                if (r > 0.0) {
-                    const double sc = log(r) + (double)g[v];
-                    if (sc > best) {  // v increases per thread: the first maximum is the lowest index
-                        best = sc;
-                        best_i = (int)v;
-                    }
-                }
-            }
+            vocab_pass(vocab,
+                       [&](int64_t v, int jj) {
+                           bb[jj] = buf[v];
+                           fb[jj] = g[v];
+                       },
+                       [&](int64_t v, int jj) {
+                           const double r = bb[jj] / den;
+                           if (r > 0.0) {
+                               const double sc = log(r) + (double)fb[jj];
+                               if (sc > best) {  // v increases per thread: the first maximum is the lowest index
+                                   best = sc;
+                                   best_i = (int)v;
+                               }
+                           }
+                       });
             final_token = block_argmax(best, best_i, s_red, s_ired);
             if (final_token == 0x7FFFFFFF) final_token = -1;
             break;
