@@ -617,6 +617,8 @@ struct MainCfg {
     static constexpr int kQloOffset = kStagesShort * kStageBytes;
     static constexpr int kQloBytes = kTile * kRowBytes;
     static constexpr int kMainBytes = kStagesLong * kStageBytes;
+    // per-lane DMA byte offsets of the issuing waves (K and V, kCpw chunks)
+    static constexpr int kOffTableBytes = kIssueWaves * TTV_WAVE * kCpw * 8;
     static_assert(kQloOffset + kQloBytes <= kMainBytes, "Q lo fits in stages 4..7");
     static constexpr int kQloChunks = kQloBytes / 1024;    // DMA instructions for the Q low parts
 };
@@ -786,8 +788,11 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const uint32_t ring = lds_offset(smem);
     const uint32_t qlo_s = ring + MC::kQloOffset;
-    const uint32_t mask_base = ring + MC::kMainBytes;
-    const uint32_t* mask_s = (const uint32_t*)(smem + MC::kMainBytes);
+    const uint32_t mask_base = ring + MC::kMainBytes + MC::kOffTableBytes;
+    const uint32_t* mask_s = (const uint32_t*)(smem + MC::kMainBytes + MC::kOffTableBytes);
+    // This issuing wave's row of the DMA offset table (its own lanes only, so
+    // it needs no barrier): chunk j's K and V byte offsets inside a stage.
+    uint32_t* const off_row = (uint32_t*)(smem + MC::kMainBytes) + (size_t)(threadIdx.x >> 6) * TTV_WAVE * MC::kCpw * 2;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -834,6 +839,16 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
     // A operand of all ones: 1^T P^T gives the row sums of P.
     const ttv_bf16x8 kOnes = __builtin_bit_cast(
         ttv_bf16x8, ttv_u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    if (wave < MC::kIssueWaves) {
+#pragma unroll
+        for (int j = 0; j < MC::kCpw; ++j) {
+            const int f_row = (wave + j * MC::kIssueWaves) * MC::kChunkRows + lane / P;
+            const int f_phys = lane % P;
+            const int f_rowb = (kPaged ? (f_row & 15) : f_row) * MC::kRowBytes;
+            off_row[(2 * j) * TTV_WAVE + lane] = f_rowb + 16 * swz_k(f_row, f_phys, P);
+            off_row[(2 * j + 1) * TTV_WAVE + lane] = f_rowb + 16 * swz_v(f_row, f_phys, P);
+        }
+    }
 
     for (int k = 0, slot = wg; k < n_mine; ++k, slot += grid) {
         const Item it = k == 0 ? first_item : items[slot];
@@ -878,42 +893,22 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         // paged block, or from the tile's first slot).  A chunk's rows of such
         // a tile lie in one paged block: slot0 is a multiple of 32 and a chunk
         // is a 16-aligned sub-range of rows.
-        auto lane_offsets = [&](uint32_t ln, int j, uint32_t& kb, uint32_t& vb) __attribute__((always_inline)) {
-            const int f_row = (wave + j * MC::kIssueWaves) * MC::kChunkRows + (int)(ln / P);
-            const int f_phys = (int)(ln % P);
-            const int f_rowb = (kPaged ? (f_row & 15) : f_row) * MC::kRowBytes;
-            kb = f_rowb + 16 * swz_k(f_row, f_phys, P);
-            vb = f_rowb + 16 * swz_v(f_row, f_phys, P);
-        };
-        // With two row blocks per wave the registers run out and the compiler
-        // spills; offsets held across the tile loop would be among the spilled
-        // values, and the vmcnt wait it then puts for their reload between
-        // these DMAs also waits for every tile still in flight (its count
-        // cannot see the DMAs, issued through asm).  So there they are
-        // recomputed at each issue from a lane id that a volatile asm
-        // produces (not hoisted); with one row block they are kept.
-        constexpr bool kOffsetsAtIssue = kMBr == 2;
-        uint32_t f_kb[MC::kCpw], f_vb[MC::kCpw];
-        if constexpr (!kOffsetsAtIssue) {
+        // A whole tile's DMA offsets come from the table: read before the
+        // wait and barrier that precede the issue (their latency hides behind
+        // them), so no offset is live across the tile loop, where the
+        // compiler would spill it and the reload's vmcnt wait would also
+        // drain the ring (its count cannot see the DMAs, issued through asm).
+        auto read_offsets = [&](uint32_t (&o)[2 * MC::kCpw]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int j = 0; j < MC::kCpw; ++j) lane_offsets(lane, j, f_kb[j], f_vb[j]);
-        }
-        auto issue_whole = [&](int tau, TileBlocks tb) __attribute__((always_inline)) {
+            for (int j = 0; j < 2 * MC::kCpw; ++j) o[j] = off_row[j * TTV_WAVE + lane];
+        };
+        auto issue_whole = [&](int tau, TileBlocks tb, const uint32_t (&o)[2 * MC::kCpw]) __attribute__((always_inline)) {
             if (wave >= MC::kIssueWaves) return;
             const int slot0 = it.c0 + tau * kKT;
             const uint32_t stage = ring + (tau & smask) * MC::kStageBytes;
-            uint32_t ln = lane;
-            if constexpr (kOffsetsAtIssue)
-                asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
 #pragma unroll
             for (int j = 0; j < MC::kCpw; ++j) {
-                uint32_t kb, vb;
-                if constexpr (kOffsetsAtIssue) {
-                    lane_offsets(ln, j, kb, vb);
-                } else {
-                    kb = f_kb[j];
-                    vb = f_vb[j];
-                }
+                const uint32_t kb = o[2 * j], vb = o[2 * j + 1];
                 const int ch = wave + j * MC::kIssueWaves;
                 int64_t row0;  // element offset of the tile's (first) row of this KV head
                 if (kPaged) {
@@ -1209,23 +1204,30 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                     TileBlocks b0 = next_blocks, b1 = next_blocks;
                     if (kPaged && t0 < n_tiles) b0 = blocks_of(t0);
                     if (kPaged && t0 + 1 < n_tiles) b1 = blocks_of(t0 + 1);
-                    if (wave < MC::kIssueWaves)
+                    uint32_t offs[2 * MC::kCpw];
+                    if (wave < MC::kIssueWaves) {
+                        read_offsets(offs);
                         wait_vmcnt_tiles<MC::kOpsPerTile>(min(3, max(0, n_tiles - 3 - tau)));
+                    }
                     raw_barrier();
                     if (t0 < n_tiles) {
-                        if (t0 < n_plain) issue_whole(t0, b0);
+                        if (t0 < n_plain) issue_whole(t0, b0, offs);
                         else issue(t0, b0);
                     }
                     if (t0 + 1 < n_tiles) {
-                        if (t0 + 1 < n_plain) issue_whole(t0 + 1, b1);
+                        if (t0 + 1 < n_plain) issue_whole(t0 + 1, b1, offs);
                         else issue(t0 + 1, b1);
                     }
                 } else {
                     constexpr int kA = (kPrecise ? MC::kStagesShort : MC::kStagesLong) - 1;
                     if (tau + kA < n_tiles) {  // steady state: kA - 2 later tiles stay in flight
-                        if (wave < MC::kIssueWaves) wait_vmcnt<MC::kOpsPerTile * (kA - 2)>();
+                        uint32_t offs[2 * MC::kCpw];
+                        if (wave < MC::kIssueWaves) {
+                            read_offsets(offs);
+                            wait_vmcnt<MC::kOpsPerTile * (kA - 2)>();
+                        }
                         raw_barrier();
-                        if (tau + kA < n_plain) issue_whole(tau + kA, next_blocks);
+                        if (tau + kA < n_plain) issue_whole(tau + kA, next_blocks, offs);
                         else issue(tau + kA, next_blocks);
                     } else {
                         if (wave < MC::kIssueWaves)
@@ -1496,7 +1498,7 @@ size_t main_lds_bytes(int G, int mask_words) {
     using MC = MainCfg<D, kW, kRows>;
     const int nodes = MC::kTile / G + 2;
     const size_t mask_bytes = (size_t)((nodes * mask_words + 63) / 64) * 256;
-    return (size_t)MC::kMainBytes + mask_bytes;
+    return (size_t)MC::kMainBytes + MC::kOffTableBytes + mask_bytes;
 }
 
 // ---------------------------------------------------------------------------
