@@ -132,6 +132,37 @@ typedef struct ttv_kv_cache {
     int32_t num_blocks;             /* paged: physical blocks in the pool */
 } ttv_kv_cache;
 
+/*
+ * Debug builds.  libtreeverify_debug.so is this library compiled with
+ * TTV_DEBUG defined: its kernels check the bounds of their data-dependent
+ * memory accesses.  A failed check counts, records the first failing site,
+ * and skips (or redirects to a valid address) the access it guards; no
+ * kernel traps.  The sites:
+ */
+#define TTV_SITE_BUILD_NODE     1   /* tree_build: an output row past total_nodes */
+#define TTV_SITE_PREP_NODE      2   /* attention prep: a node row past total_nodes */
+#define TTV_SITE_PREP_CACHE     3   /* attention prep: a tentative K/V row outside the cache */
+#define TTV_SITE_PLAN           4   /* attention plan: an item, partial or combine slot past its region */
+#define TTV_SITE_MAIN_CACHE     5   /* attention main: a K/V tile row outside the cache */
+#define TTV_SITE_MAIN_OUT       6   /* attention main: an output or partial row past its buffer */
+#define TTV_SITE_COMBINE        7   /* attention combine: a partial slot or output row past its buffer */
+#define TTV_SITE_ACCEPT_KEY     8   /* argmax: a row or chunk key past the workspace */
+#define TTV_SITE_WALK           9   /* greedy / sampled walk: a node or row index out of range */
+#define TTV_SITE_COMMIT         10  /* commit: a source or destination row outside the cache */
+#define TTV_SITE_STOCHASTIC     11  /* stochastic walk: a token or row out of range */
+#define TTV_SITE_DDTREE         12  /* DDTree build: a frontier slot, node or candidate out of range */
+#define TTV_SITE_MASK           13  /* dense masks: a row or column out of range */
+#define TTV_SITE_MERGE          14  /* SpecInfer merge / EAGLE growth: a node past its row */
+
+/*
+ * ttv_debug_report -- the debug build's failed-check count (summed over the
+ * library's kernels) and the first failing site (0 if none), for the current
+ * device; reset != 0 clears them.  Synchronous: call it after synchronising
+ * the streams the checked calls ran on.  A release build returns TTV_EINVAL
+ * and reports 0 / 0.
+ */
+TTV_API int ttv_debug_report(uint32_t* violations, int32_t* first_site, int32_t reset);
+
 /* Library version (major*10000 + minor*100 + patch). */
 TTV_API int32_t ttv_version(void);
 

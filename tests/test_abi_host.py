@@ -41,6 +41,21 @@ def test_every_declared_symbol_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_debug_build_exports_and_release_reports_none(lib):
+    """The release library answers ttv_debug_report with TTV_EINVAL (None from
+    the binding); the debug build, when built, exports the same symbols."""
+    if os.environ.get("TTV_DEBUG", "") in ("", "0") and not os.environ.get("TTV_LIBRARY"):
+        assert tta.ttv_debug_report() is None
+    dbg = os.path.join(ROOT, "token_tree_attention_amd", "libtreeverify_debug.so")
+    if not os.path.exists(dbg):
+        pytest.skip("debug library not built (python -m token_tree_attention_amd.build --debug)")
+    d = ctypes.CDLL(dbg)
+    for n in declared_functions():
+        assert hasattr(d, n), n
+    count, site = ctypes.c_uint32(7), ctypes.c_int32(7)
+    assert d.ttv_debug_report(None, ctypes.byref(site), 0) == tta.TTV_EINVAL  # null output: rejected
+
+
 def test_version_and_status(lib):
     assert tta.ttv_version() >= 100
     assert "invalid" in tta.ttv_status_string(tta.TTV_EINVAL)

@@ -24,7 +24,7 @@ import os
 from typing import Dict, Optional
 
 __all__ = [
-    "Batch", "KVCache", "library_path", "load_library", "ttv_version", "ttv_status_string",
+    "Batch", "KVCache", "library_path", "load_library", "ttv_version", "ttv_status_string", "ttv_debug_report",
     "tree_build", "tree_attention_workspace_bytes", "tree_attention_verify",
     "tree_greedy_accept_workspace_bytes", "tree_greedy_accept", "tree_greedy_accept_noalloc",
     "tree_sample_accept", "tree_stochastic_accept_workspace_bytes", "tree_stochastic_accept",
@@ -50,6 +50,7 @@ EXPORTED_SYMBOLS = (
     "tree_greedy_accept_noalloc", "tree_sample_accept", "tree_stochastic_accept_workspace_bytes",
     "tree_stochastic_accept", "tree_kv_commit", "tree_expand_mask", "tree_pack_mask",
     "tree_ddtree_workspace_bytes", "tree_ddtree_build", "tree_merge_sequences", "tree_eagle_grow",
+    "ttv_debug_report",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -57,9 +58,15 @@ _LIB: Optional[ctypes.CDLL] = None
 
 
 def library_path() -> str:
-    """The built library next to this file, or the one TTV_LIBRARY names (for
-    instance the host-sanitized build the argument-checking tests load)."""
-    return os.environ.get("TTV_LIBRARY") or os.path.join(_HERE, "libtreeverify.so")
+    """The built library next to this file; with TTV_DEBUG=1 in the
+    environment its debug build (device bounds checks, libtreeverify_debug.so);
+    or the one TTV_LIBRARY names (for instance the host-sanitized build the
+    argument-checking tests load)."""
+    if os.environ.get("TTV_LIBRARY"):
+        return os.environ["TTV_LIBRARY"]
+    if os.environ.get("TTV_DEBUG", "") not in ("", "0"):
+        return os.path.join(_HERE, "libtreeverify_debug.so")
+    return os.path.join(_HERE, "libtreeverify.so")
 
 
 class _CBatch(ctypes.Structure):
@@ -91,6 +98,8 @@ def load_library() -> ctypes.CDLL:
     lib.ttv_version.argtypes = []
     lib.ttv_status_string.restype = ctypes.c_char_p
     lib.ttv_status_string.argtypes = [I32]
+    lib.ttv_debug_report.restype = ctypes.c_int
+    lib.ttv_debug_report.argtypes = [P, P, I32]
     lib.tree_build.restype = ctypes.c_int
     lib.tree_build.argtypes = [BP, P, P, I32, P, P, P, P, P, P, P]
     lib.tree_attention_workspace_bytes.restype = SZ
@@ -133,6 +142,18 @@ def ttv_version() -> int:
 
 def ttv_status_string(status: int) -> str:
     return load_library().ttv_status_string(int(status)).decode()
+
+
+def ttv_debug_report(reset: bool = False):
+    """(failed checks, first failing site) of the debug build on the current
+    device (synchronise first), or None from a release build."""
+    lib = load_library()
+    count, site = ctypes.c_uint32(0), ctypes.c_int32(0)
+    st = lib.ttv_debug_report(ctypes.addressof(count), ctypes.addressof(site), int(bool(reset)))
+    if st == TTV_EINVAL:
+        return None
+    _check(st, "ttv_debug_report")
+    return int(count.value), int(site.value)
 
 
 def _check(status: int, what: str) -> None:

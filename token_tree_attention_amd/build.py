@@ -2,7 +2,9 @@
 
 Usage: python -m token_tree_attention_amd.build  (or call build()).
 Each .hip source compiles to an object under _build/, then one shared
-library is linked next to this file.
+library is linked next to this file.  --debug builds
+libtreeverify_debug.so (device bounds checks, TTV_DEBUG); --host-sanitized
+the ASan/UBSan build of the host code.
 """
 
 import os
@@ -37,14 +39,23 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, jobs: int = 5) -> str:
-    """Compile every source (always) and link the library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+DEBUG_OUT = os.path.join(HERE, "libtreeverify_debug.so")
+
+
+def build(verbose: bool = False, jobs: int = 5, debug: bool = False) -> str:
+    """Compile every source (always) and link the library; returns its path.
+
+    debug=True builds libtreeverify_debug.so instead: the same sources with
+    TTV_DEBUG defined, whose kernels check the bounds of their data-dependent
+    accesses (read back with ttv_debug_report)."""
+    out_dir = os.path.join(BUILD, "debug") if debug else BUILD
+    os.makedirs(out_dir, exist_ok=True)
     objs, procs = [], []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(out_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *(["-DTTV_DEBUG"] if debug else []), *EXTRA.get(src, []), "-c",
+               os.path.join(CSRC, src), "-o", obj]
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
     failed = []
     for cmd, p in procs:
@@ -56,10 +67,11 @@ def build(verbose: bool = False, jobs: int = 5) -> str:
             print(out)
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n\n".join(failed))
-    tmp = OUT + ".tmp"
+    target = DEBUG_OUT if debug else OUT
+    tmp = target + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, target)
+    return target
 
 
 SANITIZED = os.path.join(BUILD, "san", "libtreeverify_san.so")
@@ -109,5 +121,7 @@ def sanitizer_runtime() -> str:
 if __name__ == "__main__":
     if "--host-sanitized" in sys.argv:
         print(build_host_sanitized())
+    elif "--debug" in sys.argv:
+        print(build(verbose="-v" in sys.argv, debug=True))
     else:
         print(build(verbose="-v" in sys.argv))

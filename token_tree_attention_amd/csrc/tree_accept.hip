@@ -136,6 +136,7 @@ __global__ __launch_bounds__(kArgmaxThreads) void row_argmax_partial_kernel(
             if (f > best) { best = f; best_i = (uint32_t)idx; }
         }
     }
+    TTV_DCHECK(best_i == 0xFFFFFFFFu || (best_i >= (uint64_t)e0 && best_i < (uint64_t)e1), TTV_SITE_ACCEPT_KEY);
     uint64_t key = best_i == 0xFFFFFFFFu ? 0ull : ttv_argmax_key(__float_as_uint(best), best_i);
     key = ttv_wave_max_u64(key);
     if ((tid & (TTV_WAVE - 1)) == 0) s_red[tid / TTV_WAVE] = key;
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(kWalkThreads) void greedy_walk_kernel(
     }
     if (!spec || s != 0) stage(s, n);
     const int64_t row0 = (int64_t)s + b;
-    if (row_argmax)
+    if (row_argmax && TTV_DCHECK(row0 + n < total_nodes + gridDim.x, TTV_SITE_WALK))
         for (int r = tid; r <= n; r += kWalkThreads) row_argmax[row0 + r] = (int32_t)ttv_key_index(s_key[r]);
     int a = 0, flags = 0;
     int target = (int)ttv_key_index(s_key[0]);
@@ -346,7 +347,8 @@ __global__ __launch_bounds__(kWalkThreads) void greedy_walk_kernel(
     }
     __syncthreads();  // s_path, written by thread 0
     for (int k = tid; k < max_accept; k += kWalkThreads)
-        accepted_nodes[(int64_t)b * max_accept + k] = k < a ? s_path[k] : -1;
+        accepted_nodes[(int64_t)b * max_accept + k] =
+            k < a && TTV_DCHECK(s_path[k] >= 0 && s_path[k] < n, TTV_SITE_WALK) ? s_path[k] : -1;
     for (int k = tid; k <= max_accept; k += kWalkThreads)
         out_tokens[(int64_t)b * (max_accept + 1) + k] =
             k < a ? s_tok[s_path[k]] : (k == a ? target : -1);
@@ -501,3 +503,5 @@ extern "C" TTV_API int tree_sample_accept(
                          retrieve_next_token, retrieve_next_sibling, max_accept, accept_len,
                          accepted_nodes, out_tokens, row_choice, (uint64_t*)workspace, err, stream);
 }
+
+TTV_DEBUG_TU(accept)

@@ -153,6 +153,11 @@ __device__ __forceinline__ int64_t cache_row(const CacheView& c, int b, int h, i
     return (((int64_t)blk * c.hkv + h) * TTV_BLOCK_SIZE + (slot & 15)) * D;
 }
 
+// Elements of K (or V) in the cache: the bound of the debug build's checks.
+__device__ __forceinline__ int64_t cache_elems(const CacheView& c, int B, int D) {
+    return c.paged ? (int64_t)c.num_blocks * c.hkv * TTV_BLOCK_SIZE * D : (int64_t)B * c.hkv * c.cap * D;
+}
+
 // ---------------------------------------------------------------------------
 // 1. Prep: RoPE of Q (into the workspace) and K (into the cache), V copy, and
 //    (one extra workgroup) the work plan.
@@ -390,7 +395,8 @@ __device__ __attribute__((always_inline)) void build_plan(const int32_t* __restr
         for (int x = tid; x < n_items; x += kPrepThreads) {
             Item it;
             const int chunk = make_item(x, it);
-            items[(x % per_xcd) * kNumXcd + x / per_xcd] = it;
+            const int64_t slot = (int64_t)(x % per_xcd) * kNumXcd + x / per_xcd;
+            if (TTV_DCHECK(slot < max_items && it.pslot < max_partials, TTV_SITE_PLAN)) items[slot] = it;
             if (it.nc > 1 && chunk == 0) add_combine(it);
         }
     } else {
@@ -410,7 +416,8 @@ __device__ __attribute__((always_inline)) void build_plan(const int32_t* __restr
                 u.pslot = it.nc > 1 ? it.pslot + t : -1;
                 const int p = p0 + t, r = p / grid, k = p % grid;
                 const int v = (r & 1) ? grid - 1 - k : k;
-                items[r * grid + (v % per_xcd) * kNumXcd + v / per_xcd] = u;
+                const int64_t slot = (int64_t)r * grid + (v % per_xcd) * kNumXcd + v / per_xcd;
+                if (TTV_DCHECK(slot < max_items && u.pslot < max_partials, TTV_SITE_PLAN)) items[slot] = u;
             }
         }
     }
@@ -419,6 +426,9 @@ __device__ __attribute__((always_inline)) void build_plan(const int32_t* __restr
         hdr->n_items = n_items;
         hdr->n_combine = min((int64_t)s_ncomb, max_groups);
         hdr->chunk_len = chunk_len;
+        // bounds the debug build's main and combine kernels check against
+        hdr->reserved[0] = (int32_t)total_nodes;
+        hdr->reserved[1] = (int32_t)max_partials;
     }
 }
 
@@ -555,6 +565,7 @@ __global__ __launch_bounds__(kPrepThreads, 8) void attn_prep_kernel(
             if ((threadIdx.x & 63) == __builtin_ctzll(bad)) atomicOr(err + b, TTV_ERR_BLOCK_TABLE);
             continue;
         }
+        if (!TTV_DCHECK(dst + d0 + kVec <= cache_elems(cache, B, D), TTV_SITE_PREP_CACHE)) continue;
         const int64_t e = node * Hkv * D + (int64_t)v * kVec;
         const ttv_u32x4 kin = first ? k_first : *(const ttv_u32x4*)(k_new + e);
         ttv_u32x4 ko;
@@ -760,7 +771,8 @@ __device__ __forceinline__ void issue_tile(const CacheView& c, TileBlocks tb, in
         }
         const int row = ch * MC::kChunkRows + lane / P;
         const int phys = lane % P;
-        const int slot = slot0 + min(row, valid - 1);
+        int slot = slot0 + min(row, valid - 1);
+        if (!TTV_DCHECK(kPaged || (slot >= 0 && slot < c.cap), TTV_SITE_MAIN_CACHE)) slot = 0;
         const int blk = (!kPaged || (slot >> 4) == ((slot0 + r_first) >> 4)) ? bf : bl;
         const uint16_t* krow = kv_row_ptr<D, kPaged>(c, c.k, b, kvh, slot, blk);
         const uint16_t* vrow = kv_row_ptr<D, kPaged>(c, c.v, b, kvh, slot, blk);
@@ -805,6 +817,9 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
     // the plan), so the first one's load does not wait for n_items.
     const Item first_item = items[blockIdx.x];
     const int n_items = hdr->n_items;
+#ifdef TTV_DEBUG
+    const int64_t dbg_nodes = hdr->reserved[0], dbg_partials = hdr->reserved[1];
+#endif
     const int Hkv = cache.hkv;
     const int G = Hq / Hkv;
     const int grid = gridDim.x, wg = blockIdx.x;
@@ -920,7 +935,8 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                     const int blk = __builtin_amdgcn_readfirstlane(bad ? 0 : tb.first[j]);
                     row0 = ((int64_t)blk * cache.hkv + it.kvh) * TTV_BLOCK_SIZE * D;
                 } else {
-                    row0 = (((int64_t)it.b * cache.hkv + it.kvh) * cache.cap + slot0) * D;
+                    const bool in = TTV_DCHECK(slot0 >= 0 && slot0 + kKT <= cache.cap, TTV_SITE_MAIN_CACHE);
+                    row0 = (((int64_t)it.b * cache.hkv + it.kvh) * cache.cap + (in ? slot0 : 0)) * D;
                 }
                 const uint32_t chunk_off = ch * MC::kChunkRows * MC::kRowBytes;
                 dma16s(stage + chunk_off, cache.k + row0, kb);
@@ -1448,6 +1464,7 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                 if (r >= rows) continue;
                 if (it.pslot < 0) {
                     const int node = r / G, g = r % G;
+                    if (!TTV_DCHECK((int64_t)it.s + node < dbg_nodes, TTV_SITE_MAIN_OUT)) continue;
                     uint16_t* dst = out + ((int64_t)(it.s + node) * Hq + it.kvh * G + g) * D;
                     const float inv_l = 1.0f / l_run[mb];
 #pragma unroll
@@ -1469,6 +1486,7 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                         for (int q = 0; q < 4; ++q) amax = __builtin_fmaxf(amax, __builtin_fabsf(o[db][mb][q]));
                     const int e = __builtin_amdgcn_frexp_expf(group_max(amax) * inv_l);
                     const float sc = __builtin_amdgcn_ldexpf(inv_l, -e);
+                    if (!TTV_DCHECK(it.pslot < dbg_partials, TTV_SITE_MAIN_OUT)) continue;
                     ttv_f16x4* dst = part_o + (((int64_t)it.pslot * kTileR + r_local) * D) / 4;
 #pragma unroll
                     for (int db = 0; db < DB; ++db)
@@ -1516,12 +1534,19 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(
     const int n_work = hdr->n_combine * kRowBlocks;
     const int G = Hq / Hkv;
     const int tid = threadIdx.x;
+#ifdef TTV_DEBUG
+    const int64_t dbg_nodes = hdr->reserved[0], dbg_partials = hdr->reserved[1];
+#endif
     for (int wk = blockIdx.x; wk < n_work; wk += gridDim.x) {
         const Combine cb = combine[wk / kRowBlocks];
         const int r_local = (wk % kRowBlocks) * kRowsPerPass + tid / kLanesPerRow;
         const int d = (tid % kLanesPerRow) * 4;
         const int r = cb.tile * kTileR + r_local;
         if (r >= cb.n * G) continue;
+        if (!TTV_DCHECK(cb.pslot0 >= 0 && cb.pslot0 + (int64_t)(cb.nc - 1) * cb.stride < dbg_partials &&
+                            (int64_t)cb.s + r / G < dbg_nodes,
+                        TTV_SITE_COMBINE))
+            continue;
         // Chunks in batches of NB: every load of a batch is issued before any
         // is used, so one memory latency covers the batch; the batch maximum
         // then rescales the running sums once.  Past the last chunk the
@@ -1748,3 +1773,5 @@ extern "C" TTV_API int tree_attention_verify(const ttv_batch* bt, const void* q,
                                 n_heads, rope_base, scale, (uint16_t*)out, (char*)workspace, L,
                                 err, stream);
 }
+
+TTV_DEBUG_TU(attention)

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(1024) void tree_build_kernel(
         }
         __syncthreads();
     }
-    if (tid < n) {
+    if (tid < n && TTV_DCHECK((int64_t)s + tid < total_nodes, TTV_SITE_BUILD_NODE)) {
         uint32_t* out_row = mask + (int64_t)(s + tid) * mask_words;
         const int first_zero = ((used_words + kMaskPassWords - 1) / kMaskPassWords) * kMaskPassWords;
         for (int w = first_zero; w < mask_words; ++w) out_row[w] = 0u;
@@ -170,8 +170,9 @@ __global__ __launch_bounds__(1024) void tree_build_kernel(
         if (group_start && group > 0) s_first[group - 1] = node;
     }
     __syncthreads();
-    if (sibling_of >= 0) next_sibling_out[s + sibling_of] = sibling_val;
-    if (tid < n) {
+    if (sibling_of >= 0 && TTV_DCHECK(sibling_of < n && (int64_t)s + sibling_of < total_nodes, TTV_SITE_BUILD_NODE))
+        next_sibling_out[s + sibling_of] = sibling_val;
+    if (tid < n && TTV_DCHECK((int64_t)s + tid < total_nodes, TTV_SITE_BUILD_NODE)) {
         depth_out[s + tid] = depth;
         pos_out[s + tid] = ctx + depth;
         ridx_out[s + tid] = s + b + 1 + tid;
@@ -206,3 +207,5 @@ extern "C" TTV_API int tree_build(const ttv_batch* bt, const int32_t* parents, u
                        retrieve_next_sibling, err);
     return hipGetLastError() == hipSuccess ? TTV_OK : TTV_EHIP;
 }
+
+TTV_DEBUG_TU(build)

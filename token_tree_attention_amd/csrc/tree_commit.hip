@@ -138,7 +138,13 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(
                 const int piece = r % pieces_per_row;
                 const int h = unit >> 1;
                 const int i = s_path[d];
-                if (i != d) {
+                // debug build: both rows inside the cache (the request's own
+                // region when contiguous, a pool block when paged)
+                const int64_t elems = paged ? (int64_t)num_blocks * n_kv_heads * block_size * row_stride
+                                            : (int64_t)gridDim.x * n_kv_heads * capacity * row_stride;
+                if (i != d && TTV_DCHECK(slot_offset(ctx + i, h) >= 0 && slot_offset(ctx + i, h) + 8 * pieces_per_row <= elems &&
+                                             slot_offset(ctx + d, h) >= 0 && slot_offset(ctx + d, h) + 8 * pieces_per_row <= elems,
+                                         TTV_SITE_COMMIT)) {
                     uint16_t* base = (unit & 1) ? vc : kc;
                     const int64_t src = slot_offset(ctx + i, h) + piece * 8;
                     held[k] = *(const ttv_u32x4*)(base + src);
@@ -160,6 +166,7 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(
         const int first = (new_len + block_size - 1) / block_size;
         const int last = (ctx + n + block_size - 1) / block_size;
         for (int j = first + tid; j < last; j += kCommitThreads) {
+            if (!TTV_DCHECK(j < max_blocks && j - first < max_blocks, TTV_SITE_COMMIT)) continue;
             if (released_blocks)  // the staged entry (first >= ctx / block_size)
                 released_blocks[(int64_t)b * max_blocks + (j - first)] = s_blk[j - ctx / block_size];
             block_table[(int64_t)b * max_blocks + j] = -1;
@@ -207,3 +214,5 @@ extern "C" TTV_API int tree_kv_commit(const ttv_batch* bt, const ttv_kv_cache* c
                        max_accept, new_lens, released_blocks, num_released, err);
     return hipGetLastError() == hipSuccess ? TTV_OK : TTV_EHIP;
 }
+
+TTV_DEBUG_TU(commit)

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kTopkThreads) void ddtree_topk_kernel(
         base = __shfl(base, leader);
         if (keep) {
             const uint32_t pos = base + (uint32_t)__builtin_popcountll(m & ((1ull << lane) - 1ull));
-            if (pos < (uint32_t)kMaxK) s_cand[pos] = key;
+            if (TTV_DCHECK(pos < (uint32_t)kMaxK, TTV_SITE_DDTREE)) s_cand[pos] = key;
         }
     });
     __syncthreads();
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kHeapLanes) void ddtree_heap_kernel(
                 e_score[wslot] = -INFINITY;
             }
             // the first child, one depth down, in a new slot
-            if (child) {
+            if (child && TTV_DCHECK(cslot < kMaxSlots && n < kMaxK, TTV_SITE_DDTREE)) {
                 HeapKey kc = key;
                 key_set(kc, d + 1, 0);
                 e_score[cslot] = s + s_first[d + 1];
@@ -388,3 +388,5 @@ extern "C" TTV_API int tree_ddtree_build(int32_t requests, int32_t depths, int64
                        budget, parents, tokens, n_nodes);
     return hipGetLastError() == hipSuccess ? TTV_OK : TTV_EHIP;
 }
+
+TTV_DEBUG_TU(ddtree)

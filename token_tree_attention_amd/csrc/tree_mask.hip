@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_mask_kernel(
     if (bad) atomicOr(&s_bad, 1);
     // packed words: thread w gathers tree columns 32w .. 32w + 31
     uint32_t* mrow = mask + (int64_t)(s + i) * mask_words;
-    for (int w = tid; w < mask_words; w += kPackThreads) {
+    for (int w = tid; w < mask_words && TTV_DCHECK((int64_t)s + i < total_nodes, TTV_SITE_MASK); w += kPackThreads) {
         uint32_t v = 0;
         for (int k = 0; k < 32; ++k) {
             const int j = 32 * w + k;
@@ -157,3 +157,5 @@ extern "C" TTV_API int tree_pack_mask(const ttv_batch* bt, const uint8_t* dense,
                        mode, mask, mask_words, err);
     return hipGetLastError() == hipSuccess ? TTV_OK : TTV_EHIP;
 }
+
+TTV_DEBUG_TU(mask)

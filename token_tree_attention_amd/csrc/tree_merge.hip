@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sequences_kernel(
         }
         const int node = starts ? base + pre : -1;
         s_node[m] = node;
-        if (starts) {
+        if (starts && TTV_DCHECK(node >= 0 && node < max_nodes, TTV_SITE_MERGE)) {
             parents[(int64_t)r * max_nodes + node] = prev;
             tokens[(int64_t)r * max_nodes + node] = t;
         }
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kGrowThreads) void eagle_grow_kernel(
     __syncthreads();
     for (int x = tid; x < total; x += kGrowThreads) {
         const int nx = s_new[x];
-        if (nx >= 0) {
+        if (nx >= 0 && TTV_DCHECK(nx < budget && (s_par[x] < 0 || s_new[s_par[x]] >= 0), TTV_SITE_MERGE)) {
             parents[(int64_t)r * budget + nx] = s_par[x] < 0 ? -1 : s_new[s_par[x]];
             tokens[(int64_t)r * budget + nx] = s_tok[x];
         }
@@ -246,3 +246,5 @@ extern "C" TTV_API int tree_eagle_grow(int32_t requests, int32_t k, int32_t laye
                        root_tokens, root_conf, child_tokens, child_conf, budget, parents, tokens, n_nodes);
     return hipGetLastError() == hipSuccess ? TTV_OK : TTV_EHIP;
 }
+
+TTV_DEBUG_TU(merge)

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void stochastic_walk_kernel(
         if (tid == 0) s_path[a] = accepted;
         ++a;
         cur = accepted;
-        row = row0 + 1 + accepted;
+        row = row0 + 1 + (TTV_DCHECK(accepted >= 0 && accepted < n, TTV_SITE_STOCHASTIC) ? accepted : 0);
         __syncthreads();  // every thread has read buf before the next visit rewrites it
         den = visit(row);
     }
@@ -282,3 +282,5 @@ extern "C" TTV_API int tree_stochastic_accept(
     else launch(stochastic_walk_kernel<false>);
     return hipGetLastError() == hipSuccess ? TTV_OK : TTV_EHIP;
 }
+
+TTV_DEBUG_TU(stochastic)

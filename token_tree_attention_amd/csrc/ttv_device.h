@@ -8,6 +8,37 @@
 
 #define TTV_WAVE 64
 
+// ---- bounds checks of the debug build --------------------------------------
+// Compiled with TTV_DEBUG defined (libtreeverify_debug.so), TTV_DCHECK(cond,
+// site) checks a bound on the device: a failure counts in this translation
+// unit's debug word, records the first failing site (TTV_SITE_*), and yields
+// false so the caller skips or redirects the access it guards; nothing traps.
+// ttv_debug_report (abi.hip) sums the words of every translation unit.
+// Without TTV_DEBUG the check is the constant true and compiles to nothing.
+#ifdef TTV_DEBUG
+static __device__ unsigned int ttv_debug_word[2];  // failures, first failing site
+__device__ __noinline__ static void ttv_debug_fail(int site) {
+    if (atomicAdd(&ttv_debug_word[0], 1u) == 0u) atomicExch(&ttv_debug_word[1], (unsigned int)site);
+}
+#define TTV_DCHECK(cond, site) ((cond) ? true : (ttv_debug_fail(site), false))
+// Host reader of this translation unit's word (and reset), for ttv_debug_report.
+#define TTV_DEBUG_TU(name)                                                                      \
+    extern "C" int ttv_debug_take_##name(unsigned int* out, int reset) {                       \
+        if (hipMemcpyFromSymbol(out, HIP_SYMBOL(ttv_debug_word), 2 * sizeof(unsigned int)) !=   \
+            hipSuccess)                                                                         \
+            return TTV_EHIP;                                                                    \
+        if (reset) {                                                                            \
+            const unsigned int zero[2] = {0u, 0u};                                              \
+            if (hipMemcpyToSymbol(HIP_SYMBOL(ttv_debug_word), zero, sizeof zero) != hipSuccess) \
+                return TTV_EHIP;                                                                \
+        }                                                                                       \
+        return TTV_OK;                                                                          \
+    }
+#else
+#define TTV_DCHECK(cond, site) true
+#define TTV_DEBUG_TU(name)
+#endif
+
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 ttv_bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float ttv_f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t ttv_u32x4;
