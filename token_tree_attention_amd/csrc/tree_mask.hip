@@ -93,25 +93,55 @@ __global__ __launch_bounds__(kPackThreads) void pack_mask_kernel(
         if (i == 0 && tid == 0) atomicOr(err + b, TTV_ERR_CAPACITY);
         return;
     }
+    __shared__ uint32_t s_words[TTV_MAX_TREE_NODES / 32];
     if (tid == 0) s_bad = 0;
+    for (int w = tid; w < mask_words; w += kPackThreads) s_words[w] = 0u;
     __syncthreads();
     const uint8_t* drow = dense + (int64_t)(s + i) * row_stride;
     bool bad = false;
-    // context columns all visible; nothing at or past column i + 1 of the tree
-    for (int64_t c = tid; c < base; c += kPackThreads) bad |= drow[c] == 0;
-    for (int64_t c = base + i + 1 + tid; c < row_stride; c += kPackThreads) bad |= drow[c] != 0;
-    if (tid == 0) bad |= drow[base + i] == 0;  // the node sees itself
-    if (bad) atomicOr(&s_bad, 1);
-    // packed words: thread w gathers tree columns 32w .. 32w + 31
-    uint32_t* mrow = mask + (int64_t)(s + i) * mask_words;
-    for (int w = tid; w < mask_words && TTV_DCHECK((int64_t)s + i < total_nodes, TTV_SITE_MASK); w += kPackThreads) {
-        uint32_t v = 0;
-        for (int k = 0; k < 32; ++k) {
-            const int j = 32 * w + k;
-            if (j < n && drow[base + j] != 0) v |= 1u << k;
+    // Rules per column c: context columns (c < base) all visible; the tree
+    // columns up to the node's own (base .. base + i) give the packed bits,
+    // the node's own set; nothing at or past column base + i + 1.
+    auto column = [&](int64_t c, uint32_t byte, uint32_t& lo, uint32_t& hi, int w0) __attribute__((always_inline)) {
+        if (c < base) {
+            bad |= byte == 0;
+        } else if (c > base + i) {
+            bad |= byte != 0;
+        } else {
+            const int j = (int)(c - base);
+            if (j == i) bad |= byte == 0;
+            if (byte) {
+                if ((j >> 5) == w0) lo |= 1u << (j & 31);
+                else hi |= 1u << (j & 31);
+            }
         }
-        mrow[w] = v;
+    };
+    const bool vec = (row_stride % 16) == 0 && ((uintptr_t)dense % 16) == 0;
+    if (vec) {
+        // 16 columns per load; they touch at most two packed words
+        for (int64_t p = tid; p < row_stride / 16; p += kPackThreads) {
+            const ttv_u32x4 v = *(const ttv_u32x4*)(drow + 16 * p);
+            const int64_t c0 = 16 * p;
+            const int w0 = c0 >= base ? (int)((c0 - base) >> 5) : 0;
+            uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) column(c0 + q, (v[q >> 2] >> (8 * (q & 3))) & 0xFFu, lo, hi, w0);
+            if (lo && TTV_DCHECK(w0 < mask_words, TTV_SITE_MASK)) atomicOr(&s_words[w0], lo);
+            if (hi && TTV_DCHECK(w0 + 1 < mask_words, TTV_SITE_MASK)) atomicOr(&s_words[w0 + 1], hi);
+        }
+    } else {
+        for (int64_t c = tid; c < row_stride; c += kPackThreads) {
+            uint32_t lo = 0u, hi = 0u;
+            const int w0 = c >= base ? (int)((c - base) >> 5) : 0;
+            column(c, drow[c], lo, hi, w0);
+            if (lo && TTV_DCHECK(w0 < mask_words, TTV_SITE_MASK)) atomicOr(&s_words[w0], lo);
+        }
     }
+    if (bad) atomicOr(&s_bad, 1);
+    __syncthreads();
+    uint32_t* mrow = mask + (int64_t)(s + i) * mask_words;
+    for (int w = tid; w < mask_words && TTV_DCHECK((int64_t)s + i < total_nodes, TTV_SITE_MASK); w += kPackThreads)
+        mrow[w] = s_words[w];
     __syncthreads();
     if (tid == 0 && s_bad) atomicOr(err + b, TTV_ERR_BAD_MASK);
 }
