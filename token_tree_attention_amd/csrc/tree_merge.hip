@@ -9,7 +9,8 @@
 // entry; nodes are numbered level by level, and within a level in the order
 // the sequences (by index) first reach them.
 //
-// One workgroup per request, one thread per sequence, one pass per depth: a
+// One workgroup per request, one thread per sequence (its tokens loaded eight
+// depths at a time), one pass per depth: a
 // sequence's (parent node, token) pair at that depth starts a node when no
 // lower-indexed sequence has the same pair; the starting sequences are
 // numbered by a block scan; the others take the node of the lowest-indexed
@@ -25,8 +26,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sequences_kernel(
     int32_t n_seqs, int32_t seq_len, const int32_t* __restrict__ seqs, int32_t max_nodes,
     int32_t* __restrict__ parents, int32_t* __restrict__ tokens, int32_t* __restrict__ n_nodes,
     int32_t* __restrict__ err) {
-    __shared__ int32_t s_par[kMergeThreads];   // the pair of each sequence at this depth
-    __shared__ int32_t s_tok[kMergeThreads];
+    __shared__ __attribute__((aligned(16))) uint64_t s_key[kMergeThreads];  // each sequence's pair at this depth
     __shared__ int32_t s_node[kMergeThreads];  // its node at this depth (-1: none)
     __shared__ int32_t s_wsum[kMergeThreads / TTV_WAVE];
     __shared__ int32_t s_any;
@@ -38,25 +38,36 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sequences_kernel(
     bool alive = m < n_seqs;
     int base = 0;         // nodes numbered so far
     bool overflow = false;
+    constexpr int kAhead = 8;  // tokens of this sequence loaded together (one latency per 8 depths)
+    int ahead[kAhead];
     for (int d = 0; d < seq_len; ++d) {
+        if (d % kAhead == 0) {
+#pragma unroll
+            for (int k = 0; k < kAhead; ++k) ahead[k] = alive && d + k < seq_len ? seq[d + k] : -1;
+        }
         int t = -1;
         if (alive) {
-            t = seq[d];
+#pragma unroll
+            for (int k = 0; k < kAhead; ++k)
+                if (k == d % kAhead) t = ahead[k];
             if (t < 0) alive = false;
         }
-        s_par[m] = alive ? prev : -2;
-        s_tok[m] = t;
+        // (parent, token) as one 64-bit key; an ended sequence matches nothing
+        const uint64_t key = alive ? ((uint64_t)(uint32_t)(prev + 2) << 32) | (uint32_t)t : ~0ull - (uint64_t)m;
+        s_key[m] = key;
         if (m == 0) s_any = 0;
         __syncthreads();
         if (alive) atomicOr(&s_any, 1);
-        // the lowest-indexed sequence with the same pair
+        // the lowest-indexed sequence with the same pair: every lower key is
+        // compared (two per 16-byte read, no early exit, so the reads pipeline)
         int first = m;
-        if (alive)
-            for (int k = 0; k < m; ++k)
-                if (s_par[k] == prev && s_tok[k] == t) {
-                    first = k;
-                    break;
-                }
+        if (alive) {
+            for (int k = 0; k < m; k += 2) {
+                const ulonglong2 kk = *(const ulonglong2*)(s_key + k);
+                if (kk.x == key) first = min(first, k);
+                if (k + 1 < m && kk.y == key) first = min(first, k + 1);
+            }
+        }
         const int starts = alive && first == m;
         // block exclusive scan of the starts, in sequence order
         int inc = starts;
@@ -86,7 +97,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_sequences_kernel(
         __syncthreads();
         prev = alive ? (starts ? node : s_node[first]) : -1;
         base += total;
-        __syncthreads();  // s_par / s_tok / s_node / s_wsum are rewritten by the next depth
+        __syncthreads();  // s_key / s_node / s_wsum are rewritten by the next depth
     }
     if (m == 0) {
         n_nodes[r] = overflow ? 0 : base;
