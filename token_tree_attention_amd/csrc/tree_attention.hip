@@ -949,14 +949,20 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         // wait covers all of them, so the compiler tracks nothing in flight
         // afterwards.  Tiles 2 .. ahead - 1 are issued after that wait and
         // stay in flight into the loop.
-        // Row blocks of 16 rows: a tile with more than 16 kW rows gives wave w
-        // blocks 2w and 2w + 1 (NMB = 2); a tile with at most 16 kW rows
-        // gives wave w block w alone (NMB = 1, or 0 past the last row), so a
-        // partly filled tile runs one block per busy wave.  Every busy wave
-        // of an item runs the same count: waves that share a SIMD and run
-        // different counts were measured slower than both running two.
+        // Row blocks of 16 rows (nblk of them in this tile).  Paired: waves
+        // w < ceil(nblk / 2) take blocks 2w and 2w + 1 (NMB = 2; an odd
+        // count leaves the last wave one block past the tile, computed and
+        // dropped); single: waves w < nblk take block w (NMB = 1).  Pairs run
+        // when the tile has more blocks than waves, and for a partly filled
+        // 256-row tile over at least 128 key tiles: there, fewer waves with
+        // two blocks each (one per SIMD for up to 8 blocks) beat more waves
+        // with one (the long Medusa workload's 76-row tiles: about 4 % of
+        // the call); over short contexts single blocks were faster.  Every
+        // busy wave of an item runs the same count: waves that share a SIMD
+        // and run different counts were measured slower than both running two.
         const int nblk = (min(kTileR, rows - it.tile * kTileR) + 15) / 16;
-        const int nmb = wave < nblk ? (nblk > kW ? 2 : 1) : 0;
+        const int pairs_w = kMBr == 2 && (nblk > kW || (nblk >= 2 && n_tiles >= 128)) ? min(kW, (nblk + 1) / 2) : 0;
+        const int nmb = pairs_w ? (wave < pairs_w ? 2 : 0) : (wave < nblk ? 1 : 0);
         int rblk[kMB];
         rblk[0] = nmb == 2 ? 2 * wave : wave;
         rblk[1] = 2 * wave + 1;
