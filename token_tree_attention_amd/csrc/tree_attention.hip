@@ -902,6 +902,19 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                                   ring + (tau & smask) * MC::kStageBytes, wave, lane, err);
         };
         TileBlocks next_blocks{{0, 0}, {0, 0}};  // blocks of the next tile to issue
+        // Paged, two whole context tiles t0 and t0 + 1 (t0 even): their four
+        // blocks are consecutive table entries, one per 16 slots.
+        auto whole_pair_blocks = [&](int t0, TileBlocks& x0, TileBlocks& x1) __attribute__((always_inline)) {
+            if (wave >= MC::kIssueWaves) return;
+            const int32_t* tp = table + (int64_t)it.b * cache.max_blocks + (it.c0 >> 4) + 2 * t0;
+            const int32_t e0 = tp[0], e1 = tp[1], e2 = tp[2], e3 = tp[3];
+#pragma unroll
+            for (int j = 0; j < MC::kCpw; ++j) {
+                const bool second = (wave + j * MC::kIssueWaves) * MC::kChunkRows >= 16;
+                x0.first[j] = x0.last[j] = second ? e1 : e0;
+                x1.first[j] = x1.last[j] = second ? e3 : e2;
+            }
+        };
         // Fast issue path for whole context tiles (slot0 = c0 + 32 tau, no
         // clamping): an issue is a wave-uniform base plus a per-lane byte
         // offset per chunk this wave loads (from the first row of the chunk's
@@ -927,12 +940,11 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                 const int ch = wave + j * MC::kIssueWaves;
                 int64_t row0;  // element offset of the tile's (first) row of this KV head
                 if (kPaged) {
-                    // The block id stays wave-uniform (the fallback is chosen
-                    // outside the one-lane flag), so the base is scalar math.
-                    const bool bad = tb.first[j] < 0 || tb.first[j] >= cache.num_blocks;
-                    if (bad && lane == 0) atomicOr(err + it.b, TTV_ERR_BLOCK_TABLE);
-                    // an unmapped block loads block 0 instead; the request is flagged
-                    const int blk = __builtin_amdgcn_readfirstlane(bad ? 0 : tb.first[j]);
+                    // An unmapped block loads block 0 instead (the prologue
+                    // flagged the request); a select, not a branch, so the
+                    // base stays scalar math.
+                    const int32_t e = tb.first[j];
+                    const int blk = __builtin_amdgcn_readfirstlane((uint32_t)e < (uint32_t)cache.num_blocks ? e : 0);
                     row0 = ((int64_t)blk * cache.hkv + it.kvh) * TTV_BLOCK_SIZE * D;
                 } else {
                     const bool in = TTV_DCHECK(slot0 >= 0 && slot0 + kKT <= cache.cap, TTV_SITE_MAIN_CACHE);
@@ -998,6 +1010,16 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
             const uint32_t* src = mask + (int64_t)(it.s + node0) * mask_words;
             for (int j = wave; j * 64 < words; j += kW)
                 dma4(mask_base + j * 256, src + min(j * 64 + lane, words - 1));
+        }
+        if (kPaged) {
+            // Every table entry the item's tiles use, checked once here: the
+            // whole-tile loads of the loop only clamp a bad entry.
+            const int end_slot = n_tree_tiles > 0 ? tree_limit : it.c1;
+            const int e_end = min((end_slot + 15) >> 4, cache.max_blocks);
+            bool bad = false;
+            for (int e = (it.c0 >> 4) + tid; e < e_end; e += kW * TTV_WAVE)
+                bad |= (uint32_t)table[(int64_t)it.b * cache.max_blocks + e] >= (uint32_t)cache.num_blocks;
+            if (bad) atomicOr(err + it.b, TTV_ERR_BLOCK_TABLE);
         }
         for (int j = 0; j < 2 && j < n_tiles; ++j) issue(j, blocks_of(j));
         // A full wait and a fenced barrier (not the loop's raw one, so the two
@@ -1224,8 +1246,14 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                     // paged: the pair's block numbers are read here, right
                     // before the wait, so their latency hides behind it
                     TileBlocks b0 = next_blocks, b1 = next_blocks;
-                    if (kPaged && t0 < n_tiles) b0 = blocks_of(t0);
-                    if (kPaged && t0 + 1 < n_tiles) b1 = blocks_of(t0 + 1);
+                    if (kPaged) {
+                        if (t0 + 1 < n_plain) {
+                            whole_pair_blocks(t0, b0, b1);
+                        } else {
+                            if (t0 < n_tiles) b0 = blocks_of(t0);
+                            if (t0 + 1 < n_tiles) b1 = blocks_of(t0 + 1);
+                        }
+                    }
                     uint32_t offs[2 * MC::kCpw];
                     if (wave < MC::kIssueWaves) {
                         read_offsets(offs);
@@ -1513,7 +1541,13 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                 else body(std::integral_constant<int, 0>{});
             }
         }
-        __syncthreads();  // LDS (ring, Q-lo, mask) is reused by the next item
+        // The next item reuses the LDS (ring, Q-lo, mask): a barrier, but no
+        // memory fence.  Every LDS read of this item has fed an MFMA or a
+        // store by now and every tile load has landed, while the item's
+        // output stores may stay in flight into the next item (nothing in
+        // this kernel reads them): they retire under its prologue wait
+        // instead of delaying this barrier (about 3 us per item).
+        raw_barrier();
     }
 }
 
