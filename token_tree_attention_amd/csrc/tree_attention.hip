@@ -82,7 +82,8 @@ struct PlanHeader {
     int32_t n_items;
     int32_t n_combine;
     int32_t chunk_len;
-    int32_t reserved[61];
+    int32_t queue[kNumXcd];  // per-XCD work-queue cursors of the main kernel
+    int32_t reserved[53];
 };
 
 typedef __bf16 ttv_bf16x2v __attribute__((ext_vector_type(2)));
@@ -162,6 +163,24 @@ __device__ __forceinline__ int64_t cache_elems(const CacheView& c, int B, int D)
 // 1. Prep: RoPE of Q (into the workspace) and K (into the cache), V copy, and
 //    (one extra workgroup) the work plan.
 // ---------------------------------------------------------------------------
+
+// Snake placement over `grid` workgroups (per_xcd = grid / 8 per XCD),
+// n_items > grid: full rounds, then m = n_items % grid items in a last round
+// that fills positions 0 .. m-1 when its index is even and grid-m .. grid-1
+// when odd; position v belongs to XCD v / per_xcd.  XCD x's first filled
+// position (as an index inside the XCD) in such an odd round:
+__host__ __device__ inline int xcd_first_filled(int grid, int m, int x) {
+    const int per_xcd = grid / kNumXcd;
+    return min(per_xcd, max(0, grid - m - x * per_xcd));
+}
+// Items of XCD x over all rounds.
+__host__ __device__ inline int xcd_items(int grid, int n_items, int x) {
+    const int per_xcd = grid / kNumXcd;
+    const int r = n_items / grid, m = n_items % grid;
+    const int last = (r & 1) ? per_xcd - xcd_first_filled(grid, m, x)
+                             : min(per_xcd, max(0, m - x * per_xcd));
+    return r * per_xcd + last;
+}
 
 // Inlined on purpose: called out of line, its register count (over 160)
 // became the prep kernel's and held every node workgroup to one per CU.
@@ -416,7 +435,12 @@ __device__ __attribute__((always_inline)) void build_plan(const int32_t* __restr
                 u.pslot = it.nc > 1 ? it.pslot + t : -1;
                 const int p = p0 + t, r = p / grid, k = p % grid;
                 const int v = (r & 1) ? grid - 1 - k : k;
-                const int64_t slot = (int64_t)r * grid + (v % per_xcd) * kNumXcd + v / per_xcd;
+                // XCD x's items sit at slots i * 8 + x, i = 0, 1, ... with no
+                // gaps: a partial odd round (positions grid-m .. grid-1) starts
+                // each XCD's share at its first filled position
+                const int x = v / per_xcd, j = v % per_xcd;
+                const int j_lo = (r == n_items / grid && (r & 1)) ? xcd_first_filled(grid, n_items % grid, x) : 0;
+                const int64_t slot = (int64_t)r * grid + (j - j_lo) * kNumXcd + x;
                 if (TTV_DCHECK(slot < max_items && u.pslot < max_partials, TTV_SITE_PLAN)) items[slot] = u;
             }
         }
@@ -424,6 +448,7 @@ __device__ __attribute__((always_inline)) void build_plan(const int32_t* __restr
     __syncthreads();
     if (tid == 0) {
         hdr->n_items = n_items;
+        for (int x = 0; x < kNumXcd; ++x) hdr->queue[x] = 0;
         hdr->n_combine = min((int64_t)s_ncomb, max_groups);
         hdr->chunk_len = chunk_len;
         // bounds the debug build's main and combine kernels check against
@@ -630,6 +655,9 @@ struct MainCfg {
     static constexpr int kMainBytes = kStagesLong * kStageBytes;
     // per-lane DMA byte offsets of the issuing waves (K and V, kCpw chunks)
     static constexpr int kOffTableBytes = kIssueWaves * TTV_WAVE * kCpw * 8;
+    // after the offset table: the next-item slots of the work queue
+    static constexpr int kMiscBytes = 256;
+    static constexpr int kMaskOffset = kMainBytes + kOffTableBytes + kMiscBytes;
     static_assert(kQloOffset + kQloBytes <= kMainBytes, "Q lo fits in stages 4..7");
     static constexpr int kQloChunks = kQloBytes / 1024;    // DMA instructions for the Q low parts
 };
@@ -788,7 +816,8 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
     const uint16_t* q_hi,  // not __restrict__: keeps its loads ahead of the prologue fence
     const uint16_t* __restrict__ q_lo, const uint32_t* __restrict__ mask, int mask_words,
     CacheView cache, const int32_t* __restrict__ table, int Hq, uint16_t* __restrict__ out,
-    ttv_f16x4* __restrict__ part_o, float4* __restrict__ part_ml, int32_t* __restrict__ err) {
+    ttv_f16x4* __restrict__ part_o, float4* __restrict__ part_ml, int32_t* __restrict__ queue,
+    int32_t* __restrict__ err) {
     using MC = MainCfg<D, kW, kRows>;
     constexpr int kTileR = MC::kTile;
     // 16-row blocks per wave that a full tile fills (1 or 2)
@@ -800,8 +829,9 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const uint32_t ring = lds_offset(smem);
     const uint32_t qlo_s = ring + MC::kQloOffset;
-    const uint32_t mask_base = ring + MC::kMainBytes + MC::kOffTableBytes;
-    const uint32_t* mask_s = (const uint32_t*)(smem + MC::kMainBytes + MC::kOffTableBytes);
+    const uint32_t mask_base = ring + MC::kMaskOffset;
+    const uint32_t* mask_s = (const uint32_t*)(smem + MC::kMaskOffset);
+    int32_t* const s_next = (int32_t*)(smem + MC::kMainBytes + MC::kOffTableBytes);
     // This issuing wave's row of the DMA offset table (its own lanes only, so
     // it needs no barrier): chunk j's K and V byte offsets inside a stage.
     uint32_t* const off_row = (uint32_t*)(smem + MC::kMainBytes) + (size_t)(threadIdx.x >> 6) * TTV_WAVE * MC::kCpw * 2;
@@ -823,19 +853,25 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
     const int Hkv = cache.hkv;
     const int G = Hq / Hkv;
     const int grid = gridDim.x, wg = blockIdx.x;
-    int n_mine;
-    if (n_items > grid) {
-        // snake rounds: full ones, then m items on virtual workgroups
-        // 0 .. m-1 (even round) or grid-m .. grid-1 (odd round)
-        const int r = n_items / grid, m = n_items % grid;
-        const int v = (wg % kNumXcd) * (grid / kNumXcd) + wg / kNumXcd;
-        n_mine = r + ((r & 1) ? (v >= grid - m) : (v < m));
+    // More items than workgroups: XCD x = wg % 8 owns the items at slots
+    // i * 8 + x, i < xcd_items (the plan's snake order, largest estimated
+    // cost first).  Its workgroups take i = wg / 8 first, then claim the
+    // next i from the XCD's queue cursor as they finish, so a workgroup that
+    // drew short items takes more of them.  The claim for the next item is
+    // made when an item starts; its answer lands during the item.
+    // Otherwise one item each on as many workgroups as items, a multiple of
+    // 8, consecutive items on one XCD: workgroup wg holds the item at slot wg.
+    const bool dyn = n_items > grid;
+    const int xcd = wg % kNumXcd, per_xcd = grid / kNumXcd;
+    bool more;
+    int n_xcd = 0;
+    if (dyn) {
+        n_xcd = xcd_items(grid, n_items, xcd);
+        more = true;  // the first round is full
     } else {
-        // one item each on as many workgroups as items, a multiple of 8,
-        // consecutive items on one XCD: workgroup wg holds item vid(wg)
         const int active = ((n_items + kNumXcd - 1) / kNumXcd) * kNumXcd;
-        const int per_xcd = active / kNumXcd, xcd_slot = wg / kNumXcd;
-        n_mine = xcd_slot < per_xcd && (wg % kNumXcd) * per_xcd + xcd_slot < n_items;
+        const int per = active / kNumXcd, xcd_slot = wg / kNumXcd;
+        more = xcd_slot < per && xcd * per + xcd_slot < n_items;
     }
 
     // Per-lane LDS byte offsets inside a stage / the Q-lo block.
@@ -865,8 +901,10 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         }
     }
 
-    for (int k = 0, slot = wg; k < n_mine; ++k, slot += grid) {
+    for (int k = 0, slot = wg; more; ++k) {
         const Item it = k == 0 ? first_item : items[slot];
+        int claim = 0;
+        if (dyn && tid == 0) claim = __hip_atomic_fetch_add(queue + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int rows = it.n * G;
         const int n_ctx_tiles = (it.c1 - it.c0 + kKT - 1) / kKT;
         const int n_tree_tiles = (it.kmax + kKT - 1) / kKT;
@@ -1026,6 +1064,8 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         // cannot be merged).
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        // the claimed next item, for every wave after this item's last barrier
+        if (dyn && tid == 0) s_next[k & 1] = per_xcd + claim;
         // Long-context items (8 stages) issue two tiles per barrier from the
         // loop, so their prologue leaves tiles 6 and 7 to the loop's first
         // barrier; precise items (4 stages) issue one tile per barrier.
@@ -1548,6 +1588,13 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         // this kernel reads them): they retire under its prologue wait
         // instead of delaying this barrier (about 3 us per item).
         raw_barrier();
+        if (dyn) {
+            const int i = s_next[k & 1];
+            more = i < n_xcd;
+            slot = i * kNumXcd + xcd;
+        } else {
+            more = false;
+        }
     }
 }
 
@@ -1556,7 +1603,7 @@ size_t main_lds_bytes(int G, int mask_words) {
     using MC = MainCfg<D, kW, kRows>;
     const int nodes = MC::kTile / G + 2;
     const size_t mask_bytes = (size_t)((nodes * mask_words + 63) / 64) * 256;
-    return (size_t)MC::kMainBytes + MC::kOffTableBytes + mask_bytes;
+    return (size_t)MC::kMaskOffset + mask_bytes;
 }
 
 // ---------------------------------------------------------------------------
@@ -1758,7 +1805,7 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
         if (!raise_lds_limit((const void*)kern, bit, 160 * 1024)) return TTV_EHIP;
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kW * TTV_WAVE), lds, stream, hdr, items,
                            q_hi, q_lo, mask, mask_words, cv, cache->block_table, n_heads, out, po,
-                           pml, err);
+                           pml, hdr->queue, err);
         if (hipGetLastError() != hipSuccess) return TTV_EHIP;
         hipLaunchKernelGGL((attn_combine_kernel<D, MC::kTile>), dim3((unsigned)(4 * cus)), dim3(kCombThreads), 0,
                            stream, hdr, comb, n_heads, cache->n_kv_heads, po, pml, out);
