@@ -430,7 +430,7 @@ TTV_API int tree_sample_accept(const ttv_batch* bt, const void* logits, int32_t 
                                int32_t* row_choice, void* workspace, size_t workspace_bytes,
                                int32_t* err, hipStream_t stream);
 
-/* Workspace bytes tree_stochastic_accept needs (host call): fp64 [B, vocab]. */
+/* Workspace bytes tree_stochastic_accept needs (host call): fp64 [B, 2, vocab]. */
 TTV_API size_t tree_stochastic_accept_workspace_bytes(const ttv_batch* bt, int64_t vocab);
 
 /*

@@ -254,7 +254,7 @@ def test_sampled_walks_reject(lib):
     assert sample(gumbel=None) == tta.TTV_EINVAL
     assert sample(ws_bytes=need - 1) == tta.TTV_ENOSPC
     sneed = lib.tree_stochastic_accept_workspace_bytes(ctypes.byref(b), 1000)
-    assert sneed == 2 * 1000 * 8
+    assert sneed == 2 * 2 * 1000 * 8  # two float64 vocab buffers per request
 
     def stoch(T=1.0, q=FAKE, u=FAKE, ws_bytes=sneed):
         return lib.tree_stochastic_accept(ctypes.byref(b), FAKE, 1, 1000, T, q, u, FAKE, FAKE, FAKE, FAKE, 16,

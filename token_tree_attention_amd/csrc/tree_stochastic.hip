@@ -42,7 +42,7 @@ __device__ __forceinline__ double shfl_xor_f64(double v, int off) {
     return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-template <bool kMax>
+template <bool kMax, int kNW = kWaves>
 __device__ double block_reduce(double v, double* s_red) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -54,11 +54,12 @@ __device__ double block_reduce(double v, double* s_red) {
     if ((tid & (TTV_WAVE - 1)) == 0) s_red[tid / TTV_WAVE] = v;
     __syncthreads();
     double r = s_red[0];
-    for (int w = 1; w < kWaves; ++w) r = kMax ? fmax(r, s_red[w]) : r + s_red[w];
+    for (int w = 1; w < kNW; ++w) r = kMax ? fmax(r, s_red[w]) : r + s_red[w];
     return r;
 }
 
 // (score, index) maximum, lowest index on equal scores.
+template <int kNW = kWaves>
 __device__ int block_argmax(double v, int idx, double* s_val, int* s_idx) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -78,7 +79,7 @@ __device__ int block_argmax(double v, int idx, double* s_val, int* s_idx) {
     __syncthreads();
     double bv = s_val[0];
     int bi = s_idx[0];
-    for (int w = 1; w < kWaves; ++w)
+    for (int w = 1; w < kNW; ++w)
         if (s_val[w] > bv || (s_val[w] == bv && s_idx[w] < bi)) {
             bv = s_val[w];
             bi = s_idx[w];
@@ -243,11 +244,233 @@ __global__ __launch_bounds__(kThreads) void stochastic_walk_kernel(
             k < a ? tokens[s + s_path[k]] : (k == a ? final_token : -1);
 }
 
+// The same walk for a vocab that is a multiple of 8: each thread takes
+// chunks of 8 consecutive entries (one 16-byte load of bf16 logits, two of
+// fp32, four of fp64), so far more bytes are in flight per thread than with
+// one entry per load; a rejection writes the residual into the request's
+// second buffer in the same pass that sums it (the first buffer keeps the
+// current side when nothing remains above q).  Entries are visited in
+// increasing order per thread, as above.
+constexpr int kVec = 8;
+constexpr int kVThreads = 512;  // 256 registers per thread: four chunks of every pass in flight
+constexpr int kVWaves = kVThreads / TTV_WAVE;
+
+__device__ __forceinline__ void load8_logits(const void* logits, bool bf16, int64_t off, float (&x)[kVec]) {
+    if (bf16) {
+        const ttv_u32x4 w = *(const ttv_u32x4*)((const uint16_t*)logits + off);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[2 * k] = __uint_as_float(w[k] << 16);
+            x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+    } else {
+        const float4 a = *(const float4*)((const float*)logits + off);
+        const float4 c = *(const float4*)((const float*)logits + off + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+    }
+}
+__device__ __forceinline__ void load8_f32(const float* p, float (&x)[kVec]) {
+    const float4 a = *(const float4*)p, c = *(const float4*)(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+}
+__device__ __forceinline__ void load8_f64(const double* p, double (&x)[kVec]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const double2 v = *(const double2*)(p + 2 * k);
+        x[2 * k] = v.x;
+        x[2 * k + 1] = v.y;
+    }
+}
+__device__ __forceinline__ void store8_f64(double* p, const double (&x)[kVec]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) *(double2*)(p + 2 * k) = make_double2(x[2 * k], x[2 * k + 1]);
+}
+
+// Chunks c = base + j * kVThreads + tid, j < NB, of every batch (c < n_chunks):
+// load(c, j) for the whole batch, then use(c, j).
+template <int NB, typename Load, typename Use>
+__device__ __forceinline__ void chunk_pass(int64_t n_chunks, Load&& load, Use&& use) {
+    const int tid = threadIdx.x;
+    for (int64_t base = 0; base < n_chunks; base += (int64_t)NB * kVThreads) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int64_t c = base + (int64_t)j * kVThreads + tid;
+            if (c < n_chunks) load(c, j);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int64_t c = base + (int64_t)j * kVThreads + tid;
+            if (c < n_chunks) use(c, j);
+        }
+    }
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
+    const int32_t* __restrict__ node_offsets, int32_t n_max, int64_t total_nodes,
+    const void* __restrict__ logits, int64_t vocab, double temperature,
+    const float* __restrict__ draft_probs, const float* __restrict__ uniforms,
+    const float* __restrict__ gumbel, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ next_token, const int32_t* __restrict__ next_sibling,
+    int32_t max_accept, int32_t* __restrict__ accept_len, int32_t* __restrict__ accepted_nodes,
+    int32_t* __restrict__ out_tokens, double* __restrict__ work, int32_t* __restrict__ err) {
+    __shared__ int32_t s_path[TTV_MAX_TREE_NODES + 1];
+    __shared__ double s_red[kVWaves];
+    __shared__ int32_t s_ired[kVWaves];
+
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int s = node_offsets[b];
+    const int n = node_offsets[b + 1] - s;
+    if (s < 0 || n < 0 || n > n_max || (int64_t)s + n > total_nodes) {  // uniform
+        if (tid == 0) {
+            accept_len[b] = 0;
+            atomicOr(err + b, TTV_ERR_TOO_MANY_NODES);
+        }
+        return;
+    }
+    // the current side and the residual being formed, swapped on a rejection
+    double* cur_buf = work + (int64_t)(2 * b) * vocab;
+    double* alt_buf = cur_buf + vocab;
+    const int64_t n_chunks = vocab / kVec;
+    const int64_t row0 = (int64_t)s + b;  // the request's root row
+
+    // Visit a row: cur = exp((x - max) / T), den = their sum.
+    auto visit = [&](int64_t row) -> double {
+        constexpr int NB = 4;
+        float xs[NB][kVec];
+        float mf = -INFINITY;  // the logits are floats, so their maximum is exact
+        chunk_pass<NB>(n_chunks, [&](int64_t c, int j) { load8_logits(logits, kBf16, row * vocab + c * kVec, xs[j]); },
+                       [&](int64_t, int j) {
+#pragma unroll
+                           for (int k = 0; k < kVec; ++k) mf = fmaxf(mf, xs[j][k]);
+                       });
+        const double m = block_reduce<true, kVWaves>((double)mf, s_red);
+        double sum = 0.0;
+        chunk_pass<NB>(n_chunks, [&](int64_t c, int j) { load8_logits(logits, kBf16, row * vocab + c * kVec, xs[j]); },
+                       [&](int64_t c, int j) {
+                           double e[kVec];
+#pragma unroll
+                           for (int k = 0; k < kVec; ++k) {
+                               e[k] = exp(((double)xs[j][k] - m) / temperature);
+                               sum += e[k];
+                           }
+                           store8_f64(cur_buf + c * kVec, e);
+                       });
+        __syncthreads();  // cur written before any thread reads another's entry
+        return block_reduce<false, kVWaves>(sum, s_red);
+    };
+
+    int a = 0, flags = 0, final_token = -1;
+    int cur = -1;
+    int64_t row = row0;
+    double den = visit(row);
+    for (;;) {
+        int j = cur < 0 ? (n > 0 ? 0 : -1) : next_token[s + cur];
+        if (j >= 0 && (j <= cur || j >= n)) j = -1;
+        const float* q = draft_probs + row * vocab;
+        int accepted = -1;
+        while (j >= 0) {
+            const int x = tokens[s + j];
+            const double r_x = (x >= 0 && x < vocab) ? cur_buf[x] / den : 0.0;
+            const double qx = (x >= 0 && x < vocab) ? (double)q[x] : 0.0;
+            const bool take = (double)uniforms[s + j] * qx < r_x;
+            if (take) {
+                accepted = j;
+                break;
+            }
+            // rejected: the residual max(0, r - q) into the other buffer, summed
+            // in the same pass; it becomes the current side when the sum is
+            // positive (otherwise r == q up to rounding and r stays)
+            constexpr int NB = 4;
+            double bb[NB][kVec];
+            float fq[NB][kVec];
+            double z = 0.0;
+            chunk_pass<NB>(n_chunks,
+                           [&](int64_t c, int jj) {
+                               load8_f64(cur_buf + c * kVec, bb[jj]);
+                               load8_f32(q + c * kVec, fq[jj]);
+                           },
+                           [&](int64_t c, int jj) {
+                               double t[kVec];
+#pragma unroll
+                               for (int k = 0; k < kVec; ++k) {
+                                   t[k] = fmax(bb[jj][k] / den - (double)fq[jj][k], 0.0);
+                                   z += t[k];
+                               }
+                               store8_f64(alt_buf + c * kVec, t);
+                           });
+            z = block_reduce<false, kVWaves>(z, s_red);  // its barriers also publish the residual
+            if (z > 0.0) {
+                double* const t = cur_buf;
+                cur_buf = alt_buf;
+                alt_buf = t;
+                den = z;
+            }
+            const int nx = next_sibling[s + j];
+            j = (nx > j && nx < n) ? nx : -1;
+        }
+        if (accepted < 0) {
+            // correction / bonus: Gumbel-max sample of the current side
+            const float* g = gumbel + row * vocab;
+            constexpr int NB = 2;
+            double bb[NB][kVec];
+            float fg[NB][kVec];
+            double best = -INFINITY;
+            int best_i = 0x7FFFFFFF;
+            chunk_pass<NB>(n_chunks,
+                           [&](int64_t c, int jj) {
+                               load8_f64(cur_buf + c * kVec, bb[jj]);
+                               load8_f32(g + c * kVec, fg[jj]);
+                           },
+                           [&](int64_t c, int jj) {
+#pragma unroll
+                               for (int k = 0; k < kVec; ++k) {
+                                   const double r = bb[jj][k] / den;
+                                   if (r > 0.0) {
+                                       const double sc = log(r) + (double)fg[jj][k];
+                                       if (sc > best) {  // entries increase per thread: the first maximum is the lowest index
+                                           best = sc;
+                                           best_i = (int)(c * kVec + k);
+                                       }
+                                   }
+                               }
+                           });
+            final_token = block_argmax<kVWaves>(best, best_i, s_red, s_ired);
+            if (final_token == 0x7FFFFFFF) final_token = -1;
+            break;
+        }
+        if (a == max_accept) {
+            flags |= TTV_ERR_ACCEPT;
+            break;
+        }
+        if (tid == 0) s_path[a] = accepted;
+        ++a;
+        cur = accepted;
+        row = row0 + 1 + (TTV_DCHECK(accepted >= 0 && accepted < n, TTV_SITE_STOCHASTIC) ? accepted : 0);
+        __syncthreads();  // every thread has read cur before the next visit rewrites it
+        den = visit(row);
+    }
+    if (tid == 0) {
+        accept_len[b] = a;
+        if (flags) atomicOr(err + b, flags);
+    }
+    __syncthreads();  // s_path, written by thread 0
+    for (int k = tid; k < max_accept; k += kVThreads)
+        accepted_nodes[(int64_t)b * max_accept + k] = k < a ? s_path[k] : -1;
+    for (int k = tid; k <= max_accept; k += kVThreads)
+        out_tokens[(int64_t)b * (max_accept + 1) + k] =
+            k < a ? tokens[s + s_path[k]] : (k == a ? final_token : -1);
+}
+
 }  // namespace
 
 extern "C" TTV_API size_t tree_stochastic_accept_workspace_bytes(const ttv_batch* bt, int64_t vocab) {
     if (!bt || bt->batch < 0 || vocab <= 0 || vocab >= (1ll << 31)) return 0;
-    const size_t bytes = (size_t)bt->batch * (size_t)vocab * sizeof(double);
+    // two fp64 buffers of the vocab per request (the chunked path swaps them)
+    const size_t bytes = 2 * (size_t)bt->batch * (size_t)vocab * sizeof(double);
     return bytes > 0 ? bytes : 256;
 }
 
@@ -271,15 +494,20 @@ extern "C" TTV_API int tree_stochastic_accept(
     if (bt->total_nodes > 0 && (!tokens || !uniforms || !retrieve_next_token || !retrieve_next_sibling))
         return TTV_EINVAL;
     if (workspace_bytes < tree_stochastic_accept_workspace_bytes(bt, vocab)) return TTV_ENOSPC;
-    auto launch = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3(bt->batch), dim3(kThreads), 0, stream, bt->node_offsets,
+    auto launch = [&](auto kern, int threads) {
+        hipLaunchKernelGGL(kern, dim3(bt->batch), dim3(threads), 0, stream, bt->node_offsets,
                            bt->n_max, bt->total_nodes, logits, vocab, (double)temperature,
                            draft_probs, uniforms, gumbel, tokens, retrieve_next_token,
                            retrieve_next_sibling, max_accept, accept_len, accepted_nodes,
                            out_tokens, (double*)workspace, err);
     };
-    if (logits_dtype == TTV_DTYPE_BF16) launch(stochastic_walk_kernel<true>);
-    else launch(stochastic_walk_kernel<false>);
+    if (vocab % kVec == 0) {
+        if (logits_dtype == TTV_DTYPE_BF16) launch(stochastic_walk_vec_kernel<true>, kVThreads);
+        else launch(stochastic_walk_vec_kernel<false>, kVThreads);
+    } else {
+        if (logits_dtype == TTV_DTYPE_BF16) launch(stochastic_walk_kernel<true>, kThreads);
+        else launch(stochastic_walk_kernel<false>, kThreads);
+    }
     return hipGetLastError() == hipSuccess ? TTV_OK : TTV_EHIP;
 }
 
