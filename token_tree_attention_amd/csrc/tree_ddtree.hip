@@ -27,9 +27,13 @@
 // array in LDS (at most budget + 1 live entries: a popped entry's slot takes
 // its next sibling, its first child takes a new slot), each lane caching the
 // best entry among the slots it owns; a pop is a wave-wide maximum of the
-// cached scores (the rank tuples, packed for comparison, decide exact ties:
-// 11 bits per depth, rank + 1, 5 depths per 64-bit word, depth 0 in the most
-// significant field, so a shorter tuple compares below its extensions).
+// cached scores.  Exact score ties are decided by the rank tuples, compared
+// by walking the two entries' parent chains through the popped nodes (the
+// rank at the shallowest depth where they differ; a tuple before its
+// extensions).  The request's log q table is copied into LDS first when it
+// fits, so a pop reads its sibling's log q there instead of from memory.
+
+#include <atomic>
 
 #include "ttv_device.h"
 
@@ -39,8 +43,7 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / TTV_WAVE;
 constexpr int kBatch = 32;         // loads in flight per thread in a vocab pass
 constexpr int kMaxK = 1024;
-constexpr int kMaxDepths = 20;     // 4 key words x 5 fields
-constexpr int kKeyWords = 4;
+constexpr int kMaxDepths = 20;     // depths a request may have
 constexpr int kHeapLanes = TTV_WAVE;
 constexpr int kMaxSlots = kMaxK + kHeapLanes;  // live frontier entries: at most budget + 1
 
@@ -176,26 +179,6 @@ __global__ __launch_bounds__(kTopkThreads) void ddtree_topk_kernel(
     }
 }
 
-struct HeapKey {
-    uint64_t w[kKeyWords];
-};
-
-__device__ __forceinline__ bool key_less(const HeapKey& a, const HeapKey& b) {
-#pragma unroll
-    for (int i = 0; i < kKeyWords; ++i)
-        if (a.w[i] != b.w[i]) return a.w[i] < b.w[i];
-    return false;
-}
-
-// Field `depth` of the packed tuple := rank + 1.  The word is picked by
-// comparison, not by indexing, so the key stays in registers.
-__device__ __forceinline__ void key_set(HeapKey& k, int depth, int rank) {
-    const int w = depth / 5, sh = 11 * (4 - depth % 5);
-#pragma unroll
-    for (int i = 0; i < kKeyWords; ++i)
-        if (i == w) k.w[i] = (k.w[i] & ~((uint64_t)2047 << sh)) | ((uint64_t)(rank + 1) << sh);
-}
-
 // Wave-wide maximum of a double, in every lane: DPP steps inside each row of
 // 16 lanes, then the cross-row swaps (as 32-bit halves, moved together).
 template <int kCtrl>
@@ -223,9 +206,16 @@ __device__ __forceinline__ double wave_max_f64(double v) {
                 __longlong_as_double((long long)(((uint64_t)hi2[1] << 32) | lo2[1])));
 }
 
+// 16 bytes per lane from global memory into LDS at lds_base + lane * 16
+// (lds_base wave-uniform), through the direct global-to-LDS path.
+__device__ __forceinline__ void dma16(uint32_t lds_base, const void* g) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(g) : "memory", "m0");
+}
+
 __global__ __launch_bounds__(kHeapLanes) void ddtree_heap_kernel(
     const int32_t* __restrict__ toks, const double* __restrict__ logq, int32_t depths, int32_t K,
-    int32_t budget, int32_t* __restrict__ parents, int32_t* __restrict__ tokens,
+    int32_t budget, int32_t lq_in_lds, int32_t* __restrict__ parents, int32_t* __restrict__ tokens,
     int32_t* __restrict__ n_nodes) {
     constexpr int kPerLane = kMaxSlots / kHeapLanes;
     static_assert(kPerLane * kHeapLanes == kMaxSlots, "whole slots per lane");
@@ -233,7 +223,6 @@ __global__ __launch_bounds__(kHeapLanes) void ddtree_heap_kernel(
     // (log q = z - lse with finite z), so -inf marks an empty slot.
     __shared__ double e_score[kMaxSlots];
     __shared__ double e_lq[kMaxSlots];  // log q of the entry's own (last) rank
-    __shared__ HeapKey e_key[kMaxSlots];
     __shared__ int16_t e_par[kMaxSlots];
     __shared__ int16_t e_rank[kMaxSlots];
     __shared__ int8_t e_depth[kMaxSlots];
@@ -242,22 +231,59 @@ __global__ __launch_bounds__(kHeapLanes) void ddtree_heap_kernel(
     __shared__ int16_t n_rank[kMaxK];
     __shared__ int8_t n_depth[kMaxK];
     __shared__ double s_first[kMaxDepths];  // log q of rank 1 at each depth
+    extern __shared__ __attribute__((aligned(16))) double s_lq[];  // [depths, K] when lq_in_lds
     const int r = blockIdx.x;
     const int lane = threadIdx.x;
     const int32_t* tk = toks + (int64_t)r * depths * K;
     const double* lq = logq + (int64_t)r * depths * K;
+    if (lq_in_lds) {
+        // 1 KB per DMA instruction; the last one's lanes past the table load
+        // its final 16 bytes again, into LDS the launch rounded up for them
+        const int64_t bytes = (int64_t)depths * K * 8;
+        const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) double*)s_lq;
+        for (int64_t off = 0; off < bytes; off += 1024) {
+            const int64_t src = min(off + 16 * lane, bytes - 16);
+            dma16(base + (uint32_t)off, (const char*)lq + src);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+    }
     for (int i = lane; i < depths; i += kHeapLanes) s_first[i] = lq[(int64_t)i * K];
     if (lane == 0) {
-        HeapKey k0 = {{0ull, 0ull, 0ull, 0ull}};
-        key_set(k0, 0, 0);
         e_score[0] = lq[0];
         e_lq[0] = lq[0];
-        e_key[0] = k0;
         e_par[0] = -1;
         e_rank[0] = 0;
         e_depth[0] = 0;
     }
     __syncthreads();
+    // Rank-tuple order of frontier entries a and b: walk the deeper one up to
+    // the other's depth, then both up together to their common ancestor; the
+    // shallowest depth where the ranks differ decides, and equal common parts
+    // put the shorter tuple first.
+    auto tuple_less = [&](int a, int b) -> bool {
+        int da = e_depth[a], db = e_depth[b];
+        const int la = da, lb = db;
+        int ra = e_rank[a], pa = e_par[a];
+        int rb = e_rank[b], pb = e_par[b];
+        for (; da > db; --da) {
+            ra = n_rank[pa];
+            pa = n_par[pa];
+        }
+        for (; db > da; --db) {
+            rb = n_rank[pb];
+            pb = n_par[pb];
+        }
+        int res = 0;
+        for (;;) {
+            if (ra != rb) res = ra < rb ? -1 : 1;
+            if (pa == pb) break;  // the same node (or both at depth 0): the rest is equal
+            ra = n_rank[pa];
+            pa = n_par[pa];
+            rb = n_rank[pb];
+            pb = n_par[pb];
+        }
+        return res != 0 ? res < 0 : la < lb;
+    };
     // Each lane caches the best entry among its slots (score, slot; -inf and
     // -1 when it has none).  Per pop: a wave maximum of the cached scores
     // picks the entry; the popped slot takes the next sibling and the owner
@@ -276,18 +302,17 @@ __global__ __launch_bounds__(kHeapLanes) void ddtree_heap_kernel(
         while (cand) {  // exact score ties across lanes: the lowest rank tuple
             const int cs = __builtin_amdgcn_readlane(best, __builtin_ctzll(cand));
             cand &= cand - 1;
-            if (key_less(e_key[cs], e_key[wslot])) wslot = cs;
+            if (tuple_less(cs, wslot)) wslot = cs;
         }
         const double s = e_score[wslot];
         const double lq_cur = e_lq[wslot];
-        const HeapKey key = e_key[wslot];
         const int par = __builtin_amdgcn_readfirstlane(e_par[wslot]);
         const int d = __builtin_amdgcn_readfirstlane(e_depth[wslot]);
         const int rk = __builtin_amdgcn_readfirstlane(e_rank[wslot]);
         const bool sib = rk + 1 < K;
         const bool child = d + 1 < depths;
-        // uniform index: a scalar load of the sibling's log q
-        const double lq_next = sib ? lq[(int64_t)d * K + rk + 1] : 0.0;
+        // the sibling's log q: from the LDS copy, else a scalar load
+        const double lq_next = !sib ? 0.0 : lq_in_lds ? s_lq[d * K + rk + 1] : lq[(int64_t)d * K + rk + 1];
         __syncthreads();  // every lane has read the popped entry
         const int cslot = n_slots;
         if (lane == 0) {
@@ -296,22 +321,16 @@ __global__ __launch_bounds__(kHeapLanes) void ddtree_heap_kernel(
             n_rank[n] = (int16_t)rk;
             // the next sibling takes the popped slot: score - log q^(rk) + log q^(rk + 1), in that order
             if (sib) {
-                HeapKey ks = key;
-                key_set(ks, d, rk + 1);
                 e_score[wslot] = s - lq_cur + lq_next;
                 e_lq[wslot] = lq_next;
-                e_key[wslot] = ks;
                 e_rank[wslot] = (int16_t)(rk + 1);
             } else {
                 e_score[wslot] = -INFINITY;
             }
             // the first child, one depth down, in a new slot
             if (child && TTV_DCHECK(cslot < kMaxSlots && n < kMaxK, TTV_SITE_DDTREE)) {
-                HeapKey kc = key;
-                key_set(kc, d + 1, 0);
                 e_score[cslot] = s + s_first[d + 1];
                 e_lq[cslot] = s_first[d + 1];
-                e_key[cslot] = kc;
                 e_par[cslot] = (int16_t)n;
                 e_rank[cslot] = 0;
                 e_depth[cslot] = (int8_t)(d + 1);
@@ -332,7 +351,7 @@ __global__ __launch_bounds__(kHeapLanes) void ddtree_heap_kernel(
             while (c2) {
                 const int cs = owner + kHeapLanes * __builtin_ctzll(c2);
                 c2 &= c2 - 1;
-                if (key_less(e_key[cs], e_key[nb])) nb = cs;
+                if (tuple_less(cs, nb)) nb = cs;
             }
         }
         if (lane == owner) {
@@ -342,7 +361,7 @@ __global__ __launch_bounds__(kHeapLanes) void ddtree_heap_kernel(
         // the child's slot, when another lane owns it
         if (child && lane == (cslot & (kHeapLanes - 1)) && lane != owner) {
             const double cv = e_score[cslot];
-            if (best < 0 || cv > my || (cv == my && key_less(e_key[cslot], e_key[best]))) {
+            if (best < 0 || cv > my || (cv == my && tuple_less(cslot, best))) {
                 my = cv;
                 best = cslot;
             }
@@ -354,6 +373,23 @@ __global__ __launch_bounds__(kHeapLanes) void ddtree_heap_kernel(
         parents[(int64_t)r * budget + i] = live ? (int32_t)n_par[i] : -1;
         tokens[(int64_t)r * budget + i] = live ? tk[(int64_t)n_depth[i] * K + n_rank[i]] : -1;
     }
+}
+
+// Dynamic LDS the heap kernel may take beside its static arrays (about 28 KB).
+constexpr size_t kHeapLdsDynamic = 128 * 1024 + 4 * 1024;
+
+// Raises the heap kernel's dynamic-LDS limit once per device.
+bool raise_heap_lds() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<bool> done[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) dev = 0;
+    if (done[dev].load(std::memory_order_acquire)) return true;
+    if (hipFuncSetAttribute((const void*)ddtree_heap_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kHeapLdsDynamic) != hipSuccess)
+        return false;
+    done[dev].store(true, std::memory_order_release);
+    return true;
 }
 
 }  // namespace
@@ -384,8 +420,13 @@ extern "C" TTV_API int tree_ddtree_build(int32_t requests, int32_t depths, int64
     hipLaunchKernelGGL(ddtree_topk_kernel, dim3((unsigned)depths, (unsigned)requests), dim3(kTopkThreads), 0,
                        stream, draft_logits, depths, vocab, K, toks, logq);
     if (hipGetLastError() != hipSuccess) return TTV_EHIP;
-    hipLaunchKernelGGL(ddtree_heap_kernel, dim3((unsigned)requests), dim3(64), 0, stream, toks, logq, depths, K,
-                       budget, parents, tokens, n_nodes);
+    // the log q table in LDS when it fits beside the frontier (and starts
+    // 16-byte aligned in every request's slice, for the copy)
+    const size_t lq_bytes = ((size_t)depths * K * sizeof(double) + 1023) / 1024 * 1024;
+    const bool lq_in_lds = ((int64_t)depths * K) % 2 == 0 && lq_bytes <= kHeapLdsDynamic;
+    if (lq_in_lds && !raise_heap_lds()) return TTV_EHIP;
+    hipLaunchKernelGGL(ddtree_heap_kernel, dim3((unsigned)requests), dim3(64), lq_in_lds ? lq_bytes : 0, stream,
+                       toks, logq, depths, K, budget, (int32_t)lq_in_lds, parents, tokens, n_nodes);
     return hipGetLastError() == hipSuccess ? TTV_OK : TTV_EHIP;
 }
 
