@@ -52,6 +52,11 @@ SCALED = [
     # one or two 256-row tiles per request and KV head (8 query heads per KV
     # head, 16..64-node trees)
     (2, dict(batch=40, ctx=(30, 400), vocab=64, heads=(64, 8, 128))),
+    # five 256-row tiles per request and KV head over contexts of more than
+    # 128 key tiles: the partial last tile (76 rows) runs its five row blocks
+    # in pairs on three waves, and more items than workgroups go through the
+    # per-XCD work queues
+    (4, dict(batch=8, ctx=(4000, 4200), vocab=64)),
 ]
 
 
