@@ -73,44 +73,196 @@ __device__ __forceinline__ void for_each_key(const float* __restrict__ row, int6
     }
 }
 
+// The same over a row whose length is a multiple of 4 and whose start is
+// 16-byte aligned: four consecutive entries per 16-byte load, kVBatch loads
+// in flight per thread.
+constexpr int kVBatch = 8;
+template <typename F>
+__device__ __forceinline__ void for_each_key4(const float* __restrict__ row, int64_t vocab, F&& f) {
+    const int tid = threadIdx.x;
+    const int64_t n4 = vocab / 4;
+    for (int64_t base = 0; base < n4; base += (int64_t)kVBatch * kTopkThreads) {
+        float4 x[kVBatch];
+#pragma unroll
+        for (int j = 0; j < kVBatch; ++j) {
+            const int64_t c = base + (int64_t)j * kTopkThreads + tid;
+            x[j] = c < n4 ? *(const float4*)(row + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int j = 0; j < kVBatch; ++j) {
+            const int64_t c = base + (int64_t)j * kTopkThreads + tid;
+            if (c < n4) {
+                const float e[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t v = (uint32_t)(4 * c + k);
+                    f(((uint64_t)ttv_order_key(__float_as_uint(e[k])) << 32) | (uint64_t)(0xFFFFFFFFu - v));
+                }
+            }
+        }
+    }
+}
+
+constexpr int kHistBits = 12;              // first pass: the keys' top 12 bits
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kCandCap = 4096;             // candidates the fast path keeps in LDS
+
 __global__ __launch_bounds__(kTopkThreads) void ddtree_topk_kernel(
     const float* __restrict__ z, int32_t depths, int64_t vocab, int32_t K,
     int32_t* __restrict__ tok_out, double* __restrict__ logq_out) {
-    __shared__ uint32_t s_hist[256];
+    __shared__ uint32_t s_hist[kHistBins];
     __shared__ uint32_t s_sel[2];  // digit, count above it
     __shared__ uint32_t s_count;
+    __shared__ uint32_t s_wsum[kTopkWaves];
     __shared__ uint64_t s_cand[kMaxK];
+    __shared__ uint64_t s_pool[kCandCap];
     __shared__ double s_exp[kMaxK];
     __shared__ double s_lse;
     const int d = blockIdx.x;
     const int r = blockIdx.y;
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const float* row = z + ((int64_t)r * depths + d) * vocab;
+    const bool vec = (vocab % 4) == 0 && ((uintptr_t)row % 16) == 0;
+    auto each_key = [&](auto&& f) {
+        if (vec) for_each_key4(row, vocab, f);
+        else for_each_key(row, vocab, f);
+    };
+    // wave-aggregated slot claim in a buffer (order irrelevant: sorted later)
+    auto claim = [&](bool keep) -> uint32_t {
+        const uint64_t m = __ballot(keep);
+        if (m == 0) return 0xFFFFFFFFu;
+        uint32_t base = 0;
+        const int leader = __builtin_ctzll(m);
+        if (lane == leader) base = atomicAdd(&s_count, (uint32_t)__builtin_popcountll(m));
+        base = __shfl(base, leader);
+        return keep ? base + (uint32_t)__builtin_popcountll(m & ((1ull << lane) - 1ull)) : 0xFFFFFFFFu;
+    };
 
-    // ---- radix select of the K-th largest key ----------------------------
-    // High word first; the low word (the token id) only splits ties at the
-    // K-th logit, so its passes run only when the elements equal to the
-    // selected high word outnumber the slots left for them.
+    // ---- fast path: one histogram pass over the keys' top 12 bits, the bin
+    // holding the K-th largest key, then every key at or above that bin
+    // gathered into LDS (when they fit), where the exact selection runs.
+    for (int i = tid; i < kHistBins; i += kTopkThreads) s_hist[i] = 0;
+    if (tid == 0) s_count = 0;
+    __syncthreads();
+    each_key([&](uint64_t key) { atomicAdd(&s_hist[(uint32_t)(key >> (64 - kHistBits))], 1u); });
+    __syncthreads();
+    // suffix sums from the top bin: thread t owns bins 4095 - 4t .. 4092 - 4t
+    uint32_t own = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) own += s_hist[kHistBins - 1 - 4 * tid - q];
+    uint32_t inc = own;  // inclusive scan over threads (top bins first)
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t t = __shfl_up(inc, off);
+        if (lane >= off) inc += t;
+    }
+    if (lane == 63) s_wsum[tid >> 6] = inc;
+    __syncthreads();
+    uint32_t before = 0;  // keys in the bins above this thread's
+    for (int w = 0; w < (tid >> 6); ++w) before += s_wsum[w];
+    before += inc - own;
+    if (before < (uint32_t)K && before + own >= (uint32_t)K) {
+        uint32_t acc = before;
+        int bin = kHistBins - 1 - 4 * tid;
+        for (int q = 0; q < 4; ++q, --bin) {
+            acc += s_hist[bin];
+            if (acc >= (uint32_t)K) break;
+        }
+        s_sel[0] = (uint32_t)bin;  // the K-th largest key's bin
+        s_sel[1] = acc;            // keys at or above it
+    }
+    __syncthreads();
+    const uint32_t tbin = s_sel[0];
+    const uint32_t n_pool = s_sel[1];
+    const bool fast = n_pool <= (uint32_t)kCandCap;
+    __syncthreads();  // s_sel is rewritten by the selection below
     uint64_t prefix = 0, pmask = 0;
     uint32_t k_rem = (uint32_t)K;
+    if (fast) {
+        auto take = [&](uint64_t key) {
+            const uint32_t pos = claim((uint32_t)(key >> (64 - kHistBits)) >= tbin);
+            if (pos != 0xFFFFFFFFu && TTV_DCHECK(pos < (uint32_t)kCandCap, TTV_SITE_DDTREE)) s_pool[pos] = key;
+        };
+        if (vec) {
+            // most chunks of four hold no candidate: one ballot per chunk
+            // skips them, the claims run only where some lane has one
+            const uint32_t tkey = tbin << (32 - kHistBits);  // lowest order key in bin tbin
+            const int64_t n4 = vocab / 4;
+            for (int64_t base = 0; base < n4; base += (int64_t)kVBatch * kTopkThreads) {
+                float4 x[kVBatch];
+#pragma unroll
+                for (int j = 0; j < kVBatch; ++j) {
+                    const int64_t c = base + (int64_t)j * kTopkThreads + tid;
+                    x[j] = c < n4 ? *(const float4*)(row + 4 * c) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+                }
+#pragma unroll
+                for (int j = 0; j < kVBatch; ++j) {
+                    const int64_t c = base + (int64_t)j * kTopkThreads + tid;
+                    const float e[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
+                    bool any = false;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) any |= ttv_order_key(__float_as_uint(e[k])) >= tkey;
+                    if (__ballot(any && c < n4) == 0) continue;  // uniform
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t v = (uint32_t)(4 * c + k);
+                        const uint64_t key = ((uint64_t)ttv_order_key(__float_as_uint(e[k])) << 32) | (uint64_t)(0xFFFFFFFFu - v);
+                        const uint32_t pos = claim(c < n4 && (uint32_t)(key >> (64 - kHistBits)) >= tbin);
+                        if (pos != 0xFFFFFFFFu && TTV_DCHECK(pos < (uint32_t)kCandCap, TTV_SITE_DDTREE)) s_pool[pos] = key;
+                    }
+                }
+            }
+        } else {
+            each_key(take);
+        }
+        __syncthreads();
+    }
+    // ---- radix select of the K-th largest key, 8-bit digits, over the
+    // gathered pool (fast path) or the row.  High word first; the low word
+    // (the token id) only splits ties at the K-th logit, so its passes run
+    // only when the keys equal to the selected high word outnumber the slots
+    // left for them.
     for (int shift = 56; shift >= 0; shift -= 8) {
         for (int i = tid; i < 256; i += kTopkThreads) s_hist[i] = 0;
         __syncthreads();
-        for_each_key(row, vocab, [&](uint64_t key) {
+        auto count = [&](uint64_t key) {
             if ((key & pmask) == prefix) atomicAdd(&s_hist[(uint32_t)(key >> shift) & 255u], 1u);
-        });
+        };
+        if (fast) {
+            for (uint32_t i = tid; i < n_pool; i += kTopkThreads) count(s_pool[i]);
+        } else {
+            each_key(count);
+        }
         __syncthreads();
-        if (tid == 0) {
-            uint32_t above = 0;
-            int dig = 255;
-            for (; dig > 0; --dig) {
-                if (above + s_hist[dig] >= k_rem) break;
-                above += s_hist[dig];
+        if (tid < TTV_WAVE) {
+            // The digit holding the k_rem-th largest key and the count above
+            // it: wave 0, lane l owning digits 255 - 4l .. 252 - 4l, a scan
+            // over the lanes from the top digits down.
+            uint32_t own = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) own += s_hist[255 - 4 * lane - q];
+            uint32_t inc = own;
+#pragma unroll
+            for (int off = 1; off < TTV_WAVE; off <<= 1) {
+                const uint32_t t = __shfl_up(inc, off);
+                if (lane >= off) inc += t;
             }
-            s_sel[0] = (uint32_t)dig;
-            s_sel[1] = above;
-            // after the high word: stop when every element at this prefix is kept
-            s_count = (shift == 32 && above + s_hist[dig] == k_rem) ? 1u : 0u;
+            const uint32_t before = inc - own;
+            // the lane where the count reaches k_rem (the last lane takes digit
+            // 0 whatever remains, as a scan down to digit 1 would)
+            if ((before < k_rem && inc >= k_rem) || (lane == TTV_WAVE - 1 && inc < k_rem)) {
+                uint32_t above = before;
+                int dig = 255 - 4 * lane;
+                for (int q = 0; q < 3; ++q, --dig) {
+                    if (above + s_hist[dig] >= k_rem) break;
+                    above += s_hist[dig];
+                }
+                s_sel[0] = (uint32_t)dig;
+                s_sel[1] = above;
+                // after the high word: stop when every element at this prefix is kept
+                s_count = (shift == 32 && above + s_hist[dig] == k_rem) ? 1u : 0u;
+            }
         }
         __syncthreads();
         prefix |= (uint64_t)s_sel[0] << shift;
@@ -125,40 +277,49 @@ __global__ __launch_bounds__(kTopkThreads) void ddtree_topk_kernel(
     if (tid == 0) s_count = 0;
     for (int i = tid; i < kMaxK; i += kTopkThreads) s_cand[i] = 0ull;
     __syncthreads();
-    const int lane = tid & 63;
-    for_each_key(row, vocab, [&](uint64_t key) {
-        const bool keep = (key & pmask) >= prefix;
-        // wave-aggregated slot claim (candidate order is irrelevant: sorted next)
-        const uint64_t m = __ballot(keep);
-        if (m == 0) return;
-        uint32_t base = 0;
-        const int leader = __builtin_ctzll(m);
-        if (lane == leader) base = atomicAdd(&s_count, (uint32_t)__builtin_popcountll(m));
-        base = __shfl(base, leader);
-        if (keep) {
-            const uint32_t pos = base + (uint32_t)__builtin_popcountll(m & ((1ull << lane) - 1ull));
-            if (TTV_DCHECK(pos < (uint32_t)kMaxK, TTV_SITE_DDTREE)) s_cand[pos] = key;
+    auto keep_key = [&](uint64_t key) {
+        const uint32_t pos = claim((key & pmask) >= prefix);
+        if (pos != 0xFFFFFFFFu && TTV_DCHECK(pos < (uint32_t)kMaxK, TTV_SITE_DDTREE)) s_cand[pos] = key;
+    };
+    if (fast) {
+        // every lane of a wave takes part in claim's ballot
+        for (uint32_t i0 = 0; i0 < n_pool; i0 += kTopkThreads) {
+            const uint32_t i = i0 + tid;
+            const uint32_t pos = claim(i < n_pool && (s_pool[i < n_pool ? i : 0] & pmask) >= prefix);
+            if (pos != 0xFFFFFFFFu && TTV_DCHECK(pos < (uint32_t)kMaxK, TTV_SITE_DDTREE)) s_cand[pos] = s_pool[i];
         }
-    });
+    } else {
+        each_key(keep_key);
+    }
     __syncthreads();
 
-    // ---- bitonic sort, descending ------------------------------------------
+    // ---- bitonic sort, descending: one key per thread; partners closer than
+    // 64 are in the same wave (shuffles), farther ones go through LDS
+    static_assert(kMaxK == kTopkThreads, "one key per thread");
+    uint64_t key = s_cand[tid];
     for (int k = 2; k <= kMaxK; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < kMaxK; i += kTopkThreads) {
-                const int p = i ^ j;
-                if (p > i) {
-                    const uint64_t a = s_cand[i], b = s_cand[p];
-                    const bool desc = (i & k) == 0;
-                    if (desc ? (a < b) : (a > b)) {
-                        s_cand[i] = b;
-                        s_cand[p] = a;
-                    }
-                }
+            uint64_t other;
+            if (j >= TTV_WAVE) {
+                __syncthreads();  // every thread has read the previous exchange
+                s_cand[tid] = key;
+                __syncthreads();
+                other = s_cand[tid ^ j];
+            } else {
+                const uint32_t lo = __shfl_xor((uint32_t)key, j, TTV_WAVE);
+                const uint32_t hi = __shfl_xor((uint32_t)(key >> 32), j, TTV_WAVE);
+                other = ((uint64_t)hi << 32) | lo;
             }
-            __syncthreads();
+            const bool desc = (tid & k) == 0;
+            const bool lower = (tid & j) == 0;
+            const uint64_t mx = key > other ? key : other;
+            const uint64_t mn = key > other ? other : key;
+            key = (desc == lower) ? mx : mn;
         }
     }
+    __syncthreads();
+    s_cand[tid] = key;
+    __syncthreads();
 
     // ---- log q over the kept K: exp(z_r - z_1) in parallel, the sum in rank order
     const double m = (double)key_to_float((uint32_t)(s_cand[0] >> 32));
@@ -166,8 +327,17 @@ __global__ __launch_bounds__(kTopkThreads) void ddtree_topk_kernel(
         s_exp[i] = exp((double)key_to_float((uint32_t)(s_cand[i] >> 32)) - m);
     __syncthreads();
     if (tid == 0) {
+        // in rank order; the reads of a block of 16 are issued together
         double s = 0.0;
-        for (int i = 0; i < K; ++i) s += s_exp[i];
+        int i = 0;
+        for (; i + 16 <= K; i += 16) {
+            double v[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) v[q] = s_exp[i + q];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) s += v[q];
+        }
+        for (; i < K; ++i) s += s_exp[i];
         s_lse = m + log(s);
     }
     __syncthreads();
