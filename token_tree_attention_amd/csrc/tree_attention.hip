@@ -66,6 +66,7 @@ constexpr int kCostBuckets = 1024;      // plan's bucket sort of item costs (32 
 constexpr int kPreciseCtx = 256;        // requests with a shorter context run every tile precise
 constexpr int kCombThreads = 256;       // combine workgroup
 constexpr int kCombBatch = 8;           // chunk partials a combine thread loads before using any
+constexpr int kClaimLead = 4;           // tiles before an item's end at which the next is claimed
 constexpr float kLazyRescale = 8.0f;    // log2 headroom before the running max is moved
 constexpr float kNegBig = -1.0e30f;
 // Tile classes of the attention loop (see attn_main_kernel).
@@ -181,6 +182,34 @@ __host__ __device__ inline int xcd_items(int grid, int n_items, int x) {
     const int last = (r & 1) ? per_xcd - xcd_first_filled(grid, m, x)
                              : min(per_xcd, max(0, m - x * per_xcd));
     return r * per_xcd + last;
+}
+
+// Work stealing for a workgroup whose XCD's list is used up: the queue
+// cursors of all XCDs are read, the one with the most items left is claimed
+// from, and a lost race (another workgroup took the last item) tries again.
+// Returns the slot of the claimed item, or -1 once every list is used up.
+// Cursors only grow, so every pass either claims or sees less work left.
+__device__ inline int steal_item(int32_t* queue, int grid, int n_items) {
+    const int per_xcd = grid / kNumXcd;
+    for (int attempt = 0; attempt < 2 * kNumXcd; ++attempt) {
+        int cur[kNumXcd];
+#pragma unroll
+        for (int x = 0; x < kNumXcd; ++x)
+            cur[x] = __hip_atomic_load(queue + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int best = -1, best_left = 0;
+#pragma unroll
+        for (int x = 0; x < kNumXcd; ++x) {
+            const int left = xcd_items(grid, n_items, x) - per_xcd - cur[x];
+            if (left > best_left) {
+                best_left = left;
+                best = x;
+            }
+        }
+        if (best < 0) return -1;
+        const int i = per_xcd + __hip_atomic_fetch_add(queue + best, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (i < xcd_items(grid, n_items, best)) return i * kNumXcd + best;
+    }
+    return -1;
 }
 
 // Inlined on purpose: called out of line, its register count (over 160)
@@ -859,7 +888,9 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
     // cost first).  Its workgroups take i = wg / 8 first, then claim the
     // next i from the XCD's queue cursor as they finish, so a workgroup that
     // drew short items takes more of them.  The claim for the next item is
-    // made when an item starts; its answer lands during the item.
+    // made when an item starts; its answer lands during the item.  Once its
+    // XCD's list is used up, an idle workgroup takes items left on the other
+    // XCDs (steal_item).
     // Otherwise one item each on as many workgroups as items, a multiple of
     // 8, consecutive items on one XCD: workgroup wg holds the item at slot wg.
     const bool dyn = n_items > grid;
@@ -904,12 +935,19 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
 
     for (int k = 0, slot = wg; more; ++k) {
         const Item it = k == 0 ? first_item : items[slot];
-        int claim = 0;
-        if (dyn && tid == 0) claim = __hip_atomic_fetch_add(queue + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int rows = it.n * G;
         const int n_ctx_tiles = (it.c1 - it.c0 + kKT - 1) / kKT;
         const int n_tree_tiles = (it.kmax + kKT - 1) / kKT;
         const int n_tiles = n_ctx_tiles + n_tree_tiles;
+        // The next item is claimed from this XCD's cursor kClaimLead tiles
+        // before the item ends (at its start when it is shorter), so the
+        // atomic's latency hides behind the last tiles while a claimed item
+        // waits only briefly -- the longer it waits, the fewer items idle
+        // workgroups of other XCDs find to take.
+        int claim = 0;  // lane 0 of wave 0
+        const int tau_claim = n_tiles > kClaimLead ? n_tiles - kClaimLead : -1;
+        if (dyn && tid == 0 && tau_claim < 0)
+            claim = __hip_atomic_fetch_add(queue + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // Three classes of tiles.  Plain: whole context tiles.  Masked: the
         // partial context tile and the tree tiles.  Precise: every tile of a
         // request with a short context, where few keys can dominate a row's
@@ -1065,8 +1103,6 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         // cannot be merged).
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        // the claimed next item, for every wave after this item's last barrier
-        if (dyn && tid == 0) s_next[k & 1] = per_xcd + claim;
         // Long-context items (8 stages) issue two tiles per barrier from the
         // loop, so their prologue leaves tiles 6 and 7 to the loop's first
         // barrier; precise items (4 stages) issue one tile per barrier.
@@ -1365,6 +1401,10 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                 constexpr bool kNextPrecise = decltype(next)::value == kClassPrecise;
                 constexpr bool kNextMasked = decltype(next)::value != kClassPlain;
                 constexpr bool kCurShifted = decltype(cur)::value == kClassPlain;
+                if (dyn && wave == 0 && tau == tau_claim) {
+                    if (lane == 0)
+                        claim = __hip_atomic_fetch_add(queue + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
                 rescale_if_needed(cur, S_cur, tmax);
                 advance(cur, tau);
                 const char* kst = smem + ((tau + 1) & smask) * MC::kStageBytes;
@@ -1582,6 +1622,12 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                 else body(std::integral_constant<int, 0>{});
             }
         }
+        // the claimed next item, for every wave after the barrier below (the
+        // write has landed before wave 0 reaches it)
+        if (dyn && wave == 0) {
+            if (lane == 0) s_next[k & 1] = per_xcd + claim;
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        }
         // The next item reuses the LDS (ring, Q-lo, mask): a barrier, but no
         // memory fence.  Every LDS read of this item has fed an MFMA or a
         // store by now and every tile load has landed, while the item's
@@ -1591,8 +1637,18 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         raw_barrier();
         if (dyn) {
             const int i = s_next[k & 1];
-            more = i < n_xcd;
-            slot = i * kNumXcd + xcd;
+            if (i < n_xcd) {
+                slot = i * kNumXcd + xcd;
+            } else {
+                // This XCD's list is used up and the workgroup is idle: take
+                // an item from the XCD with the most left (the XCDs do not
+                // run at the same speed).  Claimed only now, not one item
+                // ahead, so a stolen item never waits behind a running one.
+                if (tid == 0) s_next[2] = steal_item(queue, grid, n_items);
+                __syncthreads();
+                slot = s_next[2];
+            }
+            more = slot >= 0;
         } else {
             more = false;
         }
