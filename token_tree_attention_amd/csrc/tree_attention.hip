@@ -14,17 +14,16 @@
 // How, on gfx950:
 //  1. attn_prep_kernel: workgroup 0 builds the work plan on the device (no
 //     host round trip); workgroup 1 + p handles nodes 2p and 2p + 1 of the
-//     batch, one per 256-thread half.  A half rotates its node's Q for every
-//     query head in fp64 (angles reduced
-//     modulo 2 pi before sincos), multiplies by scale * log2(e) and stores it
-//     as bf16 hi (+ bf16 lo for short contexts) in the workspace; it rotates
-//     K in fp64, rounds it once to bf16 and writes it with V into slot
-//     ctx + i.
+//     batch, one per 256-thread half.  A half computes its node's rotation
+//     angles in fp64 (reduced modulo 2 pi before sincos), stores cos and sin
+//     times scale * log2(e) as fp32 for the main kernel, rotates K in fp64,
+//     rounds it once to bf16 and writes it with V into slot ctx + i.
 //  2. attn_main_kernel, persistent, 8 waves: a work item is (request, KV
 //     head, row tile of 128 or 256 query rows, slot chunk).  Rows are (node,
 //     query head of the GQA group) pairs, node-major, so every context K/V
 //     byte feeds all rows of its KV head.  A wave owns one or two 16-row
-//     blocks and keeps their Q in registers.  K and V tiles of 32 slots
+//     blocks and keeps their Q in registers, rotated in fp32 in the item's
+//     prologue.  K and V tiles of 32 slots
 //     stream through an LDS ring (up to 6 tiles in flight) by direct
 //     global->LDS loads; V stays row-major and is read transposed by
 //     ds_read_b64_tr_b16.  S^T = K Q^T and O^T += V^T P^T run on
@@ -111,7 +110,7 @@ struct Combine {
 
 struct Layout {
     int64_t max_groups, max_items, max_partials;
-    size_t off_items, off_combine, off_q, off_qlo, off_po, off_pml, total;
+    size_t off_items, off_combine, off_glist, off_gpos, off_rope, off_po, off_pml, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -127,10 +126,12 @@ Layout make_layout(int64_t B, int64_t T, int64_t Hq, int64_t Hkv, int64_t D) {
     off = align256(off + (size_t)(L.max_items + kMaxGrid) * sizeof(Item));
     L.off_combine = off;
     off = align256(off + (size_t)L.max_groups * sizeof(Combine));
-    L.off_q = off;
-    off = align256(off + (size_t)T * Hq * D * 2);
-    L.off_qlo = off;
-    off = align256(off + (size_t)T * Hq * D * 2);
+    L.off_glist = off;  // the plan's groups (first item, bucket), at most one per item
+    off = align256(off + (size_t)L.max_items * sizeof(int2));
+    L.off_gpos = off;   // each group's first position, at its first item's index
+    off = align256(off + (size_t)L.max_items * sizeof(int32_t));
+    L.off_rope = off;   // per node: (cos, sin) * scale * log2(e) of each rotation pair, fp32
+    off = align256(off + (size_t)T * (D / 2) * sizeof(float2));
     L.off_po = off;
     off = align256(off + (size_t)L.max_partials * kTileM * D * 2);
     L.off_pml = off;
@@ -219,15 +220,16 @@ __device__ __attribute__((always_inline)) void build_plan(const int32_t* __restr
                            int64_t total_nodes, int G, int Hkv, int cap_limit, int tile_m,
                            int target_items, int grid, PlanHeader* hdr, Item* items,
                            Combine* combine, int64_t max_items, int64_t max_groups,
-                           int64_t max_partials, int32_t* err, int32_t* s_off, int32_t* s_ctx,
+                           int64_t max_partials, int2* group_list, int32_t* group_pos,
+                           int32_t* err, int32_t* s_off, int32_t* s_ctx,
                            int32_t* s_items, int32_t* s_parts) {  // LDS, B + 1 ints each
     __shared__ unsigned long long s_wsum[kPrepWaves];
     __shared__ int32_t s_wtot[2][kPrepWaves];
     __shared__ int32_t s_bucket[kCostBuckets];  // counts, then placement cursors
-    __shared__ int32_t s_ncomb;
+    __shared__ int32_t s_ncomb, s_ngroups;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
-    if (tid == 0) s_ncomb = 0;
+    if (tid == 0) s_ncomb = s_ngroups = 0;
     // The offsets and lengths are read once, into LDS.
     for (int j = tid; j <= B; j += kPrepThreads) {
         s_off[j] = node_offsets[j];
@@ -397,10 +399,18 @@ __device__ __attribute__((always_inline)) void build_plan(const int32_t* __restr
     if (snake) {
         for (int k = tid; k < kCostBuckets; k += kPrepThreads) s_bucket[k] = 0;
         __syncthreads();
+        // A group (request, KV head, chunk: its nt row tiles are consecutive
+        // items) is counted by its first tile, which also lists the group as
+        // (first item, bucket + 1024 nt); nt <= 512, bucket < 1024.
         for (int x = tid; x < n_items; x += kPrepThreads) {
             Item it;
             make_item(x, it);
-            if (it.tile == 0) atomicAdd(&s_bucket[cost_bucket(it)], it.nt);
+            if (it.tile == 0) {
+                const int k = cost_bucket(it);
+                atomicAdd(&s_bucket[k], it.nt);
+                const int gi = atomicAdd(&s_ngroups, 1);
+                if (TTV_DCHECK(gi < max_items, TTV_SITE_PLAN)) group_list[gi] = make_int2(x, k + 1024 * it.nt);
+            }
         }
         __syncthreads();
         // cursors: bucket k starts after every item of the buckets above it
@@ -449,30 +459,32 @@ __device__ __attribute__((always_inline)) void build_plan(const int32_t* __restr
             if (it.nc > 1 && chunk == 0) add_combine(it);
         }
     } else {
+        // Each group takes nt consecutive positions from its bucket's cursor
+        // (first position kept at its first item's index in group_pos); then
+        // every item places itself at its group's first position plus its
+        // row tile.  (A group placing its own tiles in a loop left the
+        // threads of groups with many tiles running long serial loops.)
+        const int n_groups = s_ngroups;
+        for (int g = tid; g < n_groups; g += kPrepThreads) {
+            const int2 e = group_list[g];
+            if (TTV_DCHECK(e.x >= 0 && e.x < max_items, TTV_SITE_PLAN))
+                group_pos[e.x] = atomicAdd(&s_bucket[e.y & 1023], e.y >> 10);
+        }
+        __syncthreads();
         const int per_xcd = grid / kNumXcd;
         for (int x = tid; x < n_items; x += kPrepThreads) {
             Item it;
             const int chunk = make_item(x, it);
             if (it.nc > 1 && chunk == 0) add_combine(it);
-            if (it.tile != 0) continue;
-            // the group's first tile places the group's nt tiles
-            const int p0 = atomicAdd(&s_bucket[cost_bucket(it)], it.nt);
-            for (int t = 0; t < it.nt; ++t) {
-                Item u = it;
-                u.tile = t;
-                const int last_row = min((t + 1) * tile_m, it.n * G) - 1;
-                u.kmax = chunk == it.nc - 1 ? last_row / G + 1 : 0;
-                u.pslot = it.nc > 1 ? it.pslot + t : -1;
-                const int p = p0 + t, r = p / grid, k = p % grid;
-                const int v = (r & 1) ? grid - 1 - k : k;
-                // XCD x's items sit at slots i * 8 + x, i = 0, 1, ... with no
-                // gaps: a partial odd round (positions grid-m .. grid-1) starts
-                // each XCD's share at its first filled position
-                const int x = v / per_xcd, j = v % per_xcd;
-                const int j_lo = (r == n_items / grid && (r & 1)) ? xcd_first_filled(grid, n_items % grid, x) : 0;
-                const int64_t slot = (int64_t)r * grid + (j - j_lo) * kNumXcd + x;
-                if (TTV_DCHECK(slot < max_items && u.pslot < max_partials, TTV_SITE_PLAN)) items[slot] = u;
-            }
+            const int p = group_pos[x - it.tile] + it.tile, r = p / grid, k = p % grid;
+            const int v = (r & 1) ? grid - 1 - k : k;
+            // XCD xc's items sit at slots i * 8 + xc, i = 0, 1, ... with no
+            // gaps: a partial odd round (positions grid-m .. grid-1) starts
+            // each XCD's share at its first filled position
+            const int xc = v / per_xcd, j = v % per_xcd;
+            const int j_lo = (r == n_items / grid && (r & 1)) ? xcd_first_filled(grid, n_items % grid, xc) : 0;
+            const int64_t slot = (int64_t)r * grid + (j - j_lo) * kNumXcd + xc;
+            if (TTV_DCHECK(slot < max_items && it.pslot < max_partials, TTV_SITE_PLAN)) items[slot] = it;
         }
     }
     __syncthreads();
@@ -492,12 +504,13 @@ template <int D>
 // workgroups per CU) keep a large batch's node workgroups in one round.
 __global__ __launch_bounds__(kPrepThreads, 8) void attn_prep_kernel(
     const int32_t* __restrict__ node_offsets, const int32_t* __restrict__ ctx_lens, int B,
-    int n_max, int64_t total_nodes, const uint16_t* __restrict__ q,
+    int n_max, int64_t total_nodes,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ positions, CacheView cache, int Hq, RopeTable rope,
-    double q_mult, uint16_t* __restrict__ q_hi, uint16_t* __restrict__ q_lo, int tile_m,
+    double q_mult, float2* __restrict__ rope_cs, int tile_m,
     int target_items, int grid, PlanHeader* hdr, Item* items, Combine* combine, int64_t max_items,
-    int64_t max_groups, int64_t max_partials, int32_t* __restrict__ err) {
+    int64_t max_groups, int64_t max_partials, int2* group_list, int32_t* group_pos,
+    int32_t* __restrict__ err) {
     const int Hkv = cache.hkv;
     const int G = Hq / Hkv;
     // node_offsets and ctx_lens staged in LDS (B + 1 ints each), then the
@@ -510,7 +523,8 @@ __global__ __launch_bounds__(kPrepThreads, 8) void attn_prep_kernel(
     if (blockIdx.x == 0) {
         build_plan(node_offsets, ctx_lens, B, n_max, total_nodes, G, Hkv,
                    cache.paged ? -1 : cache.cap, tile_m, target_items, grid, hdr, items, combine,
-                   max_items, max_groups, max_partials, err, s_off, s_ctx, s_dyn + 2 * (B + 1),
+                   max_items, max_groups, max_partials, group_list, group_pos, err, s_off, s_ctx,
+                   s_dyn + 2 * (B + 1),
                    s_dyn + 3 * (B + 1));
         return;
     }
@@ -522,23 +536,18 @@ __global__ __launch_bounds__(kPrepThreads, 8) void attn_prep_kernel(
     const int64_t node = 2 * ((int64_t)blockIdx.x - 1) + half;
     const bool has_node = node < total_nodes;  // uniform over the half's waves
     constexpr int kVec = 8;
-    const int q_vecs = Hq * D / kVec;
     const int kv_vecs = cache.hkv * D / kVec;
-    // Rotation in fp64: with fp32, x0 cos - x1 sin loses absolute accuracy
-    // when the two products nearly cancel, which shows up as several bf16
-    // ulps on small results.  The work is N_b * (Hq + Hkv) * D/2 pairs.
+    // K's rotation in fp64: with fp32, x0 cos - x1 sin loses absolute
+    // accuracy when the two products nearly cancel, which shows up as bf16
+    // ulps of the stored K on small results.
     __shared__ double s_cos2[2][D / 2], s_sin2[2][D / 2];
     double* s_cos = s_cos2[half];
     double* s_sin = s_sin2[half];
     // The node's own loads do not depend on which request owns it, so they
     // are issued first; the request is then found in the staged offsets.
-    ttv_u32x4 q_first = {0u, 0u, 0u, 0u}, q_second = {0u, 0u, 0u, 0u};
     ttv_u32x4 k_first = {0u, 0u, 0u, 0u}, v_first = {0u, 0u, 0u, 0u};
     int pos = 0;
     if (has_node) {
-        if (tid < q_vecs) q_first = *(const ttv_u32x4*)(q + node * Hq * D + (int64_t)tid * kVec);
-        if (tid + kHalf < q_vecs)
-            q_second = *(const ttv_u32x4*)(q + node * Hq * D + (int64_t)(tid + kHalf) * kVec);
         if (tid < kv_vecs) {
             const int64_t e = node * cache.hkv * D + (int64_t)tid * kVec;
             k_first = *(const ttv_u32x4*)(k_new + e);
@@ -559,6 +568,8 @@ __global__ __launch_bounds__(kPrepThreads, 8) void attn_prep_kernel(
         sincos(red, &sn, &cs);
         s_cos[tid] = cs;
         s_sin[tid] = sn;
+        // the main kernel rotates Q with these, scaled by scale * log2(e)
+        rope_cs[node * (D / 2) + tid] = make_float2((float)(cs * q_mult), (float)(sn * q_mult));
     }
     __syncthreads();
     if (!has_node) return;  // after the workgroup's only barrier
@@ -583,32 +594,6 @@ __global__ __launch_bounds__(kPrepThreads, 8) void attn_prep_kernel(
     if (!ok) return;  // uniform; the plan flags the request
     int64_t dst_first = -1;
     if (tid < kv_vecs) dst_first = cache_row(cache, b, (tid * kVec) / D, ctx + i, D);
-    // Q: rotated, scaled by softmax_scale*log2(e), stored as bf16 hi + lo
-    // parts; the low parts only where the main kernel reads them (requests
-    // whose items run precise).
-    const bool need_lo = ctx < kPreciseCtx;
-    for (int v = tid; v < q_vecs; v += kHalf) {
-        const int64_t e = node * Hq * D + (int64_t)v * kVec;
-        const ttv_u32x4 in = v == tid ? q_first
-                           : v == tid + kHalf ? q_second : *(const ttv_u32x4*)(q + e);
-        const int d0 = (v * kVec) % D;
-        ttv_u32x4 hi4, lo4 = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const double x0 = ttv_bf16_bits_to_f64(in[w] & 0xFFFFu);
-            const double x1 = ttv_bf16_bits_to_f64(in[w] >> 16);
-            const int m = (d0 >> 1) + w;
-            const double c = s_cos[m], sn = s_sin[m];
-            const double r0 = (x0 * c - x1 * sn) * q_mult;
-            const double r1 = (x1 * c + x0 * sn) * q_mult;
-            hi4[w] = pack_bf16_f64(r0, r1);
-            if (need_lo)
-                lo4[w] = pack_bf16_f64(r0 - ttv_bf16_bits_to_f64(hi4[w] & 0xFFFFu),
-                                       r1 - ttv_bf16_bits_to_f64(hi4[w] >> 16));
-        }
-        *(ttv_u32x4*)(q_hi + e) = hi4;
-        if (need_lo) *(ttv_u32x4*)(q_lo + e) = lo4;
-    }
     // K (rotated, rounded once from fp64) and V (copied) into slot ctx + i.
     for (int v = tid; v < kv_vecs; v += kHalf) {
         const int h = (v * kVec) / D;
@@ -689,7 +674,6 @@ struct MainCfg {
     static constexpr int kMiscBytes = 256;
     static constexpr int kMaskOffset = kMainBytes + kOffTableBytes + kMiscBytes;
     static_assert(kQloOffset + kQloBytes <= kMainBytes, "Q lo fits in stages 4..7");
-    static constexpr int kQloChunks = kQloBytes / 1024;    // DMA instructions for the Q low parts
 };
 
 __device__ __forceinline__ int swz_k(int row, int piece, int P) { return piece ^ (row & (P - 1)); }
@@ -843,8 +827,8 @@ __device__ __forceinline__ void issue_tile(const CacheView& c, TileBlocks tb, in
 template <int D, bool kPaged, int kW, int kRows>
 __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
     const PlanHeader* __restrict__ hdr, const Item* __restrict__ items,
-    const uint16_t* q_hi,  // not __restrict__: keeps its loads ahead of the prologue fence
-    const uint16_t* __restrict__ q_lo, const uint32_t* __restrict__ mask, int mask_words,
+    const uint16_t* q,  // not __restrict__: keeps its loads ahead of the prologue fence
+    const float2* __restrict__ rope_cs, const uint32_t* __restrict__ mask, int mask_words,
     CacheView cache, const int32_t* __restrict__ table, int Hq, uint16_t* __restrict__ out,
     ttv_f16x4* __restrict__ part_o, float4* __restrict__ part_ml, int32_t* __restrict__ queue,
     int32_t* __restrict__ err) {
@@ -1033,8 +1017,8 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
             }
         };
 
-        // ---- prologue: Q hi into registers (ordinary loads); Q lo, the
-        // tile nodes' mask rows and tiles 0 and 1 into LDS (DMA); one full
+        // ---- prologue: Q and its cos / sin into registers (ordinary loads);
+        // the tile nodes' mask rows and tiles 0 and 1 into LDS (DMA); one full
         // wait covers all of them, so the compiler tracks nothing in flight
         // afterwards.  Tiles 2 .. ahead - 1 are issued after that wait and
         // stay in flight into the loop.
@@ -1055,7 +1039,12 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         int rblk[kMB];
         rblk[0] = nmb == 2 ? 2 * wave : wave;
         rblk[1] = 2 * wave + 1;
+        // Q: each lane loads the 8 head-dim entries per 32-wide chunk that
+        // its B operand holds (4 rotation pairs) with their cos and sin; they
+        // are rotated after the prologue's wait (see below).
         ttv_bf16x8 qreg[kMB][KC];
+        ttv_u32x4 qraw[kMB][KC];
+        float4 qtab[kMB][KC][2];
         int row_node[kMB];
 #pragma unroll
         for (int mb = 0; mb < kMBr; ++mb) {
@@ -1064,21 +1053,13 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
             const int rc = min(r, rows - 1);  // rows past the tile end reuse its last row
             const int node = rc / G, g = rc % G;
             row_node[mb] = ok ? node - node0 : -1;
-            const uint16_t* src = q_hi + ((int64_t)(it.s + node) * Hq + it.kvh * G + g) * D;
+            const uint16_t* src = q + ((int64_t)(it.s + node) * Hq + it.kvh * G + g) * D;
+            const float4* cs = (const float4*)(rope_cs + (int64_t)(it.s + node) * (D / 2));
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc)
-                qreg[mb][kc] = *(const ttv_bf16x8*)(src + 32 * kc + 8 * g4);
-        }
-        if (precise) {
-            // Q low parts, swizzled like K; rows past the tile's last row
-            // repeat that row (finite, never written out)
-            for (int j = wave; j < MC::kQloChunks; j += kW) {
-                const int rl = j * MC::kChunkRows + lane / P;
-                const int phys = lane % P;
-                const int r = min(it.tile * kTileR + rl, rows - 1);
-                const int node = r / G, g = r % G;
-                dma16(qlo_s + j * 1024,
-                      q_lo + ((int64_t)(it.s + node) * Hq + it.kvh * G + g) * D + 8 * swz_k(rl, phys, P));
+            for (int kc = 0; kc < KC; ++kc) {
+                qraw[mb][kc] = *(const ttv_u32x4*)(src + 32 * kc + 8 * g4);
+                qtab[mb][kc][0] = cs[(16 * kc + 4 * g4) / 2];
+                qtab[mb][kc][1] = cs[(16 * kc + 4 * g4) / 2 + 1];
             }
         }
         if (n_tree_tiles > 0) {
@@ -1103,6 +1084,32 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         // cannot be merged).
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        // Q rotated in fp32 (the table carries scale * log2(e)), now that its
+        // loads have landed (rotating at once would put their latency in front
+        // of the tile loads); the bf16 result stays in registers.  Precise
+        // items also keep the bf16 residual, in LDS swizzled like K, where
+        // only this lane reads it.
+#pragma unroll
+        for (int mb = 0; mb < kMBr; ++mb) {
+            const int rl = 16 * rblk[mb] + l16;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                ttv_u32x4 hi, lo;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float4 t4 = qtab[mb][kc][w >> 1];
+                    const float c = (w & 1) ? t4.z : t4.x, sn = (w & 1) ? t4.w : t4.y;
+                    const float x0 = ttv_bf16_lo(qraw[mb][kc][w]), x1 = ttv_bf16_hi(qraw[mb][kc][w]);
+                    const float r0 = __builtin_fmaf(x0, c, -x1 * sn);
+                    const float r1 = __builtin_fmaf(x1, c, x0 * sn);
+                    hi[w] = pack_bf16(r0, r1);
+                    lo[w] = pack_bf16(r0 - ttv_bf16_lo(hi[w]), r1 - ttv_bf16_hi(hi[w]));
+                }
+                qreg[mb][kc] = __builtin_bit_cast(ttv_bf16x8, hi);
+                if (precise && mb < nmb)
+                    *(ttv_u32x4*)(smem + (qlo_s - ring) + rl * MC::kRowBytes + 16 * swz_k(rl, 4 * kc + g4, P)) = lo;
+            }
+        }
         // Long-context items (8 stages) issue two tiles per barrier from the
         // loop, so their prologue leaves tiles 6 and 7 to the loop's first
         // barrier; precise items (4 stages) issue one tile per barrier.
@@ -1815,8 +1822,7 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
     PlanHeader* hdr = (PlanHeader*)ws;
     Item* items = (Item*)(ws + L.off_items);
     Combine* comb = (Combine*)(ws + L.off_combine);
-    uint16_t* q_hi = (uint16_t*)(ws + L.off_q);
-    uint16_t* q_lo = (uint16_t*)(ws + L.off_qlo);
+    float2* rope_cs = (float2*)(ws + L.off_rope);
     ttv_f16x4* po = (ttv_f16x4*)(ws + L.off_po);
     float4* pml = (float4*)(ws + L.off_pml);
     const double q_mult = scale * 1.4426950408889634074;  // scores come out in log2 units
@@ -1846,10 +1852,11 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
     if (!raise_lds_limit((const void*)attn_prep_kernel<D>, D == 128 ? 1u : 2u, 80 * 1024))
         return TTV_EHIP;
     hipLaunchKernelGGL(attn_prep_kernel<D>, prep_grid, dim3(kPrepThreads), prep_lds, stream,
-                       bt->node_offsets, bt->ctx_lens, bt->batch, bt->n_max, bt->total_nodes, q,
-                       k_new, v_new, positions, cv, n_heads, rope, q_mult, q_hi, q_lo, tile_m,
+                       bt->node_offsets, bt->ctx_lens, bt->batch, bt->n_max, bt->total_nodes,
+                       k_new, v_new, positions, cv, n_heads, rope, q_mult, rope_cs, tile_m,
                        target_items, (int)grid, hdr, items,
-                       comb, L.max_items, L.max_groups, L.max_partials, err);
+                       comb, L.max_items, L.max_groups, L.max_partials, (int2*)(ws + L.off_glist),
+                       (int32_t*)(ws + L.off_gpos), err);
     if (hipGetLastError() != hipSuccess) return TTV_EHIP;
     auto run_main = [&](auto rows) -> int {
         constexpr int kW = 8;
@@ -1861,7 +1868,7 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
         const unsigned bit = 4u << ((D == 128 ? 0 : 4) + (cv.paged ? 0 : 2) + (kRows == kTileM ? 0 : 1));
         if (!raise_lds_limit((const void*)kern, bit, 160 * 1024)) return TTV_EHIP;
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kW * TTV_WAVE), lds, stream, hdr, items,
-                           q_hi, q_lo, mask, mask_words, cv, cache->block_table, n_heads, out, po,
+                           q, rope_cs, mask, mask_words, cv, cache->block_table, n_heads, out, po,
                            pml, hdr->queue, err);
         if (hipGetLastError() != hipSuccess) return TTV_EHIP;
         hipLaunchKernelGGL((attn_combine_kernel<D, MC::kTile>), dim3((unsigned)(4 * cus)), dim3(kCombThreads), 0,
