@@ -1679,7 +1679,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(
     const PlanHeader* __restrict__ hdr, const Combine* __restrict__ combine, int Hq, int Hkv,
     const ttv_f16x4* __restrict__ part_o, const float4* __restrict__ part_ml,
     uint16_t* __restrict__ out) {
-    constexpr int kLanesPerRow = D / 4;                 // each lane: 4 consecutive d
+    constexpr int kLanesPerRow = D / 8;                 // each lane: 8 consecutive d (16 bytes)
     constexpr int kRowsPerPass = kCombThreads / kLanesPerRow;
     constexpr int kRowBlocks = kTileR / kRowsPerPass;
     const int n_work = hdr->n_combine * kRowBlocks;
@@ -1688,10 +1688,15 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(
 #ifdef TTV_DEBUG
     const int64_t dbg_nodes = hdr->reserved[0], dbg_partials = hdr->reserved[1];
 #endif
+    // A workgroup's units are wk = blockIdx.x + i * gridDim.x; the next
+    // unit's descriptor is loaded while this one merges.
+    Combine cb_next;
+    if (blockIdx.x < n_work) cb_next = combine[blockIdx.x / kRowBlocks];
     for (int wk = blockIdx.x; wk < n_work; wk += gridDim.x) {
-        const Combine cb = combine[wk / kRowBlocks];
+        const Combine cb = cb_next;
+        if (wk + (int)gridDim.x < n_work) cb_next = combine[(wk + gridDim.x) / kRowBlocks];
         const int r_local = (wk % kRowBlocks) * kRowsPerPass + tid / kLanesPerRow;
-        const int d = (tid % kLanesPerRow) * 4;
+        const int d = (tid % kLanesPerRow) * 8;
         const int r = cb.tile * kTileR + r_local;
         if (r >= cb.n * G) continue;
         if (!TTV_DCHECK(cb.pslot0 >= 0 && cb.pslot0 + (int64_t)(cb.nc - 1) * cb.stride < dbg_partials &&
@@ -1704,31 +1709,36 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(
         // loads repeat it (in bounds, no branch) and count zero; NB = 4 for
         // tiles of at most 4 chunks keeps those repeats few.
         float mmax = kNegBig, lsum = 0.f;
-        ttv_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        ttv_f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
         auto merge = [&](auto nb_c) __attribute__((always_inline)) {
             constexpr int NB = decltype(nb_c)::value;
             for (int c0 = 0; c0 < cb.nc; c0 += NB) {
                 float4 ml[NB];  // m, l, scale of the fp16 o / l
-                ttv_f16x4 ov[NB];
+                ttv_u32x4 ov[NB];
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     const int c = min(c0 + j, cb.nc - 1);
                     const int64_t ps = cb.pslot0 + (int64_t)c * cb.stride;
                     ml[j] = part_ml[ps * kTileR + r_local];
-                    ov[j] = part_o[((ps * kTileR + r_local) * D + d) / 4];
+                    ov[j] = *(const ttv_u32x4*)(part_o + ((ps * kTileR + r_local) * D + d) / 4);
                 }
                 float m_new = mmax;
 #pragma unroll
                 for (int j = 0; j < NB; ++j) m_new = fmaxf(m_new, ml[j].x);
                 const float a_old = __builtin_amdgcn_exp2f(mmax - m_new);
                 lsum *= a_old;
-                acc *= a_old;
+                acc0 *= a_old;
+                acc1 *= a_old;
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     const float e = __builtin_amdgcn_exp2f(ml[j].x - m_new) * ml[j].y;
                     const float a = c0 + j < cb.nc ? e : 0.f;
+                    const float w = a * ml[j].z;
                     lsum += a;
-                    acc += __builtin_convertvector(ov[j], ttv_f32x4) * (a * ml[j].z);
+                    const ttv_f16x4 h0 = __builtin_bit_cast(ttv_f16x4, ttv_u32x2{ov[j][0], ov[j][1]});
+                    const ttv_f16x4 h1 = __builtin_bit_cast(ttv_f16x4, ttv_u32x2{ov[j][2], ov[j][3]});
+                    acc0 += __builtin_convertvector(h0, ttv_f32x4) * w;
+                    acc1 += __builtin_convertvector(h1, ttv_f32x4) * w;
                 }
                 mmax = m_new;
             }
@@ -1738,10 +1748,12 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(
         const float inv = 1.0f / lsum;
         const int node = r / G, g = r % G;
         uint16_t* dst = out + ((int64_t)(cb.s + node) * Hq + cb.kvh * G + g) * D + d;
-        ttv_u32x2 w2;
-        w2[0] = ttv_pack_bf16x2(acc[0] * inv, acc[1] * inv);
-        w2[1] = ttv_pack_bf16x2(acc[2] * inv, acc[3] * inv);
-        *(ttv_u32x2*)dst = w2;
+        ttv_u32x4 w4;
+        w4[0] = ttv_pack_bf16x2(acc0[0] * inv, acc0[1] * inv);
+        w4[1] = ttv_pack_bf16x2(acc0[2] * inv, acc0[3] * inv);
+        w4[2] = ttv_pack_bf16x2(acc1[0] * inv, acc1[1] * inv);
+        w4[3] = ttv_pack_bf16x2(acc1[2] * inv, acc1[3] * inv);
+        *(ttv_u32x4*)dst = w4;
     }
 }
 
