@@ -13,8 +13,8 @@
 //
 // How, on gfx950:
 //  1. attn_prep_kernel: workgroup 0 builds the work plan on the device (no
-//     host round trip); workgroup 1 + p handles nodes 2p and 2p + 1 of the
-//     batch, one per 256-thread half.  A half computes its node's rotation
+//     host round trip); workgroup 1 + p handles nodes 4p .. 4p + 3 of the
+//     batch, one per 128-thread part.  A part computes its node's rotation
 //     angles in fp64 (reduced modulo 2 pi before sincos), stores cos and sin
 //     times scale * log2(e) as fp32 for the main kernel, rotates K in fp64,
 //     rounds it once to bf16 and writes it with V into slot ctx + i.
@@ -54,6 +54,7 @@ constexpr int kTileM = kWaves * kRowsPerWave;   // largest row tile (8 waves x 3
 constexpr int kTileMin = 128;                       // row tile of small batches (16 rows per wave)
 constexpr int kPrepWaves = 8;           // prep workgroups (plan and node rotation)
 constexpr int kPrepThreads = kPrepWaves * TTV_WAVE;
+constexpr int kPrepNodes = 4;           // tree nodes per prep workgroup (one per 128 threads)
 constexpr int kKT = 32;                 // key slots per LDS tile (= one mask word)
 constexpr int kTargetItems = 448;       // chunking aims at about this many work items (batched
                                         // serving: 448 about 4 % faster than 640, 1024 or more 15-25 % slower)
@@ -528,21 +529,22 @@ __global__ __launch_bounds__(kPrepThreads, 8) void attn_prep_kernel(
                    s_dyn + 3 * (B + 1));
         return;
     }
-    // Two nodes per workgroup, one per 256-thread half (four waves each), so
-    // a large batch runs its nodes in half as many workgroups.
-    constexpr int kHalf = kPrepThreads / 2;
-    const int half = threadIdx.x / kHalf;
-    const int tid = threadIdx.x % kHalf;
-    const int64_t node = 2 * ((int64_t)blockIdx.x - 1) + half;
-    const bool has_node = node < total_nodes;  // uniform over the half's waves
+    // Four nodes per workgroup, one per 128-thread part (two waves each), so
+    // a large batch runs its nodes in a quarter as many workgroups.
+    constexpr int kPart = kPrepThreads / kPrepNodes;
+    static_assert(kPart >= 64, "a part computes D/2 <= 64 angles");
+    const int part = threadIdx.x / kPart;
+    const int tid = threadIdx.x % kPart;
+    const int64_t node = kPrepNodes * ((int64_t)blockIdx.x - 1) + part;
+    const bool has_node = node < total_nodes;  // uniform over the part's waves
     constexpr int kVec = 8;
     const int kv_vecs = cache.hkv * D / kVec;
     // K's rotation in fp64: with fp32, x0 cos - x1 sin loses absolute
     // accuracy when the two products nearly cancel, which shows up as bf16
     // ulps of the stored K on small results.
-    __shared__ double s_cos2[2][D / 2], s_sin2[2][D / 2];
-    double* s_cos = s_cos2[half];
-    double* s_sin = s_sin2[half];
+    __shared__ double s_cos2[kPrepNodes][D / 2], s_sin2[kPrepNodes][D / 2];
+    double* s_cos = s_cos2[part];
+    double* s_sin = s_sin2[part];
     // The node's own loads do not depend on which request owns it, so they
     // are issued first; the request is then found in the staged offsets.
     ttv_u32x4 k_first = {0u, 0u, 0u, 0u}, v_first = {0u, 0u, 0u, 0u};
@@ -581,7 +583,7 @@ __global__ __launch_bounds__(kPrepThreads, 8) void attn_prep_kernel(
         if (s_off[mid] <= node) lo = mid;
         else hi = mid - 1;
     }
-    // The request is uniform over the half (a wave lies in one half); saying
+    // The request is uniform over the part (a wave lies in one part); saying
     // so keeps its values in scalar registers and lets one lane per wave
     // raise a flag.
     const int b = __builtin_amdgcn_readfirstlane(lo);
@@ -595,7 +597,7 @@ __global__ __launch_bounds__(kPrepThreads, 8) void attn_prep_kernel(
     int64_t dst_first = -1;
     if (tid < kv_vecs) dst_first = cache_row(cache, b, (tid * kVec) / D, ctx + i, D);
     // K (rotated, rounded once from fp64) and V (copied) into slot ctx + i.
-    for (int v = tid; v < kv_vecs; v += kHalf) {
+    for (int v = tid; v < kv_vecs; v += kPart) {
         const int h = (v * kVec) / D;
         const int d0 = (v * kVec) % D;
         const bool first = v == tid;
@@ -1069,17 +1071,26 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
             for (int j = wave; j * 64 < words; j += kW)
                 dma4(mask_base + j * 256, src + min(j * 64 + lane, words - 1));
         }
+        for (int j = 0; j < 2 && j < n_tiles; ++j) issue(j, blocks_of(j));
         if (kPaged) {
-            // Every table entry the item's tiles use, checked once here: the
-            // whole-tile loads of the loop only clamp a bad entry.
+            // Every table entry the item's tiles use, checked once here (after
+            // the first tiles' loads are out, four loads per thread in flight
+            // at a time): the whole-tile loads of the loop only clamp a bad
+            // entry.
             const int end_slot = n_tree_tiles > 0 ? tree_limit : it.c1;
             const int e_end = min((end_slot + 15) >> 4, cache.max_blocks);
+            const int32_t* trow = table + (int64_t)it.b * cache.max_blocks;
+            constexpr int kStride = kW * TTV_WAVE;
             bool bad = false;
-            for (int e = (it.c0 >> 4) + tid; e < e_end; e += kW * TTV_WAVE)
-                bad |= (uint32_t)table[(int64_t)it.b * cache.max_blocks + e] >= (uint32_t)cache.num_blocks;
+            for (int e = (it.c0 >> 4) + tid; e < e_end; e += 4 * kStride) {
+                int32_t v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[u] = e + u * kStride < e_end ? trow[e + u * kStride] : 0;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) bad |= (uint32_t)v[u] >= (uint32_t)cache.num_blocks;
+            }
             if (bad) atomicOr(err + it.b, TTV_ERR_BLOCK_TABLE);
         }
-        for (int j = 0; j < 2 && j < n_tiles; ++j) issue(j, blocks_of(j));
         // A full wait and a fenced barrier (not the loop's raw one, so the two
         // cannot be merged).
         __builtin_amdgcn_s_waitcnt(0);
@@ -1859,7 +1870,7 @@ int launch_attention(const ttv_batch* bt, const uint16_t* q, const uint16_t* k_n
     if (grid > L.max_items) grid = ((L.max_items + kNumXcd - 1) / kNumXcd) * kNumXcd;
     grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
     if (grid > kMaxGrid) grid = kMaxGrid;
-    dim3 prep_grid((unsigned)(1 + (bt->total_nodes + 1) / 2));  // plan + two nodes per workgroup
+    dim3 prep_grid((unsigned)(1 + (bt->total_nodes + kPrepNodes - 1) / kPrepNodes));  // plan + nodes
     const size_t prep_lds = (size_t)4 * (bt->batch + 1) * sizeof(int32_t);
     if (!raise_lds_limit((const void*)attn_prep_kernel<D>, D == 128 ? 1u : 2u, 80 * 1024))
         return TTV_EHIP;
