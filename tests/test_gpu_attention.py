@@ -57,6 +57,10 @@ SCALED = [
     # in pairs on three waves, and more items than workgroups go through the
     # per-XCD work queues
     (4, dict(batch=8, ctx=(4000, 4200), vocab=64)),
+    # 12-node trees, 5 query heads per KV head: one 60-row tile per request
+    # and KV head (four single-block waves), single-chunk contexts next to
+    # ones split into two chunks
+    (4, dict(batch=64, ctx=(300, 600), vocab=64, tree=("medusa", (3, 3)))),
 ]
 
 
@@ -71,6 +75,25 @@ def test_attention_scaled(case, seed):
     d, out, err = run_attention(wl)
     assert (err == 0).all(), err
     for b in range(wl.batch):
+        sl = wl.request_nodes(b)
+        check_attention_request(wl, b, out[sl])
+        n = sl.stop - sl.start
+        kb = region_bits(d, wl, b, int(wl.ctx_lens[b]), n, "k")
+        vb = region_bits(d, wl, b, int(wl.ctx_lens[b]), n, "v")
+        check_tentative(wl, b, kb, vb)
+
+
+def test_attention_small_tiles_long_context():
+    """80-row tiles (16-node trees, 5 query heads per KV head: five row
+    blocks, run in pairs on three waves) over single-chunk contexts of at
+    least 4096 slots; every node of three requests against the oracle."""
+    require_gpu()
+    wl = synth.make_workload(4, 0, batch=56, ctx=(4096, 4200), vocab=64, tree=("medusa", (4, 3)))
+    say(f"tree_attention_verify 80-row tiles T={wl.total_nodes} ctx={int(wl.ctx_lens.min())}.."
+        f"{int(wl.ctx_lens.max())}")
+    d, out, err = run_attention(wl)
+    assert (err == 0).all(), err
+    for b in (0, wl.batch // 2, wl.batch - 1):
         sl = wl.request_nodes(b)
         check_attention_request(wl, b, out[sl])
         n = sl.stop - sl.start
