@@ -1589,10 +1589,17 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
             float l_run[kMB];
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) l_run[mb] = lacc[mb][0];
-            // Lane holds O^T[d = 16db + 4g4 + r][row 16mb + l16].
+            // Lane holds O^T[d = 16db + 4g4 + r][row 16mb + l16].  The lane's
+            // indices are taken again from a lane id the compiler cannot move
+            // above the tile loop: otherwise it computes the output addresses
+            // before the loop, spills them, and each item's end waits on their
+            // reload from scratch (about 2-3 us of a full wait per item).
+            int lane_e;
+            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+            const int l16e = lane_e & 15, g4e = lane_e >> 4;
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) {
-                const int r_local = 16 * rblk[mb] + l16;
+                const int r_local = 16 * rblk[mb] + l16e;
                 const int r = it.tile * kTileR + r_local;
                 if (r >= rows) continue;
                 if (it.pslot < 0) {
@@ -1605,7 +1612,7 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                         ttv_u32x2 w;
                         w[0] = pack_bf16(o[db][mb][0] * inv_l, o[db][mb][1] * inv_l);
                         w[1] = pack_bf16(o[db][mb][2] * inv_l, o[db][mb][3] * inv_l);
-                        *(ttv_u32x2*)(dst + 16 * db + 4 * g4) = w;
+                        *(ttv_u32x2*)(dst + 16 * db + 4 * g4e) = w;
                     }
                 } else {
                     // Partial: o / l scaled by a power of two 2^-e that brings the
@@ -1623,8 +1630,8 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                     ttv_f16x4* dst = part_o + (((int64_t)it.pslot * kTileR + r_local) * D) / 4;
 #pragma unroll
                     for (int db = 0; db < DB; ++db)
-                        dst[4 * db + g4] = __builtin_convertvector(o[db][mb] * sc, ttv_f16x4);
-                    if (g4 == 0)
+                        dst[4 * db + g4e] = __builtin_convertvector(o[db][mb] * sc, ttv_f16x4);
+                    if (g4e == 0)
                         part_ml[(int64_t)it.pslot * kTileR + r_local] =
                             make_float4(m_run[mb], l_run[mb], __builtin_amdgcn_ldexpf(1.0f, e), 0.f);
                 }
