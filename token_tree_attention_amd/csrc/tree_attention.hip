@@ -708,6 +708,19 @@ __device__ __forceinline__ void raw_barrier() {
 typedef short ttv_i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) ttv_i16x4 lds_i16x4;
 
+// The lane's id from an instruction the compiler may neither move nor reuse.
+// The tile loads' per-lane addresses and the epilogue's output indices are
+// derived from it where they are used: derived from the ordinary lane index,
+// the compiler computed them once, held them across the tile loop and spilled
+// them, and each reload's memory wait (which cannot count the loads issued
+// through asm) also waited for every tile load in flight.  (Recomputing the
+// rows' tree-mask index this way instead made the tile loop slower.)
+__device__ __forceinline__ int fresh_lane() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 // Byte address of an LDS location, as the ds_* instructions take it.
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
@@ -800,7 +813,7 @@ __device__ __forceinline__ TileBlocks tile_blocks(const CacheView& c, const int3
 // Wave w loads chunks w, w + kW, ... (kChunkRows rows each) of K and of V.
 template <int D, int kW, bool kPaged>
 __device__ __forceinline__ void issue_tile(const CacheView& c, TileBlocks tb, int b, int kvh, int slot0,
-                                           int valid, uint32_t stage, int wave, int lane, int32_t* err) {
+                                           int valid, uint32_t stage, int wave, int32_t* err) {
     using MC = MainCfg<D, kW>;
     constexpr int P = MC::kPieces;
     if (wave >= MC::kIssueWaves) return;
@@ -808,6 +821,7 @@ __device__ __forceinline__ void issue_tile(const CacheView& c, TileBlocks tb, in
     for (int j = 0; j < MC::kCpw; ++j) {
         const int ch = wave + j * MC::kIssueWaves;
         const int r_first = min(ch * MC::kChunkRows, valid - 1);
+        const int lane = fresh_lane();
         int bf = tb.first[j], bl = tb.last[j];
         if (kPaged && (bf < 0 || bf >= c.num_blocks || bl < 0 || bl >= c.num_blocks)) {
             if (lane == 0) atomicOr(err + b, TTV_ERR_BLOCK_TABLE);
@@ -962,7 +976,7 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
         auto issue = [&](int tau, TileBlocks tb) __attribute__((always_inline)) {
             const int slot0 = tile_slot0(tau);
             issue_tile<D, kW, kPaged>(cache, tb, it.b, it.kvh, slot0, tile_valid(tau, slot0),
-                                  ring + (tau & smask) * MC::kStageBytes, wave, lane, err);
+                                  ring + (tau & smask) * MC::kStageBytes, wave, err);
         };
         TileBlocks next_blocks{{0, 0}, {0, 0}};  // blocks of the next tile to issue
         // Paged, two whole context tiles t0 and t0 + 1 (t0 even): their four
@@ -1589,13 +1603,10 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
             float l_run[kMB];
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) l_run[mb] = lacc[mb][0];
-            // Lane holds O^T[d = 16db + 4g4 + r][row 16mb + l16].  The lane's
-            // indices are taken again from a lane id the compiler cannot move
-            // above the tile loop: otherwise it computes the output addresses
-            // before the loop, spills them, and each item's end waits on their
-            // reload from scratch (about 2-3 us of a full wait per item).
-            int lane_e;
-            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+            // Lane holds O^T[d = 16db + 4g4 + r][row 16mb + l16]; the lane's
+            // indices come from fresh_lane (the output addresses were held
+            // across the loop, spilled, and reloaded behind a full wait).
+            const int lane_e = fresh_lane();
             const int l16e = lane_e & 15, g4e = lane_e >> 4;
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) {
