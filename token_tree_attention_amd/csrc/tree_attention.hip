@@ -1608,6 +1608,20 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
             // across the loop, spilled, and reloaded behind a full wait).
             const int lane_e = fresh_lane();
             const int l16e = lane_e & 15, g4e = lane_e >> 4;
+            // 16-byte stores: lanes g4 and g4 ^ 1 (rows of 16 lanes, swapped by
+            // v_permlane16_swap) trade halves of their 8-byte pieces of head-dim
+            // blocks 2k (X) and 2k + 1 (Y), so an even lane stores X of both
+            // (columns 32k + 4g4 .. + 7) and an odd lane Y of both (columns
+            // 32k + 16 + 4(g4 - 1) .. + 7): the four lanes of a row cover 64
+            // contiguous bytes per store.  Both lanes of a pair hold the same
+            // row, so they skip rows together.
+            const bool odd = g4e & 1;
+            auto pair16 = [&](ttv_u32x2 X, ttv_u32x2 Y) __attribute__((always_inline)) {
+                const auto r0 = __builtin_amdgcn_permlane16_swap(X[0], Y[0], false, false);
+                const auto r1 = __builtin_amdgcn_permlane16_swap(X[1], Y[1], false, false);
+                return odd ? ttv_u32x4{r0[0], r1[0], Y[0], Y[1]} : ttv_u32x4{X[0], X[1], r0[1], r1[1]};
+            };
+            const int col16 = odd ? 16 + 4 * (g4e - 1) : 4 * g4e;  // + 32k
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb) {
                 const int r_local = 16 * rblk[mb] + l16e;
@@ -1618,13 +1632,15 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                     if (!TTV_DCHECK((int64_t)it.s + node < dbg_nodes, TTV_SITE_MAIN_OUT)) continue;
                     uint16_t* dst = out + ((int64_t)(it.s + node) * Hq + it.kvh * G + g) * D;
                     const float inv_l = 1.0f / l_run[mb];
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
+                    auto piece = [&](int db) __attribute__((always_inline)) {
                         ttv_u32x2 w;
                         w[0] = pack_bf16(o[db][mb][0] * inv_l, o[db][mb][1] * inv_l);
                         w[1] = pack_bf16(o[db][mb][2] * inv_l, o[db][mb][3] * inv_l);
-                        *(ttv_u32x2*)(dst + 16 * db + 4 * g4e) = w;
-                    }
+                        return w;
+                    };
+#pragma unroll
+                    for (int k = 0; k < DB / 2; ++k)
+                        *(ttv_u32x4*)(dst + 32 * k + col16) = pair16(piece(2 * k), piece(2 * k + 1));
                 } else {
                     // Partial: o / l scaled by a power of two 2^-e that brings the
                     // row's largest |o / l| into [0.5, 1), as fp16 (11-bit
@@ -1639,9 +1655,12 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
                     const float sc = __builtin_amdgcn_ldexpf(inv_l, -e);
                     if (!TTV_DCHECK(it.pslot < dbg_partials, TTV_SITE_MAIN_OUT)) continue;
                     ttv_f16x4* dst = part_o + (((int64_t)it.pslot * kTileR + r_local) * D) / 4;
+                    auto piece = [&](int db) __attribute__((always_inline)) {
+                        return __builtin_bit_cast(ttv_u32x2, __builtin_convertvector(o[db][mb] * sc, ttv_f16x4));
+                    };
 #pragma unroll
-                    for (int db = 0; db < DB; ++db)
-                        dst[4 * db + g4e] = __builtin_convertvector(o[db][mb] * sc, ttv_f16x4);
+                    for (int k = 0; k < DB / 2; ++k)
+                        *(ttv_u32x4*)(dst + (32 * k + col16) / 4) = pair16(piece(2 * k), piece(2 * k + 1));
                     if (g4e == 0)
                         part_ml[(int64_t)it.pslot * kTileR + r_local] =
                             make_float4(m_run[mb], l_run[mb], __builtin_amdgcn_ldexpf(1.0f, e), 0.f);
