@@ -888,9 +888,9 @@ __global__ __launch_bounds__(kW * TTV_WAVE) void attn_main_kernel(
     // cost first).  Its workgroups take i = wg / 8 first, then claim the
     // next i from the XCD's queue cursor as they finish, so a workgroup that
     // drew short items takes more of them.  The claim for the next item is
-    // made when an item starts; its answer lands during the item.  Once its
-    // XCD's list is used up, an idle workgroup takes items left on the other
-    // XCDs (steal_item).
+    // made kClaimLead tiles before an item ends; its answer lands during those
+    // tiles.  Once its XCD's list is used up, an idle workgroup takes items
+    // left on the other XCDs (steal_item).
     // Otherwise one item each on as many workgroups as items, a multiple of
     // 8, consecutive items on one XCD: workgroup wg holds the item at slot wg.
     const bool dyn = n_items > grid;
