@@ -139,6 +139,10 @@ __global__ __launch_bounds__(kThreads) void stochastic_walk_kernel(
     }
     double* buf = work + (int64_t)b * vocab;
     const int64_t row0 = (int64_t)s + b;  // the request's root row
+    // (x - max) / T as one multiply by 1 / T (the same value when T is a
+    // power of two; otherwise within an ulp): an fp64 division per entry
+    // cost about as much as the exponential
+    const double inv_t = 1.0 / temperature;
 
     // Visit a row: buf = exp((x - max) / T), den = their sum.
     double xb[kBatch], bb[kBatch];
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void stochastic_walk_kernel(
         double sum = 0.0;
         vocab_pass(vocab, [&](int64_t v, int j) { xb[j] = logit_at<kBf16>(logits, row, vocab, v); },
                    [&](int64_t v, int j) {
-                       const double e = exp((xb[j] - m) / temperature);
+                       const double e = exp((xb[j] - m) * inv_t);
                        buf[v] = e;
                        sum += e;
                    });
@@ -336,6 +340,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
     double* alt_buf = cur_buf + vocab;
     const int64_t n_chunks = vocab / kVec;
     const int64_t row0 = (int64_t)s + b;  // the request's root row
+    const double inv_t = 1.0 / temperature;  // see stochastic_walk_kernel
 
     // Visit a row: cur = exp((x - max) / T), den = their sum.
     auto visit = [&](int64_t row) -> double {
@@ -354,7 +359,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
                            double e[kVec];
 #pragma unroll
                            for (int k = 0; k < kVec; ++k) {
-                               e[k] = exp(((double)xs[j][k] - m) / temperature);
+                               e[k] = exp(((double)xs[j][k] - m) * inv_t);
                                sum += e[k];
                            }
                            store8_f64(cur_buf + c * kVec, e);
