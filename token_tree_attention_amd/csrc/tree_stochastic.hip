@@ -23,9 +23,10 @@
 // reductions, each thread loading four entries before using any.  The
 // current target side is kept as r_v = buf[v] / den: the row's exp values and
 // their sum right after a visit, the unnormalised residual and its sum after
-// a rejection (buf in the caller's workspace, fp64 [B, vocab]); r_v is formed
-// by that one division wherever it is used, as in p = e / sum(e) and
-// r = res / sum(res).
+// a rejection (buf in the caller's workspace, fp64 [B, vocab]).  The accept
+// test forms r_x by that division; the passes over the whole vocab multiply
+// by 1 / den instead (within an ulp of the quotient: a float64 division per
+// entry cost about as much as the rest of the pass).
 
 #include "ttv_device.h"
 
@@ -190,11 +191,12 @@ __global__ __launch_bounds__(kThreads) void stochastic_walk_kernel(
                 bb[jj] = buf[v];
                 fb[jj] = q[v];
             };
-            vocab_pass(vocab, load_bq, [&](int64_t, int jj) { z += fmax(bb[jj] / den - (double)fb[jj], 0.0); });
+            const double inv_den = 1.0 / den;
+            vocab_pass(vocab, load_bq, [&](int64_t, int jj) { z += fmax(bb[jj] * inv_den - (double)fb[jj], 0.0); });
             z = block_reduce<false>(z, s_red);
             if (z > 0.0) {
                 vocab_pass(vocab, load_bq,
-                           [&](int64_t v, int jj) { buf[v] = fmax(bb[jj] / den - (double)fb[jj], 0.0); });
+                           [&](int64_t v, int jj) { buf[v] = fmax(bb[jj] * inv_den - (double)fb[jj], 0.0); });
                 den = z;
                 __syncthreads();
             }
@@ -204,6 +206,7 @@ __global__ __launch_bounds__(kThreads) void stochastic_walk_kernel(
         if (accepted < 0) {
             // correction / bonus: Gumbel-max sample of the current side
             const float* g = gumbel + row * vocab;
+            const double inv_den = 1.0 / den;
             double best = -INFINITY;
             int best_i = 0x7FFFFFFF;
             vocab_pass(vocab,
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void stochastic_walk_kernel(
                            fb[jj] = g[v];
                        },
                        [&](int64_t v, int jj) {
-                           const double r = bb[jj] / den;
+                           const double r = bb[jj] * inv_den;
                            if (r > 0.0) {
                                const double sc = log(r) + (double)fb[jj];
                                if (sc > best) {  // v increases per thread: the first maximum is the lowest index
@@ -393,6 +396,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
             double bb[NB][kVec];
             float fq[NB][kVec];
             double z = 0.0;
+            const double inv_den = 1.0 / den;
             chunk_pass<NB>(n_chunks,
                            [&](int64_t c, int jj) {
                                load8_f64(cur_buf + c * kVec, bb[jj]);
@@ -402,7 +406,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
                                double t[kVec];
 #pragma unroll
                                for (int k = 0; k < kVec; ++k) {
-                                   t[k] = fmax(bb[jj][k] / den - (double)fq[jj][k], 0.0);
+                                   t[k] = fmax(bb[jj][k] * inv_den - (double)fq[jj][k], 0.0);
                                    z += t[k];
                                }
                                store8_f64(alt_buf + c * kVec, t);
@@ -423,6 +427,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
             constexpr int NB = 2;
             double bb[NB][kVec];
             float fg[NB][kVec];
+            const double inv_den = 1.0 / den;
             double best = -INFINITY;
             int best_i = 0x7FFFFFFF;
             chunk_pass<NB>(n_chunks,
@@ -433,7 +438,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
                            [&](int64_t c, int jj) {
 #pragma unroll
                                for (int k = 0; k < kVec; ++k) {
-                                   const double r = bb[jj][k] / den;
+                                   const double r = bb[jj][k] * inv_den;
                                    if (r > 0.0) {
                                        const double sc = log(r) + (double)fg[jj][k];
                                        if (sc > best) {  // entries increase per thread: the first maximum is the lowest index
