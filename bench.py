@@ -578,7 +578,7 @@ def measure_next(args, dev):
     # visited rows: a_b + 1 per request (logits and draft row each), the final row's noise, the uniforms
     hbm("tree_stochastic_accept", us, int(((a + 1) * V * (esz + 4)).sum() + B * V * 4 + T * 4),
         workload="batched", temperature=1.0, draft_boost=20.0, mean_accept_len=float(a.mean()),
-        bound_note="one workgroup per request walks its visited rows: latency of dependent full-vocab passes")
+        bound_note="a group of workgroups per request walks its visited rows: latency of dependent full-vocab passes")
     del g, q, u, ws, sws, d
 
     # -- DDTree construction

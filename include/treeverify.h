@@ -91,6 +91,9 @@ extern "C" {
 #define TTV_ERR_ACCEPT          16  /* the walk would exceed max_accept, or commit got a bad path */
 #define TTV_ERR_BAD_LENGTH      32  /* ctx_lens[b] < 0 */
 #define TTV_ERR_BAD_MASK        64  /* tree_pack_mask: a dense row the attention cannot run */
+#define TTV_ERR_SYNC            128 /* tree_stochastic_accept: a request's workgroups did not
+                                       all run at once (another stream held the device); its
+                                       outputs are undefined */
 
 /* Limits. */
 #define TTV_MAX_TREE_NODES 1024     /* N_b <= 1024, so mask rows need <= 32 words */
@@ -430,7 +433,9 @@ TTV_API int tree_sample_accept(const ttv_batch* bt, const void* logits, int32_t 
                                int32_t* row_choice, void* workspace, size_t workspace_bytes,
                                int32_t* err, hipStream_t stream);
 
-/* Workspace bytes tree_stochastic_accept needs (host call): fp64 [B, 2, vocab]. */
+/* Workspace bytes tree_stochastic_accept needs (host call): fp64 [B, 2, vocab],
+ * then 512 bytes per request for the reductions across the workgroups that
+ * share a request (padded to 256 bytes between the two). */
 TTV_API size_t tree_stochastic_accept_workspace_bytes(const ttv_batch* bt, int64_t vocab);
 
 /*
@@ -461,7 +466,11 @@ TTV_API size_t tree_stochastic_accept_workspace_bytes(const ttv_batch* bt, int64
  *      last token is the correction / bonus; -1 for a flagged request)
  *      workspace     >= tree_stochastic_accept_workspace_bytes(bt, vocab)
  *      err           OR-ed: TTV_ERR_ACCEPT if an acceptance would exceed
- *                    max_accept; TTV_ERR_TOO_MANY_NODES for bad offsets
+ *                    max_accept; TTV_ERR_TOO_MANY_NODES for bad offsets;
+ *                    TTV_ERR_SYNC if the workgroups that share a request
+ *                    (vocab a multiple of 8: up to 16 per request, as many as
+ *                    the device holds at once) waited over ~0.3 s for one
+ *                    another, which work on another stream can cause
  */
 TTV_API int tree_stochastic_accept(const ttv_batch* bt, const void* logits, int32_t logits_dtype,
                                    int64_t vocab, float temperature, const float* draft_probs,

@@ -122,7 +122,10 @@ STOCH_CASES = [
     (4, dict(vocab=2000, ctx=(4, 9), batch=6), 1.0, 5.0),
     (4, dict(vocab=2000, ctx=(4, 9), batch=6), 0.7, 200.0),   # mostly rejections: residual passes
     (3, dict(vocab=4096, ctx=(4, 4), ddtree_budget=300), 1.0, 20.0),
-    (1, dict(ctx=(4, 4)), 0.9, 20.0),                          # full 128256 vocab
+    (1, dict(ctx=(4, 4)), 0.9, 20.0),                          # full 128256 vocab: 16 workgroups walk it
+    # vocab 32000: 15 workgroups per request, many residual passes each
+    (2, dict(vocab=32000, ctx=(4, 9), batch=12), 0.7, 200.0),
+    (2, dict(vocab=32000, ctx=(4, 9), batch=20), 1.0, 20.0),   # 20 requests: the grid padded to 24
 ]
 
 

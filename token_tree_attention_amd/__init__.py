@@ -29,7 +29,7 @@ __all__ = [
     "tree_greedy_accept_workspace_bytes", "tree_greedy_accept", "tree_greedy_accept_noalloc",
     "tree_sample_accept", "tree_stochastic_accept_workspace_bytes", "tree_stochastic_accept",
     "tree_kv_commit", "tree_expand_mask", "tree_pack_mask", "tree_ddtree_workspace_bytes",
-    "tree_ddtree_build", "tree_merge_sequences", "tree_eagle_grow", "MASK_QLEN_ONLY", "MASK_FULL", "ERR_BAD_MASK",
+    "tree_ddtree_build", "tree_merge_sequences", "tree_eagle_grow", "MASK_QLEN_ONLY", "MASK_FULL", "ERR_BAD_MASK", "ERR_SYNC",
     "TTV_OK", "TTV_EINVAL", "TTV_EHIP", "TTV_ENOSPC", "ERR_BAD_PARENT", "ERR_TOO_MANY_NODES",
     "ERR_CAPACITY", "ERR_BLOCK_TABLE", "ERR_ACCEPT", "ERR_BAD_LENGTH", "MAX_TREE_NODES",
     "BLOCK_SIZE", "EXPORTED_SYMBOLS",
@@ -37,7 +37,7 @@ __all__ = [
 
 TTV_OK, TTV_EINVAL, TTV_EHIP, TTV_ENOSPC = 0, -1, -2, -3
 ERR_BAD_PARENT, ERR_TOO_MANY_NODES, ERR_CAPACITY = 1, 2, 4
-ERR_BLOCK_TABLE, ERR_ACCEPT, ERR_BAD_LENGTH, ERR_BAD_MASK = 8, 16, 32, 64
+ERR_BLOCK_TABLE, ERR_ACCEPT, ERR_BAD_LENGTH, ERR_BAD_MASK, ERR_SYNC = 8, 16, 32, 64, 128
 MASK_QLEN_ONLY, MASK_FULL = 0, 1
 MAX_TREE_NODES = 1024
 BLOCK_SIZE = 16

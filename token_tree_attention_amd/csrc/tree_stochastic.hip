@@ -28,6 +28,9 @@
 // by 1 / den instead (within an ulp of the quotient: a float64 division per
 // entry cost about as much as the rest of the pass).
 
+#include <algorithm>
+#include <atomic>
+
 #include "ttv_device.h"
 
 namespace {
@@ -61,7 +64,7 @@ __device__ double block_reduce(double v, double* s_red) {
 
 // (score, index) maximum, lowest index on equal scores.
 template <int kNW = kWaves>
-__device__ int block_argmax(double v, int idx, double* s_val, int* s_idx) {
+__device__ int block_argmax(double v, int idx, double* s_val, int* s_idx, double* best = nullptr) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         const double ov = shfl_xor_f64(v, off);
@@ -85,6 +88,7 @@ __device__ int block_argmax(double v, int idx, double* s_val, int* s_idx) {
             bv = s_val[w];
             bi = s_idx[w];
         }
+    if (best) *best = bv;
     return bi;
 }
 
@@ -257,7 +261,11 @@ __global__ __launch_bounds__(kThreads) void stochastic_walk_kernel(
 // one entry per load; a rejection writes the residual into the request's
 // second buffer in the same pass that sums it (the first buffer keeps the
 // current side when nothing remains above q).  Entries are visited in
-// increasing order per thread, as above.
+// increasing order per thread, as above.  When the device holds them all at
+// once, a request is walked by a group of up to 16 such workgroups, each over
+// its own slice of the vocab (below): the walk is a chain of dependent
+// full-vocab passes, and one workgroup per request left seven in eight CUs
+// idle on a batch of 32.
 constexpr int kVec = 8;
 constexpr int kVThreads = 512;  // 256 registers per thread: four chunks of every pass in flight
 constexpr int kVWaves = kVThreads / TTV_WAVE;
@@ -295,23 +303,85 @@ __device__ __forceinline__ void store8_f64(double* p, const double (&x)[kVec]) {
     for (int k = 0; k < 4; ++k) *(double2*)(p + 2 * k) = make_double2(x[2 * k], x[2 * k + 1]);
 }
 
-// Chunks c = base + j * kVThreads + tid, j < NB, of every batch (c < n_chunks):
-// load(c, j) for the whole batch, then use(c, j).
+// Chunks c = base + j * kVThreads + tid, j < NB, of every batch of the slice
+// [c_lo, c_hi): load(c, j) for the whole batch, then use(c, j).
 template <int NB, typename Load, typename Use>
-__device__ __forceinline__ void chunk_pass(int64_t n_chunks, Load&& load, Use&& use) {
+__device__ __forceinline__ void chunk_pass(int64_t c_lo, int64_t c_hi, Load&& load, Use&& use) {
     const int tid = threadIdx.x;
-    for (int64_t base = 0; base < n_chunks; base += (int64_t)NB * kVThreads) {
+    for (int64_t base = c_lo; base < c_hi; base += (int64_t)NB * kVThreads) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             const int64_t c = base + (int64_t)j * kVThreads + tid;
-            if (c < n_chunks) load(c, j);
+            if (c < c_hi) load(c, j);
         }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             const int64_t c = base + (int64_t)j * kVThreads + tid;
-            if (c < n_chunks) use(c, j);
+            if (c < c_hi) use(c, j);
         }
     }
+}
+
+// A request may be walked by a group of P workgroups, each over its own slice
+// of the vocab's chunks.  Every reduction is then taken over the workgroup and
+// its result put in the request's slot for that workgroup; after all P have
+// arrived each reads the P results and combines them in slot order, so the
+// whole group holds the same value and takes the same decisions.  The
+// workspace holds one record per request after the two buffers.
+constexpr int kMaxGroup = 16;
+constexpr int64_t kGroupRecord = 512;
+struct GroupRecord {
+    int32_t arrivals;  // zeroed before the walk; +1 per workgroup per reduction
+    int32_t pad[31];
+    double val[2][kMaxGroup];   // per reduction parity, one result per workgroup
+    int32_t idx[2][kMaxGroup];  // the argmax's index beside its value
+};
+static_assert(sizeof(GroupRecord) <= kGroupRecord, "group record");
+// A wait for the rest of the group gives up after this many ticks of the
+// 100 MHz real-time clock (about 0.3 s): it then flags TTV_ERR_SYNC and
+// waits no more, so every workgroup still ends.
+constexpr long long kSpinTicks = 1ll << 25;
+
+__global__ void group_clear_kernel(unsigned char* __restrict__ groups, int32_t n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) ((GroupRecord*)(groups + i * kGroupRecord))->arrivals = 0;
+}
+
+__device__ __forceinline__ double load_agent_f64(const double* p) {
+    return __longlong_as_double(
+        (long long)__hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Every thread's stores before the call are visible to the whole group after
+// it: each wave waits for its stores, then thread 0 alone releases (one L2
+// write-back for the workgroup), arrives, polls the count with relaxed loads
+// until all P * epoch arrivals are in, and acquires (one L2 invalidate); the
+// workgroup barrier passes that on to the other waves.  Fences on every
+// thread, or an acquiring poll, cost one L2 write-back or invalidate per wave
+// or per poll and made the walk three to four times slower.  Returns true
+// once a wait has timed out (late stays true and later calls do not wait).
+__device__ __forceinline__ bool group_wait(int32_t* arrivals, int target, bool late, int* s_flag) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have reached its L2
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(arrivals, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int f = late;
+        if (!late) {
+            const long long t0 = wall_clock64();
+            while (__hip_atomic_load(arrivals, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+                if (wall_clock64() - t0 > kSpinTicks) {
+                    f = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        *s_flag = f;
+    }
+    __syncthreads();
+    return *s_flag != 0;
 }
 
 template <bool kBf16>
@@ -322,17 +392,28 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
     const float* __restrict__ gumbel, const int32_t* __restrict__ tokens,
     const int32_t* __restrict__ next_token, const int32_t* __restrict__ next_sibling,
     int32_t max_accept, int32_t* __restrict__ accept_len, int32_t* __restrict__ accepted_nodes,
-    int32_t* __restrict__ out_tokens, double* __restrict__ work, int32_t* __restrict__ err) {
+    int32_t* __restrict__ out_tokens, double* __restrict__ work, int32_t* __restrict__ err,
+    int32_t batch, int32_t group, unsigned char* __restrict__ groups) {
     __shared__ int32_t s_path[TTV_MAX_TREE_NODES + 1];
     __shared__ double s_red[kVWaves];
     __shared__ int32_t s_ired[kVWaves];
+    __shared__ int s_flag;
 
-    const int b = blockIdx.x;
+    // Workgroup w serves request b as member p of its group.  With groups,
+    // the members of request b are w = (b / 8) * 8P + 8p + b % 8: all on the
+    // XCD that w % 8 names, the grid padded to a multiple of 8 requests.
+    int b = blockIdx.x, p = 0;
+    if (group > 1) {
+        const int w8 = blockIdx.x / 8;
+        p = w8 % group;
+        b = (w8 / group) * 8 + blockIdx.x % 8;
+        if (b >= batch) return;  // padding: uniform over the workgroup
+    }
     const int tid = threadIdx.x;
     const int s = node_offsets[b];
     const int n = node_offsets[b + 1] - s;
-    if (s < 0 || n < 0 || n > n_max || (int64_t)s + n > total_nodes) {  // uniform
-        if (tid == 0) {
+    if (s < 0 || n < 0 || n > n_max || (int64_t)s + n > total_nodes) {  // uniform over the group
+        if (tid == 0 && p == 0) {
             accept_len[b] = 0;
             atomicOr(err + b, TTV_ERR_TOO_MANY_NODES);
         }
@@ -342,22 +423,41 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
     double* cur_buf = work + (int64_t)(2 * b) * vocab;
     double* alt_buf = cur_buf + vocab;
     const int64_t n_chunks = vocab / kVec;
+    const int64_t c_lo = n_chunks * p / group, c_hi = n_chunks * (p + 1) / group;  // this member's slice
     const int64_t row0 = (int64_t)s + b;  // the request's root row
     const double inv_t = 1.0 / temperature;  // see stochastic_walk_kernel
+
+    GroupRecord* const grec = group > 1 ? (GroupRecord*)(groups + b * kGroupRecord) : nullptr;
+    int epoch = 0;
+    bool late = false;
+    // Sum or maximum over the request: the workgroup's, then the group's.
+    auto reduce = [&](double v, bool is_max) -> double {
+        double r = is_max ? block_reduce<true, kVWaves>(v, s_red) : block_reduce<false, kVWaves>(v, s_red);
+        if (group == 1) return r;
+        const int par = epoch & 1;
+        if (tid == 0) grec->val[par][p] = r;
+        late = group_wait(&grec->arrivals, group * ++epoch, late, &s_flag);
+        r = load_agent_f64(&grec->val[par][0]);
+        for (int k = 1; k < group; ++k) {
+            const double o = load_agent_f64(&grec->val[par][k]);
+            r = is_max ? fmax(r, o) : r + o;
+        }
+        return r;
+    };
 
     // Visit a row: cur = exp((x - max) / T), den = their sum.
     auto visit = [&](int64_t row) -> double {
         constexpr int NB = 4;
         float xs[NB][kVec];
         float mf = -INFINITY;  // the logits are floats, so their maximum is exact
-        chunk_pass<NB>(n_chunks, [&](int64_t c, int j) { load8_logits(logits, kBf16, row * vocab + c * kVec, xs[j]); },
+        chunk_pass<NB>(c_lo, c_hi, [&](int64_t c, int j) { load8_logits(logits, kBf16, row * vocab + c * kVec, xs[j]); },
                        [&](int64_t, int j) {
 #pragma unroll
                            for (int k = 0; k < kVec; ++k) mf = fmaxf(mf, xs[j][k]);
                        });
-        const double m = block_reduce<true, kVWaves>((double)mf, s_red);
+        const double m = reduce((double)mf, true);
         double sum = 0.0;
-        chunk_pass<NB>(n_chunks, [&](int64_t c, int j) { load8_logits(logits, kBf16, row * vocab + c * kVec, xs[j]); },
+        chunk_pass<NB>(c_lo, c_hi, [&](int64_t c, int j) { load8_logits(logits, kBf16, row * vocab + c * kVec, xs[j]); },
                        [&](int64_t c, int j) {
                            double e[kVec];
 #pragma unroll
@@ -368,7 +468,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
                            store8_f64(cur_buf + c * kVec, e);
                        });
         __syncthreads();  // cur written before any thread reads another's entry
-        return block_reduce<false, kVWaves>(sum, s_red);
+        return reduce(sum, false);  // with a group, its wait publishes every member's slice
     };
 
     int a = 0, flags = 0, final_token = -1;
@@ -397,7 +497,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
             float fq[NB][kVec];
             double z = 0.0;
             const double inv_den = 1.0 / den;
-            chunk_pass<NB>(n_chunks,
+            chunk_pass<NB>(c_lo, c_hi,
                            [&](int64_t c, int jj) {
                                load8_f64(cur_buf + c * kVec, bb[jj]);
                                load8_f32(q + c * kVec, fq[jj]);
@@ -411,7 +511,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
                                }
                                store8_f64(alt_buf + c * kVec, t);
                            });
-            z = block_reduce<false, kVWaves>(z, s_red);  // its barriers also publish the residual
+            z = reduce(z, false);  // its barriers (and the group's wait) also publish the residual
             if (z > 0.0) {
                 double* const t = cur_buf;
                 cur_buf = alt_buf;
@@ -430,7 +530,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
             const double inv_den = 1.0 / den;
             double best = -INFINITY;
             int best_i = 0x7FFFFFFF;
-            chunk_pass<NB>(n_chunks,
+            chunk_pass<NB>(c_lo, c_hi,
                            [&](int64_t c, int jj) {
                                load8_f64(cur_buf + c * kVec, bb[jj]);
                                load8_f32(g + c * kVec, fg[jj]);
@@ -448,7 +548,26 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
                                    }
                                }
                            });
-            final_token = block_argmax<kVWaves>(best, best_i, s_red, s_ired);
+            double bv;
+            final_token = block_argmax<kVWaves>(best, best_i, s_red, s_ired, &bv);
+            if (group > 1) {
+                const int par = epoch & 1;
+                if (tid == 0) {
+                    grec->val[par][p] = bv;
+                    grec->idx[par][p] = final_token;
+                }
+                late = group_wait(&grec->arrivals, group * ++epoch, late, &s_flag);
+                bv = load_agent_f64(&grec->val[par][0]);
+                final_token = __hip_atomic_load(&grec->idx[par][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int k = 1; k < group; ++k) {  // slices ascend with k: ties keep the lower index
+                    const double o = load_agent_f64(&grec->val[par][k]);
+                    const int oi = __hip_atomic_load(&grec->idx[par][k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (o > bv || (o == bv && oi < final_token)) {
+                        bv = o;
+                        final_token = oi;
+                    }
+                }
+            }
             if (final_token == 0x7FFFFFFF) final_token = -1;
             break;
         }
@@ -460,13 +579,17 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
         ++a;
         cur = accepted;
         row = row0 + 1 + (TTV_DCHECK(accepted >= 0 && accepted < n, TTV_SITE_STOCHASTIC) ? accepted : 0);
-        __syncthreads();  // every thread has read cur before the next visit rewrites it
+        // every thread has read cur before the next visit rewrites it (the
+        // visit's first group wait also holds back the rest of the group)
+        __syncthreads();
         den = visit(row);
     }
-    if (tid == 0) {
-        accept_len[b] = a;
+    if (late) flags |= TTV_ERR_SYNC;
+    if (tid == 0 && (p == 0 || late)) {
+        if (p == 0) accept_len[b] = a;
         if (flags) atomicOr(err + b, flags);
     }
+    if (p != 0) return;  // uniform over the workgroup: one member writes the walk
     __syncthreads();  // s_path, written by thread 0
     for (int k = tid; k < max_accept; k += kVThreads)
         accepted_nodes[(int64_t)b * max_accept + k] = k < a ? s_path[k] : -1;
@@ -477,10 +600,71 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
 
 }  // namespace
 
+namespace {
+
+// Two fp64 buffers of the vocab per request (the chunked path swaps them),
+// then, 256-byte aligned, one group record per request.
+size_t buffers_bytes(int64_t batch, int64_t vocab) {
+    return (2 * (size_t)batch * (size_t)vocab * sizeof(double) + 255) & ~(size_t)255;
+}
+
+// Workgroups of the grouped walk that the device holds at once, per device
+// and logits type (0 until asked).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_resident[kMaxDevices][2];
+
+template <bool kBf16>
+int resident_walkers() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    std::atomic<int>& slot = g_resident[dev][kBf16 ? 1 : 0];
+    int r = slot.load(std::memory_order_relaxed);
+    if (r > 0) return r;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stochastic_walk_vec_kernel<kBf16>, kVThreads, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    r = per_cu * cus;
+    if (r > 0) slot.store(r, std::memory_order_relaxed);
+    return r;
+}
+
+// Members per request: as many as the device holds for the padded batch at
+// once, up to kMaxGroup, with at least half a chunk per thread each.
+template <bool kBf16>
+int walk_group(int64_t batch, int64_t n_chunks) {
+    const int64_t padded = (batch + 7) / 8 * 8;
+    int64_t g = std::min<int64_t>(kMaxGroup, resident_walkers<kBf16>() / padded);
+    g = std::min<int64_t>(g, n_chunks / (kVThreads / 2));
+    return g > 1 ? (int)g : 1;
+}
+
+template <bool kBf16>
+void launch_vec(const ttv_batch* bt, const void* logits, int64_t vocab, float temperature,
+                const float* draft_probs, const float* uniforms, const float* gumbel, const int32_t* tokens,
+                const int32_t* next_token, const int32_t* next_sibling, int32_t max_accept,
+                int32_t* accept_len, int32_t* accepted_nodes, int32_t* out_tokens, void* workspace,
+                int32_t* err, hipStream_t stream) {
+    const int group = walk_group<kBf16>(bt->batch, vocab / kVec);
+    unsigned char* groups = (unsigned char*)workspace + buffers_bytes(bt->batch, vocab);
+    int64_t grid = bt->batch;
+    if (group > 1) {
+        hipLaunchKernelGGL(group_clear_kernel, dim3((bt->batch + 255) / 256), dim3(256), 0, stream, groups,
+                           bt->batch);
+        grid = (bt->batch + 7) / 8 * 8 * group;
+    }
+    hipLaunchKernelGGL(stochastic_walk_vec_kernel<kBf16>, dim3((unsigned)grid), dim3(kVThreads), 0, stream,
+                       bt->node_offsets, bt->n_max, bt->total_nodes, logits, vocab, (double)temperature,
+                       draft_probs, uniforms, gumbel, tokens, next_token, next_sibling, max_accept, accept_len,
+                       accepted_nodes, out_tokens, (double*)workspace, err, bt->batch, group, groups);
+}
+
+}  // namespace
+
 extern "C" TTV_API size_t tree_stochastic_accept_workspace_bytes(const ttv_batch* bt, int64_t vocab) {
     if (!bt || bt->batch < 0 || vocab <= 0 || vocab >= (1ll << 31)) return 0;
-    // two fp64 buffers of the vocab per request (the chunked path swaps them)
-    const size_t bytes = 2 * (size_t)bt->batch * (size_t)vocab * sizeof(double);
+    const size_t bytes = buffers_bytes(bt->batch, vocab) + (size_t)bt->batch * kGroupRecord;
     return bytes > 0 ? bytes : 256;
 }
 
@@ -512,8 +696,9 @@ extern "C" TTV_API int tree_stochastic_accept(
                            out_tokens, (double*)workspace, err);
     };
     if (vocab % kVec == 0) {
-        if (logits_dtype == TTV_DTYPE_BF16) launch(stochastic_walk_vec_kernel<true>, kVThreads);
-        else launch(stochastic_walk_vec_kernel<false>, kVThreads);
+        auto vec = logits_dtype == TTV_DTYPE_BF16 ? launch_vec<true> : launch_vec<false>;
+        vec(bt, logits, vocab, temperature, draft_probs, uniforms, gumbel, tokens, retrieve_next_token,
+            retrieve_next_sibling, max_accept, accept_len, accepted_nodes, out_tokens, workspace, err, stream);
     } else {
         if (logits_dtype == TTV_DTYPE_BF16) launch(stochastic_walk_kernel<true>, kThreads);
         else launch(stochastic_walk_kernel<false>, kThreads);
