@@ -434,7 +434,7 @@ TTV_API int tree_sample_accept(const ttv_batch* bt, const void* logits, int32_t 
                                int32_t* err, hipStream_t stream);
 
 /* Workspace bytes tree_stochastic_accept needs (host call): fp64 [B, 2, vocab],
- * then 512 bytes per request for the reductions across the workgroups that
+ * then 1024 bytes per request for the reductions across the workgroups that
  * share a request (padded to 256 bytes between the two). */
 TTV_API size_t tree_stochastic_accept_workspace_bytes(const ttv_batch* bt, int64_t vocab);
 

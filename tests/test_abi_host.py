@@ -255,8 +255,8 @@ def test_sampled_walks_reject(lib):
     assert sample(ws_bytes=need - 1) == tta.TTV_ENOSPC
     sneed = lib.tree_stochastic_accept_workspace_bytes(ctypes.byref(b), 1000)
     # two float64 vocab buffers per request (padded to 256 bytes), then a
-    # 512-byte record per request for the reductions of a request's workgroups
-    assert sneed == (2 * 2 * 1000 * 8 + 255) // 256 * 256 + 2 * 512
+    # 1024-byte record per request for the reductions of a request's workgroups
+    assert sneed == (2 * 2 * 1000 * 8 + 255) // 256 * 256 + 2 * 1024
 
     def stoch(T=1.0, q=FAKE, u=FAKE, ws_bytes=sneed):
         return lib.tree_stochastic_accept(ctypes.byref(b), FAKE, 1, 1000, T, q, u, FAKE, FAKE, FAKE, FAKE, 16,

@@ -329,11 +329,12 @@ __device__ __forceinline__ void chunk_pass(int64_t c_lo, int64_t c_hi, Load&& lo
 // whole group holds the same value and takes the same decisions.  The
 // workspace holds one record per request after the two buffers.
 constexpr int kMaxGroup = 16;
-constexpr int64_t kGroupRecord = 512;
+constexpr int64_t kGroupRecord = 1024;
 struct GroupRecord {
     int32_t arrivals;  // zeroed before the walk; +1 per workgroup per reduction
     int32_t pad[31];
     double val[2][kMaxGroup];   // per reduction parity, one result per workgroup
+    double val2[2][kMaxGroup];  // a second result (a visit's sum beside its maximum)
     int32_t idx[2][kMaxGroup];  // the argmax's index beside its value
 };
 static_assert(sizeof(GroupRecord) <= kGroupRecord, "group record");
@@ -398,6 +399,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
     __shared__ double s_red[kVWaves];
     __shared__ int32_t s_ired[kVWaves];
     __shared__ int s_flag;
+    __shared__ double s_scale[kMaxGroup];  // per member: exp((its maximum - the row's) / T)
 
     // Workgroup w serves request b as member p of its group.  With groups,
     // the members of request b are w = (b / 8) * 8P + 8p + b % 8: all on the
@@ -445,9 +447,17 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
         return r;
     };
 
-    // Visit a row: cur = exp((x - max) / T), den = their sum.
+    // Visit a row.  Each member takes the maximum m_p of its slice and stores
+    // cur = exp((x - m_p) / T), summing them; one group-wide reduction then
+    // gives the row's maximum M and den = sum over p (in member order) of
+    // sum_p * exp((m_p - M) / T), so the side is cur[v] * s_scale[member of
+    // v] / den: exp((x - M) / T) / den formed as a product of two
+    // exponentials (within a few ulps).  One workgroup has m_p = M and the
+    // scale exactly 1.
+    bool scaled = false;  // the side carries the members' scales (after a visit)
+    if (tid < kMaxGroup) s_scale[tid] = 1.0;
     auto visit = [&](int64_t row) -> double {
-        constexpr int NB = 4;
+        constexpr int NB = 3;
         float xs[NB][kVec];
         float mf = -INFINITY;  // the logits are floats, so their maximum is exact
         chunk_pass<NB>(c_lo, c_hi, [&](int64_t c, int j) { load8_logits(logits, kBf16, row * vocab + c * kVec, xs[j]); },
@@ -455,7 +465,9 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
 #pragma unroll
                            for (int k = 0; k < kVec; ++k) mf = fmaxf(mf, xs[j][k]);
                        });
-        const double m = reduce((double)mf, true);
+        const double m_p = block_reduce<true, kVWaves>((double)mf, s_red);
+        // a slice of -inf logits contributes nothing (rather than inf - inf)
+        const double m = m_p == -INFINITY ? 0.0 : m_p;
         double sum = 0.0;
         chunk_pass<NB>(c_lo, c_hi, [&](int64_t c, int j) { load8_logits(logits, kBf16, row * vocab + c * kVec, xs[j]); },
                        [&](int64_t c, int j) {
@@ -468,7 +480,25 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
                            store8_f64(cur_buf + c * kVec, e);
                        });
         __syncthreads();  // cur written before any thread reads another's entry
-        return reduce(sum, false);  // with a group, its wait publishes every member's slice
+        const double s_p = block_reduce<false, kVWaves>(sum, s_red);
+        scaled = true;
+        if (group == 1) return s_p;
+        const int par = epoch & 1;
+        if (tid == 0) {
+            grec->val[par][p] = m_p;
+            grec->val2[par][p] = s_p;
+        }
+        late = group_wait(&grec->arrivals, group * ++epoch, late, &s_flag);  // also publishes every slice
+        double M = load_agent_f64(&grec->val[par][0]);
+        for (int k = 1; k < group; ++k) M = fmax(M, load_agent_f64(&grec->val[par][k]));
+        if (tid < group) {
+            const double mk = load_agent_f64(&grec->val[par][tid]);
+            s_scale[tid] = mk == -INFINITY ? 0.0 : exp((mk - M) * inv_t);
+        }
+        __syncthreads();  // s_scale
+        double den = 0.0;
+        for (int k = 0; k < group; ++k) den += load_agent_f64(&grec->val2[par][k]) * s_scale[k];
+        return den;
     };
 
     int a = 0, flags = 0, final_token = -1;
@@ -482,7 +512,12 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
         int accepted = -1;
         while (j >= 0) {
             const int x = tokens[s + j];
-            const double r_x = (x >= 0 && x < vocab) ? cur_buf[x] / den : 0.0;
+            double r_x = 0.0;
+            if (x >= 0 && x < vocab) {
+                int px = 0;  // the member whose slice holds x
+                while (px + 1 < group && n_chunks * (px + 1) / group <= x / kVec) ++px;
+                r_x = (scaled ? cur_buf[x] * s_scale[px] : cur_buf[x]) / den;
+            }
             const double qx = (x >= 0 && x < vocab) ? (double)q[x] : 0.0;
             const bool take = (double)uniforms[s + j] * qx < r_x;
             if (take) {
@@ -496,7 +531,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
             double bb[NB][kVec];
             float fq[NB][kVec];
             double z = 0.0;
-            const double inv_den = 1.0 / den;
+            const double inv_den = (scaled ? s_scale[p] : 1.0) * (1.0 / den);
             chunk_pass<NB>(c_lo, c_hi,
                            [&](int64_t c, int jj) {
                                load8_f64(cur_buf + c * kVec, bb[jj]);
@@ -517,6 +552,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
                 cur_buf = alt_buf;
                 alt_buf = t;
                 den = z;
+                scaled = false;
             }
             const int nx = next_sibling[s + j];
             j = (nx > j && nx < n) ? nx : -1;
@@ -527,7 +563,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
             constexpr int NB = 2;
             double bb[NB][kVec];
             float fg[NB][kVec];
-            const double inv_den = 1.0 / den;
+            const double inv_den = (scaled ? s_scale[p] : 1.0) * (1.0 / den);
             double best = -INFINITY;
             int best_i = 0x7FFFFFFF;
             chunk_pass<NB>(c_lo, c_hi,
