@@ -156,6 +156,37 @@ def test_stochastic_accept_matches_oracle(case, seed):
     say(f"  accept lengths {got['accept_len'].tolist()[:12]}")
 
 
+def test_stochastic_accept_masked_vocab_tail():
+    """Logits of -inf over the last 12000 of 32000 tokens (a masked range):
+    with 15 workgroups per request, the last ones' slices hold no finite
+    logit and contribute nothing to a row's softmax; drafted tokens in the
+    range are rejected (p = 0 there) and the walk still matches the oracle."""
+    require_gpu()
+    cfg, seed, T, boost = 2, 5, 1.0, 20.0
+    wl = synth.make_workload(cfg, seed, vocab=32000, ctx=(4, 9), batch=12)
+    assert wl.logits_dtype == "bf16"
+    wl.logits[:, 20000:] = 0xFF80  # bf16 -inf
+    R, V = wl.total_nodes + wl.batch, wl.vocab
+    kids = children_tokens(wl)
+    q = synth.draft_distributions(seed, cfg, R, V, lambda r: kids.get(r, []), boost)
+    u = synth.uniforms(seed, cfg, wl.total_nodes)
+    g = synth.gumbel_noise(seed, cfg, R, V)
+    say(f"tree_stochastic_accept masked tail cfg={cfg} seed={seed} rows={R} V={V}")
+    torch, d, bt, meta = device_round(wl)
+    dev = d["logits"].device
+    out = tta.tree_stochastic_accept(bt, d["logits"], T, torch.from_numpy(q).to(dev), torch.from_numpy(u).to(dev),
+                                     torch.from_numpy(g).to(dev), d["tokens"], meta["retrieve_next_token"],
+                                     meta["retrieve_next_sibling"], MAX_ACCEPT, meta["err"])
+    torch.cuda.synchronize()
+    got = {k: host(v) for k, v in out.items()}
+    assert (host(meta["err"]) == 0).all()
+    ref = O_smp.stochastic_accept(rows_of(logits_f32(wl), wl), rows_of(q, wl), u, rows_of(g, wl), T,
+                                  wl.node_offsets, wl.tokens, wl.parents, MAX_ACCEPT)
+    for k in ("accept_len", "accepted_nodes", "out_tokens"):
+        np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
+    assert (got["out_tokens"][np.arange(wl.batch), got["accept_len"]] < 20000).all()  # sampled from the support
+
+
 def test_stochastic_accept_overflow_flag():
     """q = p at every row accepts first children down to a leaf; with max_accept
     below the depth the request is flagged and stops at max_accept."""
