@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void stochastic_walk_kernel(
 // full-vocab passes, and one workgroup per request left seven in eight CUs
 // idle on a batch of 32.
 constexpr int kVec = 8;
-constexpr int kVThreads = 512;  // 256 registers per thread: four chunks of every pass in flight
+constexpr int kVThreads = 512;  // 256 registers per thread: three chunks of a pass in flight
 constexpr int kVWaves = kVThreads / TTV_WAVE;
 
 __device__ __forceinline__ void load8_logits(const void* logits, bool bf16, int64_t off, float (&x)[kVec]) {
@@ -323,19 +323,22 @@ __device__ __forceinline__ void chunk_pass(int64_t c_lo, int64_t c_hi, Load&& lo
 }
 
 // A request may be walked by a group of P workgroups, each over its own slice
-// of the vocab's chunks.  Every reduction is then taken over the workgroup and
-// its result put in the request's slot for that workgroup; after all P have
-// arrived each reads the P results and combines them in slot order, so the
-// whole group holds the same value and takes the same decisions.  The
-// workspace holds one record per request after the two buffers.
+// of the vocab's chunks.  Every reduction is then taken over the workgroup
+// and exchanged: each member publishes its result and waits for the others',
+// and all combine the P results in member order, so the whole group holds the
+// same value and takes the same decisions.  A result travels as 32-bit words,
+// each in a 64-bit atomic word beside the number of the exchange (from 1), so
+// a word read with the expected number is that exchange's word: no fence is
+// needed, and no member ever reads another's entries of the request's
+// buffers (the accept test recomputes its entry, below).  Exchange e uses
+// word set e mod 2: a member writes exchange e + 2 only after every member
+// has written e + 1, i.e. has finished reading e.  The workspace holds one
+// record per request after the two buffers, zeroed before each walk.
 constexpr int kMaxGroup = 16;
+constexpr int kXWords = 4;  // 32-bit words per member per exchange
 constexpr int64_t kGroupRecord = 1024;
 struct GroupRecord {
-    int32_t arrivals;  // zeroed before the walk; +1 per workgroup per reduction
-    int32_t pad[31];
-    double val[2][kMaxGroup];   // per reduction parity, one result per workgroup
-    double val2[2][kMaxGroup];  // a second result (a visit's sum beside its maximum)
-    int32_t idx[2][kMaxGroup];  // the argmax's index beside its value
+    uint64_t w[2][kMaxGroup][kXWords];  // (exchange number << 32) | word
 };
 static_assert(sizeof(GroupRecord) <= kGroupRecord, "group record");
 // A wait for the rest of the group gives up after this many ticks of the
@@ -344,45 +347,63 @@ static_assert(sizeof(GroupRecord) <= kGroupRecord, "group record");
 constexpr long long kSpinTicks = 1ll << 25;
 
 __global__ void group_clear_kernel(unsigned char* __restrict__ groups, int32_t n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) ((GroupRecord*)(groups + i * kGroupRecord))->arrivals = 0;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    constexpr int kPer = kGroupRecord / 8;
+    if (i < (int64_t)n * kPer) ((uint64_t*)groups)[i] = 0;
 }
 
-__device__ __forceinline__ double load_agent_f64(const double* p) {
-    return __longlong_as_double(
-        (long long)__hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+__device__ __forceinline__ uint32_t lo32(double v) { return (uint32_t)__double_as_longlong(v); }
+__device__ __forceinline__ uint32_t hi32(double v) { return (uint32_t)((uint64_t)__double_as_longlong(v) >> 32); }
+__device__ __forceinline__ double f64_of(uint32_t lo, uint32_t hi) {
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-// Every thread's stores before the call are visible to the whole group after
-// it: each wave waits for its stores, then thread 0 alone releases (one L2
-// write-back for the workgroup), arrives, polls the count with relaxed loads
-// until all P * epoch arrivals are in, and acquires (one L2 invalidate); the
-// workgroup barrier passes that on to the other waves.  Fences on every
-// thread, or an acquiring poll, cost one L2 write-back or invalidate per wave
-// or per poll and made the walk three to four times slower.  Returns true
-// once a wait has timed out (late stays true and later calls do not wait).
-__device__ __forceinline__ bool group_wait(int32_t* arrivals, int target, bool late, int* s_flag) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have reached its L2
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __hip_atomic_fetch_add(arrivals, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Exchange number e: member p publishes words w0..w3 (the first n_words of
+// them; uniform over the workgroup) and waits until every member's are in;
+// member k's word i is then s_x[k * kXWords + i] for every thread.  Wave 0's
+// lanes poll one word each.  Returns true once a wait has timed out (late
+// stays true and later calls do not wait).
+__device__ __forceinline__ bool group_exchange(GroupRecord* rec, int group, int p, int e, int n_words,
+                                               uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, bool late,
+                                               uint32_t* s_x, int* s_flag) {
+    const int tid = threadIdx.x;
+    uint64_t(*const set)[kXWords] = rec->w[e & 1];
+    if (tid < n_words) {
+        const uint32_t w = tid == 0 ? w0 : tid == 1 ? w1 : tid == 2 ? w2 : w3;
+        __hip_atomic_store(&set[p][tid], ((uint64_t)(uint32_t)e << 32) | w, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid < TTV_WAVE) {
+        const int k = tid / n_words, i = tid % n_words;
+        const bool mine = k < group;
+        uint64_t v = 0;
+        bool ok = !mine;
         int f = late;
-        if (!late) {
-            const long long t0 = wall_clock64();
-            while (__hip_atomic_load(arrivals, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-                if (wall_clock64() - t0 > kSpinTicks) {
-                    f = 1;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
+        const long long t0 = wall_clock64();
+        for (;;) {
+            if (!ok) {
+                v = __hip_atomic_load(&set[k][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = (uint32_t)(v >> 32) == (uint32_t)e;
             }
+            if (__all(ok)) break;
+            if (f || wall_clock64() - t0 > kSpinTicks) {
+                f = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        *s_flag = f;
+        if (mine) s_x[k * kXWords + i] = (uint32_t)v;
+        if (tid == 0) *s_flag = f;
     }
     __syncthreads();
     return *s_flag != 0;
+}
+
+// One step of a residual at one entry: max(0, r - q) with r = side * f, one
+// fused rounding for the product and difference; the pass over a slice and
+// the accept test's recomputation both use it, so they agree bit for bit.
+__device__ __forceinline__ double residual_entry(double side, double f, double q) {
+    return fmax(__builtin_fma(side, f, -q), 0.0);
 }
 
 template <bool kBf16>
@@ -400,6 +421,13 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
     __shared__ int32_t s_ired[kVWaves];
     __shared__ int s_flag;
     __shared__ double s_scale[kMaxGroup];  // per member: exp((its maximum - the row's) / T)
+    __shared__ double s_mloc[kMaxGroup];   // per member: the maximum its exponentials subtract
+    __shared__ uint32_t s_x[kMaxGroup * kXWords];  // the last exchange's words
+    // the residuals applied at the current node, for the accept test's
+    // recomputation: 1 / den before each, and its flags (1: the side was
+    // scaled, 2: the residual replaced the side)
+    __shared__ double s_hinv[TTV_MAX_TREE_NODES];
+    __shared__ uint8_t s_hflag[TTV_MAX_TREE_NODES];
 
     // Workgroup w serves request b as member p of its group.  With groups,
     // the members of request b are w = (b / 8) * 8P + 8p + b % 8: all on the
@@ -432,18 +460,13 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
     GroupRecord* const grec = group > 1 ? (GroupRecord*)(groups + b * kGroupRecord) : nullptr;
     int epoch = 0;
     bool late = false;
-    // Sum or maximum over the request: the workgroup's, then the group's.
-    auto reduce = [&](double v, bool is_max) -> double {
-        double r = is_max ? block_reduce<true, kVWaves>(v, s_red) : block_reduce<false, kVWaves>(v, s_red);
+    // Sum over the request: the workgroup's, then the group's in member order.
+    auto reduce_sum = [&](double v) -> double {
+        double r = block_reduce<false, kVWaves>(v, s_red);
         if (group == 1) return r;
-        const int par = epoch & 1;
-        if (tid == 0) grec->val[par][p] = r;
-        late = group_wait(&grec->arrivals, group * ++epoch, late, &s_flag);
-        r = load_agent_f64(&grec->val[par][0]);
-        for (int k = 1; k < group; ++k) {
-            const double o = load_agent_f64(&grec->val[par][k]);
-            r = is_max ? fmax(r, o) : r + o;
-        }
+        late = group_exchange(grec, group, p, ++epoch, 2, lo32(r), hi32(r), 0, 0, late, s_x, &s_flag);
+        r = f64_of(s_x[0], s_x[1]);
+        for (int k = 1; k < group; ++k) r += f64_of(s_x[k * kXWords], s_x[k * kXWords + 1]);
         return r;
     };
 
@@ -455,6 +478,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
     // exponentials (within a few ulps).  One workgroup has m_p = M and the
     // scale exactly 1.
     bool scaled = false;  // the side carries the members' scales (after a visit)
+    int n_hist = 0;       // residuals applied at the current node
     if (tid < kMaxGroup) s_scale[tid] = 1.0;
     auto visit = [&](int64_t row) -> double {
         constexpr int NB = 3;
@@ -479,25 +503,26 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
                            }
                            store8_f64(cur_buf + c * kVec, e);
                        });
-        __syncthreads();  // cur written before any thread reads another's entry
         const double s_p = block_reduce<false, kVWaves>(sum, s_red);
         scaled = true;
-        if (group == 1) return s_p;
-        const int par = epoch & 1;
-        if (tid == 0) {
-            grec->val[par][p] = m_p;
-            grec->val2[par][p] = s_p;
+        n_hist = 0;
+        if (group == 1) {
+            if (tid == 0) s_mloc[0] = m;
+            __syncthreads();  // s_mloc
+            return s_p;
         }
-        late = group_wait(&grec->arrivals, group * ++epoch, late, &s_flag);  // also publishes every slice
-        double M = load_agent_f64(&grec->val[par][0]);
-        for (int k = 1; k < group; ++k) M = fmax(M, load_agent_f64(&grec->val[par][k]));
+        late = group_exchange(grec, group, p, ++epoch, 4, lo32(m_p), hi32(m_p), lo32(s_p), hi32(s_p), late, s_x,
+                              &s_flag);
+        double M = -INFINITY;
+        for (int k = 0; k < group; ++k) M = fmax(M, f64_of(s_x[k * kXWords], s_x[k * kXWords + 1]));
         if (tid < group) {
-            const double mk = load_agent_f64(&grec->val[par][tid]);
+            const double mk = f64_of(s_x[tid * kXWords], s_x[tid * kXWords + 1]);
+            s_mloc[tid] = mk == -INFINITY ? 0.0 : mk;
             s_scale[tid] = mk == -INFINITY ? 0.0 : exp((mk - M) * inv_t);
         }
-        __syncthreads();  // s_scale
+        __syncthreads();  // s_mloc, s_scale
         double den = 0.0;
-        for (int k = 0; k < group; ++k) den += load_agent_f64(&grec->val2[par][k]) * s_scale[k];
+        for (int k = 0; k < group; ++k) den += f64_of(s_x[k * kXWords + 2], s_x[k * kXWords + 3]) * s_scale[k];
         return den;
     };
 
@@ -516,7 +541,16 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
             if (x >= 0 && x < vocab) {
                 int px = 0;  // the member whose slice holds x
                 while (px + 1 < group && n_chunks * (px + 1) / group <= x / kVec) ++px;
-                r_x = (scaled ? cur_buf[x] * s_scale[px] : cur_buf[x]) / den;
+                // entry x of the side, formed as member px formed it: the
+                // visit's exponential, then each residual applied since
+                double side = exp((logit_at<kBf16>(logits, row, vocab, x) - s_mloc[px]) * inv_t);
+                const double qx = (double)q[x];
+                for (int i = 0; i < min(n_hist, TTV_MAX_TREE_NODES); ++i) {
+                    const int fl = s_hflag[i];
+                    const double t = residual_entry(side, ((fl & 1) ? s_scale[px] : 1.0) * s_hinv[i], qx);
+                    if (fl & 2) side = t;
+                }
+                r_x = (scaled ? side * s_scale[px] : side) / den;
             }
             const double qx = (x >= 0 && x < vocab) ? (double)q[x] : 0.0;
             const bool take = (double)uniforms[s + j] * qx < r_x;
@@ -527,11 +561,12 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
             // rejected: the residual max(0, r - q) into the other buffer, summed
             // in the same pass; it becomes the current side when the sum is
             // positive (otherwise r == q up to rounding and r stays)
-            constexpr int NB = 4;
+            constexpr int NB = 3;
             double bb[NB][kVec];
             float fq[NB][kVec];
             double z = 0.0;
-            const double inv_den = (scaled ? s_scale[p] : 1.0) * (1.0 / den);
+            const double inv_d = 1.0 / den;
+            const double inv_den = (scaled ? s_scale[p] : 1.0) * inv_d;
             chunk_pass<NB>(c_lo, c_hi,
                            [&](int64_t c, int jj) {
                                load8_f64(cur_buf + c * kVec, bb[jj]);
@@ -541,12 +576,18 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
                                double t[kVec];
 #pragma unroll
                                for (int k = 0; k < kVec; ++k) {
-                                   t[k] = fmax(bb[jj][k] * inv_den - (double)fq[jj][k], 0.0);
+                                   t[k] = residual_entry(bb[jj][k], inv_den, (double)fq[jj][k]);
                                    z += t[k];
                                }
                                store8_f64(alt_buf + c * kVec, t);
                            });
-            z = reduce(z, false);  // its barriers (and the group's wait) also publish the residual
+            z = reduce_sum(z);
+            if (tid == 0 && n_hist < TTV_MAX_TREE_NODES) {
+                s_hinv[n_hist] = inv_d;
+                s_hflag[n_hist] = (scaled ? 1 : 0) | (z > 0.0 ? 2 : 0);
+            }
+            ++n_hist;
+            __syncthreads();  // s_hinv, s_hflag
             if (z > 0.0) {
                 double* const t = cur_buf;
                 cur_buf = alt_buf;
@@ -587,17 +628,13 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
             double bv;
             final_token = block_argmax<kVWaves>(best, best_i, s_red, s_ired, &bv);
             if (group > 1) {
-                const int par = epoch & 1;
-                if (tid == 0) {
-                    grec->val[par][p] = bv;
-                    grec->idx[par][p] = final_token;
-                }
-                late = group_wait(&grec->arrivals, group * ++epoch, late, &s_flag);
-                bv = load_agent_f64(&grec->val[par][0]);
-                final_token = __hip_atomic_load(&grec->idx[par][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                late = group_exchange(grec, group, p, ++epoch, 3, lo32(bv), hi32(bv), (uint32_t)final_token, 0, late,
+                                      s_x, &s_flag);
+                bv = f64_of(s_x[0], s_x[1]);
+                final_token = (int)s_x[2];
                 for (int k = 1; k < group; ++k) {  // slices ascend with k: ties keep the lower index
-                    const double o = load_agent_f64(&grec->val[par][k]);
-                    const int oi = __hip_atomic_load(&grec->idx[par][k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const double o = f64_of(s_x[k * kXWords], s_x[k * kXWords + 1]);
+                    const int oi = (int)s_x[k * kXWords + 2];
                     if (o > bv || (o == bv && oi < final_token)) {
                         bv = o;
                         final_token = oi;
@@ -615,9 +652,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
         ++a;
         cur = accepted;
         row = row0 + 1 + (TTV_DCHECK(accepted >= 0 && accepted < n, TTV_SITE_STOCHASTIC) ? accepted : 0);
-        // every thread has read cur before the next visit rewrites it (the
-        // visit's first group wait also holds back the rest of the group)
-        __syncthreads();
+        __syncthreads();  // s_path, and the walk's reads of LDS before the next visit
         den = visit(row);
     }
     if (late) flags |= TTV_ERR_SYNC;
