@@ -187,6 +187,39 @@ def test_stochastic_accept_masked_vocab_tail():
     assert (got["out_tokens"][np.arange(wl.batch), got["accept_len"]] < 20000).all()  # sampled from the support
 
 
+def test_stochastic_accept_reused_workspace():
+    """Two different walks in a row on one workspace (15 workgroups per
+    request, vocab 32000): the second must not take any of the first's
+    exchanged words for its own, so both match the oracle."""
+    require_gpu()
+    ws = None
+    for seed, T, boost in ((7, 1.0, 20.0), (8, 0.8, 0.0), (7, 1.0, 200.0)):
+        cfg = 2
+        wl = synth.make_workload(cfg, seed, vocab=32000, ctx=(4, 9), batch=12)
+        R, V = wl.total_nodes + wl.batch, wl.vocab
+        kids = children_tokens(wl)
+        q = synth.draft_distributions(seed, cfg, R, V, lambda r: kids.get(r, []), boost)
+        u = synth.uniforms(seed, cfg, wl.total_nodes)
+        g = synth.gumbel_noise(seed, cfg, R, V)
+        say(f"tree_stochastic_accept reused workspace seed={seed} T={T} boost={boost}")
+        torch, d, bt, meta = device_round(wl)
+        dev = d["logits"].device
+        if ws is None:
+            ws = torch.empty(tta.tree_stochastic_accept_workspace_bytes(bt, V), dtype=torch.uint8, device=dev)
+        assert ws.numel() >= tta.tree_stochastic_accept_workspace_bytes(bt, V)
+        out = tta.tree_stochastic_accept(bt, d["logits"], T, torch.from_numpy(q).to(dev),
+                                         torch.from_numpy(u).to(dev), torch.from_numpy(g).to(dev), d["tokens"],
+                                         meta["retrieve_next_token"], meta["retrieve_next_sibling"], MAX_ACCEPT,
+                                         meta["err"], workspace=ws)
+        torch.cuda.synchronize()
+        got = {k: host(v) for k, v in out.items()}
+        assert (host(meta["err"]) == 0).all()
+        ref = O_smp.stochastic_accept(rows_of(logits_f32(wl), wl), rows_of(q, wl), u, rows_of(g, wl), T,
+                                      wl.node_offsets, wl.tokens, wl.parents, MAX_ACCEPT)
+        for k in ("accept_len", "accepted_nodes", "out_tokens"):
+            np.testing.assert_array_equal(got[k], ref[k], err_msg=k)
+
+
 def test_stochastic_accept_overflow_flag():
     """q = p at every row accepts first children down to a leaf; with max_accept
     below the depth the request is flagged and stops at max_accept."""

@@ -721,7 +721,9 @@ void launch_vec(const ttv_batch* bt, const void* logits, int64_t vocab, float te
     unsigned char* groups = (unsigned char*)workspace + buffers_bytes(bt->batch, vocab);
     int64_t grid = bt->batch;
     if (group > 1) {
-        hipLaunchKernelGGL(group_clear_kernel, dim3((bt->batch + 255) / 256), dim3(256), 0, stream, groups,
+        // every word of every request's record: a stale exchange number would pass for a fresh one
+        const int64_t words = (int64_t)bt->batch * (kGroupRecord / 8);
+        hipLaunchKernelGGL(group_clear_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream, groups,
                            bt->batch);
         grid = (bt->batch + 7) / 8 * 8 * group;
     }
