@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void stochastic_walk_kernel(
 // full-vocab passes, and one workgroup per request left seven in eight CUs
 // idle on a batch of 32.
 constexpr int kVec = 8;
-constexpr int kVThreads = 512;  // 256 registers per thread: three chunks of a pass in flight
+constexpr int kVThreads = 512;  // 128 registers per thread (two workgroups per CU): a chunk in flight
 constexpr int kVWaves = kVThreads / TTV_WAVE;
 
 __device__ __forceinline__ void load8_logits(const void* logits, bool bf16, int64_t off, float (&x)[kVec]) {
@@ -407,7 +407,8 @@ __device__ __forceinline__ double residual_entry(double side, double f, double q
 }
 
 template <bool kBf16>
-__global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
+// Four waves per SIMD: two workgroups per CU, so twice the members per request.
+__global__ __launch_bounds__(kVThreads, 4) void stochastic_walk_vec_kernel(
     const int32_t* __restrict__ node_offsets, int32_t n_max, int64_t total_nodes,
     const void* __restrict__ logits, int64_t vocab, double temperature,
     const float* __restrict__ draft_probs, const float* __restrict__ uniforms,
@@ -481,7 +482,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
     int n_hist = 0;       // residuals applied at the current node
     if (tid < kMaxGroup) s_scale[tid] = 1.0;
     auto visit = [&](int64_t row) -> double {
-        constexpr int NB = 3;
+        constexpr int NB = 1;
         float xs[NB][kVec];
         float mf = -INFINITY;  // the logits are floats, so their maximum is exact
         chunk_pass<NB>(c_lo, c_hi, [&](int64_t c, int j) { load8_logits(logits, kBf16, row * vocab + c * kVec, xs[j]); },
@@ -561,7 +562,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
             // rejected: the residual max(0, r - q) into the other buffer, summed
             // in the same pass; it becomes the current side when the sum is
             // positive (otherwise r == q up to rounding and r stays)
-            constexpr int NB = 3;
+            constexpr int NB = 1;
             double bb[NB][kVec];
             float fq[NB][kVec];
             double z = 0.0;
@@ -601,7 +602,7 @@ __global__ __launch_bounds__(kVThreads) void stochastic_walk_vec_kernel(
         if (accepted < 0) {
             // correction / bonus: Gumbel-max sample of the current side
             const float* g = gumbel + row * vocab;
-            constexpr int NB = 2;
+            constexpr int NB = 1;
             double bb[NB][kVec];
             float fg[NB][kVec];
             const double inv_den = (scaled ? s_scale[p] : 1.0) * (1.0 / den);
