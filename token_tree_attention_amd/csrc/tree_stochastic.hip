@@ -17,10 +17,12 @@
 // current target side); the correction / bonus is the Gumbel-max sample
 // argmax_v (log r_v + g_v) over r_v > 0 with the caller's noise g of that row.
 //
-// One 1024-thread workgroup per request walks the tree; each step that needs
-// the whole distribution (a visited row's softmax, a residual, the final
-// sample) is a pass of the workgroup over the vocab with fp64 block
-// reductions, each thread loading four entries before using any.  The
+// For a vocab that is not a multiple of 8, one 1024-thread workgroup per
+// request walks the tree; each step that needs the whole distribution (a
+// visited row's softmax, a residual, the final sample) is a pass of the
+// workgroup over the vocab with fp64 block reductions, each thread loading
+// four entries before using any.  Otherwise a group of up to 16 workgroups
+// per request walks it, each over a slice of the vocab (below).  The
 // current target side is kept as r_v = buf[v] / den: the row's exp values and
 // their sum right after a visit, the unnormalised residual and its sum after
 // a rejection (buf in the caller's workspace, fp64 [B, vocab]).  The accept
